@@ -1,0 +1,272 @@
+"""Benchmark of the MiniMind FFN / top-k MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cold]
+
+A step is one full forward (every kernel of the path) over one batch of
+synthetic inputs already resident in device memory.  W untimed steps, then
+exactly K steps bracketed by device synchronisation; ``value`` is tokens/s
+over those K steps.  A second pass of K steps records HIP events around every
+stage on the library's stream to get per-kernel durations, from which the
+dominant kernel's roofline fraction is computed.  The fp64 CPU oracle is then
+timed on a bounded sample of the same workload (rank 0, one GPU only).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FFN/MoE fwd tokens/s + TFLOP/s (% bf16 MFMA peak) / GB/s (% HBM) on 1 GPU"
+DEFAULT_WORKLOAD = "moe_top1_n4096_h768_e4"
+
+# MI355X published peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stage_units(w):
+    """Algorithmic work of each stage of one forward: (flops, bytes).  Bytes
+    count each tensor the stage must read or write once; re-reads, the h round
+    trip and k-slot traffic are implementation costs, not credited."""
+    el = w.elem_bytes()
+    N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
+    rows = N * k
+    if w.kind == "dense":
+        return {
+            "gateup_gemm": (4.0 * N * H * I, N * H * el + 2 * I * H * el + N * I * el),
+            "down_gemm": (2.0 * N * H * I, N * I * el + H * I * el + N * H * el),
+        }
+    touched = min(E, rows)  # upper bound; exact count is reported from the run
+    return {
+        "router": (2.0 * N * H * E, N * H * el + E * H * 4 + N * k * 8),
+        "offsets_aux": (0.0, 0.0),
+        "scatter": (0.0, N * k * 4 * 2),
+        "gateup_gemm": (4.0 * rows * H * I, N * H * el + 2 * touched * I * H * el + rows * I * el),
+        "down_gemm": (2.0 * rows * H * I, rows * I * el + touched * H * I * el + N * H * el),
+        "combine": (0.0, (rows * H * 4 + N * H * el) if k > 1 else 0.0),
+    }
+
+
+def cpu_baseline(w, inputs, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on a bounded token sample."""
+    import numpy as np
+    from oracle.cases import widen
+    from oracle import dense_ffn, moe_ffn, moe_route
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    f = widen(inputs)
+    route = None
+    t_route = 0.0
+    if w.kind == "moe":
+        t0 = time.perf_counter()
+        route = moe_route(f["x"], f["Wr"], w.k, w.coef)
+        t_route = time.perf_counter() - t0
+
+    def run(n):
+        rows = np.arange(n)
+        t0 = time.perf_counter()
+        if w.kind == "dense":
+            dense_ffn(f["x"], f["Wg"], f["Wu"], f["Wd"], rows=rows)
+        else:
+            moe_ffn(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], w.k, w.coef, rows=rows, route=route)
+        return time.perf_counter() - t0
+
+    n = min(w.N, 64)
+    dt = run(n)
+    while n < w.N and dt < budget_s / 4:
+        n = min(w.N, n * 4)
+        dt = run(n)
+    # routing of all N tokens is charged pro rata to the sample
+    dt_total = dt + t_route * n / w.N
+    return {
+        "value": n / dt_total,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle on the first {n} of {w.N} tokens of {w.name}"
+                  + (" (routing of all tokens timed and charged pro rata)" if w.kind == "moe" else "")
+                  + f"; {dt_total:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cold", action="store_true",
+                    help="flush L2 and the Infinity Cache before each step; time steps one by one")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_moe_layer_amd as tm
+    from workloads import get, make_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = get(args.workload)
+    log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype}")
+    inputs = make_inputs(w)
+
+    def dev_t(a, stored=True):
+        if stored and w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    d = {n: dev_t(inputs[n]) for n in ("x", "Wg", "Wu", "Wd")}
+    if w.kind == "moe":
+        d["Wr"] = dev_t(inputs["Wr"], stored=False)
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
+    stream = torch.cuda.current_stream(dev)
+
+    if w.kind == "dense":
+        ws = torch.empty(tm.ffn_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
+        y = torch.empty((N, H), dtype=tdt, device=dev)
+        names = tm.FFN_STAGE_NAMES
+
+        def step(ev=None):
+            tm.ffn_swiglu_fwd(d["x"], d["Wg"], d["Wu"], d["Wd"], y=y, workspace=ws,
+                              stream=stream, stage_events=ev)
+        ev = tm.StageEvents(tm.FFN_STAGES)
+    else:
+        ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8, device=dev)
+        y = torch.empty((N, H), dtype=tdt, device=dev)
+        idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+        alpha = torch.empty((N, k), dtype=torch.float32, device=dev)
+        aux = torch.empty((1,), dtype=torch.float32, device=dev)
+        offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        names = tm.MOE_STAGE_NAMES
+
+        def step(ev=None):
+            tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef, y=y,
+                           topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
+                           return_lists=False, workspace=ws, stream=stream, stage_events=ev)
+        ev = tm.StageEvents(tm.MOE_STAGES)
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    if not args.cold:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms_step = elapsed * 1e3 / args.steps
+    else:
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for _ in range(args.steps):
+            flush.zero_()
+            s0.record(stream)
+            step()
+            s1.record(stream)
+            s1.synchronize()
+            tot += s0.elapsed_time(s1)
+        ms_step = tot / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step")
+
+    # per-stage kernel durations from HIP events on the library's stream
+    per = np.zeros(len(names))
+    for _ in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        step(ev)
+        per += np.array(ev.elapsed_ms())
+    per /= args.steps
+    stages_ms = {n: round(float(v), 5) for n, v in zip(names, per)}
+    log(f"stage ms: {stages_ms}")
+
+    units = stage_units(w)
+    touched = None
+    if w.kind == "moe":
+        cnt = np.diff(offs.cpu().numpy())
+        touched = int((cnt > 0).sum())
+        units = {**units}
+        el = w.elem_bytes()
+        rows = N * k
+        units["gateup_gemm"] = (4.0 * rows * H * I, N * H * el + 2 * touched * I * H * el + rows * I * el)
+        units["down_gemm"] = (2.0 * rows * H * I, rows * I * el + touched * H * I * el + N * H * el)
+
+    total_flops = w.flops()
+    tflops = total_flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    dom = "gateup_gemm"
+    dom_ms = stages_ms[dom]
+    dflops, dbytes = units[dom]
+    decode_like = w.kind == "moe" and N * k <= 256
+    if decode_like:
+        achieved = dbytes / (dom_ms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_bytes": dbytes, "avg_launch_ms": dom_ms}
+    else:
+        achieved = dflops / (dom_ms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "algorithmic_flops": dflops, "avg_launch_ms": dom_ms}
+
+    result = {
+        "metric": METRIC,
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, shapes and distributions of the workload)",
+        "config": {"workload": w.name, "N": N, "H": H, "I": I, "E": E if w.kind == "moe" else None,
+                   "k": k if w.kind == "moe" else None, "batch": w.batch, "seq": w.seq,
+                   "cache": "cold (L2 + Infinity Cache flushed per step)" if args.cold else "warm"},
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / peak, 4),
+        "stages_ms": stages_ms,
+        "experts_touched": touched,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w, inputs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * topmoe.h — C ABI of the MI355X (gfx950) MiniMind FFN / top-k MoE forward.
+ *
+ * Operations (definitions from the MiniMind course, lesson 13 "FFN and MoE",
+ * sections 0, 1.2, 1.5, 1.6 and source walkthrough steps 3-6; minimind3
+ * chapter 4 "MLP & MoE", sections 4.2-4.4):
+ *
+ *   dense FFN      y = W_down( SiLU(W_gate x) * W_up x ),  SiLU(z) = z * sigmoid(z)
+ *   MoE router     p = softmax(W_router x);  S = TopK(p, k);
+ *                  alpha_e = p_e / (sum_{j in S} p_j + 1e-20)
+ *   MoE output     y = sum_{e in S} alpha_e * Expert_e(x), each expert a dense FFN
+ *   aux loss       aux = E * coef * sum_e load_e * prob_e,
+ *                  load_e = (tokens that selected e) / N,  prob_e = mean_t p_{t,e}
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or retains them.
+ *   - Row-major layouts.  Weights use the nn.Linear [out, in] layout.
+ *   - Calls are asynchronous: they validate synchronously on the host, then
+ *     enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *     return.  No host synchronisation, no device-to-host copy.
+ *   - On any error nothing is launched and no output is touched.  Errors are
+ *     negative status codes (topmoe_strerror gives text).  A HIP launch error
+ *     is reported as TOPMOE_ERR_HIP (outputs may then be partly written).
+ *   - Results are deterministic: the same inputs give bitwise identical
+ *     outputs (no floating-point atomics anywhere).
+ *   - `stage_events`, when not NULL, is an array of (stages + 1) hipEvent_t
+ *     handles (see topmoe_events_create); event i is recorded on `stream`
+ *     before stage i and the last one after the final stage.  Pass NULL in
+ *     production.  Stage counts: TOPMOE_FFN_STAGES, TOPMOE_MOE_STAGES.
+ *
+ * dtype
+ *   TOPMOE_DTYPE_FP32: x, W_gate, W_up, W_down, y float32; all arithmetic fp32.
+ *   TOPMOE_DTYPE_BF16: x, W_gate, W_up, W_down, y bfloat16; fp32 accumulation;
+ *                      the SiLU(g)*u intermediate is rounded to bf16; y is
+ *                      rounded once (round-to-nearest-even).
+ *   The router weight W_router is float32 in both, and routing is fp32.
+ *
+ * Shape limits: N >= 0 (N == 0 is a no-op apart from zeroed offsets and aux),
+ * H and I positive multiples of 64, 1 <= E <= 64, 1 <= k <= E,
+ * N * max(k, 1) < 2^31 and N * H, N * k * max(H, I) < 2^40.
+ */
+#ifndef TOPMOE_H
+#define TOPMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define TOPMOE_OK                        0
+#define TOPMOE_ERR_NULL_ARG             -1  /* a required pointer is NULL            */
+#define TOPMOE_ERR_BAD_SHAPE            -2  /* N, H, I, E or k outside the limits     */
+#define TOPMOE_ERR_UNSUPPORTED_DTYPE    -3  /* dtype not FP32 / BF16                  */
+#define TOPMOE_ERR_WORKSPACE_TOO_SMALL  -4  /* workspace_bytes < *_workspace_bytes()  */
+#define TOPMOE_ERR_HIP                  -5  /* a HIP runtime call or launch failed    */
+#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef negative / not finite, misaligned pointer */
+
+/* ---- dtypes ------------------------------------------------------------ */
+#define TOPMOE_DTYPE_FP32 0
+#define TOPMOE_DTYPE_BF16 1
+
+/* ---- stages (for stage_events) ------------------------------------------ */
+#define TOPMOE_FFN_STAGES 2  /* 0 gate/up GEMM + SiLU*up, 1 down GEMM                   */
+#define TOPMOE_MOE_STAGES 6  /* 0 router, 1 expert offsets + aux, 2 token scatter,
+                                3 grouped gate/up GEMM + SiLU*up, 4 grouped down GEMM
+                                + alpha, 5 combine of the k slots (empty when k == 1)   */
+
+/* Workspace needed by ffn_swiglu_fwd: the SiLU(g)*u intermediate [N, I]
+ * (dtype-sized elements), 256-byte aligned.  Returns 0 for invalid shapes. */
+size_t ffn_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype);
+
+/* Dense SwiGLU FFN forward (lesson 13, sections 0 and 1.2; walkthrough step 3;
+ * minimind3 chapter 4, section 4.2).
+ *   x   [N, H]   input tokens (B*S flattened; the caller reshapes)
+ *   Wg  [I, H]   gate_proj.weight      Wu [I, H] up_proj.weight
+ *   Wd  [H, I]   down_proj.weight
+ *   y   [N, H]   output, same dtype as x; must not alias the inputs
+ *   workspace    device scratch of at least ffn_workspace_bytes(N, H, I, dtype)
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ * All tensor pointers must be 16-byte aligned. */
+int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                   void* y, int64_t N, int64_t H, int64_t I, int dtype,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream, void* const* stage_events);
+
+/* Workspace needed by moe_ffn_fwd (routing partials, permutation, the
+ * SiLU(g)*u intermediate [N*k, I] and, for k >= 2, fp32 k-slots [N*k, H]).
+ * Returns 0 for invalid shapes. */
+size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype);
+
+/* Top-k MoE FFN forward (lesson 13, sections 0, 1.5, 1.6 and walkthrough
+ * steps 4-6; minimind3 chapter 4, sections 4.3 and 4.4).
+ *   x        [N, H]      input tokens (dtype)
+ *   Wr       [E, H]      router (gate) weight, float32
+ *   Wg, Wu   [E, I, H]   experts' gate_proj / up_proj weights, stacked (dtype)
+ *   Wd       [E, H, I]   experts' down_proj weights, stacked (dtype)
+ *   aux_coef             router_aux_loss_coef (>= 0); 0 gives aux = 0 exactly,
+ *                        which is also the module's value outside training
+ *   y        [N, H]      output (dtype): y_t = sum over the selected experts in
+ *                        ascending expert id of alpha * Expert_e(x_t),
+ *                        accumulated in fp32 and rounded once
+ *   topk_idx [N, k]      int32 selected experts, slot order = probability
+ *                        descending, equal probabilities by ascending id
+ *   alpha    [N, k]      float32 renormalised weights in the same slot order
+ *   aux_loss [1]         float32 load-balancing loss (training-mode value)
+ *   expert_offsets [E+1] optional (NULL = not returned) int32 exclusive prefix
+ *                        sum of per-expert token counts
+ *   sorted_token_ids [N*k] optional int32: tokens grouped by expert, ascending
+ *                        expert id, ascending token id within an expert
+ *   workspace            at least moe_workspace_bytes(N, H, I, E, k, dtype)
+ *                        bytes, 256-byte aligned; contents on entry ignored.
+ * Outputs must not alias inputs or each other.  Tensor pointers must be
+ * 16-byte aligned (int32/float32 outputs: 4-byte aligned). */
+int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
+                const void* Wd, int64_t N, int64_t H, int64_t I, int E, int k,
+                float aux_coef, int dtype,
+                void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
+                int32_t* expert_offsets, int32_t* sorted_token_ids,
+                void* workspace, size_t workspace_bytes,
+                void* stream, void* const* stage_events);
+
+/* Human-readable text for a status code (static storage). */
+const char* topmoe_strerror(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int topmoe_version(void);
+
+/* ---- instrumentation helpers (not on the hot path) ---------------------- */
+/* Create / destroy n timing-enabled hipEvent_t handles. */
+int topmoe_events_create(int n, void** events);
+int topmoe_events_destroy(int n, void** events);
+/* Wait for `stop` and return the elapsed milliseconds between two events. */
+int topmoe_event_elapsed_ms(void* start, void* stop, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TOPMOE_H */

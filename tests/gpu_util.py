@@ -1,0 +1,102 @@
+"""Helpers for the GPU parity tests: move generator output to the device, call
+the library, and measure the deviations from the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+TOL_Y = {"fp32": 1e-5, "bf16": 2e-2}   # max per-token relative L2 error of y
+TOL_ALPHA = 1e-5                      # relative, per entry
+TOL_AUX = 1e-5                        # relative
+
+
+def torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch, torch.device("cuda:0")
+
+
+def announce(msg: str) -> None:
+    print(f"\n[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(inputs: dict, dev):
+    import torch
+
+    dt = inputs["dtype"]
+
+    def t(a, stored=True):
+        if stored and dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    out = {n: t(inputs[n]) for n in ("x", "Wg", "Wu", "Wd")}
+    if "Wr" in inputs:
+        out["Wr"] = t(inputs["Wr"], stored=False)
+    return out
+
+
+def y_to_f64(y) -> np.ndarray:
+    import torch
+
+    return y.detach().to(torch.float64).cpu().numpy()
+
+
+def rel_l2_per_token(got: np.ndarray, ref: np.ndarray) -> float:
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    den = np.where(den == 0, 1.0, den)
+    return float((num / den).max()) if got.size else 0.0
+
+
+def rel_l2_global(got: np.ndarray, ref: np.ndarray) -> float:
+    d = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (d if d else 1.0))
+
+
+def run_moe(tm, dev_in, w, N=None):
+    return tm.moe_ffn_fwd(dev_in["x"], dev_in["Wr"], dev_in["Wg"], dev_in["Wu"], dev_in["Wd"],
+                          w.k, w.coef)
+
+
+def run_dense(tm, dev_in):
+    return tm.ffn_swiglu_fwd(dev_in["x"], dev_in["Wg"], dev_in["Wu"], dev_in["Wd"])
+
+
+def check_routing(out, ref, k, E, exact_order=True):
+    """topk_idx, per-expert lists bit-exact; alpha and aux to their tolerances."""
+    idx = out.topk_idx.cpu().numpy()
+    alpha = out.alpha.cpu().numpy().astype(np.float64)
+    if exact_order:
+        np.testing.assert_array_equal(idx, ref["topk_idx"])
+        np.testing.assert_allclose(alpha, ref["alpha"], rtol=TOL_ALPHA, atol=0)
+    else:
+        # k == E: the selected set is every expert; compare per expert id
+        oi = np.argsort(idx, axis=1)
+        ri = np.argsort(ref["topk_idx"], axis=1)
+        np.testing.assert_array_equal(np.take_along_axis(idx, oi, 1),
+                                      np.take_along_axis(ref["topk_idx"], ri, 1))
+        np.testing.assert_allclose(np.take_along_axis(alpha, oi, 1),
+                                   np.take_along_axis(ref["alpha"], ri, 1), rtol=TOL_ALPHA, atol=0)
+    np.testing.assert_array_equal(out.expert_offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(out.sorted_token_ids.cpu().numpy(), ref["sorted_token_ids"])
+    aux = float(out.aux_loss.cpu().numpy()[0])
+    if ref["aux"] == 0.0:
+        assert aux == 0.0
+    else:
+        assert abs(aux - ref["aux"]) <= TOL_AUX * abs(ref["aux"]), (aux, ref["aux"])
+
+
+def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
+    """Rows for sampled checks: the first and last tiles' edges plus random rows."""
+    if N <= n:
+        return np.arange(N)
+    rng = np.random.default_rng(seed)
+    edge = np.array([0, 1, 31, 32, 63, 64, 127, 128, 255, 256, N - 1, N - 2, N - 65])
+    edge = edge[(edge >= 0) & (edge < N)]
+    rest = rng.choice(N, size=n - len(edge), replace=False)
+    return np.unique(np.concatenate([edge, rest]))

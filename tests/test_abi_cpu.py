@@ -1,0 +1,123 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/topmoe.h declares, sizes its workspace, and rejects bad arguments
+before launching anything (every call here fails validation on the host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_moe_layer_amd as tm
+from top_moe_layer_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topmoe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libtopmoe.so is not built (run python -m top_moe_layer_amd.build)")
+    return B.lib()
+
+
+def test_header_declares_expected_functions():
+    assert declared_functions() == sorted(B.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.topmoe_version() == 100
+
+
+def test_strerror_covers_codes(L):
+    for code in (B.OK, B.ERR_NULL_ARG, B.ERR_BAD_SHAPE, B.ERR_UNSUPPORTED_DTYPE,
+                 B.ERR_WORKSPACE_TOO_SMALL, B.ERR_HIP, B.ERR_BAD_ARG):
+        assert B.strerror(code) != "unknown status"
+    assert B.strerror(-99) == "unknown status"
+
+
+def test_workspace_sizes(L):
+    # dense: the [N, I] intermediate
+    assert B.raw_ffn_workspace_bytes(100, 768, 2432, B.DTYPE_FP32) >= 100 * 2432 * 4
+    assert B.raw_ffn_workspace_bytes(16384, 2048, 6464, B.DTYPE_BF16) >= 16384 * 6464 * 2
+    # moe: intermediate [N*k, I] plus fp32 slots [N*k, H] when k >= 2
+    w1 = B.raw_moe_workspace_bytes(4096, 768, 2432, 4, 1, B.DTYPE_BF16)
+    assert 4096 * 2432 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 768 * 4
+    w2 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_BF16)
+    assert w2 >= 32768 * 2432 * 2 + 32768 * 768 * 4
+    assert B.raw_moe_workspace_bytes(0, 64, 64, 4, 2, B.DTYPE_BF16) > 0
+    for args in [(10, 65, 64, 4, 1), (10, 64, 96, 4, 1), (10, 64, 64, 0, 1), (10, 64, 64, 65, 1),
+                 (10, 64, 64, 4, 5), (10, 64, 64, 4, 0), (-1, 64, 64, 4, 1), (2**31, 64, 64, 4, 1)]:
+        assert B.raw_moe_workspace_bytes(*args, B.DTYPE_BF16) == 0, args
+    assert B.raw_moe_workspace_bytes(10, 64, 64, 4, 1, 7) == 0
+    assert B.raw_ffn_workspace_bytes(10, 64, 32, B.DTYPE_BF16) == 0
+
+
+FAKE = 1 << 20  # 256-byte aligned, never dereferenced: validation fails first
+
+
+def moe_call(**over):
+    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, N=8, H=64, I=64, E=4, k=2, coef=0.01,
+             dtype=B.DTYPE_BF16, y=FAKE, topk_idx=FAKE, alpha=FAKE, aux=FAKE, offsets=None,
+             sorted_ids=None, ws=FAKE, ws_bytes=0, stream=None, events=None)
+    a.update(over)
+    return B.raw_moe_ffn_fwd(*a.values())
+
+
+def ffn_call(**over):
+    a = dict(x=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, y=FAKE, N=8, H=64, I=64, dtype=B.DTYPE_BF16,
+             ws=FAKE, ws_bytes=0, stream=None, events=None)
+    a.update(over)
+    return B.raw_ffn_swiglu_fwd(*a.values())
+
+
+def test_moe_validation_codes(L):
+    assert moe_call(x=None) == B.ERR_NULL_ARG
+    assert moe_call(aux=None) == B.ERR_NULL_ARG
+    assert moe_call(ws=None) == B.ERR_NULL_ARG
+    assert moe_call(H=96) == B.ERR_BAD_SHAPE
+    assert moe_call(I=32) == B.ERR_BAD_SHAPE
+    assert moe_call(E=65, k=1) == B.ERR_BAD_SHAPE
+    assert moe_call(k=5) == B.ERR_BAD_SHAPE
+    assert moe_call(k=0) == B.ERR_BAD_SHAPE
+    assert moe_call(N=-3) == B.ERR_BAD_SHAPE
+    assert moe_call(dtype=2) == B.ERR_UNSUPPORTED_DTYPE
+    assert moe_call(coef=-0.5) == B.ERR_BAD_ARG
+    assert moe_call(coef=float("nan")) == B.ERR_BAD_ARG
+    assert moe_call(coef=float("inf")) == B.ERR_BAD_ARG
+    assert moe_call() == B.ERR_WORKSPACE_TOO_SMALL
+    need = B.raw_moe_workspace_bytes(8, 64, 64, 4, 2, B.DTYPE_BF16)
+    assert moe_call(ws_bytes=need - 1) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_call(ws_bytes=need, x=FAKE + 8) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, ws=FAKE + 64) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, alpha=FAKE + 2) == B.ERR_BAD_ARG
+
+
+def test_ffn_validation_codes(L):
+    assert ffn_call(y=None) == B.ERR_NULL_ARG
+    assert ffn_call(H=0) == B.ERR_BAD_SHAPE
+    assert ffn_call(I=100) == B.ERR_BAD_SHAPE
+    assert ffn_call(dtype=-1) == B.ERR_UNSUPPORTED_DTYPE
+    assert ffn_call() == B.ERR_WORKSPACE_TOO_SMALL
+    need = B.raw_ffn_workspace_bytes(8, 64, 64, B.DTYPE_BF16)
+    assert ffn_call(ws_bytes=need, Wd=FAKE + 4) == B.ERR_BAD_ARG
+
+
+def test_torch_front_end_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 64)
+    w = torch.zeros(64, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tm.ffn_swiglu_fwd(x, w, w, w)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tm.moe_ffn_fwd(x, torch.zeros(4, 64), torch.zeros(4, 64, 64), torch.zeros(4, 64, 64),
+                       torch.zeros(4, 64, 64), 1, 0.01)

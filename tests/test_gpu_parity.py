@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Bars: topk_idx, expert offsets and per-expert token lists bit-exact (inputs
+drawn with a top-k margin of 1e-3); alpha and aux_loss within 1e-5 relative;
+y within a max per-token relative L2 error of 1e-5 (fp32 path) or 2e-2 (bf16
+inputs, fp32 accumulation).  Small shapes are checked in full; the workloads
+at their full sizes are checked on every routing output and on sampled rows
+of y, in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+from oracle.cases import custom_workload, expected, make_case
+from workloads import get
+from gpu_util import (TOL_Y, announce, check_routing, rel_l2_global, rel_l2_per_token,
+                      run_dense, run_moe, sample_rows, to_dev, torch_dev, y_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch, dev = torch_dev()
+    import top_moe_layer_amd as tm
+
+    tm.lib()
+    return torch, dev, tm
+
+
+# ------------------------------------------------------------------ dense
+DENSE_SMALL = [
+    (1, 64, 64), (7, 128, 192), (129, 64, 128), (300, 128, 64), (513, 192, 320), (1000, 256, 448),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("N,H,I", DENSE_SMALL)
+def test_dense_small(env, N, H, I, dt):
+    torch, dev, tm = env
+    w = custom_workload(name=f"dense_{N}_{H}_{I}", kind="dense", N=N, H=H, I=I, E=1, k=1,
+                        coef=0.0, dtype=dt, seed=N + H + I)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"ffn_swiglu_fwd N={N} H={H} I={I} {dt}")
+    y = run_dense(tm, to_dev(inp, dev))
+    torch.cuda.synchronize()
+    err = rel_l2_per_token(y_to_f64(y), ref["y"])
+    assert err <= TOL_Y[dt], err
+
+
+# -------------------------------------------------------------------- moe
+MOE_SMALL = [
+    # N, H, I, E, k
+    (1, 64, 64, 4, 1),
+    (7, 64, 128, 2, 2),
+    (129, 128, 64, 3, 1),
+    (1000, 64, 64, 8, 2),
+    (257, 128, 192, 64, 2),
+    (100, 64, 64, 1, 1),
+    (500, 128, 128, 16, 4),
+    (2000, 64, 128, 5, 3),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("N,H,I,E,k", MOE_SMALL)
+def test_moe_small(env, N, H, I, E, k, dt):
+    torch, dev, tm = env
+    w = custom_workload(name=f"moe_{N}_{E}_{k}", N=N, H=H, I=I, E=E, k=k, coef=0.01, dtype=dt,
+                        seed=N * 7 + E + k)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"moe_ffn_fwd N={N} H={H} I={I} E={E} k={k} {dt}")
+    out = run_moe(tm, to_dev(inp, dev), w)
+    torch.cuda.synchronize()
+    check_routing(out, ref, k, E)
+    err = rel_l2_per_token(y_to_f64(out.y), ref["y"])
+    assert err <= TOL_Y[dt], err
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("N,E", [(64, 8), (33, 3), (40, 64)])
+def test_moe_k_equals_E(env, N, E, dt):
+    """k = E selects every expert (no margin needed); slots compared by id."""
+    torch, dev, tm = env
+    w = custom_workload(name=f"moe_kE_{N}_{E}", N=N, H=64, I=64, E=E, k=E, coef=0.01, dtype=dt,
+                        seed=3 * N + E)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"moe_ffn_fwd k=E N={N} E={E} {dt}")
+    out = run_moe(tm, to_dev(inp, dev), w)
+    torch.cuda.synchronize()
+    check_routing(out, ref, E, E, exact_order=False)
+    assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y[dt]
+
+
+def test_moe_top1_alpha_exactly_one(env):
+    torch, dev, tm = env
+    w = custom_workload(name="moe_alpha1", N=777, H=128, I=64, E=8, k=1, coef=0.01, seed=5)
+    inp = make_case(w)
+    announce("moe_ffn_fwd k=1 alpha == 1")
+    out = run_moe(tm, to_dev(inp, dev), w)
+    torch.cuda.synchronize()
+    assert bool((out.alpha == 1.0).all())
+
+
+def test_moe_coef_zero_gives_zero_aux(env):
+    torch, dev, tm = env
+    w = custom_workload(name="moe_coef0", N=300, H=64, I=64, E=4, k=2, coef=0.0, seed=6)
+    inp = make_case(w)
+    announce("moe_ffn_fwd coef=0")
+    out = run_moe(tm, to_dev(inp, dev), w)
+    torch.cuda.synchronize()
+    assert float(out.aux_loss.cpu()[0]) == 0.0
+
+
+def test_moe_single_expert_matches_dense(env):
+    """E = 1, k = 1 reduces the MoE to the dense FFN (both against the oracle)."""
+    torch, dev, tm = env
+    w = custom_workload(name="moe_e1", N=300, H=128, I=192, E=1, k=1, coef=0.01, seed=8)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    d = to_dev(inp, dev)
+    announce("moe_ffn_fwd E=1 vs ffn_swiglu_fwd")
+    out = run_moe(tm, d, w)
+    yd = tm.ffn_swiglu_fwd(d["x"], d["Wg"][0], d["Wu"][0], d["Wd"][0])
+    torch.cuda.synchronize()
+    assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y["bf16"]
+    assert rel_l2_per_token(y_to_f64(yd), ref["y"]) <= TOL_Y["bf16"]
+
+
+def test_empty_inputs(env):
+    torch, dev, tm = env
+    announce("N = 0")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((4, 64, 64), dtype=torch.bfloat16, device=dev)
+    Wr = torch.zeros((4, 64), dtype=torch.float32, device=dev)
+    out = tm.moe_ffn_fwd(x, Wr, W, W, W, 2, 0.01)
+    y = tm.ffn_swiglu_fwd(x, W[0], W[0], W[0])
+    torch.cuda.synchronize()
+    assert out.y.shape == (0, 64) and y.shape == (0, 64)
+    assert out.expert_offsets.cpu().tolist() == [0] * 5
+    assert float(out.aux_loss.cpu()[0]) == 0.0
+
+
+def test_bitwise_deterministic(env):
+    torch, dev, tm = env
+    w = custom_workload(name="moe_det", N=3000, H=128, I=192, E=8, k=2, coef=0.01, seed=9)
+    inp = make_case(w)
+    d = to_dev(inp, dev)
+    announce("moe_ffn_fwd run-to-run determinism")
+    a = run_moe(tm, d, w)
+    b = run_moe(tm, d, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
+    assert torch.equal(a.alpha, b.alpha) and torch.equal(a.aux_loss, b.aux_loss)
+    assert torch.equal(a.sorted_token_ids, b.sorted_token_ids)
+
+
+# ------------------------------------------------- workloads at full size
+FULL = ["dense_fp32", "moe_top1", "dense_bf16", "moe_skew", "moe_skew_literal", "moe_decode"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size(env, name):
+    torch, dev, tm = env
+    w = get(name)
+    inp = make_case(w)
+    rows = sample_rows(w.N, 384 if w.N > 1024 else w.N)
+    ref = expected(w, inp, rows=rows)
+    announce(f"{w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype}")
+    d = to_dev(inp, dev)
+    if w.kind == "dense":
+        y = run_dense(tm, d)
+        torch.cuda.synchronize()
+    else:
+        out = run_moe(tm, d, w)
+        torch.cuda.synchronize()
+        check_routing(out, ref, w.k, w.E)
+        y = out.y
+    got = y_to_f64(y)[rows]
+    err = rel_l2_per_token(got, ref["y"])
+    print(f"[gpu] {w.name}: max per-token rel L2 {err:.3e}, global {rel_l2_global(got, ref['y']):.3e}",
+          flush=True)
+    assert err <= TOL_Y[w.dtype], err

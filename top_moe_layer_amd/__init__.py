@@ -1,0 +1,30 @@
+"""MI355X (gfx950) MiniMind FFN / top-k MoE forward.
+
+The compute lives in ``lib/libtopmoe.so`` (hand-written HIP kernels behind the
+C ABI of include/topmoe.h).  This package only marshals torch tensors into
+that ABI.  Importing it does not load the library; the first call does, and
+fails loudly if the library has not been built.
+"""
+from ._binding import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_FP32,
+    FFN_STAGES,
+    FFN_STAGE_NAMES,
+    MOE_STAGES,
+    MOE_STAGE_NAMES,
+    LIB_PATH,
+    StageEvents,
+    TopmoeError,
+    lib,
+    strerror,
+)
+
+
+def __getattr__(name):
+    # torch-level wrappers are imported lazily so that ``import top_moe_layer_amd``
+    # stays cheap for tools that only need the raw binding.
+    if name in ("ffn_swiglu_fwd", "moe_ffn_fwd", "ffn_workspace_bytes", "moe_workspace_bytes",
+                "MoeOutput"):
+        from . import ops
+        return getattr(ops, name)
+    raise AttributeError(name)

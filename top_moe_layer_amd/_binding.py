@@ -1,0 +1,132 @@
+"""ctypes binding of ``lib/libtopmoe.so`` (declared in include/topmoe.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the stream.
+There is no CPU fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libtopmoe.so")
+
+# Must match include/topmoe.h
+OK = 0
+ERR_NULL_ARG = -1
+ERR_BAD_SHAPE = -2
+ERR_UNSUPPORTED_DTYPE = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+ERR_HIP = -5
+ERR_BAD_ARG = -6
+DTYPE_FP32 = 0
+DTYPE_BF16 = 1
+FFN_STAGES = 2
+MOE_STAGES = 6
+
+FFN_STAGE_NAMES = ["gateup_gemm", "down_gemm"]
+MOE_STAGE_NAMES = ["router", "offsets_aux", "scatter", "gateup_gemm", "down_gemm", "combine"]
+
+# Every function include/topmoe.h declares, with its ctypes signature.
+_vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "ffn_swiglu_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp, _vp]),
+    "moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+    "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _i32,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "topmoe_strerror": (ctypes.c_char_p, [_i32]),
+    "topmoe_version": (_i32, []),
+    "topmoe_events_create": (_i32, [_i32, _vp]),
+    "topmoe_events_destroy": (_i32, [_i32, _vp]),
+    "topmoe_event_elapsed_ms": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
+}
+
+_lib = None
+
+
+class TopmoeError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = strerror(status)
+        super().__init__(f"{what}: status {status}: {msg}" if what else f"status {status}: {msg}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m top_moe_layer_amd.build` "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().topmoe_strerror(int(status)).decode()
+
+
+def check(status: int, what: str = "") -> None:
+    if status != OK:
+        raise TopmoeError(status, what)
+
+
+# ------------------------------------------------------------ raw calls
+def raw_ffn_workspace_bytes(N, H, I, dtype) -> int:
+    return int(lib().ffn_workspace_bytes(N, H, I, dtype))
+
+
+def raw_moe_workspace_bytes(N, H, I, E, k, dtype) -> int:
+    return int(lib().moe_workspace_bytes(N, H, I, E, k, dtype))
+
+
+def raw_ffn_swiglu_fwd(x, Wg, Wu, Wd, y, N, H, I, dtype, ws, ws_bytes, stream, events) -> int:
+    return int(lib().ffn_swiglu_fwd(x, Wg, Wu, Wd, y, N, H, I, dtype, ws, ws_bytes, stream, events))
+
+
+def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, N, H, I, E, k, coef, dtype, y, topk_idx, alpha, aux,
+                    offsets, sorted_ids, ws, ws_bytes, stream, events) -> int:
+    return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, N, H, I, E, k, coef, dtype, y, topk_idx,
+                                 alpha, aux, offsets, sorted_ids, ws, ws_bytes, stream, events))
+
+
+class StageEvents:
+    """n + 1 timing events for the ``stage_events`` argument."""
+
+    def __init__(self, stages: int):
+        self.n = stages + 1
+        self.arr = (ctypes.c_void_p * self.n)()
+        check(lib().topmoe_events_create(self.n, self.arr), "topmoe_events_create")
+
+    @property
+    def ptr(self):
+        return ctypes.cast(self.arr, ctypes.c_void_p)
+
+    def elapsed_ms(self):
+        """Per-stage milliseconds of the last recorded call (waits for it)."""
+        out = []
+        ms = ctypes.c_float()
+        for i in range(self.n - 1):
+            check(lib().topmoe_event_elapsed_ms(self.arr[i], self.arr[i + 1], ctypes.byref(ms)),
+                  "topmoe_event_elapsed_ms")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        if self.arr is not None:
+            lib().topmoe_events_destroy(self.n, self.arr)
+            self.arr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,211 @@
+// C ABI entry points: validate on the host, carve the workspace, enqueue the
+// kernels.  See include/topmoe.h for the contract of every function.
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "plan.h"
+
+#include "../../include/topmoe.h"
+
+namespace topmoe {
+hipError_t launch_gemm_bf16(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
+                            hipStream_t s);
+hipError_t launch_gemm_f32(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
+                           hipStream_t s);
+
+hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
+                       int64_t mtiles, hipStream_t s) {
+  return dtype == TOPMOE_DTYPE_FP32 ? launch_gemm_f32(kind, shape, p, mtiles, s)
+                                    : launch_gemm_bf16(kind, shape, p, mtiles, s);
+}
+}  // namespace topmoe
+
+using namespace topmoe;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Events {
+  void* const* ev;
+  hipStream_t s;
+  hipError_t rec(int i) const {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  }
+};
+
+#define TOPMOE_TRY(expr)                              \
+  do {                                                \
+    if ((expr) != hipSuccess) return TOPMOE_ERR_HIP;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int topmoe_version(void) { return 100; }
+
+const char* topmoe_strerror(int status) {
+  switch (status) {
+    case TOPMOE_OK: return "ok";
+    case TOPMOE_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case TOPMOE_ERR_BAD_SHAPE:
+      return "shape outside the supported limits (H, I multiples of 64; 1 <= E <= 64; "
+             "1 <= k <= E; N >= 0; sizes within 32-bit row ids)";
+    case TOPMOE_ERR_UNSUPPORTED_DTYPE: return "dtype must be TOPMOE_DTYPE_FP32 or TOPMOE_DTYPE_BF16";
+    case TOPMOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_bytes() size";
+    case TOPMOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case TOPMOE_ERR_BAD_ARG: return "invalid argument (aux_coef negative or not finite, or a misaligned pointer)";
+  }
+  return "unknown status";
+}
+
+size_t ffn_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype) {
+  FfnPlan pl;
+  return plan_ffn(N, H, I, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
+}
+
+size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype) {
+  MoePlan pl;
+  return plan_moe(N, H, I, E, k, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
+}
+
+int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd, void* y,
+                   int64_t N, int64_t H, int64_t I, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* stage_events) {
+  FfnPlan pl;
+  const int st = plan_ffn(N, H, I, dtype, &pl);
+  if (st != TOPMOE_OK) return st;
+  if (!x || !Wg || !Wu || !Wd || !y || !workspace) return TOPMOE_ERR_NULL_ARG;
+  if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) ||
+      !aligned(y, 16) || !aligned(workspace, 256))
+    return TOPMOE_ERR_BAD_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Events ev{stage_events, s};
+  char* ws = static_cast<char*>(workspace);
+  void* h = ws + pl.off_h;
+
+  TOPMOE_TRY(ev.rec(0));
+  if (N > 0) {
+    GemmParams up{};
+    up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
+    up.entries = nullptr; up.offsets = nullptr; up.alpha = nullptr;
+    up.M = N; up.E = 1; up.k = 1; up.Nout = int(I); up.K = int(H);
+    TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, (N + pl.up.bm - 1) / pl.up.bm, s));
+  }
+  TOPMOE_TRY(ev.rec(1));
+  if (N > 0) {
+    GemmParams dn{};
+    dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = y;
+    dn.entries = nullptr; dn.offsets = nullptr; dn.alpha = nullptr;
+    dn.M = N; dn.E = 1; dn.k = 1; dn.Nout = int(H); dn.K = int(I);
+    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.down, dn, (N + pl.down.bm - 1) / pl.down.bm, s));
+  }
+  TOPMOE_TRY(ev.rec(2));
+  return TOPMOE_OK;
+}
+
+int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
+                int64_t N, int64_t H, int64_t I, int E, int k, float aux_coef, int dtype,
+                void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
+                int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
+                size_t workspace_bytes, void* stream, void* const* stage_events) {
+  MoePlan pl;
+  const int st = plan_moe(N, H, I, E, k, dtype, &pl);
+  if (st != TOPMOE_OK) return st;
+  if (!x || !Wr || !Wg || !Wu || !Wd || !y || !topk_idx || !alpha || !aux_loss || !workspace)
+    return TOPMOE_ERR_NULL_ARG;
+  if (!(aux_coef >= 0.0f) || isinf(aux_coef)) return TOPMOE_ERR_BAD_ARG;
+  if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
+      !aligned(Wd, 16) || !aligned(y, 16) || !aligned(topk_idx, 4) || !aligned(alpha, 4) ||
+      !aligned(aux_loss, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_token_ids, 4) ||
+      !aligned(workspace, 256))
+    return TOPMOE_ERR_BAD_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Events ev{stage_events, s};
+  char* ws = static_cast<char*>(workspace);
+  int32_t* count_part = reinterpret_cast<int32_t*>(ws + pl.off_count_part);
+  float* psum_part = reinterpret_cast<float*>(ws + pl.off_psum_part);
+  int32_t* blk_off = reinterpret_cast<int32_t*>(ws + pl.off_blk_off);
+  int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(ws + pl.off_offsets);
+  int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
+  void* h = ws + pl.off_h;
+  float* slots = reinterpret_cast<float*>(ws + pl.off_slots);
+
+  if (N == 0) {
+    for (int i = 0; i <= TOPMOE_MOE_STAGES; ++i) {
+      if (i == 1) TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, s));
+      TOPMOE_TRY(ev.rec(i));
+    }
+    return TOPMOE_OK;
+  }
+
+  // 0: router, softmax, top-k, alpha, per-block counts and sums of p
+  TOPMOE_TRY(ev.rec(0));
+  TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, pl.tb, pl.nblk, topk_idx, alpha,
+                           count_part, psum_part, s));
+  // 1: expert offsets, per-block scatter bases, aux loss
+  TOPMOE_TRY(ev.rec(1));
+  TOPMOE_TRY(launch_offsets_aux(count_part, psum_part, pl.nblk, E, N, aux_coef, blk_off,
+                                offsets, aux_loss, s));
+  // 2: stable scatter of entries into expert groups
+  TOPMOE_TRY(ev.rec(2));
+  TOPMOE_TRY(launch_scatter(topk_idx, blk_off, N, E, k, pl.tb, pl.nblk, sorted_entry,
+                            sorted_token_ids, s));
+  // 3: grouped gate/up GEMM + SiLU * up
+  TOPMOE_TRY(ev.rec(3));
+  GemmParams up{};
+  up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
+  up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
+  up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
+  TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, s));
+  // 4: grouped down GEMM, alpha-scaled, into y (k == 1) or the k slots
+  TOPMOE_TRY(ev.rec(4));
+  GemmParams dn{};
+  dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : static_cast<void*>(slots);
+  dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha;
+  dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
+  TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
+                         pl.down_mtiles, s));
+  // 5: fixed-order combine of the k slots
+  TOPMOE_TRY(ev.rec(5));
+  if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, N, int(H), k, dtype, y, s));
+  TOPMOE_TRY(ev.rec(6));
+  return TOPMOE_OK;
+}
+
+int topmoe_events_create(int n, void** events) {
+  if (!events || n < 0) return TOPMOE_ERR_NULL_ARG;
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return TOPMOE_ERR_HIP;
+    events[i] = e;
+  }
+  return TOPMOE_OK;
+}
+
+int topmoe_events_destroy(int n, void** events) {
+  if (!events || n < 0) return TOPMOE_ERR_NULL_ARG;
+  for (int i = 0; i < n; ++i) {
+    if (events[i] && hipEventDestroy(static_cast<hipEvent_t>(events[i])) != hipSuccess)
+      return TOPMOE_ERR_HIP;
+    events[i] = nullptr;
+  }
+  return TOPMOE_OK;
+}
+
+int topmoe_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return TOPMOE_ERR_NULL_ARG;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return TOPMOE_ERR_HIP;
+  if (hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) !=
+      hipSuccess)
+    return TOPMOE_ERR_HIP;
+  return TOPMOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,11 @@
+// bf16 instantiations of the grouped MFMA GEMM.
+#include "gemm_impl.h"
+
+namespace topmoe {
+
+hipError_t launch_gemm_bf16(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
+                            hipStream_t s) {
+  return launch_gemm_dtype<bf16_t>(kind, sh, p, mtiles, s);
+}
+
+}  // namespace topmoe

@@ -1,0 +1,211 @@
+// Token permutation, load-balancing loss and the k-slot combine.
+//
+// The MoE dispatch of MiniMind lesson 13, walkthrough step 5 visits experts in
+// ascending id and, for each, the tokens that selected it in ascending token
+// order (mask / nonzero), runs the expert on those rows and adds the weighted
+// rows back with index_add_.  Here the same grouping is built once, without a
+// host round trip:
+//   * offsets_aux: per-expert totals c_e and their exclusive prefix sum
+//     (expert offsets), per-block scatter bases, and the aux loss
+//     aux = E * coef * sum_e (c_e / N) * (sum_t p_{t,e} / N)
+//     (lesson 13, section 1.6 equation; walkthrough step 6);
+//   * scatter: a stable scatter of the entries (t, j) in t*k + j order into
+//     expert groups, so each group lists its tokens in ascending order;
+//   * combine: y_t = sum of the k alpha-scaled expert rows in ascending expert
+//     id, accumulated in fp32 and rounded once.
+// All integer work is exact; the only float reductions run in a fixed order.
+#include "device_common.h"
+#include "kernels.h"
+
+#include "../../include/topmoe.h"
+
+namespace topmoe {
+
+namespace {
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void offsets_aux_kernel(
+    const int32_t* __restrict__ count_part, const float* __restrict__ psum_part, int nblk,
+    int E, int64_t N, float coef, int32_t* __restrict__ blk_off, int32_t* __restrict__ offsets,
+    float* __restrict__ aux) {
+  __shared__ int s_cnt[64];
+  __shared__ double s_ps[64];
+  __shared__ int s_off[65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int WAVES = 1024 / 64;
+
+  // pass 1: per-expert totals (counts exact; sums of p in a fixed order, fp64)
+  for (int e = wave; e < E; e += WAVES) {
+    int c = 0;
+    double ps = 0.0;
+    for (int b = lane; b < nblk; b += 64) {
+      c += count_part[int64_t(b) * E + e];
+      ps += double(psum_part[int64_t(b) * E + e]);
+    }
+    c = wave_sum_int(c);
+    ps = wave_sum(ps);
+    if (lane == 0) { s_cnt[e] = c; s_ps[e] = ps; }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    const int c = lane < E ? s_cnt[lane] : 0;
+    const int incl = wave_inclusive_scan(c, lane);
+    if (lane < E) s_off[lane] = incl - c;
+    if (lane == E - 1) s_off[E] = incl;
+    double term = lane < E ? double(c) * s_ps[lane] : 0.0;
+    term = wave_sum(term);
+    if (lane == 0) {
+      float a = 0.f;
+      if (coef != 0.f && N > 0) a = float(double(E) * double(coef) * term / (double(N) * double(N)));
+      *aux = a;
+    }
+  }
+  __syncthreads();
+  if (tid <= E) offsets[tid] = s_off[tid];
+
+  // pass 2: per-block exclusive scan of each expert's counts, plus its offset
+  for (int e = wave; e < E; e += WAVES) {
+    int run = s_off[e];
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+      const int b = b0 + lane;
+      const int c = b < nblk ? count_part[int64_t(b) * E + e] : 0;
+      const int incl = wave_inclusive_scan(c, lane);
+      if (b < nblk) blk_off[int64_t(b) * E + e] = run + incl - c;
+      run += __shfl(incl, 63, 64);
+    }
+  }
+}
+
+// One wavefront per router block: ranks each entry among the same-expert
+// entries of its block (in t*k + j order) and writes it to its group slot.
+__global__ __launch_bounds__(64) void scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_off, int64_t N, int E,
+    int k, int tb, int32_t* __restrict__ sorted_entry, int32_t* __restrict__ sorted_tok) {
+  __shared__ int run[64];
+  const int lane = threadIdx.x;
+  run[lane] = 0;
+  __syncthreads();
+  const int64_t tok0 = int64_t(blockIdx.x) * tb;
+  const int64_t tok1 = (tok0 + tb < N) ? tok0 + tb : N;
+  const int64_t e0 = tok0 * k, e1 = tok1 * k;
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = e0; base < e1; base += 64) {
+    const int64_t ent = base + lane;
+    const bool valid = ent < e1;
+    const int ex = valid ? topk_idx[ent] : -1;
+    // lanes holding the same expert
+    uint64_t peers = 0ull;
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int le = __shfl(ex, leader, 64);
+      const uint64_t m = __ballot(valid && ex == le);
+      if (valid && ex == le) peers = m;
+      todo &= ~m;
+    }
+    int dest = 0;
+    if (valid) {
+      dest = blk_off[int64_t(blockIdx.x) * E + ex] + run[ex] + __popcll(peers & lt_mask);
+      sorted_entry[dest] = int32_t(ent);
+      if (sorted_tok) sorted_tok[dest] = int32_t(ent / k);
+    }
+    __syncthreads();
+    if (valid && (peers & lt_mask) == 0ull) run[ex] += __popcll(peers);
+    __syncthreads();
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, f32x4 v);
+
+template <>
+__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, f32x4 v) {
+  uint2 q;
+  q.x = uint32_t(f32_to_bf16(v.x)) | (uint32_t(f32_to_bf16(v.y)) << 16);
+  q.y = uint32_t(f32_to_bf16(v.z)) | (uint32_t(f32_to_bf16(v.w)) << 16);
+  *reinterpret_cast<uint2*>(p) = q;
+}
+
+// y[t, 4q..4q+3] = sum of slot rows of token t, ascending expert id.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ slots,
+                                                      const int32_t* __restrict__ topk_idx,
+                                                      int64_t N, int H, int k,
+                                                      T* __restrict__ y) {
+  const int hq = H >> 2;
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= N * hq) return;
+  const int64_t t = gid / hq;
+  const int h = int(gid - t * hq) * 4;
+  const int32_t* ids = topk_idx + t * k;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int prev = -1;
+  for (int r = 0; r < k; ++r) {
+    int best_j = 0, best_e = 1 << 30;
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[j];
+      if (e > prev && e < best_e) { best_e = e; best_j = j; }
+    }
+    prev = best_e;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(slots + (t * k + best_j) * H + h);
+    acc += v;
+  }
+  store4<T>(y + t * H + h, acc);
+}
+
+__global__ void empty_route_kernel(int E, int32_t* offsets, float* aux) {
+  const int tid = threadIdx.x;
+  if (tid <= E) offsets[tid] = 0;
+  if (tid == 0) *aux = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_offsets_aux(const int32_t* count_part, const float* psum_part, int nblk,
+                              int E, int64_t N, float coef, int32_t* blk_off,
+                              int32_t* offsets, float* aux, hipStream_t s) {
+  hipLaunchKernelGGL(offsets_aux_kernel, dim3(1), dim3(1024), 0, s, count_part, psum_part,
+                     nblk, E, N, coef, blk_off, offsets, aux);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_off, int64_t N, int E,
+                          int k, int tb, int nblk, int32_t* sorted_entry,
+                          int32_t* sorted_tok, hipStream_t s) {
+  if (nblk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(64), 0, s, topk_idx, blk_off, N, E, k,
+                     tb, sorted_entry, sorted_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,
+                          int dtype, void* y, hipStream_t s) {
+  const int64_t work = N * (H / 4);
+  if (work <= 0) return hipSuccess;
+  const int64_t grid = (work + 255) / 256;
+  if (dtype == TOPMOE_DTYPE_FP32)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
+                       H, k, static_cast<float*>(y));
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
+                       H, k, static_cast<bf16_t*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, hipStream_t s) {
+  hipLaunchKernelGGL(empty_route_kernel, dim3(1), dim3(128), 0, s, E, offsets, aux);
+  return hipGetLastError();
+}
+
+}  // namespace topmoe

@@ -1,0 +1,109 @@
+// Host-side planning: validation, workspace layout, launch shapes.
+#include "plan.h"
+
+#include "../../include/topmoe.h"
+
+namespace topmoe {
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // int32 row / entry ids
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool dtype_ok(int dtype) { return dtype == TOPMOE_DTYPE_FP32 || dtype == TOPMOE_DTYPE_BF16; }
+
+int elem_bytes(int dtype) { return dtype == TOPMOE_DTYPE_FP32 ? 4 : 2; }
+
+struct Cand {
+  int bm, bn;
+  double eff;  // relative MFMA efficiency of one tile (bigger tiles reuse operands more)
+};
+
+// Pick the tile minimising (rounds of 256 CUs) x (cost of one tile).
+GemmShape choose(const Cand* cands, int n, int64_t M, int64_t Nout, int groups) {
+  GemmShape best{cands[n - 1].bm, cands[n - 1].bn};
+  double best_cost = -1.0;
+  for (int i = 0; i < n; ++i) {
+    const Cand& c = cands[i];
+    int64_t mt = grouped_mtiles_bound(M, groups, c.bm);
+    // expected tiles: ceil per group is at most one extra tile per group
+    int64_t nt = (Nout + c.bn - 1) / c.bn;
+    int64_t tiles = mt * nt;
+    if (tiles <= 0) continue;
+    int64_t rounds = (tiles + 255) / 256;
+    double cost = double(rounds) * double(c.bm) * double(c.bn) / c.eff;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = GemmShape{c.bm, c.bn};
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int groups, int dtype) {
+  static const Cand c[] = {{256, 128, 1.0}, {128, 128, 0.85}, {128, 64, 0.65}, {64, 64, 0.45}};
+  (void)dtype;
+  return choose(c, 4, M, Nout, groups);
+}
+
+GemmShape choose_down_tile(int64_t M, int64_t Nout, int groups, int dtype) {
+  static const Cand c[] = {{256, 128, 1.0}, {128, 128, 0.85}, {128, 64, 0.65}, {64, 64, 0.45}};
+  (void)dtype;
+  return choose(c, 4, M, Nout, groups);
+}
+
+int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
+  if (!dtype_ok(dtype)) return TOPMOE_ERR_UNSUPPORTED_DTYPE;
+  if (N < 0 || H < 64 || I < 64 || H % 64 || I % 64) return TOPMOE_ERR_BAD_SHAPE;
+  if (N > kMaxRows || N * H >= kMaxElems || N * I >= kMaxElems || H * I >= kMaxElems)
+    return TOPMOE_ERR_BAD_SHAPE;
+  FfnPlan q;
+  q.N = N; q.H = H; q.I = I; q.dtype = dtype; q.elem = elem_bytes(dtype);
+  q.up = choose_gateup_tile(N, I, 1, dtype);
+  q.down = choose_down_tile(N, H, 1, dtype);
+  q.off_h = 0;
+  q.total = align_up(size_t(N) * size_t(I) * q.elem);
+  if (q.total == 0) q.total = kAlign;
+  *p = q;
+  return TOPMOE_OK;
+}
+
+int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* p) {
+  if (!dtype_ok(dtype)) return TOPMOE_ERR_UNSUPPORTED_DTYPE;
+  if (N < 0 || H < 64 || I < 64 || H % 64 || I % 64) return TOPMOE_ERR_BAD_SHAPE;
+  if (E < 1 || E > 64 || k < 1 || k > E) return TOPMOE_ERR_BAD_SHAPE;
+  const int64_t rows = N * k;
+  if (rows > kMaxRows || rows * H >= kMaxElems || rows * I >= kMaxElems ||
+      int64_t(E) * H * I >= kMaxElems)
+    return TOPMOE_ERR_BAD_SHAPE;
+  MoePlan q;
+  q.N = N; q.H = H; q.I = I; q.E = E; q.k = k; q.dtype = dtype; q.elem = elem_bytes(dtype);
+  q.rows = rows;
+  // Router: one token per wavefront, 4 wavefronts per block; at most 4096
+  // blocks so the single-block offset scan stays short.
+  int64_t tb = 16;
+  while (N > 0 && (N + tb - 1) / tb > 4096) tb *= 2;
+  q.tb = int(tb);
+  q.nblk = int((N + tb - 1) / tb);
+  q.up = choose_gateup_tile(rows, I, E, dtype);
+  q.down = choose_down_tile(rows, H, E, dtype);
+  q.up_mtiles = grouped_mtiles_bound(rows, E, q.up.bm);
+  q.down_mtiles = grouped_mtiles_bound(rows, E, q.down.bm);
+  size_t o = 0;
+  const size_t nbe = size_t(q.nblk) * size_t(E);
+  q.off_count_part = o; o = align_up(o + nbe * 4);
+  q.off_psum_part = o;  o = align_up(o + nbe * 4);
+  q.off_blk_off = o;    o = align_up(o + nbe * 4);
+  q.off_offsets = o;    o = align_up(o + size_t(E + 1) * 4);
+  q.off_sorted = o;     o = align_up(o + size_t(rows) * 4);
+  q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);
+  q.off_slots = o;
+  if (k >= 2) o = align_up(o + size_t(rows) * size_t(H) * 4);
+  q.total = o == 0 ? kAlign : o;
+  *p = q;
+  return TOPMOE_OK;
+}
+
+}  // namespace topmoe

@@ -1,0 +1,65 @@
+// Host-side planning for the FFN / MoE forward: argument validation, the
+// workspace layout and launch-shape choices.  Plain C++ (no HIP types) so the
+// same logic is testable on a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace topmoe {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+// One GEMM launch shape: block tile BM x BN (per output matrix).
+struct GemmShape {
+  int bm = 0, bn = 0;
+};
+
+struct FfnPlan {
+  int64_t N = 0, H = 0, I = 0;
+  int dtype = 0;
+  int elem = 0;            // bytes per x / W / y element
+  GemmShape up, down;      // gate/up and down GEMM tiles
+  size_t off_h = 0;        // SiLU(g)*u intermediate [N, I]
+  size_t total = 0;        // workspace bytes
+};
+
+struct MoePlan {
+  int64_t N = 0, H = 0, I = 0;
+  int E = 0, k = 0, dtype = 0;
+  int elem = 0;
+  int64_t rows = 0;        // N * k expert rows
+  int tb = 0;              // router / scatter tokens per block
+  int nblk = 0;            // router / scatter blocks
+  GemmShape up, down;
+  int64_t up_mtiles = 0;   // upper bound on grouped M tiles (gate/up)
+  int64_t down_mtiles = 0; // upper bound on grouped M tiles (down)
+  // workspace layout (byte offsets)
+  size_t off_count_part = 0;  // int32 [nblk, E] per-block expert counts
+  size_t off_psum_part = 0;   // f32   [nblk, E] per-block sums of p
+  size_t off_blk_off = 0;     // int32 [nblk, E] scatter base per block and expert
+  size_t off_offsets = 0;     // int32 [E+1] expert offsets (when the caller passes none)
+  size_t off_sorted = 0;      // int32 [N*k] entry ids (t*k + j) grouped by expert
+  size_t off_h = 0;           // elem  [N*k, I] SiLU(g)*u in grouped row order
+  size_t off_slots = 0;       // f32   [N*k, H] alpha-scaled expert outputs (k >= 2)
+  size_t total = 0;
+};
+
+// Returns TOPMOE_OK or a negative status; fills `plan` on success.
+int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* plan);
+int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* plan);
+
+// Tile choice for an M x Nout GEMM with `groups` row groups (experts).
+GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int groups, int dtype);
+GemmShape choose_down_tile(int64_t M, int64_t Nout, int groups, int dtype);
+
+// Upper bound on the number of BM-row tiles over `groups` groups of total M rows.
+inline int64_t grouped_mtiles_bound(int64_t M, int groups, int bm) {
+  if (M <= 0) return 0;
+  int64_t g = groups < M ? groups : M;
+  return (M + bm - 1) / bm + (groups > 1 ? g : 0);
+}
+
+}  // namespace topmoe

@@ -1,0 +1,152 @@
+"""Torch-tensor front end of the C ABI: shape / dtype checks, output and
+workspace allocation through PyTorch, the current HIP stream.  Nothing here
+computes any part of the forward pass."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return B.DTYPE_FP32
+    if t == torch.bfloat16:
+        return B.DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t}; use float32 or bfloat16")
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); the library has no CPU path")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+    return ws
+
+
+def ffn_workspace_bytes(N: int, H: int, I: int, dtype: torch.dtype) -> int:
+    return B.raw_ffn_workspace_bytes(N, H, I, _dtype_code(dtype))
+
+
+def moe_workspace_bytes(N: int, H: int, I: int, E: int, k: int, dtype: torch.dtype) -> int:
+    return B.raw_moe_workspace_bytes(N, H, I, E, k, _dtype_code(dtype))
+
+
+def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, *,
+                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None, stage_events: Optional[B.StageEvents] = None) -> torch.Tensor:
+    """Dense SwiGLU FFN: y = Wd (SiLU(Wg x) * Wu x).  x [..., H]; Wg, Wu [I, H];
+    Wd [H, I].  Returns y with x's shape and dtype."""
+    dev = x.device
+    H = x.shape[-1]
+    I = Wg.shape[0]
+    xf = x.reshape(-1, H)
+    N = xf.shape[0]
+    dt = x.dtype
+    _need(xf, "x", (N, H), dt, dev)
+    _need(Wg, "Wg", (I, H), dt, dev)
+    _need(Wu, "Wu", (I, H), dt, dev)
+    _need(Wd, "Wd", (H, I), dt, dev)
+    if y is None:
+        y = torch.empty((N, H), dtype=dt, device=dev)
+    _need(y, "y", (N, H), dt, dev)
+    code = _dtype_code(dt)
+    nbytes = B.raw_ffn_workspace_bytes(N, H, I, code)
+    if nbytes == 0:
+        B.check(B.ERR_BAD_SHAPE, "ffn_swiglu_fwd")
+    ws = _workspace(nbytes, dev, workspace)
+    st = B.raw_ffn_swiglu_fwd(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y), N, H, I, code,
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
+                              stage_events.ptr if stage_events is not None else None)
+    B.check(st, "ffn_swiglu_fwd")
+    return y.view(x.shape)
+
+
+@dataclass
+class MoeOutput:
+    y: torch.Tensor
+    topk_idx: torch.Tensor
+    alpha: torch.Tensor
+    aux_loss: torch.Tensor
+    expert_offsets: Optional[torch.Tensor]
+    sorted_token_ids: Optional[torch.Tensor]
+
+
+def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
+                Wd: torch.Tensor, k: int, aux_coef: float, *,
+                y: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                alpha: Optional[torch.Tensor] = None, aux_loss: Optional[torch.Tensor] = None,
+                expert_offsets: Optional[torch.Tensor] = None,
+                sorted_token_ids: Optional[torch.Tensor] = None, return_lists: bool = True,
+                workspace: Optional[torch.Tensor] = None, stream=None,
+                stage_events: Optional[B.StageEvents] = None) -> MoeOutput:
+    """Top-k MoE FFN forward.  x [..., H]; Wr [E, H] float32; Wg, Wu [E, I, H];
+    Wd [E, H, I].  Returns y (x's shape), topk_idx / alpha [N, k], aux_loss [1]
+    and, when ``return_lists``, expert_offsets [E+1] and sorted_token_ids [N*k]."""
+    dev = x.device
+    H = x.shape[-1]
+    E, I = Wg.shape[0], Wg.shape[1]
+    xf = x.reshape(-1, H)
+    N = xf.shape[0]
+    dt = x.dtype
+    _need(xf, "x", (N, H), dt, dev)
+    _need(Wr, "Wr", (E, H), torch.float32, dev)
+    _need(Wg, "Wg", (E, I, H), dt, dev)
+    _need(Wu, "Wu", (E, I, H), dt, dev)
+    _need(Wd, "Wd", (E, H, I), dt, dev)
+    new = lambda shape, d: torch.empty(shape, dtype=d, device=dev)
+    y = new((N, H), dt) if y is None else y
+    topk_idx = new((N, k), torch.int32) if topk_idx is None else topk_idx
+    alpha = new((N, k), torch.float32) if alpha is None else alpha
+    aux_loss = new((1,), torch.float32) if aux_loss is None else aux_loss
+    if return_lists:
+        expert_offsets = new((E + 1,), torch.int32) if expert_offsets is None else expert_offsets
+        sorted_token_ids = new((N * k,), torch.int32) if sorted_token_ids is None else sorted_token_ids
+    _need(y, "y", (N, H), dt, dev)
+    _need(topk_idx, "topk_idx", (N, k), torch.int32, dev)
+    _need(alpha, "alpha", (N, k), torch.float32, dev)
+    _need(aux_loss, "aux_loss", (1,), torch.float32, dev)
+    if expert_offsets is not None:
+        _need(expert_offsets, "expert_offsets", (E + 1,), torch.int32, dev)
+    if sorted_token_ids is not None:
+        _need(sorted_token_ids, "sorted_token_ids", (N * k,), torch.int32, dev)
+    code = _dtype_code(dt)
+    nbytes = B.raw_moe_workspace_bytes(N, H, I, E, k, code)
+    if nbytes == 0:
+        B.check(B.ERR_BAD_SHAPE, "moe_ffn_fwd")
+    ws = _workspace(nbytes, dev, workspace)
+    st = B.raw_moe_ffn_fwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), N, H, I, E, k,
+                           float(aux_coef), code, _ptr(y), _ptr(topk_idx), _ptr(alpha),
+                           _ptr(aux_loss), _ptr(expert_offsets), _ptr(sorted_token_ids),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
+                           stage_events.ptr if stage_events is not None else None)
+    B.check(st, "moe_ffn_fwd")
+    return MoeOutput(y.view(x.shape), topk_idx, alpha, aux_loss, expert_offsets, sorted_token_ids)
