@@ -36,7 +36,8 @@
  *                      rounded once (round-to-nearest-even).
  *   The router weight W_router is float32 in both, and routing is fp32.
  *
- * Shape limits: N >= 0 (N == 0 is a no-op apart from zeroed offsets and aux),
+ * Shape limits: N >= 0 (N == 0 is a no-op apart from zeroed offsets and aux;
+ * then x, y, topk_idx, alpha and sorted_token_ids may be NULL),
  * H and I positive multiples of 64, 1 <= E <= 64, 1 <= k <= E,
  * N * max(k, 1) < 2^31 and N * H, N * k * max(H, I) < 2^40.
  */

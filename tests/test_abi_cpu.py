@@ -82,6 +82,9 @@ def ffn_call(**over):
 
 def test_moe_validation_codes(L):
     assert moe_call(x=None) == B.ERR_NULL_ARG
+    # N == 0: the zero-size tensors may be NULL (validation reaches the workspace check)
+    assert moe_call(N=0, x=None, y=None, topk_idx=None, alpha=None) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_call(N=0, aux=None) == B.ERR_NULL_ARG
     assert moe_call(aux=None) == B.ERR_NULL_ARG
     assert moe_call(ws=None) == B.ERR_NULL_ARG
     assert moe_call(H=96) == B.ERR_BAD_SHAPE
@@ -104,6 +107,7 @@ def test_moe_validation_codes(L):
 
 def test_ffn_validation_codes(L):
     assert ffn_call(y=None) == B.ERR_NULL_ARG
+    assert ffn_call(N=0, x=None, y=None) == B.ERR_WORKSPACE_TOO_SMALL
     assert ffn_call(H=0) == B.ERR_BAD_SHAPE
     assert ffn_call(I=100) == B.ERR_BAD_SHAPE
     assert ffn_call(dtype=-1) == B.ERR_UNSUPPORTED_DTYPE

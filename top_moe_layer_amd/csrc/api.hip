@@ -77,7 +77,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   FfnPlan pl;
   const int st = plan_ffn(N, H, I, dtype, &pl);
   if (st != TOPMOE_OK) return st;
-  if (!x || !Wg || !Wu || !Wd || !y || !workspace) return TOPMOE_ERR_NULL_ARG;
+  // zero-size tensors (N == 0) are never touched and may be NULL
+  if (!Wg || !Wu || !Wd || !workspace || (N > 0 && (!x || !y))) return TOPMOE_ERR_NULL_ARG;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) ||
       !aligned(y, 16) || !aligned(workspace, 256))
@@ -116,7 +117,9 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   MoePlan pl;
   const int st = plan_moe(N, H, I, E, k, dtype, &pl);
   if (st != TOPMOE_OK) return st;
-  if (!x || !Wr || !Wg || !Wu || !Wd || !y || !topk_idx || !alpha || !aux_loss || !workspace)
+  // zero-size tensors (N == 0) are never touched and may be NULL
+  if (!Wr || !Wg || !Wu || !Wd || !aux_loss || !workspace ||
+      (N > 0 && (!x || !y || !topk_idx || !alpha)))
     return TOPMOE_ERR_NULL_ARG;
   if (!(aux_coef >= 0.0f) || isinf(aux_coef)) return TOPMOE_ERR_BAD_ARG;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
