@@ -10,10 +10,12 @@
 //
 // Block: 256 threads = 4 wavefronts in a 2 x 2 arrangement; block tile BM x BN
 // of every output matrix (two matrices, gate and up, for the first
-// projection), K stepped by one 128-byte row chunk (64 bf16 or 32 fp32).
-// Operands are staged global -> registers -> LDS with double buffering; the
-// 128-byte LDS rows keep their eight 16-byte chunks XOR-swizzled by (row & 7)
-// so the 16-byte fragment reads of a wavefront are bank-conflict free.
+// projection).  K advances in slices of one 128-byte row chunk (64 bf16 or 32
+// fp32).  Slices are fetched straight into an S-deep LDS ring with
+// global_load_lds_dwordx4 (no register staging), so up to S slices are in
+// flight while the MFMAs consume the oldest one.  LDS rows keep their eight
+// 16-byte chunks at slot chunk ^ ((row >> 1) & 7), which makes the 16-byte
+// fragment reads bank-conflict free on the 64-bank LDS.
 // MFMA: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32),
 // fp32 accumulation.
 //
@@ -62,21 +64,109 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-template <typename T, int BM, int BN, int KIND>
+// Scheduling hints for one MFMA region: spread NDS LDS operations (mask
+// DSMASK: 0x100 reads, 0x200 writes) over the first MFMAs of the region and
+// NVM global loads over all of them, so the memory pipes work while the MFMA
+// pipe is busy instead of before or after it.
+template <int I, int NMFMA, int NDS, int DSMASK, int NVM>
+struct Interleave {
+  __device__ static __forceinline__ void run() {
+    if constexpr (I < NMFMA) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      constexpr int spread = NMFMA > 1 ? (NMFMA + 1) / 2 : 1;  // LDS ops in the first half
+      constexpr int ds = (I < spread) ? ((I + 1) * NDS / spread - I * NDS / spread) : 0;
+      if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(DSMASK, ds, 0);
+      constexpr int vm = (I + 1) * NVM / NMFMA - I * NVM / NMFMA;
+      if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);
+      Interleave<I + 1, NMFMA, NDS, DSMASK, NVM>::run();
+    }
+  }
+};
+
+// One 16-byte-per-lane direct-to-LDS load (global_load_lds_dwordx4): lane i
+// writes lds + 16 i.  `lds` must be the same for every lane of the wavefront.
+// (Kept out of the kernel template: called directly from the template, the
+// target builtin suppresses the kernel's host launch stub.)
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt(N) and the other counters left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for data written to LDS by direct-to-LDS loads: every
+// wavefront first waits for its own loads (vmcnt) and its own LDS reads
+// (lgkmcnt, so no read of a slot is outstanding when it is refilled), then
+// s_barrier; the acquire fence keeps later LDS reads below the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 0xC00F);  // lgkmcnt(0), vm/exp at max
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <typename T, int BM, int BN, int S, int KIND>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
   constexpr int NB = KIND == KIND_GATEUP ? 2 : 1;
   constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wavefront
-  constexpr int AR = BM / 32, BR = BN / 32;  // 16-byte loads per thread per operand
+  constexpr int R = BM + NB * BN;            // LDS rows per slice: A, then B0 (, B1)
   constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  static_assert(TM >= 1 && TN >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-  __shared__ int s_tile[3];
+  constexpr int STAGE = R * 128;
+  constexpr int LPW = R / 32;                // 1 KB direct-to-LDS loads per wavefront per slice
+  static_assert(TM >= 1 && TN >= 1 && R % 32 == 0, "tile shape");
+  static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring exceeds 160 KB");
+  static_assert((S - 1) * LPW < 64, "vmcnt range");
+  // One __shared__ object per ring slot: the compiler then sees that LDS reads
+  // of one slot never alias direct-to-LDS loads into another and does not
+  // drain the load queue before each read.
+  __shared__ __attribute__((aligned(1024))) char ring0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring2[S > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char ring3[S > 3 ? STAGE : 16];
+  __shared__ int s_scan[64];
 
   const int tid = threadIdx.x;
   const int nt_count = (p.Nout + BN - 1) / BN;
-  const int nt = int(blockIdx.x % unsigned(nt_count));
-  const int mt = int(blockIdx.x / unsigned(nt_count));
+
+  // ---- number of real M tiles: per-group tile counts from the device-side
+  // offsets (grouped) or ceil(M / BM) (single group)
+  int total_mt;
+  if (p.offsets == nullptr) {
+    total_mt = int((p.M + BM - 1) / BM);
+  } else {
+    if (tid < 64) {
+      const int lane = tid;
+      int c = 0;
+      if (lane < p.E) c = p.offsets[lane + 1] - p.offsets[lane];
+      const int tiles = (c + BM - 1) / BM;
+      const int incl = wave_inclusive_scan(tiles, lane);
+      s_scan[lane] = incl;
+    }
+    __syncthreads();
+    total_mt = s_scan[p.E - 1];
+  }
+
+  // ---- XCD-aware work mapping.  Blocks are dispatched to the 8 XCDs round
+  // robin (block b runs on XCD b % 8), each with its own L2.  Give XCD x the
+  // contiguous range [x*per, (x+1)*per) of the real tiles, walked in groups of
+  // GM M-tiles (column by column inside a group), so the blocks resident on
+  // one XCD share their A rows and weight panels in that XCD's L2.  The grid
+  // is an upper bound rounded to a multiple of 8; blocks past the real work
+  // leave at once.
+  constexpr int GM = 8;
+  const int total = total_mt * nt_count;
+  const int per = (total + 7) >> 3;
+  const int local = int(blockIdx.x >> 3);
+  const int L = int(blockIdx.x & 7) * per + local;
+  if (local >= per || L >= total) return;
+  const int first_m = (L / (GM * nt_count)) * GM;
+  const int gsz = min(total_mt - first_m, GM);
+  const int in_group = L - first_m * nt_count;
+  const int mt = first_m + in_group % gsz;
+  const int nt = in_group / gsz;
 
   // ---- which group (expert) and rows this tile covers
   int e = 0;
@@ -87,81 +177,58 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
     const int64_t left = p.M - row0;
     rows = left < BM ? int(left) : BM;
   } else {
-    if (tid < 64) {
-      const int lane = tid;
-      int off = 0, c = 0;
-      if (lane < p.E) {
-        off = p.offsets[lane];
-        c = p.offsets[lane + 1] - off;
-      }
-      const int tiles = (c + BM - 1) / BM;
-      const int incl = wave_inclusive_scan(tiles, lane);
-      const uint64_t before = __ballot(lane < p.E && incl <= mt);
-      const int ge = __popcll(before);
-      if (lane == 0) s_tile[0] = ge;
-      if (lane == ge && ge < p.E) {
-        const int local = mt - (incl - tiles);
-        s_tile[1] = off + local * BM;
-        const int left = c - local * BM;
-        s_tile[2] = left < BM ? left : BM;
-      }
-    }
-    __syncthreads();
-    e = s_tile[0];
-    if (e >= p.E) return;  // past the last tile: the whole block leaves
-    row0 = s_tile[1];
-    rows = s_tile[2];
+    // expert = number of groups whose tiles all precede mt
+    int ge = 0;
+    for (int g = 0; g < p.E; ++g) ge += (s_scan[g] <= mt) ? 1 : 0;
+    e = ge;
+    const int tiles_before = ge > 0 ? s_scan[ge - 1] : 0;
+    const int off = p.offsets[ge];
+    const int c = p.offsets[ge + 1] - off;
+    const int local_t = mt - tiles_before;
+    row0 = off + int64_t(local_t) * BM;
+    const int left = c - local_t * BM;
+    rows = left < BM ? left : BM;
   }
   if (rows <= 0) return;
-
-  // ---- global source addresses (rows clamped into the valid range)
-  const int lc = tid & 7, lr = tid >> 3;
-  const char* a_src[AR];
-#pragma unroll
-  for (int i = 0; i < AR; ++i) {
-    const int r = lr + 32 * i;
-    const int64_t gr = row0 + (r < rows ? r : rows - 1);
-    int64_t arow = gr;
-    if (KIND == KIND_GATEUP && p.entries != nullptr) arow = p.entries[gr] / p.k;
-    a_src[i] = static_cast<const char*>(p.A) + (arow * p.K) * int64_t(sizeof(T)) + lc * 16;
-  }
   const int n0 = nt * BN;
-  const char* b_src[NB][BR];
+
+  // ---- direct-to-LDS load sources.  Wavefront w fills LDS row blocks
+  // w*LPW .. w*LPW+LPW-1 (8 rows = 1 KB each) of every slice.  Lane i of a
+  // load writes slot base + 16 i, i.e. row 8b + i/8, slot i%8; it therefore
+  // fetches logical chunk (i%8) ^ ((row >> 1) & 7) of that row.  Rows past the
+  // tile's valid rows / columns are clamped to the last valid one (in bounds,
+  // results discarded).
+  const int wid = tid >> 6, lane = tid & 63;
+  const char* src[LPW];
 #pragma unroll
-  for (int i = 0; i < BR; ++i) {
-    int n = n0 + lr + 32 * i;
-    n = n < p.Nout ? n : p.Nout - 1;
-    const int64_t off = ((int64_t(e) * p.Nout + n) * p.K) * int64_t(sizeof(T)) + lc * 16;
-    b_src[0][i] = static_cast<const char*>(p.B0) + off;
-    if (NB == 2) b_src[NB - 1][i] = static_cast<const char*>(p.B1) + off;
+  for (int j = 0; j < LPW; ++j) {
+    const int r = (wid * LPW + j) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    const char* base;
+    if (r < BM) {
+      const int64_t gr = row0 + (r < rows ? r : rows - 1);
+      int64_t arow = gr;
+      if (KIND == KIND_GATEUP && p.entries != nullptr) arow = p.entries[gr] / p.k;
+      base = static_cast<const char*>(p.A) + arow * p.K * int64_t(sizeof(T));
+    } else {
+      const int rb = r - BM;
+      const int which = rb >= BN ? 1 : 0;
+      int n = n0 + rb - which * BN;
+      n = n < p.Nout ? n : p.Nout - 1;
+      const void* W = which ? p.B1 : p.B0;
+      base = static_cast<const char*>(W) + (int64_t(e) * p.Nout + n) * p.K * int64_t(sizeof(T));
+    }
+    src[j] = base + chunk * 16;
   }
-  const int w_off = lr * 128 + ((lc ^ (lr & 7)) << 4);
-
-  u32x4 ra[AR], rb[NB][BR];
-  auto gload = [&](int kt) {
+  auto slot_ptr = [&](int slot) -> char* {
+    return slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
+  };
+  auto issue = [&](int kt, char* slot_base) {
     const int64_t ko = int64_t(kt) * 128;
+    char* dst = slot_base + wid * LPW * 1024;
 #pragma unroll
-    for (int i = 0; i < AR; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + ko);
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < BR; ++i) rb[b][i] = *reinterpret_cast<const u32x4*>(b_src[b][i] + ko);
+    for (int j = 0; j < LPW; ++j) lds_dma16(src[j] + ko, dst + j * 1024);
   };
-  auto lstore = [&](int stage) {
-    char* s = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < AR; ++i) *reinterpret_cast<u32x4*>(s + w_off + i * 4096) = ra[i];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < BR; ++i)
-        *reinterpret_cast<u32x4*>(s + A_BYTES + b * B_BYTES + w_off + i * 4096) = rb[b][i];
-  };
-
-  const int KT = p.K / Mfma<T>::BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
 
   f32x16 acc[NB][TM][TN];
 #pragma unroll
@@ -173,36 +240,95 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
 
-  const int wid = tid >> 6, lane = tid & 63;
   const int fr = lane & 31, fg = lane >> 5;
   const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
+  const int sw = (fr >> 1) & 7;
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const char* sA = smem + cur * STAGE;
+  // MFMA operand fragments, double-buffered in registers: the fragments of
+  // sub-step q + 1 are read from LDS while the MFMAs of sub-step q run.
+  u32x4 fa0[TM], fb0[NB][TN], fa1[TM], fb1[NB][TN];
+  auto frag_load = [&](const char* sb, int q, u32x4(&fa)[TM], u32x4(&fb)[NB][TN]) {
+    const int rd = ((2 * q + fg) ^ sw) << 4;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rd = ((2 * q + fg) ^ (fr & 7)) << 4;
-      u32x4 af[TM], bfr[NB][TN];
+    for (int i = 0; i < TM; ++i)
+      fa[i] = *reinterpret_cast<const u32x4*>(sb + (wm + 32 * i + fr) * 128 + rd);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        fb[b][j] = *reinterpret_cast<const u32x4*>(sb + A_BYTES + b * B_BYTES +
+                                                   (wn + 32 * j + fr) * 128 + rd);
+  };
+  auto mma_all = [&](const u32x4(&fa)[TM], const u32x4(&fb)[NB][TN]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(sA + (wm + 32 * i + fr) * 128 + rd);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[b][j] = *reinterpret_cast<const u32x4*>(sA + A_BYTES + b * B_BYTES +
-                                                      (wn + 32 * j + fr) * 128 + rd);
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) Mfma<T>::mma(acc[b][i][j], af[i], bfr[b][j]);
+        for (int j = 0; j < TN; ++j) Mfma<T>::mma(acc[b][i][j], fa[i], fb[b][j]);
+  };
+
+  constexpr int MF = NB * TM * TN * (sizeof(T) == 4 ? 4 : 1);  // MFMAs per sub-step
+  constexpr int DSR = TM + NB * TN;                            // LDS reads per sub-step
+  const int KT = p.K / Mfma<T>::BK;
+
+  // prologue: fill the ring, wait for slice 0
+  const int npro = KT < S ? KT : S;
+  for (int sl = 0; sl < npro; ++sl) issue(sl, slot_ptr(sl));
+  if (npro == S) wait_vmcnt<(S - 1) * LPW>();
+  else wait_vmcnt<0>();
+  ring_barrier();
+  frag_load(ring0, 0, fa0, fb0);
+
+  // One K slice (four MFMA sub-steps of 16 k), reading slot `cur`:
+  //   A, B, C: LDS reads of sub-step q+1 | MFMAs of sub-step q
+  //   wait for the next slice, barrier, refill `cur` with slice kt + S
+  //   D: LDS reads of the next slice's sub-step 0 (slot `nxt`) | MFMAs of sub-step 3
+  // In the tail (no slice left to fetch) the wait drains everything.
+  auto step = [&](int kt, bool tail, char* cur, char* nxt) {
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load(cur, 1, fa1, fb1);
+    mma_all(fa0, fb0);
+    Interleave<0, MF, DSR, 0x100, 0>::run();
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load(cur, 2, fa0, fb0);
+    mma_all(fa1, fb1);
+    Interleave<0, MF, DSR, 0x100, 0>::run();
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load(cur, 3, fa1, fb1);
+    mma_all(fa0, fb0);
+    Interleave<0, MF, DSR, 0x100, 0>::run();
+    __builtin_amdgcn_sched_barrier(0);
+    if (tail) wait_vmcnt<0>();
+    else wait_vmcnt<(S - 2) * LPW>();
+    ring_barrier();
+    if (!tail) issue(kt + S, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load(nxt, 0, fa0, fb0);
+    mma_all(fa1, fb1);
+    Interleave<0, MF, DSR, 0x100, 0>::run();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Steady state: groups of S steps with static slots (slice kt lives in slot
+  // kt % S) while every step of the group still has a slice to fetch.
+  int kt = 0;
+  for (; kt + 2 * S - 1 < KT; kt += S) {
+    step(kt, false, ring0, ring1);
+    if constexpr (S == 2) {
+      step(kt + 1, false, ring1, ring0);
+    } else if constexpr (S == 3) {
+      step(kt + 1, false, ring1, ring2);
+      step(kt + 2, false, ring2, ring0);
+    } else {
+      step(kt + 1, false, ring1, ring2);
+      step(kt + 2, false, ring2, ring3);
+      step(kt + 3, false, ring3, ring0);
     }
-    if (kt + 1 < KT) lstore(cur ^ 1);
-    __syncthreads();
+  }
+  // Remaining steps (fewer than 2S): slots chosen at run time.
+  for (; kt < KT; ++kt) {
+    const int sl = kt % S;
+    step(kt, kt + S >= KT, slot_ptr(sl), slot_ptr(sl + 1 == S ? 0 : sl + 1));
   }
 
   // ---- epilogue.  32x32 accumulator layout: lane (fr, fg), register v holds
@@ -244,22 +370,43 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
   }
 }
 
-template <typename T, int BM, int BN, int KIND>
+template <typename T, int BM, int BN, int S, int KIND>
 hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, hipStream_t s) {
   const int64_t nt = (p.Nout + BN - 1) / BN;
-  const int64_t grid = mtiles * nt;
-  if (grid <= 0) return hipSuccess;
+  const int64_t grid = (mtiles * nt + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+  if (mtiles * nt <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, KIND>), dim3(unsigned(grid)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, S, KIND>), dim3(unsigned(grid)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
+// The instantiated launch shapes (block tile BM x BN, LDS ring depth S).
+#define TOPMOE_GEMM_SHAPES(X) \
+  X(256, 128, 2) X(256, 128, 3) X(128, 128, 2) X(128, 128, 3) X(128, 128, 4) X(128, 64, 2) X(128, 64, 3) \
+  X(128, 64, 4) X(64, 64, 3) X(64, 64, 4)
+
+// Launches a shape only when its LDS ring fits in 160 KB (a plain
+// specialisation rather than if-constexpr, so every kernel that can be
+// launched is instantiated at namespace scope with its host stub).
+template <typename T, int BM, int BN, int S, int KIND,
+          bool FITS = (S * (BM + (KIND == KIND_GATEUP ? 2 : 1) * BN) * 128 <= 160 * 1024)>
+struct ShapeLauncher {
+  static hipError_t run(const GemmParams&, int64_t, hipStream_t) { return hipErrorInvalidValue; }
+};
+template <typename T, int BM, int BN, int S, int KIND>
+struct ShapeLauncher<T, BM, BN, S, KIND, true> {
+  static hipError_t run(const GemmParams& p, int64_t mtiles, hipStream_t s) {
+    return launch_gemm_t<T, BM, BN, S, KIND>(p, mtiles, s);
+  }
+};
+
 template <typename T, int KIND>
 hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, hipStream_t s) {
-  if (sh.bm == 256 && sh.bn == 128) return launch_gemm_t<T, 256, 128, KIND>(p, mtiles, s);
-  if (sh.bm == 128 && sh.bn == 128) return launch_gemm_t<T, 128, 128, KIND>(p, mtiles, s);
-  if (sh.bm == 128 && sh.bn == 64) return launch_gemm_t<T, 128, 64, KIND>(p, mtiles, s);
-  if (sh.bm == 64 && sh.bn == 64) return launch_gemm_t<T, 64, 64, KIND>(p, mtiles, s);
+#define TOPMOE_TRY_SHAPE(BM_, BN_, S_)                               \
+  if (sh.bm == (BM_) && sh.bn == (BN_) && sh.stages == (S_))        \
+    return ShapeLauncher<T, BM_, BN_, S_, KIND>::run(p, mtiles, s);
+  TOPMOE_GEMM_SHAPES(TOPMOE_TRY_SHAPE)
+#undef TOPMOE_TRY_SHAPE
   return hipErrorInvalidValue;
 }
 

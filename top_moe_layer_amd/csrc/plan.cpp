@@ -1,6 +1,9 @@
 // Host-side planning: validation, workspace layout, launch shapes.
 #include "plan.h"
 
+#include <cstdio>
+#include <cstdlib>
+
 #include "../../include/topmoe.h"
 
 namespace topmoe {
@@ -15,18 +18,17 @@ bool dtype_ok(int dtype) { return dtype == TOPMOE_DTYPE_FP32 || dtype == TOPMOE_
 int elem_bytes(int dtype) { return dtype == TOPMOE_DTYPE_FP32 ? 4 : 2; }
 
 struct Cand {
-  int bm, bn;
+  int bm, bn, stages;
   double eff;  // relative MFMA efficiency of one tile (bigger tiles reuse operands more)
 };
 
 // Pick the tile minimising (rounds of 256 CUs) x (cost of one tile).
 GemmShape choose(const Cand* cands, int n, int64_t M, int64_t Nout, int groups) {
-  GemmShape best{cands[n - 1].bm, cands[n - 1].bn};
+  GemmShape best{cands[n - 1].bm, cands[n - 1].bn, cands[n - 1].stages};
   double best_cost = -1.0;
   for (int i = 0; i < n; ++i) {
     const Cand& c = cands[i];
     int64_t mt = grouped_mtiles_bound(M, groups, c.bm);
-    // expected tiles: ceil per group is at most one extra tile per group
     int64_t nt = (Nout + c.bn - 1) / c.bn;
     int64_t tiles = mt * nt;
     if (tiles <= 0) continue;
@@ -34,24 +36,40 @@ GemmShape choose(const Cand* cands, int n, int64_t M, int64_t Nout, int groups) 
     double cost = double(rounds) * double(c.bm) * double(c.bn) / c.eff;
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
-      best = GemmShape{c.bm, c.bn};
+      best = GemmShape{c.bm, c.bn, c.stages};
     }
   }
   return best;
 }
 
+// "BMxBNxS" from the environment (launch-shape sweeps); must name an
+// instantiated shape, otherwise the launch reports an invalid value.
+bool env_shape(const char* name, GemmShape* out) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return false;
+  int bm = 0, bn = 0, st = 0;
+  if (std::sscanf(v, "%dx%dx%d", &bm, &bn, &st) != 3) return false;
+  *out = GemmShape{bm, bn, st};
+  return true;
+}
+
 }  // namespace
 
 GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int groups, int dtype) {
-  static const Cand c[] = {{256, 128, 1.0}, {128, 128, 0.85}, {128, 64, 0.65}, {64, 64, 0.45}};
+  // Measured on MI355X: tiles whose LDS ring lets two blocks share a CU win.
+  static const Cand c[] = {{128, 64, 2, 1.0}, {64, 64, 3, 0.8}};
   (void)dtype;
-  return choose(c, 4, M, Nout, groups);
+  GemmShape sh = choose(c, 2, M, Nout, groups);
+  env_shape("TOPMOE_GATEUP_TILE", &sh);
+  return sh;
 }
 
 GemmShape choose_down_tile(int64_t M, int64_t Nout, int groups, int dtype) {
-  static const Cand c[] = {{256, 128, 1.0}, {128, 128, 0.85}, {128, 64, 0.65}, {64, 64, 0.45}};
+  static const Cand c[] = {{128, 128, 2, 1.0}, {128, 64, 3, 0.9}, {64, 64, 4, 0.7}};
   (void)dtype;
-  return choose(c, 4, M, Nout, groups);
+  GemmShape sh = choose(c, 3, M, Nout, groups);
+  env_shape("TOPMOE_DOWN_TILE", &sh);
+  return sh;
 }
 
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {

@@ -12,9 +12,10 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
-// One GEMM launch shape: block tile BM x BN (per output matrix).
+// One GEMM launch shape: block tile BM x BN (per output matrix) and the
+// depth of the LDS ring of K slices.
 struct GemmShape {
-  int bm = 0, bn = 0;
+  int bm = 0, bn = 0, stages = 0;
 };
 
 struct FfnPlan {
