@@ -51,8 +51,7 @@ def stage_units(w):
     touched = min(E, rows)  # upper bound; exact count is reported from the run
     return {
         "router": (2.0 * N * H * E, N * H * el + E * H * 4 + N * k * 8),
-        "offsets_aux": (0.0, 0.0),
-        "scatter": (0.0, N * k * 4 * 2),
+        "permute": (0.0, N * k * 4 * 2),
         "gateup_gemm": (4.0 * rows * H * I, N * H * el + 2 * touched * I * H * el + rows * I * el),
         "down_gemm": (2.0 * rows * H * I, rows * I * el + touched * H * I * el + N * H * el),
         "combine": (0.0, (rows * H * 4 + N * H * el) if k > 1 else 0.0),

@@ -66,9 +66,9 @@ extern "C" {
 
 /* ---- stages (for stage_events) ------------------------------------------ */
 #define TOPMOE_FFN_STAGES 2  /* 0 gate/up GEMM + SiLU*up, 1 down GEMM                   */
-#define TOPMOE_MOE_STAGES 6  /* 0 router, 1 expert offsets + aux, 2 token scatter,
-                                3 grouped gate/up GEMM + SiLU*up, 4 grouped down GEMM
-                                + alpha, 5 combine of the k slots (empty when k == 1)   */
+#define TOPMOE_MOE_STAGES 5  /* 0 router, 1 expert offsets + aux + token scatter,
+                                2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
+                                + alpha, 4 combine of the k slots (empty when k == 1)   */
 
 /* Workspace needed by ffn_swiglu_fwd: the SiLU(g)*u intermediate [N, I]
  * (dtype-sized elements), 256-byte aligned.  Returns 0 for invalid shapes. */

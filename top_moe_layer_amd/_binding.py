@@ -23,10 +23,10 @@ ERR_BAD_ARG = -6
 DTYPE_FP32 = 0
 DTYPE_BF16 = 1
 FFN_STAGES = 2
-MOE_STAGES = 6
+MOE_STAGES = 5
 
 FFN_STAGE_NAMES = ["gateup_gemm", "down_gemm"]
-MOE_STAGE_NAMES = ["router", "offsets_aux", "scatter", "gateup_gemm", "down_gemm", "combine"]
+MOE_STAGE_NAMES = ["router", "permute", "gateup_gemm", "down_gemm", "combine"]
 
 # Every function include/topmoe.h declares, with its ctypes signature.
 _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float

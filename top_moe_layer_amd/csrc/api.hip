@@ -134,7 +134,6 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   char* ws = static_cast<char*>(workspace);
   int32_t* count_part = reinterpret_cast<int32_t*>(ws + pl.off_count_part);
   float* psum_part = reinterpret_cast<float*>(ws + pl.off_psum_part);
-  int32_t* blk_off = reinterpret_cast<int32_t*>(ws + pl.off_blk_off);
   int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(ws + pl.off_offsets);
   int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
   void* h = ws + pl.off_h;
@@ -150,35 +149,31 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
 
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   TOPMOE_TRY(ev.rec(0));
-  TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, pl.tb, pl.nblk, topk_idx, alpha,
-                           count_part, psum_part, s));
-  // 1: expert offsets, per-block scatter bases, aux loss
+  TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, pl.tb, pl.nblk, pl.router_mode,
+                           topk_idx, alpha, count_part, psum_part, s));
+  // 1: expert offsets, aux loss, stable scatter of entries into expert groups
   TOPMOE_TRY(ev.rec(1));
-  TOPMOE_TRY(launch_offsets_aux(count_part, psum_part, pl.nblk, E, N, aux_coef, blk_off,
-                                offsets, aux_loss, s));
-  // 2: stable scatter of entries into expert groups
+  TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, pl.nblk, E, k, pl.tb, N, aux_coef,
+                            offsets, aux_loss, sorted_entry, sorted_token_ids, s));
+  // 2: grouped gate/up GEMM + SiLU * up
   TOPMOE_TRY(ev.rec(2));
-  TOPMOE_TRY(launch_scatter(topk_idx, blk_off, N, E, k, pl.tb, pl.nblk, sorted_entry,
-                            sorted_token_ids, s));
-  // 3: grouped gate/up GEMM + SiLU * up
-  TOPMOE_TRY(ev.rec(3));
   GemmParams up{};
   up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
   up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
   up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
   TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, s));
-  // 4: grouped down GEMM, alpha-scaled, into y (k == 1) or the k slots
-  TOPMOE_TRY(ev.rec(4));
+  // 3: grouped down GEMM, alpha-scaled, into y (k == 1) or the k slots
+  TOPMOE_TRY(ev.rec(3));
   GemmParams dn{};
   dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : static_cast<void*>(slots);
   dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
                          pl.down_mtiles, s));
-  // 5: fixed-order combine of the k slots
-  TOPMOE_TRY(ev.rec(5));
+  // 4: fixed-order combine of the k slots
+  TOPMOE_TRY(ev.rec(4));
   if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, N, int(H), k, dtype, y, s));
-  TOPMOE_TRY(ev.rec(6));
+  TOPMOE_TRY(ev.rec(5));
   return TOPMOE_OK;
 }
 

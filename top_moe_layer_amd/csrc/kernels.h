@@ -27,16 +27,18 @@ struct GemmParams {
   int Nout, K;
 };
 
+enum RouterMode {
+  ROUTER_MODE_LDS = 0,    // W_router staged in LDS, one token per wavefront
+  ROUTER_MODE_SPLIT = 1,  // one token per block, H split over the wavefronts
+};
+
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
-                         int k, int tb, int nblk, int32_t* topk_idx, float* alpha,
+                         int k, int tb, int nblk, int mode, int32_t* topk_idx, float* alpha,
                          int32_t* count_part, float* psum_part, hipStream_t s);
 
-hipError_t launch_offsets_aux(const int32_t* count_part, const float* psum_part, int nblk,
-                              int E, int64_t N, float coef, int32_t* blk_off,
-                              int32_t* offsets, float* aux, hipStream_t s);
-
-hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_off, int64_t N, int E,
-                          int k, int tb, int nblk, int32_t* sorted_entry,
+hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
+                          const int32_t* topk_idx, int nblk, int E, int k, int tb, int64_t N,
+                          float coef, int32_t* offsets, float* aux, int32_t* sorted_entry,
                           int32_t* sorted_tok, hipStream_t s);
 
 hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,

@@ -5,12 +5,11 @@
 // order (mask / nonzero), runs the expert on those rows and adds the weighted
 // rows back with index_add_.  Here the same grouping is built once, without a
 // host round trip:
-//   * offsets_aux: per-expert totals c_e and their exclusive prefix sum
-//     (expert offsets), per-block scatter bases, and the aux loss
-//     aux = E * coef * sum_e (c_e / N) * (sum_t p_{t,e} / N)
-//     (lesson 13, section 1.6 equation; walkthrough step 6);
-//   * scatter: a stable scatter of the entries (t, j) in t*k + j order into
-//     expert groups, so each group lists its tokens in ascending order;
+//   * permute: per-expert totals c_e and their exclusive prefix sum (expert
+//     offsets), the aux loss aux = E * coef * sum_e (c_e / N) * (sum_t p_{t,e} / N)
+//     (lesson 13, section 1.6 equation; walkthrough step 6), and a stable
+//     scatter of the entries (t, j) in t*k + j order into expert groups, so
+//     each group lists its tokens in ascending order;
 //   * combine: y_t = sum of the k alpha-scaled expert rows in ascending expert
 //     id, accumulated in fp32 and rounded once.
 // All integer work is exact; the only float reductions run in a fixed order.
@@ -29,95 +28,101 @@ __device__ __forceinline__ int wave_sum_int(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(1024) void offsets_aux_kernel(
-    const int32_t* __restrict__ count_part, const float* __restrict__ psum_part, int nblk,
-    int E, int64_t N, float coef, int32_t* __restrict__ blk_off, int32_t* __restrict__ offsets,
-    float* __restrict__ aux) {
-  __shared__ int s_cnt[64];
-  __shared__ double s_ps[64];
-  __shared__ int s_off[65];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int WAVES = 1024 / 64;
+// Offsets, aux loss and scatter in one launch.  count_part / psum_part are
+// expert-major [E, nblk] (nblk router blocks, E * nblk <= 8192).  Scatter
+// block s owns router blocks [s*G, s*G + G): it stages all counts in LDS,
+// derives every expert's total and the count of entries in router blocks
+// before its own, and so its base slot per expert; it then ranks its entries
+// (t*k + j order) among equal experts with wavefront ballots.  Block 0 also
+// writes the expert offsets and the aux loss (sums of p in a fixed order).
+constexpr int kScanMax = 8192;
 
-  // pass 1: per-expert totals (counts exact; sums of p in a fixed order, fp64)
-  for (int e = wave; e < E; e += WAVES) {
-    int c = 0;
+__global__ __launch_bounds__(256) void permute_kernel(
+    const int32_t* __restrict__ count_part, const float* __restrict__ psum_part,
+    const int32_t* __restrict__ topk_idx, int nblk, int G, int E, int k, int tb, int64_t N,
+    float coef, int32_t* __restrict__ offsets, float* __restrict__ aux,
+    int32_t* __restrict__ sorted_entry, int32_t* __restrict__ sorted_tok) {
+  __shared__ int s_c[kScanMax];
+  __shared__ float s_p[kScanMax];  // block 0 only
+  __shared__ int s_tot[64];
+  __shared__ int s_base[64];
+  __shared__ double s_ps[64];
+  __shared__ int run[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool first = blockIdx.x == 0;
+  const int total = E * nblk;
+  // one batch of independent loads: all counts (and, in block 0, all sums of p)
+  for (int i = tid; i < total; i += 256) {
+    s_c[i] = count_part[i];
+    if (first) s_p[i] = psum_part[i];
+  }
+  if (tid < 64) run[tid] = 0;
+  __syncthreads();
+
+  const int bfirst = int(blockIdx.x) * G;
+  for (int e = wave; e < E; e += 4) {
+    int tot = 0, pre = 0;
     double ps = 0.0;
     for (int b = lane; b < nblk; b += 64) {
-      c += count_part[int64_t(b) * E + e];
-      ps += double(psum_part[int64_t(b) * E + e]);
+      const int c = s_c[e * nblk + b];
+      tot += c;
+      pre += b < bfirst ? c : 0;
+      if (first) ps += double(s_p[e * nblk + b]);
     }
-    c = wave_sum_int(c);
-    ps = wave_sum(ps);
-    if (lane == 0) { s_cnt[e] = c; s_ps[e] = ps; }
+    tot = wave_sum_int(tot);
+    pre = wave_sum_int(pre);
+    if (first) ps = wave_sum(ps);
+    if (lane == 0) { s_tot[e] = tot; s_base[e] = pre; s_ps[e] = ps; }
   }
   __syncthreads();
 
   if (wave == 0) {
-    const int c = lane < E ? s_cnt[lane] : 0;
+    const int c = lane < E ? s_tot[lane] : 0;
     const int incl = wave_inclusive_scan(c, lane);
-    if (lane < E) s_off[lane] = incl - c;
-    if (lane == E - 1) s_off[E] = incl;
-    double term = lane < E ? double(c) * s_ps[lane] : 0.0;
-    term = wave_sum(term);
-    if (lane == 0) {
-      float a = 0.f;
-      if (coef != 0.f && N > 0) a = float(double(E) * double(coef) * term / (double(N) * double(N)));
-      *aux = a;
+    if (lane < E) s_base[lane] += incl - c;  // expert offset + entries of earlier blocks
+    if (first) {
+      if (lane < E) offsets[lane] = incl - c;
+      if (lane == E - 1) offsets[E] = incl;
+      // aux = E * coef * sum_e c_e * (sum_t p_{t,e}) / N^2 (fixed summation order)
+      double term = lane < E ? double(c) * s_ps[lane] : 0.0;
+      term = wave_sum(term);
+      if (lane == 0) {
+        float a = 0.f;
+        if (coef != 0.f && N > 0) a = float(double(E) * double(coef) * term / (double(N) * double(N)));
+        *aux = a;
+      }
     }
   }
   __syncthreads();
-  if (tid <= E) offsets[tid] = s_off[tid];
 
-  // pass 2: per-block exclusive scan of each expert's counts, plus its offset
-  for (int e = wave; e < E; e += WAVES) {
-    int run = s_off[e];
-    for (int b0 = 0; b0 < nblk; b0 += 64) {
-      const int b = b0 + lane;
-      const int c = b < nblk ? count_part[int64_t(b) * E + e] : 0;
-      const int incl = wave_inclusive_scan(c, lane);
-      if (b < nblk) blk_off[int64_t(b) * E + e] = run + incl - c;
-      run += __shfl(incl, 63, 64);
+  if (wave == 0) {
+    const int64_t tok0 = int64_t(bfirst) * tb;
+    int64_t tok1 = tok0 + int64_t(G) * tb;
+    tok1 = tok1 < N ? tok1 : N;
+    const int64_t e0 = tok0 * k, e1 = tok1 * k;
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t base = e0; base < e1; base += 64) {
+      const int64_t ent = base + lane;
+      const bool valid = ent < e1;
+      const int ex = valid ? topk_idx[ent] : -1;
+      uint64_t peers = 0ull;  // lanes holding the same expert
+      uint64_t todo = __ballot(valid);
+      while (todo) {
+        const int leader = __ffsll((long long)todo) - 1;
+        const int le = __shfl(ex, leader, 64);
+        const uint64_t m = __ballot(valid && ex == le);
+        if (valid && ex == le) peers = m;
+        todo &= ~m;
+      }
+      if (valid) {
+        const int dest = s_base[ex] + run[ex] + __popcll(peers & lt_mask);
+        sorted_entry[dest] = int32_t(ent);
+        if (sorted_tok) sorted_tok[dest] = int32_t(ent / k);
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (peers & lt_mask) == 0ull) run[ex] += __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
     }
-  }
-}
-
-// One wavefront per router block: ranks each entry among the same-expert
-// entries of its block (in t*k + j order) and writes it to its group slot.
-__global__ __launch_bounds__(64) void scatter_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ blk_off, int64_t N, int E,
-    int k, int tb, int32_t* __restrict__ sorted_entry, int32_t* __restrict__ sorted_tok) {
-  __shared__ int run[64];
-  const int lane = threadIdx.x;
-  run[lane] = 0;
-  __syncthreads();
-  const int64_t tok0 = int64_t(blockIdx.x) * tb;
-  const int64_t tok1 = (tok0 + tb < N) ? tok0 + tb : N;
-  const int64_t e0 = tok0 * k, e1 = tok1 * k;
-  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = e0; base < e1; base += 64) {
-    const int64_t ent = base + lane;
-    const bool valid = ent < e1;
-    const int ex = valid ? topk_idx[ent] : -1;
-    // lanes holding the same expert
-    uint64_t peers = 0ull;
-    uint64_t todo = __ballot(valid);
-    while (todo) {
-      const int leader = __ffsll((long long)todo) - 1;
-      const int le = __shfl(ex, leader, 64);
-      const uint64_t m = __ballot(valid && ex == le);
-      if (valid && ex == le) peers = m;
-      todo &= ~m;
-    }
-    int dest = 0;
-    if (valid) {
-      dest = blk_off[int64_t(blockIdx.x) * E + ex] + run[ex] + __popcll(peers & lt_mask);
-      sorted_entry[dest] = int32_t(ent);
-      if (sorted_tok) sorted_tok[dest] = int32_t(ent / k);
-    }
-    __syncthreads();
-    if (valid && (peers & lt_mask) == 0ull) run[ex] += __popcll(peers);
-    __syncthreads();
   }
 }
 
@@ -172,20 +177,16 @@ __global__ void empty_route_kernel(int E, int32_t* offsets, float* aux) {
 
 }  // namespace
 
-hipError_t launch_offsets_aux(const int32_t* count_part, const float* psum_part, int nblk,
-                              int E, int64_t N, float coef, int32_t* blk_off,
-                              int32_t* offsets, float* aux, hipStream_t s) {
-  hipLaunchKernelGGL(offsets_aux_kernel, dim3(1), dim3(1024), 0, s, count_part, psum_part,
-                     nblk, E, N, coef, blk_off, offsets, aux);
-  return hipGetLastError();
-}
-
-hipError_t launch_scatter(const int32_t* topk_idx, const int32_t* blk_off, int64_t N, int E,
-                          int k, int tb, int nblk, int32_t* sorted_entry,
+hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
+                          const int32_t* topk_idx, int nblk, int E, int k, int tb, int64_t N,
+                          float coef, int32_t* offsets, float* aux, int32_t* sorted_entry,
                           int32_t* sorted_tok, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_kernel, dim3(nblk), dim3(64), 0, s, topk_idx, blk_off, N, E, k,
-                     tb, sorted_entry, sorted_tok);
+  if (int64_t(E) * nblk > kScanMax) return hipErrorInvalidValue;
+  const int G = nblk > 256 ? (nblk + 255) / 256 : 1;  // router blocks per scatter block
+  const int nsb = (nblk + G - 1) / G;
+  hipLaunchKernelGGL(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part, topk_idx,
+                     nblk, G, E, k, tb, N, coef, offsets, aux, sorted_entry, sorted_tok);
   return hipGetLastError();
 }
 

@@ -99,10 +99,20 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   MoePlan q;
   q.N = N; q.H = H; q.I = I; q.E = E; q.k = k; q.dtype = dtype; q.elem = elem_bytes(dtype);
   q.rows = rows;
-  // Router: one token per wavefront, 4 wavefronts per block; at most 4096
-  // blocks so the single-block offset scan stays short.
-  int64_t tb = 16;
-  while (N > 0 && (N + tb - 1) / tb > 4096) tb *= 2;
+  // Router.  W_router in LDS (<= 64 KB, so two blocks share a CU) with one
+  // token per wavefront when there are tokens enough to fill the chip;
+  // otherwise every block splits each of its tokens over its 4 wavefronts.
+  // Tokens per block: enough blocks to cover the 256 CUs, at most 4096 blocks
+  // so the single-block offset scan stays short.
+  int ep = 1;
+  while (ep < E) ep *= 2;
+  const bool lds_fits = int64_t(ep) * H * 4 <= 64 * 1024 && H <= 2048;
+  q.router_mode = (lds_fits && N >= 4096) ? 0 : 1;
+  // mode 0: about 1024 blocks of whole-wavefront token groups (multiples of 4)
+  int64_t tb = q.router_mode == 0 ? 4 : 1;
+  while (q.router_mode == 0 && (N + tb - 1) / tb > 1024) tb += 4;
+  // the permutation kernel stages E * blocks counts in LDS: at most 8192
+  while (N > 0 && ((N + tb - 1) / tb) * E > 8192) tb *= 2;
   q.tb = int(tb);
   q.nblk = int((N + tb - 1) / tb);
   q.up = choose_gateup_tile(rows, I, E, dtype);
@@ -113,7 +123,6 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   const size_t nbe = size_t(q.nblk) * size_t(E);
   q.off_count_part = o; o = align_up(o + nbe * 4);
   q.off_psum_part = o;  o = align_up(o + nbe * 4);
-  q.off_blk_off = o;    o = align_up(o + nbe * 4);
   q.off_offsets = o;    o = align_up(o + size_t(E + 1) * 4);
   q.off_sorted = o;     o = align_up(o + size_t(rows) * 4);
   q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);

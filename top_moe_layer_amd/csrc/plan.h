@@ -34,13 +34,13 @@ struct MoePlan {
   int64_t rows = 0;        // N * k expert rows
   int tb = 0;              // router / scatter tokens per block
   int nblk = 0;            // router / scatter blocks
+  int router_mode = 0;     // 0: W_router in LDS, token per wavefront; 1: H split per token
   GemmShape up, down;
   int64_t up_mtiles = 0;   // upper bound on grouped M tiles (gate/up)
   int64_t down_mtiles = 0; // upper bound on grouped M tiles (down)
   // workspace layout (byte offsets)
-  size_t off_count_part = 0;  // int32 [nblk, E] per-block expert counts
-  size_t off_psum_part = 0;   // f32   [nblk, E] per-block sums of p
-  size_t off_blk_off = 0;     // int32 [nblk, E] scatter base per block and expert
+  size_t off_count_part = 0;  // int32 [E, nblk] per-block expert counts
+  size_t off_psum_part = 0;   // f32   [E, nblk] per-block sums of p
   size_t off_offsets = 0;     // int32 [E+1] expert offsets (when the caller passes none)
   size_t off_sorted = 0;      // int32 [N*k] entry ids (t*k + j) grouped by expert
   size_t off_h = 0;           // elem  [N*k, I] SiLU(g)*u in grouped row order
