@@ -36,6 +36,34 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+GEMM_SOURCES = ["top_moe_layer_amd/csrc/gemm_impl.h", "top_moe_layer_amd/csrc/gemm_bf16.hip",
+                "top_moe_layer_amd/csrc/plan.cpp"]
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters and
+    stored in profiles/traffic.json; None if absent or if the GEMM sources
+    have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh).get(workload, {}).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def stage_units(w):
     """Algorithmic work of each stage of one forward: (flops, bytes).  Bytes
     count each tensor the stage must read or write once; re-reads, the h round
@@ -58,8 +86,10 @@ def stage_units(w):
     }
 
 
-def cpu_baseline(w, inputs, budget_s=12.0):
-    """Time the fp64 oracle (as it stands) on a bounded token sample."""
+def cpu_baseline(w, inputs, budget_s=10.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
+    the first n tokens (n grown by 4x until one pass takes a quarter of the
+    budget, at most all N), repeated until the budget is spent."""
     import numpy as np
     from oracle.cases import widen
     from oracle import dense_ffn, moe_ffn, moe_route
@@ -70,12 +100,6 @@ def cpu_baseline(w, inputs, budget_s=12.0):
     except Exception:
         threads = os.cpu_count() or 1
     f = widen(inputs)
-    route = None
-    t_route = 0.0
-    if w.kind == "moe":
-        t0 = time.perf_counter()
-        route = moe_route(f["x"], f["Wr"], w.k, w.coef)
-        t_route = time.perf_counter() - t0
 
     def run(n):
         rows = np.arange(n)
@@ -83,7 +107,13 @@ def cpu_baseline(w, inputs, budget_s=12.0):
         if w.kind == "dense":
             dense_ffn(f["x"], f["Wg"], f["Wu"], f["Wd"], rows=rows)
         else:
+            # routing always covers all N tokens (aux and the lists need them);
+            # it is charged pro rata to the n tokens whose outputs are computed
+            t1 = time.perf_counter()
+            route = moe_route(f["x"], f["Wr"], w.k, w.coef)
+            tr = time.perf_counter() - t1
             moe_ffn(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], w.k, w.coef, rows=rows, route=route)
+            return time.perf_counter() - t0 - tr + tr * n / w.N
         return time.perf_counter() - t0
 
     n = min(w.N, 64)
@@ -91,16 +121,17 @@ def cpu_baseline(w, inputs, budget_s=12.0):
     while n < w.N and dt < budget_s / 4:
         n = min(w.N, n * 4)
         dt = run(n)
-    # routing of all N tokens is charged pro rata to the sample
-    dt_total = dt + t_route * n / w.N
+    reps, total = 1, dt
+    while total < budget_s:
+        total += run(n)
+        reps += 1
     return {
-        "value": n / dt_total,
+        "value": n * reps / total,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle on the first {n} of {w.N} tokens of {w.name}"
-                  + (" (routing of all tokens timed and charged pro rata)" if w.kind == "moe" else "")
-                  + f"; {dt_total:.2f} s",
+        "sample": f"fp64 numpy oracle, first {n} of {w.N} tokens of {w.name}, {reps} passes, "
+                  f"{total:.1f} s" + (" (routing of all tokens charged pro rata)" if w.kind == "moe" else ""),
     }
 
 
@@ -113,6 +144,8 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="flush L2 and the Infinity Cache before each step; time steps one by one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device-to-device copies of BYTES (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -130,6 +163,14 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 5}), flush=True)
+        return
     w = get(args.workload)
     log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype}")
     inputs = make_inputs(w)
@@ -231,12 +272,14 @@ def main():
     if decode_like:
         achieved = dbytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": recorded_traffic(w.name, dom),
                 "algorithmic_bytes": dbytes, "avg_launch_ms": dom_ms}
     else:
         achieved = dflops / (dom_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": recorded_traffic(w.name, dom),
                 "algorithmic_flops": dflops, "avg_launch_ms": dom_ms}
 
     result = {
