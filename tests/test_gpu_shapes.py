@@ -1,0 +1,67 @@
+"""Every instantiated GEMM launch shape (block tile, wavefront grid, LDS row
+bytes, ring depth), forced through the planner's override, against the fp64
+oracle on dense and MoE cases with ragged tails."""
+import os
+
+import pytest
+
+from oracle.cases import custom_workload, expected, make_case
+from gpu_util import TOL_Y, announce, check_routing, rel_l2_per_token, run_dense, run_moe, to_dev, torch_dev, y_to_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_SHAPES = [
+    "128x64x2x2x128x2", "128x64x2x2x128x3", "128x64x2x2x64x4",
+    "128x128x2x2x128x2", "128x128x2x2x128x3", "128x128x2x2x64x4",
+    "64x64x2x2x128x3", "64x64x2x2x128x4",
+    "256x128x4x2x64x4", "256x128x4x2x64x3", "256x256x4x2x64x4",
+    "128x128x2x4x64x4", "256x128x4x2x128x2",
+]
+# shapes whose LDS ring does not fit for the gate/up projection (two weight panels)
+GATEUP_TOO_BIG = {"128x128x2x2x128x3", "256x256x4x2x64x4"}
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch, dev = torch_dev()
+    import top_moe_layer_amd as tm
+
+    tm.lib()
+    return torch, dev, tm
+
+
+@pytest.fixture
+def shape_env():
+    saved = {k: os.environ.get(k) for k in ("TOPMOE_GATEUP_TILE", "TOPMOE_DOWN_TILE")}
+    yield
+    for k, v in saved.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES)
+def test_shape_dense_and_moe(env, shape_env, shape):
+    torch, dev, tm = env
+    if shape not in GATEUP_TOO_BIG:
+        os.environ["TOPMOE_GATEUP_TILE"] = shape
+    os.environ["TOPMOE_DOWN_TILE"] = shape
+    w = custom_workload(name="shape_dense", kind="dense", N=777, H=320, I=448, E=1, k=1,
+                        coef=0.0, dtype="bf16", seed=11)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"ffn_swiglu_fwd shape {shape} N=777 H=320 I=448")
+    y = run_dense(tm, to_dev(inp, dev))
+    torch.cuda.synchronize()
+    assert rel_l2_per_token(y_to_f64(y), ref["y"]) <= TOL_Y["bf16"]
+
+    w = custom_workload(name="shape_moe", N=1500, H=256, I=320, E=6, k=2, coef=0.01,
+                        dtype="bf16", seed=12)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"moe_ffn_fwd shape {shape} N=1500 H=256 I=320 E=6 k=2")
+    out = run_moe(tm, to_dev(inp, dev), w)
+    torch.cuda.synchronize()
+    check_routing(out, ref, w.k, w.E)
+    assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y["bf16"]

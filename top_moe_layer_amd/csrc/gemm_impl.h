@@ -8,14 +8,17 @@
 // work items whose group boundaries it reads from the device-side expert
 // offsets, so no host synchronisation is needed.
 //
-// Block: 256 threads = 4 wavefronts in a 2 x 2 arrangement; block tile BM x BN
-// of every output matrix (two matrices, gate and up, for the first
-// projection).  K advances in slices of one 128-byte row chunk (64 bf16 or 32
-// fp32).  Slices are fetched straight into an S-deep LDS ring with
-// global_load_lds_dwordx4 (no register staging), so up to S slices are in
-// flight while the MFMAs consume the oldest one.  LDS rows keep their eight
-// 16-byte chunks at slot chunk ^ ((row >> 1) & 7), which makes the 16-byte
-// fragment reads bank-conflict free on the 64-bank LDS.
+// Block: WM x WN wavefronts; block tile BM x BN of every output matrix (two
+// matrices, gate and up, for the first projection).  K advances in slices of
+// RB bytes per row (RB / sizeof(T) elements).  Slices are fetched straight
+// into an S-deep LDS ring with global_load_lds_dwordx4 (no register staging),
+// so up to S slices are in flight while the MFMAs consume the oldest one.
+// LDS rows keep their 16-byte chunks at slot chunk ^ ((row / (256 / RB)) % CH)
+// (CH chunks per row), which makes the 16-byte fragment reads bank-conflict
+// free on the 64-bank LDS.  Arithmetic intensity against the L2 -> LDS
+// traffic is BM*BN*NB / (BM + NB*BN) flop per byte, which is what bounds these
+// kernels on MI355X; the 8-wavefront 256-row tiles double it over 4-wavefront
+// 128-row tiles while keeping two wavefronts per SIMD.
 // MFMA: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32),
 // fp32 accumulation.
 //
@@ -108,15 +111,23 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <typename T, int BM, int BN, int S, int KIND>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   constexpr int NB = KIND == KIND_GATEUP ? 2 : 1;
-  constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wavefront
+  constexpr int NW = WM * WN;                // wavefronts: WM along rows x WN along columns
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wavefront and matrix
   constexpr int R = BM + NB * BN;            // LDS rows per slice: A, then B0 (, B1)
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
-  constexpr int STAGE = R * 128;
-  constexpr int LPW = R / 32;                // 1 KB direct-to-LDS loads per wavefront per slice
-  static_assert(TM >= 1 && TN >= 1 && R % 32 == 0, "tile shape");
+  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int STAGE = R * RB;
+  constexpr int CH = RB / 16;                // 16-byte chunks per LDS row
+  constexpr int RPW = 256 / RB;              // rows per 256-byte bank window
+  constexpr int RPI = 1024 / RB;             // rows per 1 KB direct-to-LDS load
+  constexpr int LPW = R / RPI / NW;          // direct-to-LDS loads per wavefront per slice
+  constexpr int QS = RB / 32;                // MFMA sub-steps per slice
+  static_assert(RB == 64 || RB == 128, "row bytes");
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
+  static_assert((R / RPI) % NW == 0 && LPW >= 1, "slice rows must split evenly over wavefronts");
   static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert((S - 1) * LPW < 64, "vmcnt range");
   // One __shared__ object per ring slot: the compiler then sees that LDS reads
@@ -193,17 +204,17 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
   const int n0 = nt * BN;
 
   // ---- direct-to-LDS load sources.  Wavefront w fills LDS row blocks
-  // w*LPW .. w*LPW+LPW-1 (8 rows = 1 KB each) of every slice.  Lane i of a
-  // load writes slot base + 16 i, i.e. row 8b + i/8, slot i%8; it therefore
-  // fetches logical chunk (i%8) ^ ((row >> 1) & 7) of that row.  Rows past the
+  // w*LPW .. w*LPW+LPW-1 (RPI rows = 1 KB each) of every slice.  Lane i of a
+  // load writes slot base + 16 i, i.e. row RPI*b + i/CH, slot i%CH; it
+  // therefore fetches logical chunk (i%CH) ^ swizzle(row).  Rows past the
   // tile's valid rows / columns are clamped to the last valid one (in bounds,
   // results discarded).
   const int wid = tid >> 6, lane = tid & 63;
   const char* src[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
-    const int r = (wid * LPW + j) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = (wid * LPW + j) * RPI + lane / CH;
+    const int chunk = (lane % CH) ^ ((r / RPW) % CH);
     const char* base;
     if (r < BM) {
       const int64_t gr = row0 + (r < rows ? r : rows - 1);
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
     return slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
   };
   auto issue = [&](int kt, char* slot_base) {
-    const int64_t ko = int64_t(kt) * 128;
+    const int64_t ko = int64_t(kt) * RB;
     char* dst = slot_base + wid * LPW * 1024;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) lds_dma16(src[j] + ko, dst + j * 1024);
@@ -241,8 +252,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
         for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
 
   const int fr = lane & 31, fg = lane >> 5;
-  const int wm = (wid >> 1) * (BM / 2), wn = (wid & 1) * (BN / 2);
-  const int sw = (fr >> 1) & 7;
+  const int wm = (wid / WN) * WTM, wn = (wid % WN) * WTN;
+  const int sw = (fr / RPW) % CH;  // row swizzle (32-row fragment blocks keep it)
 
   // MFMA operand fragments, double-buffered in registers: the fragments of
   // sub-step q + 1 are read from LDS while the MFMAs of sub-step q run.
@@ -251,13 +262,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
     const int rd = ((2 * q + fg) ^ sw) << 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      fa[i] = *reinterpret_cast<const u32x4*>(sb + (wm + 32 * i + fr) * 128 + rd);
+      fa[i] = *reinterpret_cast<const u32x4*>(sb + (wm + 32 * i + fr) * RB + rd);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         fb[b][j] = *reinterpret_cast<const u32x4*>(sb + A_BYTES + b * B_BYTES +
-                                                   (wn + 32 * j + fr) * 128 + rd);
+                                                   (wn + 32 * j + fr) * RB + rd);
   };
   auto mma_all = [&](const u32x4(&fa)[TM], const u32x4(&fb)[NB][TN]) {
 #pragma unroll
@@ -270,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
 
   constexpr int MF = NB * TM * TN * (sizeof(T) == 4 ? 4 : 1);  // MFMAs per sub-step
   constexpr int DSR = TM + NB * TN;                            // LDS reads per sub-step
-  const int KT = p.K / Mfma<T>::BK;
+  const int KT = p.K / (RB / int(sizeof(T)));
 
   // prologue: fill the ring, wait for slice 0
   const int npro = KT < S ? KT : S;
@@ -280,10 +291,10 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
   ring_barrier();
   frag_load(ring0, 0, fa0, fb0);
 
-  // One K slice (four MFMA sub-steps of 16 k), reading slot `cur`:
-  //   A, B, C: LDS reads of sub-step q+1 | MFMAs of sub-step q
+  // One K slice (QS MFMA sub-steps of 16 k), reading slot `cur`:
+  //   LDS reads of sub-step q+1 | MFMAs of sub-step q   (q < QS - 1)
   //   wait for the next slice, barrier, refill `cur` with slice kt + S
-  //   D: LDS reads of the next slice's sub-step 0 (slot `nxt`) | MFMAs of sub-step 3
+  //   LDS reads of the next slice's sub-step 0 (slot `nxt`) | MFMAs of the last sub-step
   // In the tail (no slice left to fetch) the wait drains everything.
   auto step = [&](int kt, bool tail, char* cur, char* nxt) {
     __builtin_amdgcn_sched_barrier(0);
@@ -291,14 +302,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
     mma_all(fa0, fb0);
     Interleave<0, MF, DSR, 0x100, 0>::run();
     __builtin_amdgcn_sched_barrier(0);
-    frag_load(cur, 2, fa0, fb0);
-    mma_all(fa1, fb1);
-    Interleave<0, MF, DSR, 0x100, 0>::run();
-    __builtin_amdgcn_sched_barrier(0);
-    frag_load(cur, 3, fa1, fb1);
-    mma_all(fa0, fb0);
-    Interleave<0, MF, DSR, 0x100, 0>::run();
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (QS == 4) {
+      frag_load(cur, 2, fa0, fb0);
+      mma_all(fa1, fb1);
+      Interleave<0, MF, DSR, 0x100, 0>::run();
+      __builtin_amdgcn_sched_barrier(0);
+      frag_load(cur, 3, fa1, fb1);
+      mma_all(fa0, fb0);
+      Interleave<0, MF, DSR, 0x100, 0>::run();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (tail) wait_vmcnt<0>();
     else wait_vmcnt<(S - 2) * LPW>();
     ring_barrier();
@@ -370,42 +383,63 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmParams p) {
   }
 }
 
-template <typename T, int BM, int BN, int S, int KIND>
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, hipStream_t s) {
   const int64_t nt = (p.Nout + BN - 1) / BN;
   const int64_t grid = (mtiles * nt + 7) / 8 * 8;  // whole rounds of the 8 XCDs
   if (mtiles * nt <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, S, KIND>), dim3(unsigned(grid)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, KIND>), dim3(unsigned(grid)),
+                     dim3(64 * WM * WN), 0, s, p);
   return hipGetLastError();
 }
 
-// The instantiated launch shapes (block tile BM x BN, LDS ring depth S).
-#define TOPMOE_GEMM_SHAPES(X) \
-  X(256, 128, 2) X(256, 128, 3) X(128, 128, 2) X(128, 128, 3) X(128, 128, 4) X(128, 64, 2) X(128, 64, 3) \
-  X(128, 64, 4) X(64, 64, 3) X(64, 64, 4)
-
-// Launches a shape only when its LDS ring fits in 160 KB (a plain
+// Launches a shape only when it is valid for the projection (LDS ring fits in
+// 160 KB, slice rows split evenly over the wavefronts).  A plain
 // specialisation rather than if-constexpr, so every kernel that can be
-// launched is instantiated at namespace scope with its host stub).
-template <typename T, int BM, int BN, int S, int KIND,
-          bool FITS = (S * (BM + (KIND == KIND_GATEUP ? 2 : 1) * BN) * 128 <= 160 * 1024)>
+// launched is instantiated at namespace scope with its host stub.
+template <int BM, int BN, int WM, int WN, int RB, int S, int KIND>
+constexpr bool shape_ok() {
+  constexpr int NB = KIND == KIND_GATEUP ? 2 : 1;
+  constexpr int R = BM + NB * BN;
+  constexpr int NW = WM * WN;
+  return S * R * RB <= 160 * 1024 && (R / (1024 / RB)) % NW == 0 &&
+         (S - 1) * (R / (1024 / RB) / NW) < 64 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0;
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND,
+          bool OK = shape_ok<BM, BN, WM, WN, RB, S, KIND>()>
 struct ShapeLauncher {
   static hipError_t run(const GemmParams&, int64_t, hipStream_t) { return hipErrorInvalidValue; }
 };
-template <typename T, int BM, int BN, int S, int KIND>
-struct ShapeLauncher<T, BM, BN, S, KIND, true> {
+template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
+struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
   static hipError_t run(const GemmParams& p, int64_t mtiles, hipStream_t s) {
-    return launch_gemm_t<T, BM, BN, S, KIND>(p, mtiles, s);
+    return launch_gemm_t<T, BM, BN, WM, WN, RB, S, KIND>(p, mtiles, s);
   }
 };
 
+// The instantiated launch shapes: (BM, BN, WM, WN, RB, S) = block tile, wave
+// grid, LDS row bytes (K slice of RB / sizeof(T) elements), ring depth.
+#define TOPMOE_GEMM_SHAPES_BF16(X)                                                        \
+  X(128, 64, 2, 2, 128, 2) X(128, 64, 2, 2, 128, 3) X(128, 64, 2, 2, 64, 4)               \
+  X(128, 128, 2, 2, 128, 2) X(128, 128, 2, 2, 128, 3) X(128, 128, 2, 2, 64, 4)            \
+  X(64, 64, 2, 2, 128, 3) X(64, 64, 2, 2, 128, 4)                                          \
+  X(256, 128, 4, 2, 64, 4) X(256, 128, 4, 2, 64, 3) X(256, 256, 4, 2, 64, 4)              \
+  X(128, 128, 2, 4, 64, 4) X(256, 128, 4, 2, 128, 2)
+#define TOPMOE_GEMM_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
+
 template <typename T, int KIND>
 hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, hipStream_t s) {
-#define TOPMOE_TRY_SHAPE(BM_, BN_, S_)                               \
-  if (sh.bm == (BM_) && sh.bn == (BN_) && sh.stages == (S_))        \
-    return ShapeLauncher<T, BM_, BN_, S_, KIND>::run(p, mtiles, s);
-  TOPMOE_GEMM_SHAPES(TOPMOE_TRY_SHAPE)
+#define TOPMOE_TRY_SHAPE(BM_, BN_, WM_, WN_, RB_, S_)                                     \
+  if (sh.bm == (BM_) && sh.bn == (BN_) && sh.wm == (WM_) && sh.wn == (WN_) &&            \
+      sh.rb == (RB_) && sh.stages == (S_))                                               \
+    return ShapeLauncher<T, BM_, BN_, WM_, WN_, RB_, S_, KIND>::run(p, mtiles, s);
+  if constexpr (sizeof(T) == 2) {
+    TOPMOE_GEMM_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+  } else {
+    TOPMOE_GEMM_SHAPES_F32(TOPMOE_TRY_SHAPE)
+  }
 #undef TOPMOE_TRY_SHAPE
   return hipErrorInvalidValue;
 }

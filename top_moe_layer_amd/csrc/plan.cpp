@@ -18,56 +18,95 @@ bool dtype_ok(int dtype) { return dtype == TOPMOE_DTYPE_FP32 || dtype == TOPMOE_
 int elem_bytes(int dtype) { return dtype == TOPMOE_DTYPE_FP32 ? 4 : 2; }
 
 struct Cand {
-  int bm, bn, stages;
-  double eff;  // relative MFMA efficiency of one tile (bigger tiles reuse operands more)
+  GemmShape sh;
+  double tflops;  // measured sustained rate of the whole chip with this shape (MI355X)
+  int per_cu;     // blocks resident per CU (LDS / registers)
 };
 
-// Pick the tile minimising (rounds of 256 CUs) x (cost of one tile).
-GemmShape choose(const Cand* cands, int n, int64_t M, int64_t Nout, int groups) {
-  GemmShape best{cands[n - 1].bm, cands[n - 1].bn, cands[n - 1].stages};
+// Pick the launch shape minimising rounds x (tile time + fixed per-tile
+// cost), with the tile time from the shape's measured sustained rate.
+// Tiles: M tiles over `groups` groups x ceil(Nout / BN).
+GemmShape choose(const Cand* cands, int n, int64_t M, int64_t Nout, int64_t K, int groups,
+                 int nmat) {
+  constexpr double kTileOverheadUs = 3.0;  // prologue fill + epilogue, measured order
+  GemmShape best = cands[n - 1].sh;
   double best_cost = -1.0;
   for (int i = 0; i < n; ++i) {
-    const Cand& c = cands[i];
-    int64_t mt = grouped_mtiles_bound(M, groups, c.bm);
-    int64_t nt = (Nout + c.bn - 1) / c.bn;
-    int64_t tiles = mt * nt;
+    const GemmShape& c = cands[i].sh;
+    const int64_t mt = grouped_mtiles_bound(M, groups, c.bm);
+    const int64_t nt = (Nout + c.bn - 1) / c.bn;
+    const int64_t tiles = mt * nt;
     if (tiles <= 0) continue;
-    int64_t rounds = (tiles + 255) / 256;
-    double cost = double(rounds) * double(c.bm) * double(c.bn) / c.eff;
+    const int64_t slots = 256 * int64_t(cands[i].per_cu);
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double tile_flop = 2.0 * nmat * c.bm * c.bn * double(K);
+    const double slot_tflops = cands[i].tflops / double(slots);
+    const double cost = double(rounds) * (tile_flop / (slot_tflops * 1e6) + kTileOverheadUs);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;
-      best = GemmShape{c.bm, c.bn, c.stages};
+      best = c;
     }
   }
   return best;
 }
 
-// "BMxBNxS" from the environment (launch-shape sweeps); must name an
+// "BMxBNxWMxWNxRBxS" (or "BMxBNxS" for a 2x2 wavefront grid with 128-byte
+// rows) from the environment, for launch-shape sweeps; it must name an
 // instantiated shape, otherwise the launch reports an invalid value.
 bool env_shape(const char* name, GemmShape* out) {
   const char* v = std::getenv(name);
   if (!v || !*v) return false;
-  int bm = 0, bn = 0, st = 0;
-  if (std::sscanf(v, "%dx%dx%d", &bm, &bn, &st) != 3) return false;
-  *out = GemmShape{bm, bn, st};
-  return true;
+  GemmShape g;
+  if (std::sscanf(v, "%dx%dx%dx%dx%dx%d", &g.bm, &g.bn, &g.wm, &g.wn, &g.rb, &g.stages) == 6) {
+    *out = g;
+    return true;
+  }
+  GemmShape h;
+  if (std::sscanf(v, "%dx%dx%d", &h.bm, &h.bn, &h.stages) == 3) {
+    *out = h;
+    return true;
+  }
+  return false;
 }
+
+// Launch-shape tables: rates measured on MI355X over the dense bf16
+// 16384 x 2048 x 6464 projections (sustained whole-chip TFLOP/s).
+const Cand kGateupBf16[] = {
+    {{256, 128, 4, 2, 64, 3}, 1120.0, 1},
+    {{128, 128, 2, 4, 64, 4}, 890.0, 1},
+    {{128, 64, 2, 2, 128, 2}, 890.0, 2},
+    {{64, 64, 2, 2, 128, 3}, 840.0, 2},
+};
+const Cand kDownBf16[] = {
+    {{256, 256, 4, 2, 64, 4}, 1090.0, 1},
+    {{128, 128, 2, 2, 128, 2}, 960.0, 2},
+    {{128, 128, 2, 4, 64, 4}, 810.0, 1},
+    {{128, 64, 2, 2, 128, 3}, 780.0, 2},
+    {{64, 64, 2, 2, 128, 4}, 640.0, 2},
+};
+const Cand kFp32[] = {
+    {{128, 64, 2, 2, 128, 2}, 100.0, 2},
+    {{64, 64, 2, 2, 128, 3}, 90.0, 2},
+};
+
+// Few rows per group and long K: the projection streams weights from HBM, so
+// the smallest tile (least wasted MFMA work, most blocks) wins.
+bool weight_streaming(int64_t M, int groups) { return M <= int64_t(groups) * 32; }
 
 }  // namespace
 
-GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int groups, int dtype) {
-  // Measured on MI355X: tiles whose LDS ring lets two blocks share a CU win.
-  static const Cand c[] = {{128, 64, 2, 1.0}, {64, 64, 3, 0.8}};
-  (void)dtype;
-  GemmShape sh = choose(c, 2, M, Nout, groups);
+GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
+  if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 2);
+  GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 64, 2, 2, 128, 3}
+                                             : choose(kGateupBf16, 4, M, Nout, K, groups, 2);
   env_shape("TOPMOE_GATEUP_TILE", &sh);
   return sh;
 }
 
-GemmShape choose_down_tile(int64_t M, int64_t Nout, int groups, int dtype) {
-  static const Cand c[] = {{128, 128, 2, 1.0}, {128, 64, 3, 0.9}, {64, 64, 4, 0.7}};
-  (void)dtype;
-  GemmShape sh = choose(c, 3, M, Nout, groups);
+GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
+  if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 1);
+  GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 64, 2, 2, 128, 4}
+                                             : choose(kDownBf16, 5, M, Nout, K, groups, 1);
   env_shape("TOPMOE_DOWN_TILE", &sh);
   return sh;
 }
@@ -79,8 +118,8 @@ int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
     return TOPMOE_ERR_BAD_SHAPE;
   FfnPlan q;
   q.N = N; q.H = H; q.I = I; q.dtype = dtype; q.elem = elem_bytes(dtype);
-  q.up = choose_gateup_tile(N, I, 1, dtype);
-  q.down = choose_down_tile(N, H, 1, dtype);
+  q.up = choose_gateup_tile(N, I, H, 1, dtype);
+  q.down = choose_down_tile(N, H, I, 1, dtype);
   q.off_h = 0;
   q.total = align_up(size_t(N) * size_t(I) * q.elem);
   if (q.total == 0) q.total = kAlign;
@@ -115,8 +154,8 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   while (N > 0 && ((N + tb - 1) / tb) * E > 8192) tb *= 2;
   q.tb = int(tb);
   q.nblk = int((N + tb - 1) / tb);
-  q.up = choose_gateup_tile(rows, I, E, dtype);
-  q.down = choose_down_tile(rows, H, E, dtype);
+  q.up = choose_gateup_tile(rows, I, H, E, dtype);
+  q.down = choose_down_tile(rows, H, I, E, dtype);
   q.up_mtiles = grouped_mtiles_bound(rows, E, q.up.bm);
   q.down_mtiles = grouped_mtiles_bound(rows, E, q.down.bm);
   size_t o = 0;

@@ -15,7 +15,10 @@ inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a
 // One GEMM launch shape: block tile BM x BN (per output matrix) and the
 // depth of the LDS ring of K slices.
 struct GemmShape {
-  int bm = 0, bn = 0, stages = 0;
+  int bm = 0, bn = 0;      // block tile
+  int wm = 2, wn = 2;      // wavefront grid (wm * wn wavefronts of 64 lanes)
+  int rb = 128;            // LDS row bytes per K slice
+  int stages = 2;          // ring depth
 };
 
 struct FfnPlan {
@@ -52,9 +55,9 @@ struct MoePlan {
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* plan);
 int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* plan);
 
-// Tile choice for an M x Nout GEMM with `groups` row groups (experts).
-GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int groups, int dtype);
-GemmShape choose_down_tile(int64_t M, int64_t Nout, int groups, int dtype);
+// Launch shape for an M x Nout x K GEMM with `groups` row groups (experts).
+GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype);
+GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype);
 
 // Upper bound on the number of BM-row tiles over `groups` groups of total M rows.
 inline int64_t grouped_mtiles_bound(int64_t M, int groups, int bm) {
