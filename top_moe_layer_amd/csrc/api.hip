@@ -136,6 +136,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   float* psum_part = reinterpret_cast<float*>(ws + pl.off_psum_part);
   int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(ws + pl.off_offsets);
   int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
+  float* alpha_g = reinterpret_cast<float*>(ws + pl.off_alpha_g);
   void* h = ws + pl.off_h;
   float* slots = reinterpret_cast<float*>(ws + pl.off_slots);
 
@@ -153,8 +154,9 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
                            topk_idx, alpha, count_part, psum_part, s));
   // 1: expert offsets, aux loss, stable scatter of entries into expert groups
   TOPMOE_TRY(ev.rec(1));
-  TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, pl.nblk, E, k, pl.tb, N, aux_coef,
-                            offsets, aux_loss, sorted_entry, sorted_token_ids, s));
+  TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, alpha, pl.nblk, E, k, pl.tb, N,
+                            aux_coef, offsets, aux_loss, sorted_entry, alpha_g,
+                            sorted_token_ids, s));
   // 2: grouped gate/up GEMM + SiLU * up
   TOPMOE_TRY(ev.rec(2));
   GemmParams up{};
@@ -166,7 +168,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   TOPMOE_TRY(ev.rec(3));
   GemmParams dn{};
   dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : static_cast<void*>(slots);
-  dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha;
+  dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha_g;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
                          pl.down_mtiles, s));

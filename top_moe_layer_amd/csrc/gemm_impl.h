@@ -111,10 +111,18 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Workgroup barrier for plain LDS stores: waits for this wavefront's LDS
+// operations only (not for its direct-to-LDS loads in flight); the memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   constexpr int NB = KIND == KIND_GATEUP ? 2 : 1;
   constexpr int NW = WM * WN;                // wavefronts: WM along rows x WN along columns
+  constexpr int NTHR = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wavefront and matrix
   constexpr int R = BM + NB * BN;            // LDS rows per slice: A, then B0 (, B1)
@@ -125,11 +133,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   constexpr int RPI = 1024 / RB;             // rows per 1 KB direct-to-LDS load
   constexpr int LPW = R / RPI / NW;          // direct-to-LDS loads per wavefront per slice
   constexpr int QS = RB / 32;                // MFMA sub-steps per slice
+  constexpr bool META = KIND != KIND_GATEUP;  // down epilogue needs per-row entry / alpha
   static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
   static_assert((R / RPI) % NW == 0 && LPW >= 1, "slice rows must split evenly over wavefronts");
   static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring exceeds 160 KB");
   static_assert((S - 1) * LPW < 64, "vmcnt range");
+  static_assert(BM <= NTHR, "one thread per tile row for the epilogue metadata");
   // One __shared__ object per ring slot: the compiler then sees that LDS reads
   // of one slot never alias direct-to-LDS loads into another and does not
   // drain the load queue before each read.
@@ -138,99 +148,123 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char ring2[S > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char ring3[S > 3 ? STAGE : 16];
   __shared__ int s_scan[64];
+  __shared__ int s_off[65];
+  __shared__ int s_ment[META ? BM : 1];
+  __shared__ float s_malpha[META ? BM : 1];
 
   const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nt_count = (p.Nout + BN - 1) / BN;
+  const int KT = p.K / (RB / int(sizeof(T)));
 
-  // ---- number of real M tiles: per-group tile counts from the device-side
-  // offsets (grouped) or ceil(M / BM) (single group)
+  // ---- real M tiles: per-group tile counts from the device-side offsets
+  // (grouped) or ceil(M / BM) (single group); offsets cached in LDS.
   int total_mt;
   if (p.offsets == nullptr) {
     total_mt = int((p.M + BM - 1) / BM);
   } else {
     if (tid < 64) {
-      const int lane = tid;
       int c = 0;
-      if (lane < p.E) c = p.offsets[lane + 1] - p.offsets[lane];
+      if (lane < p.E) {
+        const int o0 = p.offsets[lane], o1 = p.offsets[lane + 1];
+        c = o1 - o0;
+        s_off[lane] = o0;
+        if (lane == p.E - 1) s_off[p.E] = o1;
+      }
       const int tiles = (c + BM - 1) / BM;
-      const int incl = wave_inclusive_scan(tiles, lane);
-      s_scan[lane] = incl;
+      s_scan[lane] = wave_inclusive_scan(tiles, lane);
     }
     __syncthreads();
-    total_mt = s_scan[p.E - 1];
+    total_mt = __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
   }
 
-  // ---- XCD-aware work mapping.  Blocks are dispatched to the 8 XCDs round
-  // robin (block b runs on XCD b % 8), each with its own L2.  Give XCD x the
-  // contiguous range [x*per, (x+1)*per) of the real tiles, walked in groups of
-  // GM M-tiles (column by column inside a group), so the blocks resident on
-  // one XCD share their A rows and weight panels in that XCD's L2.  The grid
-  // is an upper bound rounded to a multiple of 8; blocks past the real work
-  // leave at once.
+  // ---- persistent, XCD-aware work list.  Blocks are dispatched to the 8
+  // XCDs round robin (block b runs on XCD b % 8), each XCD with its own L2.
+  // XCD x owns the contiguous range [x*per, (x+1)*per) of the real tiles,
+  // ordered in groups of GM M-tiles (column by column inside a group), so
+  // co-resident blocks share A rows and weight panels in that L2; its
+  // gridDim/8 blocks take the range round robin.
   constexpr int GM = 8;
   const int total = total_mt * nt_count;
   const int per = (total + 7) >> 3;
-  const int local = int(blockIdx.x >> 3);
-  const int L = int(blockIdx.x & 7) * per + local;
-  if (local >= per || L >= total) return;
-  const int first_m = (L / (GM * nt_count)) * GM;
-  const int gsz = min(total_mt - first_m, GM);
-  const int in_group = L - first_m * nt_count;
-  const int mt = first_m + in_group % gsz;
-  const int nt = in_group / gsz;
+  const int nbx = int(gridDim.x >> 3);
+  const int lb = int(blockIdx.x >> 3);
+  const int xbase = int(blockIdx.x & 7) * per;
+  int n_my = 0;
+  for (int l = lb; l < per && xbase + l < total; l += nbx) ++n_my;
+  if (n_my == 0) return;
 
-  // ---- which group (expert) and rows this tile covers
-  int e = 0;
-  int64_t row0;
-  int rows;
-  if (p.offsets == nullptr) {
-    row0 = int64_t(mt) * BM;
-    const int64_t left = p.M - row0;
-    rows = left < BM ? int(left) : BM;
-  } else {
-    // expert = number of groups whose tiles all precede mt
-    int ge = 0;
-    for (int g = 0; g < p.E; ++g) ge += (s_scan[g] <= mt) ? 1 : 0;
-    e = ge;
-    const int tiles_before = ge > 0 ? s_scan[ge - 1] : 0;
-    const int off = p.offsets[ge];
-    const int c = p.offsets[ge + 1] - off;
-    const int local_t = mt - tiles_before;
-    row0 = off + int64_t(local_t) * BM;
-    const int left = c - local_t * BM;
-    rows = left < BM ? left : BM;
-  }
-  if (rows <= 0) return;
-  const int n0 = nt * BN;
+  struct Tile {
+    int e, rows, n0;
+    int64_t row0;
+  };
+  auto decode = [&](int j) -> Tile {
+    const int L = xbase + lb + j * nbx;
+    const int first_m = (L / (GM * nt_count)) * GM;
+    const int gsz = min(total_mt - first_m, GM);
+    const int in_group = L - first_m * nt_count;
+    const int mt = first_m + in_group % gsz;
+    Tile t;
+    t.n0 = (in_group / gsz) * BN;
+    if (p.offsets == nullptr) {
+      t.e = 0;
+      t.row0 = int64_t(mt) * BM;
+      const int64_t left = p.M - t.row0;
+      t.rows = left < BM ? int(left) : BM;
+    } else {
+      int ge = 0;  // expert = number of groups whose tiles all precede mt
+      for (int g = 0; g < p.E; ++g) ge += (s_scan[g] <= mt) ? 1 : 0;
+      const int local_t = mt - (ge > 0 ? s_scan[ge - 1] : 0);
+      t.e = ge;
+      t.row0 = s_off[ge] + int64_t(local_t) * BM;
+      const int left = s_off[ge + 1] - int(t.row0);
+      t.rows = left < BM ? left : BM;
+    }
+    // uniform over the block: keep the tile in scalar registers
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.row0 = __builtin_amdgcn_readfirstlane(int(t.row0));
+    return t;
+  };
 
   // ---- direct-to-LDS load sources.  Wavefront w fills LDS row blocks
   // w*LPW .. w*LPW+LPW-1 (RPI rows = 1 KB each) of every slice.  Lane i of a
   // load writes slot base + 16 i, i.e. row RPI*b + i/CH, slot i%CH; it
   // therefore fetches logical chunk (i%CH) ^ swizzle(row).  Rows past the
   // tile's valid rows / columns are clamped to the last valid one (in bounds,
-  // results discarded).
-  const int wid = tid >> 6, lane = tid & 63;
-  const char* src[LPW];
+  // results discarded).  A-row indices of a tile are fetched early (`rid`)
+  // and turned into addresses only when that tile's first slice is issued.
+  auto load_rows = [&](const Tile& t, int32_t(&rid)[LPW]) {
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = (wid * LPW + j) * RPI + lane / CH;
-    const int chunk = (lane % CH) ^ ((r / RPW) % CH);
-    const char* base;
-    if (r < BM) {
-      const int64_t gr = row0 + (r < rows ? r : rows - 1);
-      int64_t arow = gr;
-      if (KIND == KIND_GATEUP && p.entries != nullptr) arow = p.entries[gr] / p.k;
-      base = static_cast<const char*>(p.A) + arow * p.K * int64_t(sizeof(T));
-    } else {
-      const int rb = r - BM;
-      const int which = rb >= BN ? 1 : 0;
-      int n = n0 + rb - which * BN;
-      n = n < p.Nout ? n : p.Nout - 1;
-      const void* W = which ? p.B1 : p.B0;
-      base = static_cast<const char*>(W) + (int64_t(e) * p.Nout + n) * p.K * int64_t(sizeof(T));
+    for (int j = 0; j < LPW; ++j) {
+      const int r = (wid * LPW + j) * RPI + lane / CH;
+      int gr = int(t.row0) + (r < t.rows ? r : t.rows - 1);
+      if (r >= BM) gr = 0;
+      rid[j] = (KIND == KIND_GATEUP && p.entries != nullptr && r < BM) ? p.entries[gr] / p.k : gr;
     }
-    src[j] = base + chunk * 16;
-  }
+  };
+  auto make_src = [&](const Tile& t, const int32_t(&rid)[LPW], const char* (&src)[LPW]) {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int r = (wid * LPW + j) * RPI + lane / CH;
+      const int chunk = (lane % CH) ^ ((r / RPW) % CH);
+      const char* base;
+      if (r < BM) {
+        base = static_cast<const char*>(p.A) + int64_t(rid[j]) * p.K * int64_t(sizeof(T));
+      } else {
+        const int rb = r - BM;
+        const int which = rb >= BN ? 1 : 0;
+        int n = t.n0 + rb - which * BN;
+        n = n < p.Nout ? n : p.Nout - 1;
+        const void* W = which ? p.B1 : p.B0;
+        base = static_cast<const char*>(W) + (int64_t(t.e) * p.Nout + n) * p.K * int64_t(sizeof(T));
+      }
+      src[j] = base + chunk * 16;
+    }
+  };
+  int32_t rid[LPW];      // A-row indices of the next tile
+  const char* src[LPW];  // load sources of the tile whose slices are being issued
   auto slot_ptr = [&](int slot) -> char* {
     return slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
   };
@@ -242,14 +276,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   };
 
   f32x16 acc[NB][TM][TN];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
+          for (int v = 0; v < 16; ++v) acc[b][i][j][v] = 0.f;
+  };
 
   const int fr = lane & 31, fg = lane >> 5;
   const int wm = (wid / WN) * WTM, wn = (wid % WN) * WTN;
@@ -281,22 +317,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 
   constexpr int MF = NB * TM * TN * (sizeof(T) == 4 ? 4 : 1);  // MFMAs per sub-step
   constexpr int DSR = TM + NB * TN;                            // LDS reads per sub-step
-  const int KT = p.K / (RB / int(sizeof(T)));
-
-  // prologue: fill the ring, wait for slice 0
-  const int npro = KT < S ? KT : S;
-  for (int sl = 0; sl < npro; ++sl) issue(sl, slot_ptr(sl));
-  if (npro == S) wait_vmcnt<(S - 1) * LPW>();
-  else wait_vmcnt<0>();
-  ring_barrier();
-  frag_load(ring0, 0, fa0, fb0);
 
   // One K slice (QS MFMA sub-steps of 16 k), reading slot `cur`:
   //   LDS reads of sub-step q+1 | MFMAs of sub-step q   (q < QS - 1)
-  //   wait for the next slice, barrier, refill `cur` with slice kt + S
+  //   wait for the next slice, barrier, refill `cur` (see `what`)
   //   LDS reads of the next slice's sub-step 0 (slot `nxt`) | MFMAs of the last sub-step
-  // In the tail (no slice left to fetch) the wait drains everything.
-  auto step = [&](int kt, bool tail, char* cur, char* nxt) {
+  // `full_wait`: the next slice is the last one in flight, so drain everything.
+  auto step = [&](char* cur, char* nxt, bool full_wait, bool refill, int ikt) {
     __builtin_amdgcn_sched_barrier(0);
     frag_load(cur, 1, fa1, fb1);
     mma_all(fa0, fb0);
@@ -312,85 +339,184 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       Interleave<0, MF, DSR, 0x100, 0>::run();
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (tail) wait_vmcnt<0>();
+    if (full_wait) wait_vmcnt<0>();
     else wait_vmcnt<(S - 2) * LPW>();
     ring_barrier();
-    if (!tail) issue(kt + S, cur);
+    if (refill) issue(ikt, cur);
     __builtin_amdgcn_sched_barrier(0);
     frag_load(nxt, 0, fa0, fb0);
     mma_all(fa1, fb1);
     Interleave<0, MF, DSR, 0x100, 0>::run();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Steady state: groups of S steps with static slots (slice kt lives in slot
-  // kt % S) while every step of the group still has a slice to fetch.
-  int kt = 0;
-  for (; kt + 2 * S - 1 < KT; kt += S) {
-    step(kt, false, ring0, ring1);
-    if constexpr (S == 2) {
-      step(kt + 1, false, ring1, ring0);
-    } else if constexpr (S == 3) {
-      step(kt + 1, false, ring1, ring2);
-      step(kt + 2, false, ring2, ring0);
-    } else {
-      step(kt + 1, false, ring1, ring2);
-      step(kt + 2, false, ring2, ring3);
-      step(kt + 3, false, ring3, ring0);
-    }
-  }
-  // Remaining steps (fewer than 2S): slots chosen at run time.
-  for (; kt < KT; ++kt) {
-    const int sl = kt % S;
-    step(kt, kt + S >= KT, slot_ptr(sl), slot_ptr(sl + 1 == S ? 0 : sl + 1));
-  }
 
   // ---- epilogue.  32x32 accumulator layout: lane (fr, fg), register v holds
   // row 8*(v/4) + 4*fg + v%4, column fr of the MFMA tile.
+  int m_ent = 0;
+  float m_alpha = 1.f;
+  auto load_meta = [&](const Tile& t) {  // one row per thread, ahead of the epilogue
+    if (META && tid < BM) {
+      const int64_t g = t.row0 + (tid < t.rows ? tid : t.rows - 1);
+      m_ent = p.entries != nullptr ? p.entries[g] : int(g);
+      m_alpha = p.alpha != nullptr ? p.alpha[g] : 1.f;
+    }
+  };
+  auto epilogue = [&](const Tile& t) {
+    if constexpr (META) {
+      // The previous tile's reads of s_ment / s_malpha finished before the
+      // ring barriers of this tile's steps (each drains this wavefront's LDS
+      // operations first), so the rows can be overwritten here.
+      if (tid < BM) { s_ment[tid] = m_ent; s_malpha[tid] = m_alpha; }
+      lds_barrier();
+    }
+    // The lane's first row / column in the tile, made opaque so that the
+    // per-register row numbers are not hoisted out of the tile loop (they
+    // would hold dozens of registers for the whole block).
+    int rl = wm + 4 * fg, cl = wn + fr;
+    asm volatile("" : "+v"(rl), "+v"(cl));
+    const int rows_left = t.rows - rl;            // valid: 32 i + 8 (v / 4) + v % 4 < rows_left
+    const int cols_left = p.Nout - (t.n0 + cl);   // valid: 32 j < cols_left
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm + 32 * i + 8 * (v >> 2) + 4 * fg + (v & 3);
-      if (r >= rows) continue;
-      const int64_t grow = row0 + r;
-      if (KIND == KIND_GATEUP) {
-        T* out = static_cast<T*>(p.out) + grow * p.Nout;
+      for (int v = 0; v < 16; ++v) {
+        const int ro = 32 * i + 8 * (v >> 2) + (v & 3);
+        if (ro >= rows_left) continue;
+        if constexpr (KIND == KIND_GATEUP) {
+          T* out = static_cast<T*>(p.out) + (t.row0 + rl + ro) * p.Nout + t.n0 + cl;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = n0 + wn + 32 * j + fr;
-          if (col < p.Nout) out[col] = from_f32<T>(silu_mul(acc[0][i][j][v], acc[NB - 1][i][j][v]));
-        }
-      } else {
-        const int64_t ent = p.entries != nullptr ? int64_t(p.entries[grow]) : grow;
-        const float a = p.alpha != nullptr ? p.alpha[ent] : 1.0f;
-        if (KIND == KIND_DOWN_Y) {
-          T* out = static_cast<T*>(p.out) + (ent / p.k) * p.Nout;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn + 32 * j + fr;
-            if (col < p.Nout) out[col] = from_f32<T>(acc[0][i][j][v] * a);
-          }
+          for (int j = 0; j < TN; ++j)
+            if (32 * j < cols_left)
+              out[32 * j] = from_f32<T>(silu_mul(acc[0][i][j][v], acc[NB - 1][i][j][v]));
         } else {
-          float* out = static_cast<float*>(p.out) + ent * p.Nout;
+          const int64_t ent = s_ment[rl + ro];
+          const float a = s_malpha[rl + ro];
+          if constexpr (KIND == KIND_DOWN_Y) {
+            T* out = static_cast<T*>(p.out) + (ent / p.k) * p.Nout + t.n0 + cl;
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn + 32 * j + fr;
-            if (col < p.Nout) out[col] = acc[0][i][j][v] * a;
+            for (int j = 0; j < TN; ++j)
+              if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[0][i][j][v] * a);
+          } else {
+            float* out = static_cast<float*>(p.out) + ent * p.Nout + t.n0 + cl;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              if (32 * j < cols_left) out[32 * j] = acc[0][i][j][v] * a;
           }
         }
       }
     }
+  };
+
+  // ---- the block's tiles.  When S divides the number of K slices every tile
+  // starts in slot 0 and the ring streams straight on into the next tile
+  // (its first S slices are issued during this tile's last S steps);
+  // otherwise each tile fills and drains the ring on its own.
+  const bool stream = (KT % S) == 0;
+  Tile cur = decode(0);
+  load_rows(cur, rid);
+  make_src(cur, rid, src);
+  Tile nxt = cur;
+  if (stream && n_my > 1) {
+    nxt = decode(1);
+    load_rows(nxt, rid);
   }
+
+  for (int cj = 0; cj < n_my; ++cj) {
+    const bool has_next = cj + 1 < n_my;
+    const bool xnext = stream && has_next;
+    zero_acc();
+    if (cj == 0 || !stream) {
+      // fill the ring with the tile's first slices, wait for slice 0
+      const int npro = KT < S ? KT : S;
+      for (int sl = 0; sl < npro; ++sl) issue(sl, slot_ptr(sl));
+      if (npro == S) wait_vmcnt<(S - 1) * LPW>();
+      else wait_vmcnt<0>();
+      ring_barrier();
+      frag_load(ring0, 0, fa0, fb0);
+    }
+    int kt = 0;
+    // Groups of S steps with static slots (slice kt lives in slot kt % S).
+    // In a group every step refills its slot with slice kt + S: of this tile,
+    // or, in the last group of a streaming tile, of the next tile.
+    for (; stream ? (kt < KT) : (kt + 2 * S - 1 < KT); kt += S) {
+      const bool last_group = kt + S >= KT;
+      if (last_group) {
+        // this tile's slices are all issued: `src` moves on to the next tile
+        if (xnext) make_src(nxt, rid, src);
+        load_meta(cur);
+      }
+      // the very last slices of the block: nothing left to fetch, drain
+      const bool tail = last_group && !xnext;
+      const bool refill = !last_group || xnext;
+      const int ik = last_group ? kt + S - KT : kt + S;  // slice index (in its tile) to issue
+      step(ring0, ring1, false, refill, ik);
+      if constexpr (S == 2) {
+        step(ring1, ring0, tail, refill, ik + 1);
+      } else if constexpr (S == 3) {
+        step(ring1, ring2, tail, refill, ik + 1);
+        step(ring2, ring0, tail, refill, ik + 2);
+      } else {
+        step(ring1, ring2, tail, refill, ik + 1);
+        step(ring2, ring3, tail, refill, ik + 2);
+        step(ring3, ring0, tail, refill, ik + 3);
+      }
+    }
+    // Non-streaming tiles: the remaining steps (fewer than 2S) with run-time
+    // slots; in the last S - 1 of them there is nothing left to fetch.
+    if (!stream) {
+      load_meta(cur);
+      for (; kt < KT; ++kt) {
+        const int sl = kt % S;
+        const bool more = kt + S < KT;
+        step(slot_ptr(sl), slot_ptr(sl + 1 == S ? 0 : sl + 1), !more, more, kt + S);
+      }
+    }
+    epilogue(cur);
+    if (xnext) {
+      cur = nxt;
+      if (cj + 2 < n_my) {
+        nxt = decode(cj + 2);
+        load_rows(nxt, rid);
+      }
+    } else if (has_next) {
+      cur = decode(cj + 1);
+      load_rows(cur, rid);
+      make_src(cur, rid, src);
+    }
+  }
+}
+
+// Blocks of one kernel that fit on the device at once (CUs x resident
+// blocks per CU), queried once per kernel and device.
+template <typename K>
+int resident_blocks(K kernel, int threads) {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, hipStream_t s) {
   const int64_t nt = (p.Nout + BN - 1) / BN;
-  const int64_t grid = (mtiles * nt + 7) / 8 * 8;  // whole rounds of the 8 XCDs
   if (mtiles * nt <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB, S, KIND>), dim3(unsigned(grid)),
-                     dim3(64 * WM * WN), 0, s, p);
+  // persistent grid: at most the blocks resident at once, in whole rounds of
+  // the 8 XCDs (blocks beyond the real tile count exit at once)
+  auto kernel = gemm_kernel<T, BM, BN, WM, WN, RB, S, KIND>;
+  const int64_t cap = resident_blocks(kernel, 64 * WM * WN) / 8 * 8;
+  int64_t grid = (mtiles * nt + 7) / 8 * 8;
+  if (grid > cap && cap >= 8) grid = cap;
+  hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ struct GemmParams {
   void* out;               // gate/up: h [rows, Nout]; down: y [N, Nout] or slots [rows, Nout]
   const int32_t* entries;  // grouped row -> entry id t*k + j; NULL = identity (dense)
   const int32_t* offsets;  // [E+1] group row offsets; NULL = one group of M rows
-  const float* alpha;      // [N*k] per-entry weight (down); NULL = 1
+  const float* alpha;      // [rows] weight of each grouped row (down); NULL = 1
   int64_t M;               // rows when offsets == NULL
   int E, k;
   int Nout, K;
@@ -37,9 +37,10 @@ hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, i
                          int32_t* count_part, float* psum_part, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
-                          const int32_t* topk_idx, int nblk, int E, int k, int tb, int64_t N,
-                          float coef, int32_t* offsets, float* aux, int32_t* sorted_entry,
-                          int32_t* sorted_tok, hipStream_t s);
+                          const int32_t* topk_idx, const float* alpha, int nblk, int E, int k,
+                          int tb, int64_t N, float coef, int32_t* offsets, float* aux,
+                          int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
+                          hipStream_t s);
 
 hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,
                           int dtype, void* y, hipStream_t s);

@@ -9,7 +9,8 @@
 //     offsets), the aux loss aux = E * coef * sum_e (c_e / N) * (sum_t p_{t,e} / N)
 //     (lesson 13, section 1.6 equation; walkthrough step 6), and a stable
 //     scatter of the entries (t, j) in t*k + j order into expert groups, so
-//     each group lists its tokens in ascending order;
+//     each group lists its tokens in ascending order (with each entry's alpha
+//     copied beside it for the down projection's epilogue);
 //   * combine: y_t = sum of the k alpha-scaled expert rows in ascending expert
 //     id, accumulated in fp32 and rounded once.
 // All integer work is exact; the only float reductions run in a fixed order.
@@ -39,9 +40,10 @@ constexpr int kScanMax = 8192;
 
 __global__ __launch_bounds__(256) void permute_kernel(
     const int32_t* __restrict__ count_part, const float* __restrict__ psum_part,
-    const int32_t* __restrict__ topk_idx, int nblk, int G, int E, int k, int tb, int64_t N,
-    float coef, int32_t* __restrict__ offsets, float* __restrict__ aux,
-    int32_t* __restrict__ sorted_entry, int32_t* __restrict__ sorted_tok) {
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ alpha, int nblk, int G,
+    int E, int k, int tb, int64_t N, float coef, int32_t* __restrict__ offsets,
+    float* __restrict__ aux, int32_t* __restrict__ sorted_entry, float* __restrict__ alpha_g,
+    int32_t* __restrict__ sorted_tok) {
   __shared__ int s_c[kScanMax];
   __shared__ float s_p[kScanMax];  // block 0 only
   __shared__ int s_tot[64];
@@ -105,6 +107,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
       const int64_t ent = base + lane;
       const bool valid = ent < e1;
       const int ex = valid ? topk_idx[ent] : -1;
+      const float al = valid ? alpha[ent] : 0.f;
       uint64_t peers = 0ull;  // lanes holding the same expert
       uint64_t todo = __ballot(valid);
       while (todo) {
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
       if (valid) {
         const int dest = s_base[ex] + run[ex] + __popcll(peers & lt_mask);
         sorted_entry[dest] = int32_t(ent);
+        alpha_g[dest] = al;
         if (sorted_tok) sorted_tok[dest] = int32_t(ent / k);
       }
       __builtin_amdgcn_wave_barrier();
@@ -178,15 +182,17 @@ __global__ void empty_route_kernel(int E, int32_t* offsets, float* aux) {
 }  // namespace
 
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
-                          const int32_t* topk_idx, int nblk, int E, int k, int tb, int64_t N,
-                          float coef, int32_t* offsets, float* aux, int32_t* sorted_entry,
-                          int32_t* sorted_tok, hipStream_t s) {
+                          const int32_t* topk_idx, const float* alpha, int nblk, int E, int k,
+                          int tb, int64_t N, float coef, int32_t* offsets, float* aux,
+                          int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
+                          hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   if (int64_t(E) * nblk > kScanMax) return hipErrorInvalidValue;
   const int G = nblk > 256 ? (nblk + 255) / 256 : 1;  // router blocks per scatter block
   const int nsb = (nblk + G - 1) / G;
   hipLaunchKernelGGL(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part, topk_idx,
-                     nblk, G, E, k, tb, N, coef, offsets, aux, sorted_entry, sorted_tok);
+                     alpha, nblk, G, E, k, tb, N, coef, offsets, aux, sorted_entry, alpha_g,
+                     sorted_tok);
   return hipGetLastError();
 }
 
