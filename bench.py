@@ -195,7 +195,7 @@ def main():
         def step(ev=None):
             tm.ffn_swiglu_fwd(d["x"], d["Wg"], d["Wu"], d["Wd"], y=y, workspace=ws,
                               stream=stream, stage_events=ev)
-        ev = tm.StageEvents(tm.FFN_STAGES)
+        make_events = lambda: tm.StageEvents(tm.FFN_STAGES)
     else:
         ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8, device=dev)
         y = torch.empty((N, H), dtype=tdt, device=dev)
@@ -209,12 +209,13 @@ def main():
             tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef, y=y,
                            topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
                            return_lists=False, workspace=ws, stream=stream, stage_events=ev)
-        ev = tm.StageEvents(tm.MOE_STAGES)
+        make_events = lambda: tm.StageEvents(tm.MOE_STAGES)
 
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
 
-    for _ in range(args.warmup):
-        step()
+    warm_ev = make_events()
+    for i in range(args.warmup):
+        step(warm_ev if i == 0 else None)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
@@ -240,16 +241,22 @@ def main():
         ms_step = tot / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step")
 
-    # per-stage kernel durations from HIP events on the library's stream
-    per = np.zeros(len(names))
-    for _ in range(args.steps):
+    # Per-kernel durations: the same K steps again, each with its own start /
+    # stop events per stage, stamped by the kernel dispatches themselves
+    # (hipExtLaunchKernel) on the library's stream, so each pair brackets
+    # exactly one kernel.  Attaching the events costs a few microseconds of
+    # dispatch per kernel, which is why the step time above is taken without.
+    ev_sets = [make_events() for _ in range(args.steps)]
+    for i in range(args.steps):
         if flush is not None:
             flush.zero_()
-        step(ev)
-        per += np.array(ev.elapsed_ms())
-    per /= args.steps
+        step(ev_sets[i])
+    torch.cuda.synchronize()
+    per = np.mean([e.elapsed_ms() for e in ev_sets], axis=0)
+    for e in ev_sets:
+        e.close()
     stages_ms = {n: round(float(v), 5) for n, v in zip(names, per)}
-    log(f"stage ms: {stages_ms}")
+    log(f"stage kernel ms: {stages_ms}")
 
     units = stage_units(w)
     touched = None

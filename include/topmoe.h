@@ -24,10 +24,13 @@
  *     is reported as TOPMOE_ERR_HIP (outputs may then be partly written).
  *   - Results are deterministic: the same inputs give bitwise identical
  *     outputs (no floating-point atomics anywhere).
- *   - `stage_events`, when not NULL, is an array of (stages + 1) hipEvent_t
- *     handles (see topmoe_events_create); event i is recorded on `stream`
- *     before stage i and the last one after the final stage.  Pass NULL in
- *     production.  Stage counts: TOPMOE_FFN_STAGES, TOPMOE_MOE_STAGES.
+ *   - `stage_events`, when not NULL, is an array of 2 * stages hipEvent_t
+ *     handles (see topmoe_events_create); events 2i and 2i+1 are stamped by
+ *     the dispatch of stage i's kernel at its start and end (AMD's
+ *     hipExtLaunchKernel start / stop events), so they bracket exactly that
+ *     kernel's execution; a stage that launches no kernel records both back
+ *     to back.  Pass NULL in production.  Stage counts: TOPMOE_FFN_STAGES,
+ *     TOPMOE_MOE_STAGES.
  *
  * dtype
  *   TOPMOE_DTYPE_FP32: x, W_gate, W_up, W_down, y float32; all arithmetic fp32.

@@ -99,10 +99,11 @@ def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, N, H, I, E, k, coef, dtype, y, topk_idx, 
 
 
 class StageEvents:
-    """n + 1 timing events for the ``stage_events`` argument."""
+    """Start / stop events of every stage (2 * stages) for ``stage_events``."""
 
     def __init__(self, stages: int):
-        self.n = stages + 1
+        self.stages = stages
+        self.n = 2 * stages
         self.arr = (ctypes.c_void_p * self.n)()
         check(lib().topmoe_events_create(self.n, self.arr), "topmoe_events_create")
 
@@ -111,11 +112,12 @@ class StageEvents:
         return ctypes.cast(self.arr, ctypes.c_void_p)
 
     def elapsed_ms(self):
-        """Per-stage milliseconds of the last recorded call (waits for it)."""
+        """Kernel milliseconds of each stage of the last recorded call (waits for it)."""
         out = []
         ms = ctypes.c_float()
-        for i in range(self.n - 1):
-            check(lib().topmoe_event_elapsed_ms(self.arr[i], self.arr[i + 1], ctypes.byref(ms)),
+        for i in range(self.stages):
+            check(lib().topmoe_event_elapsed_ms(self.arr[2 * i], self.arr[2 * i + 1],
+                                                ctypes.byref(ms)),
                   "topmoe_event_elapsed_ms")
             out.append(ms.value)
         return out

@@ -10,12 +10,12 @@
 
 namespace topmoe {
 hipError_t launch_gemm_bf16(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
-                            hipStream_t s);
+                            const Launch& s);
 hipError_t launch_gemm_f32(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
-                           hipStream_t s);
+                           const Launch& s);
 
 hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
-                       int64_t mtiles, hipStream_t s) {
+                       int64_t mtiles, const Launch& s) {
   return dtype == TOPMOE_DTYPE_FP32 ? launch_gemm_f32(kind, shape, p, mtiles, s)
                                     : launch_gemm_bf16(kind, shape, p, mtiles, s);
 }
@@ -27,11 +27,25 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-struct Events {
+// Stage i's launch: the stream plus, when timing is requested, events
+// 2i / 2i+1 stamped by the stage's kernel dispatch.
+struct Stages {
   void* const* ev;
   hipStream_t s;
-  hipError_t rec(int i) const {
-    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  Launch at(int i) const {
+    Launch L;
+    L.s = s;
+    if (ev) {
+      L.start = static_cast<hipEvent_t>(ev[2 * i]);
+      L.stop = static_cast<hipEvent_t>(ev[2 * i + 1]);
+    }
+    return L;
+  }
+  // A stage that enqueued no kernel still gets both events (zero length).
+  hipError_t close(const Launch& L) const {
+    if (!ev || L.launched) return hipSuccess;
+    const hipError_t e = hipEventRecord(L.start, s);
+    return e != hipSuccess ? e : hipEventRecord(L.stop, s);
   }
 };
 
@@ -75,8 +89,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
                    int64_t N, int64_t H, int64_t I, int dtype, void* workspace,
                    size_t workspace_bytes, void* stream, void* const* stage_events) {
   FfnPlan pl;
-  const int st = plan_ffn(N, H, I, dtype, &pl);
-  if (st != TOPMOE_OK) return st;
+  const int status = plan_ffn(N, H, I, dtype, &pl);
+  if (status != TOPMOE_OK) return status;
   // zero-size tensors (N == 0) are never touched and may be NULL
   if (!Wg || !Wu || !Wd || !workspace || (N > 0 && (!x || !y))) return TOPMOE_ERR_NULL_ARG;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
@@ -84,28 +98,28 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
       !aligned(y, 16) || !aligned(workspace, 256))
     return TOPMOE_ERR_BAD_ARG;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Events ev{stage_events, s};
+  const Stages st{stage_events, static_cast<hipStream_t>(stream)};
   char* ws = static_cast<char*>(workspace);
   void* h = ws + pl.off_h;
 
-  TOPMOE_TRY(ev.rec(0));
+  const Launch l0 = st.at(0);
   if (N > 0) {
     GemmParams up{};
     up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
     up.entries = nullptr; up.offsets = nullptr; up.alpha = nullptr;
     up.M = N; up.E = 1; up.k = 1; up.Nout = int(I); up.K = int(H);
-    TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, (N + pl.up.bm - 1) / pl.up.bm, s));
+    TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, (N + pl.up.bm - 1) / pl.up.bm, l0));
   }
-  TOPMOE_TRY(ev.rec(1));
+  TOPMOE_TRY(st.close(l0));
+  const Launch l1 = st.at(1);
   if (N > 0) {
     GemmParams dn{};
     dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = y;
     dn.entries = nullptr; dn.offsets = nullptr; dn.alpha = nullptr;
     dn.M = N; dn.E = 1; dn.k = 1; dn.Nout = int(H); dn.K = int(I);
-    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.down, dn, (N + pl.down.bm - 1) / pl.down.bm, s));
+    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.down, dn, (N + pl.down.bm - 1) / pl.down.bm, l1));
   }
-  TOPMOE_TRY(ev.rec(2));
+  TOPMOE_TRY(st.close(l1));
   return TOPMOE_OK;
 }
 
@@ -115,8 +129,8 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
                 int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
                 size_t workspace_bytes, void* stream, void* const* stage_events) {
   MoePlan pl;
-  const int st = plan_moe(N, H, I, E, k, dtype, &pl);
-  if (st != TOPMOE_OK) return st;
+  const int status = plan_moe(N, H, I, E, k, dtype, &pl);
+  if (status != TOPMOE_OK) return status;
   // zero-size tensors (N == 0) are never touched and may be NULL
   if (!Wr || !Wg || !Wu || !Wd || !aux_loss || !workspace ||
       (N > 0 && (!x || !y || !topk_idx || !alpha)))
@@ -129,8 +143,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
       !aligned(workspace, 256))
     return TOPMOE_ERR_BAD_ARG;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Events ev{stage_events, s};
+  const Stages st{stage_events, static_cast<hipStream_t>(stream)};
   char* ws = static_cast<char*>(workspace);
   int32_t* count_part = reinterpret_cast<int32_t*>(ws + pl.off_count_part);
   float* psum_part = reinterpret_cast<float*>(ws + pl.off_psum_part);
@@ -141,41 +154,46 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   float* slots = reinterpret_cast<float*>(ws + pl.off_slots);
 
   if (N == 0) {
-    for (int i = 0; i <= TOPMOE_MOE_STAGES; ++i) {
-      if (i == 1) TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, s));
-      TOPMOE_TRY(ev.rec(i));
+    for (int i = 0; i < TOPMOE_MOE_STAGES; ++i) {
+      const Launch L = st.at(i);
+      if (i == 1) TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, L));
+      TOPMOE_TRY(st.close(L));
     }
     return TOPMOE_OK;
   }
 
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
-  TOPMOE_TRY(ev.rec(0));
+  const Launch l0 = st.at(0);
   TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, pl.tb, pl.nblk, pl.router_mode,
-                           topk_idx, alpha, count_part, psum_part, s));
+                           topk_idx, alpha, count_part, psum_part, l0));
+  TOPMOE_TRY(st.close(l0));
   // 1: expert offsets, aux loss, stable scatter of entries into expert groups
-  TOPMOE_TRY(ev.rec(1));
+  const Launch l1 = st.at(1);
   TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, alpha, pl.nblk, E, k, pl.tb, N,
                             aux_coef, offsets, aux_loss, sorted_entry, alpha_g,
-                            sorted_token_ids, s));
+                            sorted_token_ids, l1));
+  TOPMOE_TRY(st.close(l1));
   // 2: grouped gate/up GEMM + SiLU * up
-  TOPMOE_TRY(ev.rec(2));
+  const Launch l2 = st.at(2);
   GemmParams up{};
   up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
   up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
   up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
-  TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, s));
+  TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
+  TOPMOE_TRY(st.close(l2));
   // 3: grouped down GEMM, alpha-scaled, into y (k == 1) or the k slots
-  TOPMOE_TRY(ev.rec(3));
+  const Launch l3 = st.at(3);
   GemmParams dn{};
   dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : static_cast<void*>(slots);
   dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha_g;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
-                         pl.down_mtiles, s));
+                         pl.down_mtiles, l3));
+  TOPMOE_TRY(st.close(l3));
   // 4: fixed-order combine of the k slots
-  TOPMOE_TRY(ev.rec(4));
-  if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, N, int(H), k, dtype, y, s));
-  TOPMOE_TRY(ev.rec(5));
+  const Launch l4 = st.at(4);
+  if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, N, int(H), k, dtype, y, l4));
+  TOPMOE_TRY(st.close(l4));
   return TOPMOE_OK;
 }
 

@@ -4,7 +4,7 @@
 namespace topmoe {
 
 hipError_t launch_gemm_f32(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
-                           hipStream_t s) {
+                           const Launch& s) {
   return launch_gemm_dtype<float>(kind, sh, p, mtiles, s);
 }
 

@@ -507,7 +507,7 @@ int resident_blocks(K kernel, int threads) {
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
-hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, hipStream_t s) {
+hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, const Launch& s) {
   const int64_t nt = (p.Nout + BN - 1) / BN;
   if (mtiles * nt <= 0) return hipSuccess;
   // persistent grid: at most the blocks resident at once, in whole rounds of
@@ -516,8 +516,7 @@ hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, hipStream_t s) {
   const int64_t cap = resident_blocks(kernel, 64 * WM * WN) / 8 * 8;
   int64_t grid = (mtiles * nt + 7) / 8 * 8;
   if (grid > cap && cap >= 8) grid = cap;
-  hipLaunchKernelGGL(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
 }
 
 // Launches a shape only when it is valid for the projection (LDS ring fits in
@@ -536,11 +535,11 @@ constexpr bool shape_ok() {
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND,
           bool OK = shape_ok<BM, BN, WM, WN, RB, S, KIND>()>
 struct ShapeLauncher {
-  static hipError_t run(const GemmParams&, int64_t, hipStream_t) { return hipErrorInvalidValue; }
+  static hipError_t run(const GemmParams&, int64_t, const Launch&) { return hipErrorInvalidValue; }
 };
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
-  static hipError_t run(const GemmParams& p, int64_t mtiles, hipStream_t s) {
+  static hipError_t run(const GemmParams& p, int64_t mtiles, const Launch& s) {
     return launch_gemm_t<T, BM, BN, WM, WN, RB, S, KIND>(p, mtiles, s);
   }
 };
@@ -556,7 +555,7 @@ struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
 #define TOPMOE_GEMM_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
 
 template <typename T, int KIND>
-hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, hipStream_t s) {
+hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, const Launch& s) {
 #define TOPMOE_TRY_SHAPE(BM_, BN_, WM_, WN_, RB_, S_)                                     \
   if (sh.bm == (BM_) && sh.bn == (BN_) && sh.wm == (WM_) && sh.wn == (WN_) &&            \
       sh.rb == (RB_) && sh.stages == (S_))                                               \
@@ -572,7 +571,7 @@ hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, 
 
 template <typename T>
 hipError_t launch_gemm_dtype(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
-                             hipStream_t s) {
+                             const Launch& s) {
   switch (kind) {
     case KIND_GATEUP: return launch_gemm_tiles<T, KIND_GATEUP>(sh, p, mtiles, s);
     case KIND_DOWN_Y: return launch_gemm_tiles<T, KIND_DOWN_Y>(sh, p, mtiles, s);

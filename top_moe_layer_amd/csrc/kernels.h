@@ -2,11 +2,42 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
+
+#include <tuple>
 
 #include "plan.h"
 
 namespace topmoe {
+
+// Where a launcher enqueues its kernel: the stream and, for stage timing,
+// optional events that the dispatch itself timestamps at the kernel's start
+// and end (hipExtLaunchKernel), so they bracket exactly the kernel's
+// execution.  `launched` tells the caller whether a kernel consumed them.
+struct Launch {
+  hipStream_t s = nullptr;
+  hipEvent_t start = nullptr, stop = nullptr;
+  mutable bool launched = false;
+};
+
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, unsigned shm,
+                         const Launch& L, A... a) {
+  L.launched = true;
+  if (L.start == nullptr && L.stop == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, shm, L.s, a...);
+    return hipGetLastError();
+  }
+  std::tuple<P...> args{P(a)...};
+  void* ptrs[sizeof...(P)];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, args);
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shm, L.s,
+                            L.start, L.stop, 0);
+}
 
 enum GemmKind {
   KIND_GATEUP = 0,      // h = SiLU(A Wg^T) * (A Wu^T), rows gathered from x
@@ -34,20 +65,20 @@ enum RouterMode {
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
                          int k, int tb, int nblk, int mode, int32_t* topk_idx, float* alpha,
-                         int32_t* count_part, float* psum_part, hipStream_t s);
+                         int32_t* count_part, float* psum_part, const Launch& s);
 
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                           const int32_t* topk_idx, const float* alpha, int nblk, int E, int k,
                           int tb, int64_t N, float coef, int32_t* offsets, float* aux,
                           int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
-                          hipStream_t s);
+                          const Launch& s);
 
 hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,
-                          int dtype, void* y, hipStream_t s);
+                          int dtype, void* y, const Launch& s);
 
-hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, hipStream_t s);
+hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s);
 
 hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
-                       int64_t mtiles, hipStream_t s);
+                       int64_t mtiles, const Launch& s);
 
 }  // namespace topmoe

@@ -185,34 +185,30 @@ hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                           const int32_t* topk_idx, const float* alpha, int nblk, int E, int k,
                           int tb, int64_t N, float coef, int32_t* offsets, float* aux,
                           int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
-                          hipStream_t s) {
+                          const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (int64_t(E) * nblk > kScanMax) return hipErrorInvalidValue;
   const int G = nblk > 256 ? (nblk + 255) / 256 : 1;  // router blocks per scatter block
   const int nsb = (nblk + G - 1) / G;
-  hipLaunchKernelGGL(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part, topk_idx,
-                     alpha, nblk, G, E, k, tb, N, coef, offsets, aux, sorted_entry, alpha_g,
-                     sorted_tok);
-  return hipGetLastError();
+  return launch_kernel(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part,
+                       topk_idx, alpha, nblk, G, E, k, tb, N, coef, offsets, aux, sorted_entry,
+                       alpha_g, sorted_tok);
 }
 
 hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,
-                          int dtype, void* y, hipStream_t s) {
+                          int dtype, void* y, const Launch& s) {
   const int64_t work = N * (H / 4);
   if (work <= 0) return hipSuccess;
   const int64_t grid = (work + 255) / 256;
   if (dtype == TOPMOE_DTYPE_FP32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
-                       H, k, static_cast<float*>(y));
-  else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
+    return launch_kernel(combine_kernel<float>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
+                         H, k, static_cast<float*>(y));
+  return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
                        H, k, static_cast<bf16_t*>(y));
-  return hipGetLastError();
 }
 
-hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, hipStream_t s) {
-  hipLaunchKernelGGL(empty_route_kernel, dim3(1), dim3(128), 0, s, E, offsets, aux);
-  return hipGetLastError();
+hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s) {
+  return launch_kernel(empty_route_kernel, dim3(1), dim3(128), 0, s, E, offsets, aux);
 }
 
 }  // namespace topmoe

@@ -254,33 +254,31 @@ __global__ __launch_bounds__(256, 1) void router_split_kernel(
 template <typename T>
 hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E, int k, int tb,
                            int nblk, int mode, int32_t* topk_idx, float* alpha,
-                           int32_t* count_part, float* psum_part, hipStream_t s) {
+                           int32_t* count_part, float* psum_part, const Launch& s) {
   int ep = 1;
   while (ep < E) ep *= 2;
   const size_t lds = mode == ROUTER_MODE_LDS ? size_t(ep) * H * sizeof(float) : 0;
-#define TOPMOE_ROUTER(EPV)                                                                 \
-  if (mode == ROUTER_MODE_LDS)                                                             \
-    hipLaunchKernelGGL((router_lds_kernel<T, EPV>), dim3(nblk), dim3(256), lds, s, x, Wr, N, \
-                       H, E, k, tb, topk_idx, alpha, count_part, psum_part);              \
-  else                                                                                     \
-    hipLaunchKernelGGL((router_split_kernel<T, EPV>), dim3(nblk), dim3(256), 0, s, x, Wr,   \
-                       N, H, E, k, tb, topk_idx, alpha, count_part, psum_part)
-  if (E <= 1) { TOPMOE_ROUTER(1); }
-  else if (E <= 2) { TOPMOE_ROUTER(2); }
-  else if (E <= 4) { TOPMOE_ROUTER(4); }
-  else if (E <= 8) { TOPMOE_ROUTER(8); }
-  else if (E <= 16) { TOPMOE_ROUTER(16); }
-  else if (E <= 32) { TOPMOE_ROUTER(32); }
-  else { TOPMOE_ROUTER(64); }
+#define TOPMOE_ROUTER(EPV)                                                                  \
+  return mode == ROUTER_MODE_LDS                                                            \
+             ? launch_kernel(router_lds_kernel<T, EPV>, dim3(nblk), dim3(256), unsigned(lds), \
+                             s, x, Wr, N, H, E, k, tb, topk_idx, alpha, count_part, psum_part) \
+             : launch_kernel(router_split_kernel<T, EPV>, dim3(nblk), dim3(256), 0, s, x, Wr,  \
+                             N, H, E, k, tb, topk_idx, alpha, count_part, psum_part)
+  if (E <= 1) TOPMOE_ROUTER(1);
+  if (E <= 2) TOPMOE_ROUTER(2);
+  if (E <= 4) TOPMOE_ROUTER(4);
+  if (E <= 8) TOPMOE_ROUTER(8);
+  if (E <= 16) TOPMOE_ROUTER(16);
+  if (E <= 32) TOPMOE_ROUTER(32);
+  TOPMOE_ROUTER(64);
 #undef TOPMOE_ROUTER
-  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
                          int k, int tb, int nblk, int mode, int32_t* topk_idx, float* alpha,
-                         int32_t* count_part, float* psum_part, hipStream_t s) {
+                         int32_t* count_part, float* psum_part, const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (dtype == TOPMOE_DTYPE_FP32)
     return launch_router_t(static_cast<const float*>(x), Wr, N, H, E, k, tb, nblk, mode,
