@@ -42,7 +42,9 @@
  * Shape limits: N >= 0 (N == 0 is a no-op apart from zeroed offsets and aux;
  * then x, y, topk_idx, alpha and sorted_token_ids may be NULL),
  * H and I positive multiples of 64, 1 <= E <= 64, 1 <= k <= E,
- * N * max(k, 1) < 2^31 and N * H, N * k * max(H, I) < 2^40.
+ * N * max(k, 1) < 2^31, and every GEMM operand below 4 GiB: x (N * H), the
+ * intermediate (N * k * I) and one expert's W_gate / W_up / W_down (I * H),
+ * counted in bytes of the dtype.
  */
 #ifndef TOPMOE_H
 #define TOPMOE_H

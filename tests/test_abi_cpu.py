@@ -93,6 +93,13 @@ def test_moe_validation_codes(L):
     assert moe_call(k=5) == B.ERR_BAD_SHAPE
     assert moe_call(k=0) == B.ERR_BAD_SHAPE
     assert moe_call(N=-3) == B.ERR_BAD_SHAPE
+    # every GEMM operand below 4 GiB: x (N*H), the intermediate (N*k*I), one expert's weights
+    assert moe_call(N=1 << 21, H=1024, k=1) == B.ERR_BAD_SHAPE            # x = 4 GiB bf16
+    assert moe_call(N=(1 << 21) - 1, H=1024, k=1) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_call(N=1 << 20, I=1024, k=2) == B.ERR_BAD_SHAPE            # h = 4 GiB bf16
+    assert moe_call(H=1 << 16, I=1 << 15) == B.ERR_BAD_SHAPE              # W_e = 4 GiB bf16
+    assert moe_call(H=1 << 16, I=(1 << 15) - 64) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_call(H=1 << 15, I=1 << 15, dtype=B.DTYPE_FP32) == B.ERR_BAD_SHAPE
     assert moe_call(dtype=2) == B.ERR_UNSUPPORTED_DTYPE
     assert moe_call(coef=-0.5) == B.ERR_BAD_ARG
     assert moe_call(coef=float("nan")) == B.ERR_BAD_ARG
@@ -110,6 +117,8 @@ def test_ffn_validation_codes(L):
     assert ffn_call(N=0, x=None, y=None) == B.ERR_WORKSPACE_TOO_SMALL
     assert ffn_call(H=0) == B.ERR_BAD_SHAPE
     assert ffn_call(I=100) == B.ERR_BAD_SHAPE
+    assert ffn_call(N=1 << 20, I=2048) == B.ERR_BAD_SHAPE                  # h = 4 GiB bf16
+    assert ffn_call(N=1 << 20, I=2048 - 64) == B.ERR_WORKSPACE_TOO_SMALL
     assert ffn_call(dtype=-1) == B.ERR_UNSUPPORTED_DTYPE
     assert ffn_call() == B.ERR_WORKSPACE_TOO_SMALL
     need = B.raw_ffn_workspace_bytes(8, 64, 64, B.DTYPE_BF16)

@@ -94,6 +94,15 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// A pointer that is the same on every lane, moved to scalar registers so that
+// base + 32-bit lane offset compiles to the saddr + voffset load form.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
+
 // s_waitcnt with vmcnt(N) and the other counters left at their maxima.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -244,35 +253,43 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       rid[j] = (KIND == KIND_GATEUP && p.entries != nullptr && r < BM) ? p.entries[gr] / p.k : gr;
     }
   };
-  auto make_src = [&](const Tile& t, const int32_t(&rid)[LPW], const char* (&src)[LPW]) {
+  int32_t rid[LPW];          // A-row indices of the next tile
+  const char* sbase[LPW];    // per-load base pointers (uniform) of the tile being issued
+  uint32_t voff[LPW];        // per-lane byte offsets from them
+  // Load j of a wavefront covers RPI consecutive LDS rows, all in one of the
+  // A, B0, B1 regions (BM, BN are multiples of 32), so its base pointer is
+  // uniform (scalar registers) and each lane keeps only a 32-bit byte offset
+  // (the global_load_lds saddr + voffset form).  Operand matrices are below
+  // 4 GiB (x and h as a whole, each expert's weight matrix on its own).
+  auto make_src = [&](const Tile& t, const int32_t(&rid)[LPW]) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int r = (wid * LPW + j) * RPI + lane / CH;
+      const int r0 = (wid * LPW + j) * RPI;  // first row of the load (uniform)
+      const int r = r0 + lane / CH;
       const int chunk = (lane % CH) ^ ((r / RPW) % CH);
-      const char* base;
-      if (r < BM) {
-        base = static_cast<const char*>(p.A) + int64_t(rid[j]) * p.K * int64_t(sizeof(T));
+      if (r0 < BM) {
+        sbase[j] = static_cast<const char*>(p.A);
+        voff[j] = uint32_t(rid[j]) * uint32_t(p.K * int(sizeof(T))) + uint32_t(chunk * 16);
       } else {
         const int rb = r - BM;
-        const int which = rb >= BN ? 1 : 0;
+        const int which = (r0 - BM) >= BN ? 1 : 0;
         int n = t.n0 + rb - which * BN;
         n = n < p.Nout ? n : p.Nout - 1;
-        const void* W = which ? p.B1 : p.B0;
-        base = static_cast<const char*>(W) + (int64_t(t.e) * p.Nout + n) * p.K * int64_t(sizeof(T));
+        sbase[j] = static_cast<const char*>(which ? p.B1 : p.B0) +
+                   int64_t(t.e) * p.Nout * p.K * int64_t(sizeof(T));
+        voff[j] = uint32_t(n) * uint32_t(p.K * int(sizeof(T))) + uint32_t(chunk * 16);
       }
-      src[j] = base + chunk * 16;
     }
   };
-  int32_t rid[LPW];      // A-row indices of the next tile
-  const char* src[LPW];  // load sources of the tile whose slices are being issued
   auto slot_ptr = [&](int slot) -> char* {
     return slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
   };
   auto issue = [&](int kt, char* slot_base) {
-    const int64_t ko = int64_t(kt) * RB;
+    const uint32_t ko = uint32_t(kt) * RB;
     char* dst = slot_base + wid * LPW * 1024;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) lds_dma16(src[j] + ko, dst + j * 1024);
+    for (int j = 0; j < LPW; ++j)
+      lds_dma16(uniform_ptr(sbase[j]) + uint64_t(voff[j] + ko), dst + j * 1024);
   };
 
   f32x16 acc[NB][TM][TN];
@@ -414,7 +431,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   const bool stream = (KT % S) == 0;
   Tile cur = decode(0);
   load_rows(cur, rid);
-  make_src(cur, rid, src);
+  make_src(cur, rid);
   Tile nxt = cur;
   if (stream && n_my > 1) {
     nxt = decode(1);
@@ -441,8 +458,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     for (; stream ? (kt < KT) : (kt + 2 * S - 1 < KT); kt += S) {
       const bool last_group = kt + S >= KT;
       if (last_group) {
-        // this tile's slices are all issued: `src` moves on to the next tile
-        if (xnext) make_src(nxt, rid, src);
+        // this tile's slices are all issued: the sources move on to the next tile
+        if (xnext) make_src(nxt, rid);
         load_meta(cur);
       }
       // the very last slices of the block: nothing left to fetch, drain
@@ -481,7 +498,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     } else if (has_next) {
       cur = decode(cj + 1);
       load_rows(cur, rid);
-      make_src(cur, rid, src);
+      make_src(cur, rid);
     }
   }
 }

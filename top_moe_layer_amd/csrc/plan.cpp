@@ -11,7 +11,13 @@ namespace topmoe {
 namespace {
 
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // int32 row / entry ids
-constexpr int64_t kMaxElems = int64_t(1) << 40;
+// The GEMMs address operand rows with 32-bit byte offsets from a per-matrix
+// (per-expert for weights) base, so each operand matrix stays below 4 GiB.
+// (Products are formed in double: exact below 2^53, and anything near or past
+// that is far over the limit anyway.)
+bool operand_ok(int64_t rows, int64_t cols, int elem) {
+  return double(rows) * double(cols) * double(elem) < 4294967296.0;
+}
 
 bool dtype_ok(int dtype) { return dtype == TOPMOE_DTYPE_FP32 || dtype == TOPMOE_DTYPE_BF16; }
 
@@ -117,7 +123,8 @@ GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int d
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
   if (!dtype_ok(dtype)) return TOPMOE_ERR_UNSUPPORTED_DTYPE;
   if (N < 0 || H < 64 || I < 64 || H % 64 || I % 64) return TOPMOE_ERR_BAD_SHAPE;
-  if (N > kMaxRows || N * H >= kMaxElems || N * I >= kMaxElems || H * I >= kMaxElems)
+  const int el = elem_bytes(dtype);
+  if (N > kMaxRows || !operand_ok(N, H, el) || !operand_ok(N, I, el) || !operand_ok(I, H, el))
     return TOPMOE_ERR_BAD_SHAPE;
   FfnPlan q;
   q.N = N; q.H = H; q.I = I; q.dtype = dtype; q.elem = elem_bytes(dtype);
@@ -135,8 +142,9 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   if (N < 0 || H < 64 || I < 64 || H % 64 || I % 64) return TOPMOE_ERR_BAD_SHAPE;
   if (E < 1 || E > 64 || k < 1 || k > E) return TOPMOE_ERR_BAD_SHAPE;
   const int64_t rows = N * k;
-  if (rows > kMaxRows || rows * H >= kMaxElems || rows * I >= kMaxElems ||
-      int64_t(E) * H * I >= kMaxElems)
+  const int el = elem_bytes(dtype);
+  if (rows > kMaxRows || !operand_ok(N, H, el) || !operand_ok(rows, I, el) ||
+      !operand_ok(I, H, el))
     return TOPMOE_ERR_BAD_SHAPE;
   MoePlan q;
   q.N = N; q.H = H; q.I = I; q.E = E; q.k = k; q.dtype = dtype; q.elem = elem_bytes(dtype);
