@@ -53,15 +53,40 @@ __global__ __launch_bounds__(256) void permute_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool first = blockIdx.x == 0;
   const int total = E * nblk;
-  // one batch of independent loads: all counts (and, in block 0, all sums of p)
-  for (int i = tid; i < total; i += 256) {
-    s_c[i] = count_part[i];
-    if (first) s_p[i] = psum_part[i];
+  const int bfirst = int(blockIdx.x) * G;
+  // This block's entries: wavefront 0 fetches the first 64 now, so their
+  // latency overlaps the staging below.
+  const int64_t tok0 = int64_t(bfirst) * tb;
+  const int64_t tok1 = tok0 + int64_t(G) * tb < N ? tok0 + int64_t(G) * tb : N;
+  const int64_t e0 = tok0 * k, e1 = tok1 * k;
+  int ex_first = -1;
+  float al_first = 0.f;
+  if (wave == 0 && e0 + lane < e1) {
+    ex_first = topk_idx[e0 + lane];
+    al_first = alpha[e0 + lane];
+  }
+  // All counts (and, in block 0, all sums of p), 8 loads per thread in flight.
+  for (int base = 0; base < total; base += 256 * 8) {
+    int c[8];
+    float ps[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * 256 + tid;
+      c[j] = i < total ? count_part[i] : 0;
+      ps[j] = (first && i < total) ? psum_part[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * 256 + tid;
+      if (i < total) {
+        s_c[i] = c[j];
+        if (first) s_p[i] = ps[j];
+      }
+    }
   }
   if (tid < 64) run[tid] = 0;
   __syncthreads();
 
-  const int bfirst = int(blockIdx.x) * G;
   for (int e = wave; e < E; e += 4) {
     int tot = 0, pre = 0;
     double ps = 0.0;
@@ -98,16 +123,12 @@ __global__ __launch_bounds__(256) void permute_kernel(
   __syncthreads();
 
   if (wave == 0) {
-    const int64_t tok0 = int64_t(bfirst) * tb;
-    int64_t tok1 = tok0 + int64_t(G) * tb;
-    tok1 = tok1 < N ? tok1 : N;
-    const int64_t e0 = tok0 * k, e1 = tok1 * k;
     const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     for (int64_t base = e0; base < e1; base += 64) {
       const int64_t ent = base + lane;
       const bool valid = ent < e1;
-      const int ex = valid ? topk_idx[ent] : -1;
-      const float al = valid ? alpha[ent] : 0.f;
+      const int ex = base == e0 ? ex_first : valid ? topk_idx[ent] : -1;
+      const float al = base == e0 ? al_first : valid ? alpha[ent] : 0.f;
       uint64_t peers = 0ull;  // lanes holding the same expert
       uint64_t todo = __ballot(valid);
       while (todo) {

@@ -76,19 +76,20 @@ bool env_shape(const char* name, GemmShape* out) {
 }
 
 // Launch-shape tables: rates measured on MI355X over the dense bf16
-// 16384 x 2048 x 6464 projections (sustained whole-chip TFLOP/s).
+// 16384 x 2048 x 6464 projections (sustained whole-chip TFLOP/s).  All are
+// 8-wavefront tiles with 128-byte LDS rows: a direct-to-LDS load of 64-byte
+// row pieces touches half of each 128-byte cache line and moves about half
+// the bytes per clock (measured 32 against 59 B/clk/CU from L2).
 const Cand kGateupBf16[] = {
-    {{256, 128, 4, 2, 64, 3}, 1120.0, 1},
-    {{128, 128, 2, 4, 64, 4}, 890.0, 1},
-    {{128, 64, 2, 2, 128, 2}, 890.0, 2},
-    {{64, 64, 2, 2, 128, 3}, 840.0, 2},
+    {{256, 128, 4, 2, 128, 2}, 1146.0, 1},
+    {{128, 128, 2, 4, 128, 3}, 1056.0, 1},
+    {{256, 64, 4, 2, 128, 3}, 1033.0, 1},
 };
 const Cand kDownBf16[] = {
-    {{256, 256, 4, 2, 64, 4}, 1090.0, 1},
-    {{128, 128, 2, 2, 128, 2}, 960.0, 2},
-    {{128, 128, 2, 4, 64, 4}, 810.0, 1},
-    {{128, 64, 2, 2, 128, 3}, 780.0, 2},
-    {{64, 64, 2, 2, 128, 4}, 640.0, 2},
+    {{256, 128, 4, 2, 128, 3}, 1093.0, 1},
+    {{256, 256, 4, 2, 64, 4}, 1025.0, 1},
+    {{128, 128, 2, 4, 128, 3}, 893.0, 1},
+    {{256, 64, 4, 2, 128, 3}, 786.0, 1},
 };
 const Cand kFp32[] = {
     {{128, 64, 2, 2, 128, 2}, 100.0, 2},
@@ -96,26 +97,26 @@ const Cand kFp32[] = {
 };
 
 // Few rows per group and long K: the projection streams weights from HBM.
-// MFMA work is then nearly free; what counts is the number of weight bytes in
-// flight per CU, which the 8-wavefront 128 x 128 tile with a 4-deep ring
-// maximises (measured on the 32-token decode step: 41 us gate/up and 25 us
-// down against 46 / 27 us with 64 x 64 tiles).
+// MFMA work is then nearly free; what counts is the weight bytes in flight
+// per CU, which the 8-wavefront 128 x 128 tile with 128-byte rows maximises
+// (measured on the 32-token decode step: 30 us gate/up with a 3-deep ring and
+// 19 us down with a 4-deep ring, against 41 / 24 us with 64 x 64 tiles).
 bool weight_streaming(int64_t M, int groups) { return M <= int64_t(groups) * 32; }
 
 }  // namespace
 
 GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 2);
-  GemmShape sh = weight_streaming(M, groups) ? GemmShape{128, 128, 2, 4, 64, 4}
-                                             : choose(kGateupBf16, 4, M, Nout, K, groups, 2);
+  GemmShape sh = weight_streaming(M, groups) ? GemmShape{128, 128, 2, 4, 128, 3}
+                                             : choose(kGateupBf16, 3, M, Nout, K, groups, 2);
   env_shape("TOPMOE_GATEUP_TILE", &sh);
   return sh;
 }
 
 GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 1);
-  GemmShape sh = weight_streaming(M, groups) ? GemmShape{128, 128, 2, 4, 64, 4}
-                                             : choose(kDownBf16, 5, M, Nout, K, groups, 1);
+  GemmShape sh = weight_streaming(M, groups) ? GemmShape{128, 128, 2, 4, 128, 4}
+                                             : choose(kDownBf16, 4, M, Nout, K, groups, 1);
   env_shape("TOPMOE_DOWN_TILE", &sh);
   return sh;
 }
@@ -149,18 +150,20 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   MoePlan q;
   q.N = N; q.H = H; q.I = I; q.E = E; q.k = k; q.dtype = dtype; q.elem = elem_bytes(dtype);
   q.rows = rows;
-  // Router.  W_router in LDS (<= 64 KB, so two blocks share a CU) with one
-  // token per wavefront when there are tokens enough to fill the chip;
-  // otherwise every block splits each of its tokens over its 4 wavefronts.
-  // Tokens per block: enough blocks to cover the 256 CUs, at most 4096 blocks
-  // so the single-block offset scan stays short.
+  // Router.  With W_router small enough for LDS (<= 64 KB, so two blocks
+  // share a CU) and enough tokens, one-wavefront blocks copy it once and
+  // route 16 tokens per pass (four lanes per token); about 1024 blocks of
+  // whole passes.  With few tokens (decode) or a large W_router, one token
+  // per 4-wavefront block, H split over the wavefronts.
   int ep = 1;
   while (ep < E) ep *= 2;
-  const bool lds_fits = int64_t(ep) * H * 4 <= 64 * 1024 && H <= 2048;
-  q.router_mode = (lds_fits && N >= 4096) ? 0 : 1;
-  // mode 0: about 1024 blocks of whole-wavefront token groups (multiples of 4)
-  int64_t tb = q.router_mode == 0 ? 4 : 1;
-  while (q.router_mode == 0 && (N + tb - 1) / tb > 1024) tb += 4;
+  const bool lds_fits = int64_t(ep) * H * 4 <= 64 * 1024;
+  q.router_mode = (lds_fits && N >= 256) ? 0 : 1;
+  int64_t tb = 1;
+  if (q.router_mode == 0) {
+    const int64_t passes = (N + 15) / 16;
+    tb = 16 * ((passes + 1023) / 1024);
+  }
   // the permutation kernel stages E * blocks counts in LDS: at most 8192
   while (N > 0 && ((N + tb - 1) / tb) * E > 8192) tb *= 2;
   q.tb = int(tb);

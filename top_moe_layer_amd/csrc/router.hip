@@ -1,14 +1,16 @@
 // Router: logits r = W_router x, p = softmax(r), S = TopK(p, k) and the
-// renormalised weights alpha = p_S / (sum p_S + 1e-20), one token per
-// wavefront (MiniMind lesson 13, section 1.5 router equations and walkthrough
-// steps 4-5).  Each block also emits, for its tokens, the per-expert
-// selection counts and the per-expert sums of p that the offsets and
-// load-balancing loss need (lesson 13, section 1.6), stored expert-major
-// ([E, blocks]) so the offset scan reads them contiguously.
+// renormalised weights alpha = p_S / (sum p_S + 1e-20) (MiniMind lesson 13,
+// section 1.5 router equations and walkthrough steps 4-5).  Each block also
+// emits, for its tokens, the per-expert selection counts and the per-expert
+// sums of p that the offsets and load-balancing loss need (lesson 13, section
+// 1.6), stored expert-major ([E, blocks]) so the offset scan reads them
+// contiguously.
 //
-// Work layout: a lane owns x[h] for h = 4l + 256i (of the whole row or of one
+// Work layout: a lane owns x[h] for h = 4l + 256g (of the whole row or of one
 // quarter of it) and accumulates one partial dot product per expert; a
-// transposing butterfly then leaves expert e's logit on lane e.
+// transposing butterfly then leaves expert e's logit on lane e.  Softmax and
+// top-k reduce over the first EP lanes only (EP = E rounded up to a power of
+// two; the other lanes hold -inf / 0 and would not change the result).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -41,10 +43,6 @@ struct Log2 { static constexpr int v = 1 + Log2<EP / 2>::v; };
 template <>
 struct Log2<1> { static constexpr int v = 0; };
 
-// Transposing butterfly: lane l holds EP partial sums (one per expert); after
-// log2(EP) exchange steps each lane keeps one expert, l >> (6 - log2 EP), and
-// plain butterfly steps finish the sum.  Lane e (< EP) then receives expert e.
-// E - 1 + log2(64 / E) + 1 shuffles instead of 6 E.
 // One exchange step of the transposing butterfly (S-th of log2 EP): lanes
 // with bit (32 >> S) set keep the upper half of their values, the others the
 // lower half, each adding its partner's copy.  Indices are compile-time.
@@ -75,114 +73,86 @@ __device__ __forceinline__ float reduce_logits(float (&acc)[EP], int lane) {
   return __shfl(acc[0], (lane << (6 - LOG_EP)) & 63, 64);
 }
 
-// Softmax over the E logits held by lanes 0..E-1, then k rounds of a
-// wave-wide max over (p bits, 64 - lane): larger p first, equal p to the
-// lower expert id (p >= 0, so its bits order it).  Writes topk_idx / alpha
-// for token t, counts the selections in s_cnt and adds p to psum (lane e).
-__device__ __forceinline__ void route_token(float r_lane, int lane, int E, int k, int64_t t,
-                                            int32_t* __restrict__ topk_idx,
-                                            float* __restrict__ alpha, int* s_cnt,
-                                            float& psum) {
-  const float r = lane < E ? r_lane : -INFINITY;
-  const float m = wave_max(r);
-  const float ex = lane < E ? expf(r - m) : 0.f;
-  const float s = wave_sum(ex);
-  const float p = ex / s;
-  psum += p;
-  uint64_t key = lane < E ? ((uint64_t(__float_as_uint(p)) << 32) | uint32_t(64 - lane)) : 0ull;
-  int my_e = 0;
-  float my_p = 0.f, ssum = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_u64(key);
-    const int e = 64 - int(uint32_t(best));
-    const float pv = __uint_as_float(uint32_t(best >> 32));
-    ssum += pv;
-    if (lane == j) { my_e = e; my_p = pv; }
-    if (lane == e) key = 0ull;
+// Reductions over lanes 0..W-1 (and, identically, every aligned group of W).
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+template <int W>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) {
+    const uint64_t w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
   }
-  if (lane < k) {
-    topk_idx[t * k + lane] = my_e;
-    alpha[t * k + lane] = my_p / (ssum + 1e-20f);
-    atomicAdd(&s_cnt[my_e], 1);  // integer count: order-independent
+  return v;
+}
+
+// Softmax over the E logits of each of TPW tokens (token u's logit e on lane
+// e < E of r[u]), then k rounds of a max over (p bits, 64 - lane): larger p
+// first, equal p to the lower expert id (p >= 0, so its bits order it).  The
+// TPW tokens go through each step together, so their shuffle chains overlap.
+// Writes topk_idx / alpha of the valid tokens, counts their selections in
+// s_cnt and adds their p to psum (lane e).
+template <int EP, int TPW>
+__device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, int E, int k,
+                                             int64_t t_first, int64_t t_end,
+                                             int32_t* __restrict__ topk_idx,
+                                             float* __restrict__ alpha, int* s_cnt,
+                                             float& psum) {
+  const bool expert_lane = lane < E;
+  float p[TPW];
+  uint64_t key[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const float ru = expert_lane ? r[u] : -INFINITY;
+    const float m = group_max<EP>(ru);
+    const float ex = expert_lane ? expf(ru - m) : 0.f;
+    const float sum = group_sum<EP>(ex);
+    p[u] = expert_lane ? ex / sum : 0.f;  // (lanes past EP see an all-zero group)
+    if (t_first + u < t_end) psum += p[u];
+    key[u] = expert_lane ? ((uint64_t(__float_as_uint(p[u])) << 32) | uint32_t(64 - lane)) : 0ull;
+  }
+  int my_e[TPW];
+  float my_p[TPW], ssum[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) { my_e[u] = 0; my_p[u] = 0.f; ssum[u] = 0.f; }
+  for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const uint64_t best = group_max_u64<EP>(key[u]);
+      const int e = 64 - int(uint32_t(best));
+      const float pv = __uint_as_float(uint32_t(best >> 32));
+      ssum[u] += pv;
+      if (lane == j) { my_e[u] = e; my_p[u] = pv; }
+      if (lane == e) key[u] = 0ull;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int64_t t = t_first + u;
+    if (lane < k && t < t_end) {
+      topk_idx[t * k + lane] = my_e[u];
+      alpha[t * k + lane] = my_p[u] / (ssum[u] + 1e-20f);
+      atomicAdd(&s_cnt[my_e[u]], 1);  // integer count: order-independent
+    }
   }
 }
 
-// Mode 1 (EP * H * 4 <= 64 KB, H <= 2048): the block stages W_router in LDS
-// once, padded with zero rows to EP experts; each wavefront routes tokens
-// t0 + w, t0 + w + 4, ...  Lane l owns x[h] for h = 4l + 256g; lanes past H
-// read a clamped address and use x = 0, so the inner loops have no branches.
-// The next token's row is loaded into registers while the current one runs.
-template <typename T, int EP>
-__global__ __launch_bounds__(256, 1) void router_lds_kernel(
-    const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
-    int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
-    int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
-  constexpr int NG = 8;  // H <= 256 * NG
-  extern __shared__ __attribute__((aligned(16))) f32x4 s_w4[];  // [EP, H / 4]
-  __shared__ int s_cnt[64];
-  __shared__ float s_ps[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 64) s_cnt[tid] = 0;
-  const int h4 = H >> 2;
-  const int nreal = E * h4, nall = EP * h4;
-  for (int i = tid; i < nall; i += 256)
-    s_w4[i] = i < nreal ? reinterpret_cast<const f32x4*>(Wr)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int ng = (H + 255) >> 8;
-  const int64_t t0 = int64_t(blockIdx.x) * tb;
-  const int64_t t1 = (t0 + tb < N) ? t0 + tb : N;
-  auto load_row = [&](int64_t t, float (&dst)[NG][4]) {
-    const T* xr = x + t * H;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g < ng) {  // wave-uniform
-        const int h = lane * 4 + 256 * g;
-        const bool ok = h < H;
-        load4<T>(xr + (ok ? h : 0), dst[g]);
-        if (!ok) dst[g][0] = dst[g][1] = dst[g][2] = dst[g][3] = 0.f;
-      }
-    }
-  };
-  float psum = 0.f;
-  auto compute = [&](int64_t t, const float (&xv)[NG][4]) {
-    float acc[EP];
-#pragma unroll
-    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (g < ng) {  // wave-uniform
-        const int h = lane * 4 + 256 * g;
-        const int q = (h < H ? h : 0) >> 2;
-#pragma unroll
-        for (int e = 0; e < EP; ++e) {
-          const f32x4 w = s_w4[e * h4 + q];
-          float a = acc[e];
-          a = fmaf(xv[g][0], w.x, a);
-          a = fmaf(xv[g][1], w.y, a);
-          a = fmaf(xv[g][2], w.z, a);
-          a = fmaf(xv[g][3], w.w, a);
-          acc[e] = a;
-        }
-      }
-    }
-    const float r = reduce_logits<EP>(acc, lane);
-    route_token(r, lane, E, k, t, topk_idx, alpha, s_cnt, psum);
-  };
-  // two statically named row buffers, so the prefetch stays in registers
-  float xa[NG][4], xb[NG][4];
-  int64_t t = t0 + wave;
-  if (t < t1) load_row(t, xa);
-  __syncthreads();  // W_router staged
-  for (; t < t1; t += 8) {
-    if (t + 4 < t1) load_row(t + 4, xb);
-    compute(t, xa);
-    if (t + 4 >= t1) break;
-    if (t + 8 < t1) load_row(t + 8, xa);
-    compute(t + 4, xb);
-  }
-
-  s_ps[wave][lane] = psum;
-  __syncthreads();
+// Block epilogue: per-expert count and sum of p of the block's tokens,
+// written expert-major at [e * gridDim.x + block].
+__device__ __forceinline__ void write_block_partials(int tid, int E, const int* s_cnt,
+                                                     const float (*s_ps)[64],
+                                                     int32_t* __restrict__ count_part,
+                                                     float* __restrict__ psum_part) {
   if (tid < E) {
     const int64_t o = int64_t(tid) * gridDim.x + blockIdx.x;
     psum_part[o] = (s_ps[0][tid] + s_ps[1][tid]) + (s_ps[2][tid] + s_ps[3][tid]);
@@ -190,17 +160,208 @@ __global__ __launch_bounds__(256, 1) void router_lds_kernel(
   }
 }
 
-// Mode 2 (large W_router, or few tokens): the four wavefronts of a block
-// split H into quarters of one token; partial logits meet in LDS and
-// wavefront 0 finishes the token.  The block walks its tokens in order.
-// Experts past E read row E-1 (in bounds); their lanes are masked later.
+// Sum over the 4 lanes of a quad (lanes 4q..4q+3) with two DPP moves; every
+// lane of the quad gets (v0 + v1) + (v2 + v3) (the same bits, as + commutes).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // xor 1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // xor 2
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack16(const u32x4& q, float (&v)[16 / sizeof(T)]);
+template <>
+__device__ __forceinline__ void unpack16<float>(const u32x4& q, float (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(q[i]);
+}
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const u32x4& q, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(q[i] << 16);
+    v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+  }
+}
+
+// Mode LDS (EP * H * 4 <= 64 KB): one wavefront per block routes 16 tokens
+// per pass, four lanes per token.  W_router is copied into LDS once per block
+// with direct-to-LDS loads (all in flight together) and padded with zero rows
+// to EP experts.  Lane 4u + j of token u loads 16-byte pieces j, j + 4,
+// j + 8, ... of the token's row (the token's four lanes read 64 contiguous
+// bytes per load) and accumulates E partial logits against W_router columns
+// read from LDS (the 16 tokens share each read); a quad sum completes the
+// logits, and every lane of the quad then runs the softmax and the top-k of
+// its token on its own, with no cross-lane traffic.  The block owns tokens
+// [t0, t0 + tb).  Per-expert sums of p go through LDS in token order.
 template <typename T, int EP>
-__global__ __launch_bounds__(256, 1) void router_split_kernel(
+__global__ __launch_bounds__(64) void router_lds_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
     int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
     int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
+  constexpr int VE = 16 / int(sizeof(T));  // elements per 16-byte load
+  constexpr int CI = 8;                    // loads per lane in flight per chunk
+  extern __shared__ __attribute__((aligned(1024))) f32x4 s_w4[];  // [EP, H / 4], 1 KB-rounded
+  __shared__ int s_cnt[64];
+  __shared__ float s_pt[16][EP + 1];  // p of the pass's 16 tokens
+  const int lane = threadIdx.x;
+  const int part = lane & 3, tok = lane >> 2;
+  const int h4 = H >> 2;
+  const int ni = H / (4 * VE);  // loads per lane per row (H is a multiple of 64)
+  const int64_t t0 = int64_t(blockIdx.x) * tb;
+  const int64_t t1 = (t0 + tb < N) ? t0 + tb : N;
+
+  // W_router: 1 KB direct-to-LDS loads (lanes past the real rows fetch a
+  // clamped element; those slots are zeroed afterwards).
+  const int nreal = E * h4, nall = EP * h4;
+  {
+    const f32x4* W4 = reinterpret_cast<const f32x4*>(Wr);
+    for (int c = 0; c * 64 < nreal; ++c) {
+      const int i = c * 64 + lane;
+      __builtin_amdgcn_global_load_lds(W4 + (i < nreal ? i : nreal - 1),
+                                       (__attribute__((address_space(3))) void*)(s_w4 + c * 64),
+                                       16, 0, 0);
+    }
+  }
+  s_cnt[lane] = 0;
+  float psum = 0.f;  // lane e < E: sum of p_e over the block's tokens
+  bool staged = false;
+
+  for (int64_t tp = t0; tp < t1; tp += 16) {
+    const int64_t t = tp + tok;
+    const bool valid = t < t1;
+    const T* xr = x + (valid ? t : t1 - 1) * H + part * VE;
+    float acc[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+    // Row pieces in chunks of CI loads, double-buffered: chunk c + 1 is in
+    // flight while chunk c is multiplied.
+    auto load_chunk = [&](int i0, u32x4(&xq)[CI]) {
+#pragma unroll
+      for (int c = 0; c < CI; ++c) {
+        const int i = i0 + c < ni ? i0 + c : ni - 1;
+        xq[c] = *reinterpret_cast<const u32x4*>(xr + i * 4 * VE);
+      }
+    };
+    auto fma_chunk = [&](int i0, const u32x4(&xq)[CI]) {
+#pragma unroll
+      for (int c = 0; c < CI; ++c) {
+        if (i0 + c < ni) {  // wave-uniform
+          float xv[VE];
+          unpack16<T>(xq[c], xv);
+          const int q = (i0 + c) * VE + part * (VE / 4);  // f32x4 column of xv[0]
+#pragma unroll
+          for (int e = 0; e < EP; ++e) {
+#pragma unroll
+            for (int j = 0; j < VE / 4; ++j) {
+              const f32x4 w = s_w4[e * h4 + q + j];
+              float a = acc[e];
+              a = fmaf(xv[4 * j + 0], w.x, a);
+              a = fmaf(xv[4 * j + 1], w.y, a);
+              a = fmaf(xv[4 * j + 2], w.z, a);
+              a = fmaf(xv[4 * j + 3], w.w, a);
+              acc[e] = a;
+            }
+          }
+        }
+      }
+    };
+    u32x4 xa[CI], xb[CI];
+    load_chunk(0, xa);
+    if (CI < ni) load_chunk(CI, xb);
+    if (!staged) {  // the first row loads are in flight: finish the W_router copy
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+      for (int i = nreal + lane; i < ((nall + 63) & ~63); i += 64)
+        s_w4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      staged = true;
+    }
+    for (int i0 = 0; i0 < ni; i0 += 2 * CI) {
+      fma_chunk(i0, xa);
+      if (i0 + 2 * CI < ni) load_chunk(i0 + 2 * CI, xa);
+      if (i0 + CI < ni) fma_chunk(i0 + CI, xb);
+      if (i0 + 3 * CI < ni) load_chunk(i0 + 3 * CI, xb);
+    }
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] = quad_sum(acc[e]);
+
+    // softmax over the E logits (fixed order), in the lane
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EP; ++e)
+      if (e < E) m = fmaxf(m, acc[e]);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EP; ++e) {
+      acc[e] = e < E ? expf(acc[e] - m) : 0.f;
+      s += acc[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] = acc[e] / s;  // p (0 past E)
+
+    // top-k: k rounds of the largest remaining p, equal p to the lower id;
+    // the first sweep gives the renormaliser, the second writes (lane j of
+    // the quad writes selections j, j + 4, ...).
+    float ssum = 0.f;
+    uint64_t taken = 0ull;
+    for (int r = 0; r < k; ++r) {
+      int be = 0;
+      float bp = -1.f;
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+        if (e < E && !((taken >> e) & 1ull) && acc[e] > bp) { bp = acc[e]; be = e; }
+      taken |= 1ull << be;
+      ssum += bp;
+    }
+    taken = 0ull;
+    for (int r = 0; r < k; ++r) {
+      int be = 0;
+      float bp = -1.f;
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+        if (e < E && !((taken >> e) & 1ull) && acc[e] > bp) { bp = acc[e]; be = e; }
+      taken |= 1ull << be;
+      if (valid && (r & 3) == part) {
+        topk_idx[t * k + r] = be;
+        alpha[t * k + r] = bp / (ssum + 1e-20f);
+        atomicAdd(&s_cnt[be], 1);  // integer count: order-independent
+      }
+    }
+
+    if (part == 0) {
+#pragma unroll
+      for (int e = 0; e < EP; ++e) s_pt[tok][e] = valid ? acc[e] : 0.f;
+    }
+    __syncthreads();
+    if (lane < E) {
+      for (int u = 0; u < 16; ++u) psum += s_pt[u][lane];
+    }
+    __syncthreads();
+  }
+
+  if (lane < E) {
+    const int64_t o = int64_t(lane) * gridDim.x + blockIdx.x;
+    psum_part[o] = psum;
+    count_part[o] = s_cnt[lane];
+  }
+}
+
+// Mode split (large W_router, or few tokens): the four wavefronts of a block
+// split H into quarters of one token; partial logits meet in LDS and
+// wavefront 0 finishes the token.  Each wavefront issues the loads of CG
+// groups of 256 elements (its x and the matching W_router columns of up to 16
+// experts) before their arithmetic.  Experts past E read row E-1 (in bounds);
+// their lanes are masked later.
+template <typename T, int EP>
+__global__ __launch_bounds__(256) void router_split_kernel(
+    const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
+    int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
+    int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
+  constexpr int CG = EP <= 16 ? 2 : 1;   // groups of 256 elements in flight per wavefront
+  constexpr int EC = EP < 16 ? EP : 16;  // experts' W_router columns held at once
   __shared__ int s_cnt[64];
   __shared__ float s_part[4][64];
+  __shared__ float s_ps[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < 64) s_cnt[tid] = 0;
   const int hq = H >> 2;  // H is a multiple of 64, so hq is a multiple of 16
@@ -215,23 +376,36 @@ __global__ __launch_bounds__(256, 1) void router_split_kernel(
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[e] = 0.f;
     const T* xr = x + t * H;
-    for (int hh = hbeg; hh < hend; hh += 256) {  // wave-uniform trip count
-      const int h = hh + lane * 4;
-      const bool ok = h < hend;
-      float xv[4];
-      load4<T>(xr + (ok ? h : hbeg), xv);
-      if (!ok) xv[0] = xv[1] = xv[2] = xv[3] = 0.f;
-      const int q = (ok ? h : hbeg) >> 2;
+    for (int hh = hbeg; hh < hend; hh += 256 * CG) {  // wave-uniform trip count
+      float xv[CG][4];
+      int q[CG];
 #pragma unroll
-      for (int e = 0; e < EP; ++e) {
-        const int er = e < E ? e : E - 1;
-        const f32x4 w = W4[int64_t(er) * h4 + q];
-        float a = acc[e];
-        a = fmaf(xv[0], w.x, a);
-        a = fmaf(xv[1], w.y, a);
-        a = fmaf(xv[2], w.z, a);
-        a = fmaf(xv[3], w.w, a);
-        acc[e] = a;
+      for (int c = 0; c < CG; ++c) {
+        const int h = hh + 256 * c + lane * 4;
+        const bool ok = h < hend;
+        q[c] = (ok ? h : hbeg) >> 2;
+        load4<T>(xr + 4 * q[c], xv[c]);
+        if (!ok) xv[c][0] = xv[c][1] = xv[c][2] = xv[c][3] = 0.f;
+      }
+#pragma unroll
+      for (int e0 = 0; e0 < EP; e0 += EC) {  // W_router columns of EC experts at a time
+        f32x4 w[CG][EC];
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int e = 0; e < EC; ++e)
+            w[c][e] = W4[int64_t(e0 + e < E ? e0 + e : E - 1) * h4 + q[c]];
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int e = 0; e < EC; ++e) {
+            float a = acc[e0 + e];
+            a = fmaf(xv[c][0], w[c][e].x, a);
+            a = fmaf(xv[c][1], w[c][e].y, a);
+            a = fmaf(xv[c][2], w[c][e].z, a);
+            a = fmaf(xv[c][3], w[c][e].w, a);
+            acc[e0 + e] = a;
+          }
       }
     }
     const float rq = reduce_logits<EP>(acc, lane);
@@ -239,31 +413,35 @@ __global__ __launch_bounds__(256, 1) void router_split_kernel(
     if (lane < E) s_part[wave][lane] = rq;
     __syncthreads();
     if (wave == 0) {
-      const float r = (s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane]);
-      route_token(r, lane, E, k, t, topk_idx, alpha, s_cnt, psum);
+      const float r[1] = {(s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane])};
+      route_tokens<EP, 1>(r, lane, E, k, t, t1, topk_idx, alpha, s_cnt, psum);
     }
   }
+  s_ps[wave][lane] = psum;  // only wave 0 routed: the other rows are zero
   __syncthreads();
-  if (tid < E) {
-    const int64_t o = int64_t(tid) * gridDim.x + blockIdx.x;
-    psum_part[o] = psum;  // wave 0's lanes hold the sums
-    count_part[o] = s_cnt[tid];
-  }
+  write_block_partials(tid, E, s_cnt, s_ps, count_part, psum_part);
+}
+
+template <typename T, int EP>
+hipError_t launch_router_ep(const T* x, const float* Wr, int64_t N, int H, int E, int k, int tb,
+                            int nblk, int mode, int32_t* topk_idx, float* alpha,
+                            int32_t* count_part, float* psum_part, const Launch& s) {
+  if (mode == ROUTER_MODE_SPLIT)
+    return launch_kernel(router_split_kernel<T, EP>, dim3(nblk), dim3(256), 0, s, x, Wr, N, H,
+                         E, k, tb, topk_idx, alpha, count_part, psum_part);
+  // W_router rounded up to whole 1 KB direct-to-LDS loads
+  const unsigned lds = (unsigned(EP) * unsigned(H) * sizeof(float) + 1023u) & ~1023u;
+  return launch_kernel(router_lds_kernel<T, EP>, dim3(nblk), dim3(64), lds, s, x, Wr, N, H, E, k,
+                       tb, topk_idx, alpha, count_part, psum_part);
 }
 
 template <typename T>
 hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E, int k, int tb,
                            int nblk, int mode, int32_t* topk_idx, float* alpha,
                            int32_t* count_part, float* psum_part, const Launch& s) {
-  int ep = 1;
-  while (ep < E) ep *= 2;
-  const size_t lds = mode == ROUTER_MODE_LDS ? size_t(ep) * H * sizeof(float) : 0;
-#define TOPMOE_ROUTER(EPV)                                                                  \
-  return mode == ROUTER_MODE_LDS                                                            \
-             ? launch_kernel(router_lds_kernel<T, EPV>, dim3(nblk), dim3(256), unsigned(lds), \
-                             s, x, Wr, N, H, E, k, tb, topk_idx, alpha, count_part, psum_part) \
-             : launch_kernel(router_split_kernel<T, EPV>, dim3(nblk), dim3(256), 0, s, x, Wr,  \
-                             N, H, E, k, tb, topk_idx, alpha, count_part, psum_part)
+#define TOPMOE_ROUTER(EPV)                                                                 \
+  return launch_router_ep<T, EPV>(x, Wr, N, H, E, k, tb, nblk, mode, topk_idx, alpha,      \
+                                  count_part, psum_part, s)
   if (E <= 1) TOPMOE_ROUTER(1);
   if (E <= 2) TOPMOE_ROUTER(2);
   if (E <= 4) TOPMOE_ROUTER(4);
