@@ -60,6 +60,13 @@ MOE_SMALL = [
     (100, 64, 64, 1, 1),
     (500, 128, 128, 16, 4),
     (2000, 64, 128, 5, 3),
+    # router layouts: W_router in LDS with long rows (H = 2048, and 4096 at the
+    # 64 KB limit), and the H-split layout with many tokens (W_router 128 KB)
+    # or many experts with long rows
+    (600, 2048, 128, 8, 2),
+    (300, 4096, 64, 4, 1),
+    (300, 2048, 64, 16, 2),
+    (20, 4096, 64, 32, 2),
 ]
 
 
