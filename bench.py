@@ -1,11 +1,15 @@
 """Benchmark of the MiniMind FFN / top-k MoE forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cold]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cold | --warm]
 
 A step is one full forward (every kernel of the path) over one batch of
 synthetic inputs already resident in device memory.  W untimed steps, then
 exactly K steps bracketed by device synchronisation; ``value`` is tokens/s
-over those K steps.  A second pass of K steps records HIP events around every
+over those K steps.  Decode-sized workloads (N*k <= 256) are timed cold by
+default: L2 and the Infinity Cache are flushed before every step, outside
+per-step events, by reading a 1 GiB buffer (a read leaves clean lines; a
+write would leave the caches full of dirty lines whose write-back then
+competes with the step), and ``value`` comes from those events.  A second pass of K steps records HIP events around every
 stage on the library's stream to get per-kernel durations, from which the
 dominant kernel's roofline fraction is computed.  The fp64 CPU oracle is then
 timed on a bounded sample of the same workload (rank 0, one GPU only).
@@ -141,8 +145,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cold", action="store_true",
-                    help="flush L2 and the Infinity Cache before each step; time steps one by one")
+    cache = ap.add_mutually_exclusive_group()
+    cache.add_argument("--cold", action="store_const", const="cold", dest="cache",
+                       help="flush L2 and the Infinity Cache before each step; time steps one by one "
+                            "(default for decode-sized workloads, N*k <= 256)")
+    cache.add_argument("--warm", action="store_const", const="warm", dest="cache",
+                       help="back-to-back steps with warm caches (default otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES (counter calibration)")
@@ -173,6 +181,10 @@ def main():
         return
     w = get(args.workload)
     log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype}")
+    decode_like = w.kind == "moe" and w.N * w.k <= 256
+    # Decode-sized steps stream their weights; with warm caches part of them
+    # would come from the 256 MB Infinity Cache, so they are timed cold.
+    cold = (args.cache or ("cold" if decode_like else "warm")) == "cold"
     inputs = make_inputs(w)
 
     def dev_t(a, stored=True):
@@ -211,7 +223,10 @@ def main():
                            return_lists=False, workspace=ws, stream=stream, stage_events=ev)
         make_events = lambda: tm.StageEvents(tm.MOE_STAGES)
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
+    flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if cold else None
+
+    def flush():  # evict L2 and the Infinity Cache with clean lines
+        flush_buf.sum()
 
     warm_ev = make_events()
     for i in range(args.warmup):
@@ -219,7 +234,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    if not args.cold:
+    if not cold:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -232,7 +247,7 @@ def main():
         s1 = torch.cuda.Event(enable_timing=True)
         tot = 0.0
         for _ in range(args.steps):
-            flush.zero_()
+            flush()
             s0.record(stream)
             step()
             s1.record(stream)
@@ -248,11 +263,13 @@ def main():
     # dispatch per kernel, which is why the step time above is taken without.
     ev_sets = [make_events() for _ in range(args.steps)]
     for i in range(args.steps):
-        if flush is not None:
-            flush.zero_()
+        if cold:
+            flush()
         step(ev_sets[i])
     torch.cuda.synchronize()
-    per = np.mean([e.elapsed_ms() for e in ev_sets], axis=0)
+    per_step = np.array([e.elapsed_ms() for e in ev_sets])  # [steps, stages]
+    per = per_step.mean(axis=0)
+    pct = lambda v: {q: round(float(np.percentile(v, p)), 5) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     for e in ev_sets:
         e.close()
     stages_ms = {n: round(float(v), 5) for n, v in zip(names, per)}
@@ -274,20 +291,20 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     dom = "gateup_gemm"
     dom_ms = stages_ms[dom]
+    dom_pct = pct(per_step[:, names.index(dom)])
     dflops, dbytes = units[dom]
-    decode_like = w.kind == "moe" and N * k <= 256
     if decode_like:
         achieved = dbytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": recorded_traffic(w.name, dom),
-                "algorithmic_bytes": dbytes, "avg_launch_ms": dom_ms}
+                "algorithmic_bytes": dbytes, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
     else:
         achieved = dflops / (dom_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": recorded_traffic(w.name, dom),
-                "algorithmic_flops": dflops, "avg_launch_ms": dom_ms}
+                "algorithmic_flops": dflops, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
 
     result = {
         "metric": METRIC,
@@ -304,10 +321,11 @@ def main():
         "data": "synthetic (seeded, shapes and distributions of the workload)",
         "config": {"workload": w.name, "N": N, "H": H, "I": I, "E": E if w.kind == "moe" else None,
                    "k": k if w.kind == "moe" else None, "batch": w.batch, "seq": w.seq,
-                   "cache": "cold (L2 + Infinity Cache flushed per step)" if args.cold else "warm"},
+                   "cache": "cold (L2 + Infinity Cache flushed per step)" if cold else "warm"},
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / peak, 4),
         "stages_ms": stages_ms,
+        "kernel_ms_per_step": pct(per_step.sum(axis=1)),
         "experts_touched": touched,
         "roofline": roof,
     }

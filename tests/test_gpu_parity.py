@@ -102,6 +102,33 @@ def test_moe_k_equals_E(env, N, E, dt):
     assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y[dt]
 
 
+# Decode-sized calls: a few rows per expert, some experts empty, and with a
+# skewed router (bias_std / bias_scale shift the logits) one expert holding
+# many of the rows.
+DECODE_CASES = [
+    # N, H, I, E, k, bias_scale
+    (1, 128, 192, 8, 2, 0.0),
+    (30, 256, 128, 8, 2, 0.0),
+    (32, 256, 128, 16, 2, 1.0),
+    (5, 64, 64, 1, 1, 0.0),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("N,H,I,E,k,bias", DECODE_CASES)
+def test_moe_decode_sized(env, N, H, I, E, k, bias, dt):
+    torch, dev, tm = env
+    w = custom_workload(name=f"moe_decode_{N}_{E}_{k}", N=N, H=H, I=I, E=E, k=k, coef=0.01,
+                        dtype=dt, bias_std=1.5 if bias else 0.0, bias_scale=bias, seed=N + 3 * E)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"moe_ffn_fwd (decode-sized) N={N} H={H} I={I} E={E} k={k} {dt}")
+    out = run_moe(tm, to_dev(inp, dev), w)
+    torch.cuda.synchronize()
+    check_routing(out, ref, w.k, w.E)
+    assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y[dt]
+
+
 def test_moe_top1_alpha_exactly_one(env):
     torch, dev, tm = env
     w = custom_workload(name="moe_alpha1", N=777, H=128, I=64, E=8, k=1, coef=0.01, seed=5)

@@ -36,6 +36,13 @@ __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
+// SiLU(g) * u = g * u / (1 + e^-g) (SwiGLU, lesson 13, section 1.2), as
+// g * u / (1 + 2^(-g log2 e)) with v_exp_f32 and v_rcp_f32 (about 1 ulp each).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Wavefront (64 lanes) reductions; the butterfly order is fixed, so results
 // are identical run to run.
 __device__ __forceinline__ float wave_max(float v) {

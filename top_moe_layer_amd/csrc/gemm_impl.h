@@ -61,12 +61,6 @@ struct Mfma<float> {
   }
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  // g * u / (1 + 2^(-g log2 e)); v_exp_f32 and v_rcp_f32 (about 1 ulp each)
-  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-  return g * u * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
 // Scheduling hints for one MFMA region: spread NDS LDS operations (mask
 // DSMASK: 0x100 reads, 0x200 writes) over the first MFMAs of the region and
 // NVM global loads over all of them, so the memory pipes work while the MFMA
