@@ -94,7 +94,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
                    void* stream, void* const* stage_events);
 
 /* Workspace needed by moe_ffn_fwd (routing partials, permutation, the
- * SiLU(g)*u intermediate [N*k, I] and, for k >= 2, fp32 k-slots [N*k, H]).
+ * SiLU(g)*u intermediate [N*k, I] and, for k >= 2, the k-slots [N*k, H] of
+ * alpha-scaled expert outputs in the dtype).
  * Returns 0 for invalid shapes. */
 size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype);
 
@@ -107,8 +108,10 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
  *   aux_coef             router_aux_loss_coef (>= 0); 0 gives aux = 0 exactly,
  *                        which is also the module's value outside training
  *   y        [N, H]      output (dtype): y_t = sum over the selected experts in
- *                        ascending expert id of alpha * Expert_e(x_t),
- *                        accumulated in fp32 and rounded once
+ *                        ascending expert id of alpha * Expert_e(x_t); with
+ *                        k >= 2 each term is first rounded to the dtype (the
+ *                        terms the pages' index_add_ adds), the sum is taken
+ *                        in fp32 and rounded once
  *   topk_idx [N, k]      int32 selected experts, slot order = probability
  *                        descending, equal probabilities by ascending id
  *   alpha    [N, k]      float32 renormalised weights in the same slot order

@@ -49,11 +49,13 @@ def test_workspace_sizes(L):
     # dense: the [N, I] intermediate
     assert B.raw_ffn_workspace_bytes(100, 768, 2432, B.DTYPE_FP32) >= 100 * 2432 * 4
     assert B.raw_ffn_workspace_bytes(16384, 2048, 6464, B.DTYPE_BF16) >= 16384 * 6464 * 2
-    # moe: intermediate [N*k, I] plus fp32 slots [N*k, H] when k >= 2
+    # moe: intermediate [N*k, I] plus the k-slots [N*k, H] (dtype) when k >= 2
     w1 = B.raw_moe_workspace_bytes(4096, 768, 2432, 4, 1, B.DTYPE_BF16)
-    assert 4096 * 2432 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 768 * 4
+    assert 4096 * 2432 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 768 * 2
     w2 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_BF16)
-    assert w2 >= 32768 * 2432 * 2 + 32768 * 768 * 4
+    assert w2 >= 32768 * 2432 * 2 + 32768 * 768 * 2
+    w3 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_FP32)
+    assert w3 >= 32768 * 2432 * 4 + 32768 * 768 * 4
     assert B.raw_moe_workspace_bytes(0, 64, 64, 4, 2, B.DTYPE_BF16) > 0
     for args in [(10, 65, 64, 4, 1), (10, 64, 96, 4, 1), (10, 64, 64, 0, 1), (10, 64, 64, 65, 1),
                  (10, 64, 64, 4, 5), (10, 64, 64, 4, 0), (-1, 64, 64, 4, 1), (2**31, 64, 64, 4, 1)]:

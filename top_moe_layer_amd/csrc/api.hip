@@ -151,7 +151,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
   float* alpha_g = reinterpret_cast<float*>(ws + pl.off_alpha_g);
   void* h = ws + pl.off_h;
-  float* slots = reinterpret_cast<float*>(ws + pl.off_slots);
+  void* slots = ws + pl.off_slots;
 
   if (N == 0) {
     for (int i = 0; i < TOPMOE_MOE_STAGES; ++i) {
@@ -184,7 +184,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   // 3: grouped down GEMM, alpha-scaled, into y (k == 1) or the k slots
   const Launch l3 = st.at(3);
   GemmParams dn{};
-  dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : static_cast<void*>(slots);
+  dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : slots;
   dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha_g;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,

@@ -26,8 +26,8 @@
 //   gate/up : h = SiLU(g) * u = g * u / (1 + e^-g)  (lesson 13, section 1.2),
 //             stored in the operand dtype in grouped row order;
 //   down    : o * alpha_{t,j} (the renormalised router weight; 1 for the dense
-//             FFN), written to y[t] (k == 1 or dense) or to the fp32 slot of
-//             entry (t, j) (k >= 2) for the fixed-order combine.
+//             FFN), written to y[t] (k == 1 or dense) or to the slot of entry
+//             (t, j) (k >= 2, in the operand dtype) for the fixed-order combine.
 #pragma once
 
 #include "device_common.h"
@@ -408,10 +408,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
             for (int j = 0; j < TN; ++j)
               if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[0][i][j][v] * a);
           } else {
-            float* out = static_cast<float*>(p.out) + ent * p.Nout + t.n0 + cl;
+            T* out = static_cast<T*>(p.out) + ent * p.Nout + t.n0 + cl;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              if (32 * j < cols_left) out[32 * j] = acc[0][i][j][v] * a;
+              if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[0][i][j][v] * a);
           }
         }
       }

@@ -42,7 +42,7 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, unsigned s
 enum GemmKind {
   KIND_GATEUP = 0,      // h = SiLU(A Wg^T) * (A Wu^T), rows gathered from x
   KIND_DOWN_Y = 1,      // y[token] = alpha * (h Wd^T), written in the output dtype
-  KIND_DOWN_SLOTS = 2,  // slot[entry] = alpha * (h Wd^T), float32
+  KIND_DOWN_SLOTS = 2,  // slot[entry] = alpha * (h Wd^T), in the operand dtype
 };
 
 struct GemmParams {
@@ -73,7 +73,7 @@ hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                           int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
                           const Launch& s);
 
-hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,
+hipError_t launch_combine(const void* slots, const int32_t* topk_idx, int64_t N, int H, int k,
                           int dtype, void* y, const Launch& s);
 
 hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s);

@@ -11,8 +11,8 @@
 //     scatter of the entries (t, j) in t*k + j order into expert groups, so
 //     each group lists its tokens in ascending order (with each entry's alpha
 //     copied beside it for the down projection's epilogue);
-//   * combine: y_t = sum of the k alpha-scaled expert rows in ascending expert
-//     id, accumulated in fp32 and rounded once.
+//   * combine: y_t = sum of the k alpha-scaled expert rows (each in the output
+//     dtype) in ascending expert id, accumulated in fp32 and rounded once.
 // All integer work is exact; the only float reductions run in a fixed order.
 #include "device_common.h"
 #include "kernels.h"
@@ -151,35 +151,60 @@ __global__ __launch_bounds__(256) void permute_kernel(
   }
 }
 
+// 16 bytes of the dtype (8 bf16 or 4 fp32 values) to / from fp32.
 template <typename T>
-__device__ __forceinline__ void store4(T* p, f32x4 v);
-
+struct Vec16 {
+  static constexpr int n = 16 / int(sizeof(T));
+};
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, float (&v)[16 / sizeof(T)]);
 template <>
-__device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
-  *reinterpret_cast<f32x4*>(p) = v;
+__device__ __forceinline__ void load16<float>(const float* p, float (&v)[4]) {
+  const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+template <>
+__device__ __forceinline__ void load16<bf16_t>(const bf16_t* p, float (&v)[8]) {
+  const u32x4 q = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(q[i] << 16);
+    v[2 * i + 1] = __uint_as_float(q[i] & 0xffff0000u);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store16(T* p, const float (&v)[16 / sizeof(T)]);
+template <>
+__device__ __forceinline__ void store16<float>(float* p, const float (&v)[4]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <>
+__device__ __forceinline__ void store16<bf16_t>(bf16_t* p, const float (&v)[8]) {
+  u32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = uint32_t(f32_to_bf16(v[2 * i])) | (uint32_t(f32_to_bf16(v[2 * i + 1])) << 16);
+  *reinterpret_cast<u32x4*>(p) = q;
 }
 
-template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, f32x4 v) {
-  uint2 q;
-  q.x = uint32_t(f32_to_bf16(v.x)) | (uint32_t(f32_to_bf16(v.y)) << 16);
-  q.y = uint32_t(f32_to_bf16(v.z)) | (uint32_t(f32_to_bf16(v.w)) << 16);
-  *reinterpret_cast<uint2*>(p) = q;
-}
-
-// y[t, 4q..4q+3] = sum of slot rows of token t, ascending expert id.
+// y[t, 16 bytes] = sum of the k slot rows of token t (each already rounded to
+// the output dtype, like the terms the pages' index_add_ accumulates), in
+// ascending expert id, accumulated in fp32 and rounded once.
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ slots,
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slots,
                                                       const int32_t* __restrict__ topk_idx,
                                                       int64_t N, int H, int k,
                                                       T* __restrict__ y) {
-  const int hq = H >> 2;
+  constexpr int V = Vec16<T>::n;
+  const int hv = H / V;  // H is a multiple of 64
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (gid >= N * hq) return;
-  const int64_t t = gid / hq;
-  const int h = int(gid - t * hq) * 4;
+  if (gid >= N * hv) return;
+  const int64_t t = gid / hv;
+  const int h = int(gid - t * hv) * V;
   const int32_t* ids = topk_idx + t * k;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
   int prev = -1;
   for (int r = 0; r < k; ++r) {
     int best_j = 0, best_e = 1 << 30;
@@ -188,10 +213,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       if (e > prev && e < best_e) { best_e = e; best_j = j; }
     }
     prev = best_e;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(slots + (t * k + best_j) * H + h);
-    acc += v;
+    float v[V];
+    load16<T>(slots + (t * k + best_j) * H + h, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] += v[i];
   }
-  store4<T>(y + t * H + h, acc);
+  store16<T>(y + t * H + h, acc);
 }
 
 __global__ void empty_route_kernel(int E, int32_t* offsets, float* aux) {
@@ -216,16 +243,16 @@ hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                        alpha_g, sorted_tok);
 }
 
-hipError_t launch_combine(const float* slots, const int32_t* topk_idx, int64_t N, int H, int k,
+hipError_t launch_combine(const void* slots, const int32_t* topk_idx, int64_t N, int H, int k,
                           int dtype, void* y, const Launch& s) {
-  const int64_t work = N * (H / 4);
+  const int64_t work = N * (H / (dtype == TOPMOE_DTYPE_FP32 ? 4 : 8));  // 16-byte pieces
   if (work <= 0) return hipSuccess;
   const int64_t grid = (work + 255) / 256;
   if (dtype == TOPMOE_DTYPE_FP32)
-    return launch_kernel(combine_kernel<float>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
-                         H, k, static_cast<float*>(y));
-  return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s, slots, topk_idx, N,
-                       H, k, static_cast<bf16_t*>(y));
+    return launch_kernel(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
+                         static_cast<const float*>(slots), topk_idx, N, H, k, static_cast<float*>(y));
+  return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(slots), topk_idx, N, H, k, static_cast<bf16_t*>(y));
 }
 
 hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s) {

@@ -181,7 +181,7 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_alpha_g = o;    o = align_up(o + size_t(rows) * 4);
   q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);
   q.off_slots = o;
-  if (k >= 2) o = align_up(o + size_t(rows) * size_t(H) * 4);
+  if (k >= 2) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
   q.total = o == 0 ? kAlign : o;
   *p = q;
   return TOPMOE_OK;

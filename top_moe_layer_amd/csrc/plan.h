@@ -48,7 +48,7 @@ struct MoePlan {
   size_t off_sorted = 0;      // int32 [N*k] entry ids (t*k + j) grouped by expert
   size_t off_alpha_g = 0;     // f32   [N*k] alpha of each grouped row
   size_t off_h = 0;           // elem  [N*k, I] SiLU(g)*u in grouped row order
-  size_t off_slots = 0;       // f32   [N*k, H] alpha-scaled expert outputs (k >= 2)
+  size_t off_slots = 0;       // elem  [N*k, H] alpha-scaled expert outputs (k >= 2)
   size_t total = 0;
 };
 
