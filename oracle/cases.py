@@ -24,8 +24,9 @@ def widen(inputs: dict) -> dict:
     """Float64 views of the stored tensors (exact widening)."""
     dt = inputs["dtype"]
     out = {"x": to_f64(inputs["x"], dt)}
-    for n in ("Wg", "Wu", "Wd"):
-        out[n] = to_f64(inputs[n], dt)
+    for n in ("Wg", "Wu", "Wd", "residual"):
+        if n in inputs:
+            out[n] = to_f64(inputs[n], dt)
     if "Wr" in inputs:
         out["Wr"] = inputs["Wr"].astype(np.float64)
     return out
@@ -73,15 +74,17 @@ def make_case(w: Workload, seed=None, N=None, margin=True) -> dict:
 def expected(w: Workload, inputs: dict, rows=None) -> dict:
     """Oracle outputs for ``inputs``; ``rows`` restricts y to those tokens."""
     f = widen(inputs)
+    res = f.get("residual")
     if w.kind == "dense":
-        return {"y": dense_ffn(f["x"], f["Wg"], f["Wu"], f["Wd"], rows=rows),
+        return {"y": dense_ffn(f["x"], f["Wg"], f["Wu"], f["Wd"], rows=rows, residual=res),
                 "rows": np.arange(f["x"].shape[0]) if rows is None else np.asarray(rows)}
-    return moe_ffn(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], w.k, w.coef, rows=rows)
+    return moe_ffn(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], w.k, w.coef, rows=rows,
+                   residual=res, norm_topk_prob=w.norm_topk_prob)
 
 
 def expected_route(w: Workload, inputs: dict) -> dict:
     f = widen(inputs)
-    return moe_route(f["x"], f["Wr"], w.k, w.coef)
+    return moe_route(f["x"], f["Wr"], w.k, w.coef, w.norm_topk_prob)
 
 
 def custom_workload(**kw) -> Workload:

@@ -56,13 +56,21 @@ def swiglu_ffn(x, Wg, Wu, Wd):
     return h @ np.asarray(Wd, dtype=np.float64).T  # [T, H]
 
 
-def dense_ffn(x, Wg, Wu, Wd, rows=None):
+def dense_ffn(x, Wg, Wu, Wd, rows=None, residual=None):
     """Dense FFN forward; ``rows`` restricts the output to those token rows
-    (each token is transformed independently, [L13] section 1.1)."""
+    (each token is transformed independently, [L13] section 1.1).
+
+    ``residual`` [N, H] (optional): the block's residual stream, returned as
+    residual + FFN(x) ([L13] section 1.3: hidden_states + mlp(...)).
+    """
     x = np.asarray(x, dtype=np.float64)
     if rows is not None:
         x = x[np.asarray(rows)]
-    return swiglu_ffn(x, Wg, Wu, Wd)
+    y = swiglu_ffn(x, Wg, Wu, Wd)
+    if residual is not None:
+        r = np.asarray(residual, dtype=np.float64)
+        y = (r[np.asarray(rows)] if rows is not None else r) + y
+    return y
 
 
 # ------------------------------------------------------------------ router
@@ -89,11 +97,17 @@ def topk_canonical(p, k):
     return order[:, :k].copy()
 
 
-def renorm_weights(p, idx):
+def renorm_weights(p, idx, normalize=True):
     """alpha_{t,j} = p_{t,S_j} / (sum_{j'} p_{t,S_j'} + 1e-20)
-    ([L13] section 0 alpha equation; section 3 step 5 norm_topk_prob line)."""
+    ([L13] section 0 alpha equation; section 3 step 5 norm_topk_prob line).
+
+    normalize=False is the config's norm_topk_prob = False branch ([L13]
+    section 3 step 1 config, step 5): the selected probabilities as they are.
+    """
     p = np.asarray(p, dtype=np.float64)
     ps = np.take_along_axis(p, np.asarray(idx), axis=1)
+    if not normalize:
+        return ps
     return ps / (ps.sum(axis=1, keepdims=True) + EPS_RENORM)
 
 
@@ -134,13 +148,14 @@ def aux_loss(p, idx, E, coef):
 
 
 # --------------------------------------------------------------------- MoE
-def moe_route(x, Wr, k, coef):
+def moe_route(x, Wr, k, coef, norm_topk_prob=True):
     """Routing half of the MoE forward: probabilities, top-k, renormalised
-    weights, per-expert lists and aux_loss ([L13] section 3 steps 4-6)."""
+    (or, with norm_topk_prob False, raw) weights, per-expert lists and
+    aux_loss ([L13] section 3 steps 4-6)."""
     p = router_probs(x, Wr)
     E = p.shape[1]
     idx = topk_canonical(p, k)
-    alpha = renorm_weights(p, idx)
+    alpha = renorm_weights(p, idx, normalize=norm_topk_prob)
     counts, offsets, sorted_ids = expert_lists(idx, E)
     return {
         "p": p,
@@ -153,7 +168,8 @@ def moe_route(x, Wr, k, coef):
     }
 
 
-def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None):
+def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None, residual=None,
+            norm_topk_prob=True):
     """MoE FFN forward ([L13] section 0 MoE equations, section 3 steps 4-6;
     [MM4] 4.3 steps 1-3):
 
@@ -164,11 +180,13 @@ def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None):
 
     x [N, H]; Wr [E, H]; Wg, Wu [E, I, H]; Wd [E, H, I].  ``rows`` (sorted or
     not) restricts y to those tokens; routing statistics always use all N.
+    ``residual`` [N, H] (optional) starts y from the residual stream instead of
+    zeros ([L13] section 1.3 and 1.4: hidden_states + mlp(...)).
     Returns the routing dict plus ``y`` ([len(rows), H] or [N, H]).
     """
     x = np.asarray(x, dtype=np.float64)
     N = x.shape[0]
-    r = moe_route(x, Wr, k, coef) if route is None else route
+    r = moe_route(x, Wr, k, coef, norm_topk_prob) if route is None else route
     idx, alpha = r["topk_idx"], r["alpha"]
     E = r["p"].shape[1]
     if rows is None:
@@ -176,7 +194,10 @@ def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None):
     rows = np.asarray(rows, dtype=np.int64)
     where = -np.ones(N, dtype=np.int64)
     where[rows] = np.arange(len(rows))
-    y = np.zeros((len(rows), x.shape[1]))
+    if residual is None:
+        y = np.zeros((len(rows), x.shape[1]))
+    else:
+        y = np.asarray(residual, dtype=np.float64)[rows].copy()
     for e in range(E):
         mask = idx == e                                  # [N, k]
         tok = np.nonzero(mask.any(axis=1))[0]            # ascending tokens that chose e

@@ -156,6 +156,33 @@ def test_topk_tie_goes_to_lower_id():
     assert topk_canonical(p, 2).tolist() == [[0, 1], [1, 3]]
 
 
+@pytest.mark.parametrize("case", gold("routing_worked_example.json")["raw_cases"], ids=lambda c: f"k{c['k']}")
+def test_alpha_raw_without_renormalisation(case):
+    """norm_topk_prob False (lesson 13 section 3 step 5; chapter 4 section 4.3
+    step 2): alpha is the selected probabilities, the printed 0.80 and 0.10."""
+    p = np.array([gold("routing_worked_example.json")["p"]])
+    idx = topk_canonical(p, case["k"])
+    assert idx[0].tolist() == case["topk_idx"]
+    alpha = renorm_weights(p, idx, normalize=False)
+    np.testing.assert_array_equal(alpha[0], case["alpha"])
+    r = moe_route(np.ones((1, 1)), np.log(p[0])[:, None], case["k"], 0.0, norm_topk_prob=False)
+    np.testing.assert_allclose(r["alpha"][0], case["alpha"], rtol=1e-14)
+
+
+def test_alpha_raw_sums_below_one_unless_all_experts():
+    """Without renormalisation sum_j alpha = sum of the selected p: below 1 for
+    k < E, 1 (up to rounding) for k = E, and the top-k set is unchanged."""
+    p = router_probs(rnd((100, 32), 31), rnd((6, 32), 32, 0.5))
+    for k in (1, 3, 6):
+        idx = topk_canonical(p, k)
+        a = renorm_weights(p, idx, normalize=False)
+        if k < 6:
+            assert np.all(a.sum(1) < 1.0)
+        else:
+            np.testing.assert_allclose(a.sum(1), 1.0, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(a / a.sum(1, keepdims=True), renorm_weights(p, idx), rtol=1e-12)
+
+
 def test_alpha_sums_to_one_and_top1_is_one():
     """norm_topk_prob renormalisation (lesson 13 section 3 step 5; chapter-4
     example 6 checks the sum against 1 with atol 1e-5); k = 1 gives 1 exactly."""
@@ -165,6 +192,36 @@ def test_alpha_sums_to_one_and_top1_is_one():
         np.testing.assert_allclose(a.sum(1), 1.0, rtol=0, atol=1e-12)
         if k == 1:
             assert np.all(a == 1.0)
+
+
+# ------------------------------------------------------- residual stream
+def test_residual_with_zero_down_projection_is_the_residual():
+    """hidden_states + mlp(...) (lesson 13 section 1.3): W_down = 0 makes the
+    FFN output 0, so y is the residual exactly (dense and MoE)."""
+    x, R = rnd((9, 16), 41), rnd((9, 16), 42)
+    Wg, Wu = rnd((24, 16), 43, 0.3), rnd((24, 16), 44, 0.3)
+    y = dense_ffn(x, Wg, Wu, np.zeros((16, 24)), residual=R)
+    np.testing.assert_array_equal(y, R)
+    Wr = rnd((3, 16), 45, 0.5)
+    out = moe_ffn(x, Wr, rnd((3, 24, 16), 46, 0.3), rnd((3, 24, 16), 47, 0.3),
+                  np.zeros((3, 16, 24)), 2, 0.01, residual=R)
+    np.testing.assert_array_equal(out["y"], R)
+
+
+def test_residual_rows_subset_and_single_expert():
+    """The residual is added on each token's own row: a row subset of the full
+    result, and E = k = 1 equals the dense FFN with the same residual."""
+    x, R = rnd((12, 16), 51), rnd((12, 16), 52)
+    Wg, Wu, Wd = rnd((1, 24, 16), 53, 0.3), rnd((1, 24, 16), 54, 0.3), rnd((1, 16, 24), 55, 0.3)
+    Wr = rnd((1, 16), 56)
+    full = moe_ffn(x, Wr, Wg, Wu, Wd, 1, 0.0, residual=R)["y"]
+    rows = [7, 2, 11]
+    sub_y = moe_ffn(x, Wr, Wg, Wu, Wd, 1, 0.0, rows=rows, residual=R)["y"]
+    np.testing.assert_array_equal(sub_y, full[rows])
+    dense = dense_ffn(x, Wg[0], Wu[0], Wd[0], residual=R)
+    np.testing.assert_allclose(full, dense, rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(dense_ffn(x, Wg[0], Wu[0], Wd[0], rows=rows, residual=R),
+                                  dense[rows])
 
 
 # ---------------------------------------------------- per-expert lists

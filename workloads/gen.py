@@ -115,6 +115,8 @@ def make_inputs(w: Workload, seed: int | None = None, N: int | None = None) -> d
     out["shift"] = shift
     z = _rng(seed, "x").standard_normal((N, H))
     out["x"] = round_to(z + shift, dt)
+    if w.residual:
+        out["residual"] = round_to(_rng(seed, "residual").standard_normal((N, H)), dt)
     return out
 
 

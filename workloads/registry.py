@@ -35,6 +35,10 @@ class Workload:
     # Skewed routing: per-expert logit offset b = bias_scale * z, z ~ N(0, bias_std).
     bias_std: float = 0.0
     bias_scale: float = 0.0
+    # Block context: a residual stream [N, H] (dtype) that y is added to, and
+    # the config's norm_topk_prob (False: alpha = the raw top-k probabilities).
+    residual: bool = False
+    norm_topk_prob: bool = True
     seed: int = 0
     note: str = ""
     extra: dict = field(default_factory=dict)
