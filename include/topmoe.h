@@ -63,7 +63,8 @@ extern "C" {
 #define TOPMOE_ERR_UNSUPPORTED_DTYPE    -3  /* dtype not FP32 / BF16                  */
 #define TOPMOE_ERR_WORKSPACE_TOO_SMALL  -4  /* workspace_bytes < *_workspace_bytes()  */
 #define TOPMOE_ERR_HIP                  -5  /* a HIP runtime call or launch failed    */
-#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef negative / not finite, misaligned pointer */
+#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef negative / not finite, unknown flag bits,
+                                               misaligned pointer */
 
 /* ---- dtypes ------------------------------------------------------------ */
 #define TOPMOE_DTYPE_FP32 0
@@ -75,6 +76,12 @@ extern "C" {
                                 2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
                                 + alpha, 4 combine of the k slots (empty when k == 1)   */
 
+/* ---- moe_ffn_fwd flags -------------------------------------------------- */
+/* The config's norm_topk_prob = False (lesson 13, walkthrough steps 1 and 5;
+ * minimind3 chapter 4, section 4.3 step 2): alpha is the selected
+ * probabilities as they are, without renormalisation to sum 1. */
+#define TOPMOE_MOE_RAW_TOPK_WEIGHTS 1
+
 /* Workspace needed by ffn_swiglu_fwd: the SiLU(g)*u intermediate [N, I]
  * (dtype-sized elements), 256-byte aligned.  Returns 0 for invalid shapes. */
 size_t ffn_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype);
@@ -84,12 +91,16 @@ size_t ffn_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype);
  *   x   [N, H]   input tokens (B*S flattened; the caller reshapes)
  *   Wg  [I, H]   gate_proj.weight      Wu [I, H] up_proj.weight
  *   Wd  [H, I]   down_proj.weight
- *   y   [N, H]   output, same dtype as x; must not alias the inputs
+ *   residual [N, H]  optional (NULL = none), same dtype: the block's residual
+ *                stream; y = residual + FFN(x) (lesson 13, sections 1.3-1.4:
+ *                hidden_states + mlp(...)), summed in fp32 and rounded once.
+ *                May alias y (each element is read before it is written).
+ *   y   [N, H]   output, same dtype as x; must not alias x or the weights
  *   workspace    device scratch of at least ffn_workspace_bytes(N, H, I, dtype)
  *                bytes, 256-byte aligned; contents on entry are ignored.
  * All tensor pointers must be 16-byte aligned. */
 int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
-                   void* y, int64_t N, int64_t H, int64_t I, int dtype,
+                   const void* residual, void* y, int64_t N, int64_t H, int64_t I, int dtype,
                    void* workspace, size_t workspace_bytes,
                    void* stream, void* const* stage_events);
 
@@ -105,16 +116,22 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
  *   Wr       [E, H]      router (gate) weight, float32
  *   Wg, Wu   [E, I, H]   experts' gate_proj / up_proj weights, stacked (dtype)
  *   Wd       [E, H, I]   experts' down_proj weights, stacked (dtype)
+ *   residual [N, H]      optional (NULL = none), dtype: y starts from it
+ *                        instead of zeros (y = residual + MoE(x), lesson 13,
+ *                        sections 1.3-1.4).  May alias y.
  *   aux_coef             router_aux_loss_coef (>= 0); 0 gives aux = 0 exactly,
  *                        which is also the module's value outside training
- *   y        [N, H]      output (dtype): y_t = sum over the selected experts in
- *                        ascending expert id of alpha * Expert_e(x_t); with
- *                        k >= 2 each term is first rounded to the dtype (the
- *                        terms the pages' index_add_ adds), the sum is taken
- *                        in fp32 and rounded once
+ *   flags                0 or TOPMOE_MOE_RAW_TOPK_WEIGHTS
+ *   y        [N, H]      output (dtype): y_t = residual_t (or 0) + the sum over
+ *                        the selected experts in ascending expert id of
+ *                        alpha * Expert_e(x_t); with k >= 2 each expert term
+ *                        is first rounded to the dtype (the terms the pages'
+ *                        index_add_ adds); the sum is taken in fp32 and
+ *                        rounded once
  *   topk_idx [N, k]      int32 selected experts, slot order = probability
  *                        descending, equal probabilities by ascending id
- *   alpha    [N, k]      float32 renormalised weights in the same slot order
+ *   alpha    [N, k]      float32 weights in the same slot order: renormalised
+ *                        to sum 1 (default) or the raw probabilities (flag)
  *   aux_loss [1]         float32 load-balancing loss (training-mode value)
  *   expert_offsets [E+1] optional (NULL = not returned) int32 exclusive prefix
  *                        sum of per-expert token counts
@@ -125,8 +142,8 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
  * Outputs must not alias inputs or each other.  Tensor pointers must be
  * 16-byte aligned (int32/float32 outputs: 4-byte aligned). */
 int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
-                const void* Wd, int64_t N, int64_t H, int64_t I, int E, int k,
-                float aux_coef, int dtype,
+                const void* Wd, const void* residual, int64_t N, int64_t H, int64_t I,
+                int E, int k, float aux_coef, int flags, int dtype,
                 void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
                 int32_t* expert_offsets, int32_t* sorted_token_ids,
                 void* workspace, size_t workspace_bytes,

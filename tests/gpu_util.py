@@ -34,7 +34,7 @@ def to_dev(inputs: dict, dev):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    out = {n: t(inputs[n]) for n in ("x", "Wg", "Wu", "Wd")}
+    out = {n: t(inputs[n]) for n in ("x", "Wg", "Wu", "Wd", "residual") if n in inputs}
     if "Wr" in inputs:
         out["Wr"] = t(inputs["Wr"], stored=False)
     return out
@@ -58,13 +58,15 @@ def rel_l2_global(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(got - ref) / (d if d else 1.0))
 
 
-def run_moe(tm, dev_in, w, N=None):
+def run_moe(tm, dev_in, w, N=None, y=None):
     return tm.moe_ffn_fwd(dev_in["x"], dev_in["Wr"], dev_in["Wg"], dev_in["Wu"], dev_in["Wd"],
-                          w.k, w.coef)
+                          w.k, w.coef, residual=dev_in.get("residual"),
+                          norm_topk_prob=w.norm_topk_prob, y=y)
 
 
-def run_dense(tm, dev_in):
-    return tm.ffn_swiglu_fwd(dev_in["x"], dev_in["Wg"], dev_in["Wu"], dev_in["Wd"])
+def run_dense(tm, dev_in, y=None):
+    return tm.ffn_swiglu_fwd(dev_in["x"], dev_in["Wg"], dev_in["Wu"], dev_in["Wd"],
+                             residual=dev_in.get("residual"), y=y)
 
 
 def check_routing(out, ref, k, E, exact_order=True):

@@ -35,7 +35,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.topmoe_version() == 100
+    assert L.topmoe_version() == 110
 
 
 def test_strerror_covers_codes(L):
@@ -68,15 +68,17 @@ FAKE = 1 << 20  # 256-byte aligned, never dereferenced: validation fails first
 
 
 def moe_call(**over):
-    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, N=8, H=64, I=64, E=4, k=2, coef=0.01,
-             dtype=B.DTYPE_BF16, y=FAKE, topk_idx=FAKE, alpha=FAKE, aux=FAKE, offsets=None,
+    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, residual=None, N=8, H=64, I=64, E=4, k=2,
+             coef=0.01, flags=0, dtype=B.DTYPE_BF16, y=FAKE, topk_idx=FAKE, alpha=FAKE, aux=FAKE,
+             offsets=None,
              sorted_ids=None, ws=FAKE, ws_bytes=0, stream=None, events=None)
     a.update(over)
     return B.raw_moe_ffn_fwd(*a.values())
 
 
 def ffn_call(**over):
-    a = dict(x=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, y=FAKE, N=8, H=64, I=64, dtype=B.DTYPE_BF16,
+    a = dict(x=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, residual=None, y=FAKE, N=8, H=64, I=64,
+             dtype=B.DTYPE_BF16,
              ws=FAKE, ws_bytes=0, stream=None, events=None)
     a.update(over)
     return B.raw_ffn_swiglu_fwd(*a.values())
@@ -112,6 +114,9 @@ def test_moe_validation_codes(L):
     assert moe_call(ws_bytes=need, x=FAKE + 8) == B.ERR_BAD_ARG
     assert moe_call(ws_bytes=need, ws=FAKE + 64) == B.ERR_BAD_ARG
     assert moe_call(ws_bytes=need, alpha=FAKE + 2) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, residual=FAKE + 8) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, flags=2) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, flags=-1) == B.ERR_BAD_ARG
 
 
 def test_ffn_validation_codes(L):
@@ -125,6 +130,7 @@ def test_ffn_validation_codes(L):
     assert ffn_call() == B.ERR_WORKSPACE_TOO_SMALL
     need = B.raw_ffn_workspace_bytes(8, 64, 64, B.DTYPE_BF16)
     assert ffn_call(ws_bytes=need, Wd=FAKE + 4) == B.ERR_BAD_ARG
+    assert ffn_call(ws_bytes=need, residual=FAKE + 4) == B.ERR_BAD_ARG
 
 
 def test_torch_front_end_rejects_bad_tensors():

@@ -129,6 +129,45 @@ def test_moe_decode_sized(env, N, H, I, E, k, bias, dt):
     assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y[dt]
 
 
+# Block context (lesson 13, sections 1.3-1.4: hidden_states + mlp(...)) and
+# norm_topk_prob False (walkthrough step 5): the residual stream is added to y
+# before its single rounding, also when y is the residual tensor itself.
+BLOCK_CASES = [
+    # kind, N, H, I, E, k, residual, norm, in_place
+    ("dense", 300, 128, 192, 1, 1, True, True, False),
+    ("dense", 5, 64, 128, 1, 1, True, True, True),
+    ("moe", 700, 128, 128, 8, 1, True, True, False),
+    ("moe", 700, 128, 128, 8, 2, True, True, True),
+    ("moe", 700, 128, 128, 8, 2, False, False, False),
+    ("moe", 33, 256, 64, 16, 3, True, False, True),
+    ("moe", 1500, 64, 128, 4, 1, False, False, False),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind,N,H,I,E,k,res,norm,in_place", BLOCK_CASES)
+def test_block_context(env, kind, N, H, I, E, k, res, norm, in_place, dt):
+    torch, dev, tm = env
+    w = custom_workload(name=f"block_{kind}_{N}_{E}_{k}", kind=kind, N=N, H=H, I=I, E=E, k=k,
+                        coef=0.01 if kind == "moe" else 0.0, dtype=dt, residual=res,
+                        norm_topk_prob=norm, seed=N + 5 * E + k)
+    inp = make_case(w)
+    ref = expected(w, inp)
+    announce(f"{kind} residual={res} norm_topk_prob={norm} in_place={in_place} N={N} E={E} k={k} {dt}")
+    d = to_dev(inp, dev)
+    y = d["residual"] if in_place else None
+    if kind == "dense":
+        out_y = run_dense(tm, d, y=y)
+    else:
+        out = run_moe(tm, d, w, y=y)
+        out_y = out.y
+        check_routing(out, ref, w.k, w.E)
+    torch.cuda.synchronize()
+    if in_place:
+        assert out_y.data_ptr() == d["residual"].data_ptr()
+    assert rel_l2_per_token(y_to_f64(out_y), ref["y"]) <= TOL_Y[dt]
+
+
 def test_moe_top1_alpha_exactly_one(env):
     torch, dev, tm = env
     w = custom_workload(name="moe_alpha1", N=777, H=128, I=64, E=8, k=1, coef=0.01, seed=5)

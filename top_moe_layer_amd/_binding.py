@@ -22,6 +22,7 @@ ERR_HIP = -5
 ERR_BAD_ARG = -6
 DTYPE_FP32 = 0
 DTYPE_BF16 = 1
+MOE_RAW_TOPK_WEIGHTS = 1
 FFN_STAGES = 2
 MOE_STAGES = 5
 
@@ -32,10 +33,11 @@ MOE_STAGE_NAMES = ["router", "permute", "gateup_gemm", "down_gemm", "combine"]
 _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
 SIGNATURES = {
     "ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
-    "ffn_swiglu_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp, _vp]),
+    "ffn_swiglu_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp,
+                              _vp]),
     "moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
-    "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _i32,
-                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _i32,
+                           _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "topmoe_strerror": (ctypes.c_char_p, [_i32]),
     "topmoe_version": (_i32, []),
     "topmoe_events_create": (_i32, [_i32, _vp]),
@@ -88,14 +90,17 @@ def raw_moe_workspace_bytes(N, H, I, E, k, dtype) -> int:
     return int(lib().moe_workspace_bytes(N, H, I, E, k, dtype))
 
 
-def raw_ffn_swiglu_fwd(x, Wg, Wu, Wd, y, N, H, I, dtype, ws, ws_bytes, stream, events) -> int:
-    return int(lib().ffn_swiglu_fwd(x, Wg, Wu, Wd, y, N, H, I, dtype, ws, ws_bytes, stream, events))
+def raw_ffn_swiglu_fwd(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, ws, ws_bytes, stream,
+                       events) -> int:
+    return int(lib().ffn_swiglu_fwd(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, ws, ws_bytes,
+                                    stream, events))
 
 
-def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, N, H, I, E, k, coef, dtype, y, topk_idx, alpha, aux,
-                    offsets, sorted_ids, ws, ws_bytes, stream, events) -> int:
-    return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, N, H, I, E, k, coef, dtype, y, topk_idx,
-                                 alpha, aux, offsets, sorted_ids, ws, ws_bytes, stream, events))
+def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, flags, dtype, y, topk_idx,
+                    alpha, aux, offsets, sorted_ids, ws, ws_bytes, stream, events) -> int:
+    return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, flags, dtype,
+                                 y, topk_idx, alpha, aux, offsets, sorted_ids, ws, ws_bytes,
+                                 stream, events))
 
 
 class StageEvents:

@@ -58,7 +58,7 @@ struct Stages {
 
 extern "C" {
 
-int topmoe_version(void) { return 100; }
+int topmoe_version(void) { return 110; }
 
 const char* topmoe_strerror(int status) {
   switch (status) {
@@ -70,7 +70,9 @@ const char* topmoe_strerror(int status) {
     case TOPMOE_ERR_UNSUPPORTED_DTYPE: return "dtype must be TOPMOE_DTYPE_FP32 or TOPMOE_DTYPE_BF16";
     case TOPMOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_bytes() size";
     case TOPMOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    case TOPMOE_ERR_BAD_ARG: return "invalid argument (aux_coef negative or not finite, or a misaligned pointer)";
+    case TOPMOE_ERR_BAD_ARG:
+      return "invalid argument (aux_coef negative or not finite, unknown flag bits, or a "
+             "misaligned pointer)";
   }
   return "unknown status";
 }
@@ -85,9 +87,10 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
   return plan_moe(N, H, I, E, k, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
 }
 
-int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd, void* y,
-                   int64_t N, int64_t H, int64_t I, int dtype, void* workspace,
-                   size_t workspace_bytes, void* stream, void* const* stage_events) {
+int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                   const void* residual, void* y, int64_t N, int64_t H, int64_t I, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream,
+                   void* const* stage_events) {
   FfnPlan pl;
   const int status = plan_ffn(N, H, I, dtype, &pl);
   if (status != TOPMOE_OK) return status;
@@ -95,7 +98,7 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   if (!Wg || !Wu || !Wd || !workspace || (N > 0 && (!x || !y))) return TOPMOE_ERR_NULL_ARG;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) ||
-      !aligned(y, 16) || !aligned(workspace, 256))
+      !aligned(residual, 16) || !aligned(y, 16) || !aligned(workspace, 256))
     return TOPMOE_ERR_BAD_ARG;
 
   const Stages st{stage_events, static_cast<hipStream_t>(stream)};
@@ -114,7 +117,7 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   const Launch l1 = st.at(1);
   if (N > 0) {
     GemmParams dn{};
-    dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = y;
+    dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = y; dn.residual = residual;
     dn.entries = nullptr; dn.offsets = nullptr; dn.alpha = nullptr;
     dn.M = N; dn.E = 1; dn.k = 1; dn.Nout = int(H); dn.K = int(I);
     TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.down, dn, (N + pl.down.bm - 1) / pl.down.bm, l1));
@@ -124,7 +127,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
 }
 
 int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
-                int64_t N, int64_t H, int64_t I, int E, int k, float aux_coef, int dtype,
+                const void* residual, int64_t N, int64_t H, int64_t I, int E, int k,
+                float aux_coef, int flags, int dtype,
                 void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
                 int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
                 size_t workspace_bytes, void* stream, void* const* stage_events) {
@@ -136,9 +140,12 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
       (N > 0 && (!x || !y || !topk_idx || !alpha)))
     return TOPMOE_ERR_NULL_ARG;
   if (!(aux_coef >= 0.0f) || isinf(aux_coef)) return TOPMOE_ERR_BAD_ARG;
+  if (flags & ~TOPMOE_MOE_RAW_TOPK_WEIGHTS) return TOPMOE_ERR_BAD_ARG;
+  const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
-      !aligned(Wd, 16) || !aligned(y, 16) || !aligned(topk_idx, 4) || !aligned(alpha, 4) ||
+      !aligned(Wd, 16) || !aligned(residual, 16) || !aligned(y, 16) || !aligned(topk_idx, 4) ||
+      !aligned(alpha, 4) ||
       !aligned(aux_loss, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_token_ids, 4) ||
       !aligned(workspace, 256))
     return TOPMOE_ERR_BAD_ARG;
@@ -164,8 +171,8 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
 
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   const Launch l0 = st.at(0);
-  TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, pl.tb, pl.nblk, pl.router_mode,
-                           topk_idx, alpha, count_part, psum_part, l0));
+  TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, renorm, pl.tb, pl.nblk,
+                           pl.router_mode, topk_idx, alpha, count_part, psum_part, l0));
   TOPMOE_TRY(st.close(l0));
   // 1: expert offsets, aux loss, stable scatter of entries into expert groups
   const Launch l1 = st.at(1);
@@ -185,6 +192,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   const Launch l3 = st.at(3);
   GemmParams dn{};
   dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : slots;
+  dn.residual = k == 1 ? residual : nullptr;  // k >= 2: added by the combine
   dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha_g;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
@@ -192,7 +200,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   TOPMOE_TRY(st.close(l3));
   // 4: fixed-order combine of the k slots
   const Launch l4 = st.at(4);
-  if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, N, int(H), k, dtype, y, l4));
+  if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, residual, N, int(H), k, dtype, y, l4));
   TOPMOE_TRY(st.close(l4));
   return TOPMOE_OK;
 }

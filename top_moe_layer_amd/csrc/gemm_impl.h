@@ -25,9 +25,10 @@
 // Epilogues:
 //   gate/up : h = SiLU(g) * u = g * u / (1 + e^-g)  (lesson 13, section 1.2),
 //             stored in the operand dtype in grouped row order;
-//   down    : o * alpha_{t,j} (the renormalised router weight; 1 for the dense
-//             FFN), written to y[t] (k == 1 or dense) or to the slot of entry
-//             (t, j) (k >= 2, in the operand dtype) for the fixed-order combine.
+//   down    : o * alpha_{t,j} (the router weight; 1 for the dense FFN),
+//             written to y[t] (k == 1 or dense; plus the residual stream when
+//             given, rounded once) or to the slot of entry (t, j) (k >= 2, in
+//             the operand dtype) for the fixed-order combine.
 #pragma once
 
 #include "device_common.h"
@@ -403,10 +404,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
           const int64_t ent = s_ment[rl + ro];
           const float a = s_malpha[rl + ro];
           if constexpr (KIND == KIND_DOWN_Y) {
-            T* out = static_cast<T*>(p.out) + (ent / p.k) * p.Nout + t.n0 + cl;
+            const int64_t o = (ent / p.k) * p.Nout + t.n0 + cl;
+            T* out = static_cast<T*>(p.out) + o;
+            const T* res = p.residual != nullptr ? static_cast<const T*>(p.residual) + o : nullptr;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[0][i][j][v] * a);
+              if (32 * j < cols_left) {
+                const float r = res != nullptr ? to_f32<T>(res[32 * j]) : 0.f;
+                out[32 * j] = from_f32<T>(r + acc[0][i][j][v] * a);
+              }
           } else {
             T* out = static_cast<T*>(p.out) + ent * p.Nout + t.n0 + cl;
 #pragma unroll

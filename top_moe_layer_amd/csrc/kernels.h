@@ -53,6 +53,7 @@ struct GemmParams {
   const int32_t* entries;  // grouped row -> entry id t*k + j; NULL = identity (dense)
   const int32_t* offsets;  // [E+1] group row offsets; NULL = one group of M rows
   const float* alpha;      // [rows] weight of each grouped row (down); NULL = 1
+  const void* residual;    // down into y: [N, Nout] added before rounding; NULL = none
   int64_t M;               // rows when offsets == NULL
   int E, k;
   int Nout, K;
@@ -64,7 +65,8 @@ enum RouterMode {
 };
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
-                         int k, int tb, int nblk, int mode, int32_t* topk_idx, float* alpha,
+                         int k, bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
+                         float* alpha,
                          int32_t* count_part, float* psum_part, const Launch& s);
 
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
@@ -73,8 +75,8 @@ hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                           int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
                           const Launch& s);
 
-hipError_t launch_combine(const void* slots, const int32_t* topk_idx, int64_t N, int H, int k,
-                          int dtype, void* y, const Launch& s);
+hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const void* residual,
+                          int64_t N, int H, int k, int dtype, void* y, const Launch& s);
 
 hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s);
 

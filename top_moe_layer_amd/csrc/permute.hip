@@ -187,14 +187,16 @@ __device__ __forceinline__ void store16<bf16_t>(bf16_t* p, const float (&v)[8]) 
   *reinterpret_cast<u32x4*>(p) = q;
 }
 
-// y[t, 16 bytes] = sum of the k slot rows of token t (each already rounded to
-// the output dtype, like the terms the pages' index_add_ accumulates), in
-// ascending expert id, accumulated in fp32 and rounded once.
+// y[t, 16 bytes] = residual (or 0) + the k slot rows of token t (each already
+// rounded to the output dtype, like the terms the pages' index_add_
+// accumulates), in ascending expert id, accumulated in fp32 and rounded once.
+// The residual may alias y: each thread reads its residual piece before
+// writing the same piece of y.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slots,
                                                       const int32_t* __restrict__ topk_idx,
-                                                      int64_t N, int H, int k,
-                                                      T* __restrict__ y) {
+                                                      const T* residual, int64_t N, int H, int k,
+                                                      T* y) {
   constexpr int V = Vec16<T>::n;
   const int hv = H / V;  // H is a multiple of 64
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -203,8 +205,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
   const int h = int(gid - t * hv) * V;
   const int32_t* ids = topk_idx + t * k;
   float acc[V];
+  if (residual != nullptr) {
+    load16<T>(residual + t * H + h, acc);  // y starts from the residual stream
+  } else {
 #pragma unroll
-  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  }
   int prev = -1;
   for (int r = 0; r < k; ++r) {
     int best_j = 0, best_e = 1 << 30;
@@ -243,16 +249,18 @@ hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                        alpha_g, sorted_tok);
 }
 
-hipError_t launch_combine(const void* slots, const int32_t* topk_idx, int64_t N, int H, int k,
-                          int dtype, void* y, const Launch& s) {
+hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const void* residual,
+                          int64_t N, int H, int k, int dtype, void* y, const Launch& s) {
   const int64_t work = N * (H / (dtype == TOPMOE_DTYPE_FP32 ? 4 : 8));  // 16-byte pieces
   if (work <= 0) return hipSuccess;
   const int64_t grid = (work + 255) / 256;
   if (dtype == TOPMOE_DTYPE_FP32)
     return launch_kernel(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
-                         static_cast<const float*>(slots), topk_idx, N, H, k, static_cast<float*>(y));
+                         static_cast<const float*>(slots), topk_idx,
+                         static_cast<const float*>(residual), N, H, k, static_cast<float*>(y));
   return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(slots), topk_idx, N, H, k, static_cast<bf16_t*>(y));
+                       static_cast<const bf16_t*>(slots), topk_idx,
+                       static_cast<const bf16_t*>(residual), N, H, k, static_cast<bf16_t*>(y));
 }
 
 hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s) {

@@ -1,5 +1,6 @@
 // Router: logits r = W_router x, p = softmax(r), S = TopK(p, k) and the
-// renormalised weights alpha = p_S / (sum p_S + 1e-20) (MiniMind lesson 13,
+// weights alpha = p_S / (sum p_S + 1e-20), or p_S as it is when the config's
+// norm_topk_prob is off (MiniMind lesson 13,
 // section 1.5 router equations and walkthrough steps 4-5).  Each block also
 // emits, for its tokens, the per-expert selection counts and the per-expert
 // sums of p that the offsets and load-balancing loss need (lesson 13, section
@@ -104,7 +105,7 @@ __device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
 // s_cnt and adds their p to psum (lane e).
 template <int EP, int TPW>
 __device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, int E, int k,
-                                             int64_t t_first, int64_t t_end,
+                                             bool renorm, int64_t t_first, int64_t t_end,
                                              int32_t* __restrict__ topk_idx,
                                              float* __restrict__ alpha, int* s_cnt,
                                              float& psum) {
@@ -141,7 +142,7 @@ __device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, in
     const int64_t t = t_first + u;
     if (lane < k && t < t_end) {
       topk_idx[t * k + lane] = my_e[u];
-      alpha[t * k + lane] = my_p[u] / (ssum[u] + 1e-20f);
+      alpha[t * k + lane] = renorm ? my_p[u] / (ssum[u] + 1e-20f) : my_p[u];
       atomicAdd(&s_cnt[my_e[u]], 1);  // integer count: order-independent
     }
   }
@@ -197,7 +198,7 @@ __device__ __forceinline__ void unpack16<bf16_t>(const u32x4& q, float (&v)[8]) 
 template <typename T, int EP>
 __global__ __launch_bounds__(64) void router_lds_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
-    int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
+    bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
     int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
   constexpr int VE = 16 / int(sizeof(T));  // elements per 16-byte load
   constexpr int CI = 8;                    // loads per lane in flight per chunk
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
     // the quad writes selections j, j + 4, ...).
     float ssum = 0.f;
     uint64_t taken = 0ull;
-    for (int r = 0; r < k; ++r) {
+    for (int r = 0; renorm && r < k; ++r) {
       int be = 0;
       float bp = -1.f;
 #pragma unroll
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
       taken |= 1ull << be;
       if (valid && (r & 3) == part) {
         topk_idx[t * k + r] = be;
-        alpha[t * k + r] = bp / (ssum + 1e-20f);
+        alpha[t * k + r] = renorm ? bp / (ssum + 1e-20f) : bp;
         atomicAdd(&s_cnt[be], 1);  // integer count: order-independent
       }
     }
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
 template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_split_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
-    int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
+    bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
     int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
   constexpr int CG = EP <= 16 ? 2 : 1;   // groups of 256 elements in flight per wavefront
   constexpr int EC = EP < 16 ? EP : 16;  // experts' W_router columns held at once
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(
     __syncthreads();
     if (wave == 0) {
       const float r[1] = {(s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane])};
-      route_tokens<EP, 1>(r, lane, E, k, t, t1, topk_idx, alpha, s_cnt, psum);
+      route_tokens<EP, 1>(r, lane, E, k, renorm, t, t1, topk_idx, alpha, s_cnt, psum);
     }
   }
   s_ps[wave][lane] = psum;  // only wave 0 routed: the other rows are zero
@@ -423,25 +424,27 @@ __global__ __launch_bounds__(256) void router_split_kernel(
 }
 
 template <typename T, int EP>
-hipError_t launch_router_ep(const T* x, const float* Wr, int64_t N, int H, int E, int k, int tb,
-                            int nblk, int mode, int32_t* topk_idx, float* alpha,
+hipError_t launch_router_ep(const T* x, const float* Wr, int64_t N, int H, int E, int k,
+                            bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
+                            float* alpha,
                             int32_t* count_part, float* psum_part, const Launch& s) {
   if (mode == ROUTER_MODE_SPLIT)
     return launch_kernel(router_split_kernel<T, EP>, dim3(nblk), dim3(256), 0, s, x, Wr, N, H,
-                         E, k, tb, topk_idx, alpha, count_part, psum_part);
+                         E, k, renorm, tb, topk_idx, alpha, count_part, psum_part);
   // W_router rounded up to whole 1 KB direct-to-LDS loads
   const unsigned lds = (unsigned(EP) * unsigned(H) * sizeof(float) + 1023u) & ~1023u;
   return launch_kernel(router_lds_kernel<T, EP>, dim3(nblk), dim3(64), lds, s, x, Wr, N, H, E, k,
-                       tb, topk_idx, alpha, count_part, psum_part);
+                       renorm, tb, topk_idx, alpha, count_part, psum_part);
 }
 
 template <typename T>
-hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E, int k, int tb,
-                           int nblk, int mode, int32_t* topk_idx, float* alpha,
+hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E, int k,
+                           bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
+                           float* alpha,
                            int32_t* count_part, float* psum_part, const Launch& s) {
 #define TOPMOE_ROUTER(EPV)                                                                 \
-  return launch_router_ep<T, EPV>(x, Wr, N, H, E, k, tb, nblk, mode, topk_idx, alpha,      \
-                                  count_part, psum_part, s)
+  return launch_router_ep<T, EPV>(x, Wr, N, H, E, k, renorm, tb, nblk, mode, topk_idx,    \
+                                  alpha, count_part, psum_part, s)
   if (E <= 1) TOPMOE_ROUTER(1);
   if (E <= 2) TOPMOE_ROUTER(2);
   if (E <= 4) TOPMOE_ROUTER(4);
@@ -455,14 +458,15 @@ hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E,
 }  // namespace
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
-                         int k, int tb, int nblk, int mode, int32_t* topk_idx, float* alpha,
+                         int k, bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
+                         float* alpha,
                          int32_t* count_part, float* psum_part, const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (dtype == TOPMOE_DTYPE_FP32)
-    return launch_router_t(static_cast<const float*>(x), Wr, N, H, E, k, tb, nblk, mode,
+    return launch_router_t(static_cast<const float*>(x), Wr, N, H, E, k, renorm, tb, nblk, mode,
                            topk_idx, alpha, count_part, psum_part, s);
-  return launch_router_t(static_cast<const bf16_t*>(x), Wr, N, H, E, k, tb, nblk, mode, topk_idx,
-                         alpha, count_part, psum_part, s);
+  return launch_router_t(static_cast<const bf16_t*>(x), Wr, N, H, E, k, renorm, tb, nblk, mode,
+                         topk_idx, alpha, count_part, psum_part, s);
 }
 
 }  // namespace topmoe

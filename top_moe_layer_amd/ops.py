@@ -61,10 +61,12 @@ def moe_workspace_bytes(N: int, H: int, I: int, E: int, k: int, dtype: torch.dty
 
 
 def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, *,
-                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   stream=None, stage_events: Optional[B.StageEvents] = None) -> torch.Tensor:
-    """Dense SwiGLU FFN: y = Wd (SiLU(Wg x) * Wu x).  x [..., H]; Wg, Wu [I, H];
-    Wd [H, I].  Returns y with x's shape and dtype."""
+                   residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   stage_events: Optional[B.StageEvents] = None) -> torch.Tensor:
+    """Dense SwiGLU FFN: y = residual + Wd (SiLU(Wg x) * Wu x) (residual
+    optional, x's shape and dtype; it may be y itself).  x [..., H];
+    Wg, Wu [I, H]; Wd [H, I].  Returns y with x's shape and dtype."""
     dev = x.device
     H = x.shape[-1]
     I = Wg.shape[0]
@@ -75,6 +77,9 @@ def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
     _need(Wg, "Wg", (I, H), dt, dev)
     _need(Wu, "Wu", (I, H), dt, dev)
     _need(Wd, "Wd", (H, I), dt, dev)
+    rf = None if residual is None else residual.reshape(-1, H)
+    if rf is not None:
+        _need(rf, "residual", (N, H), dt, dev)
     if y is None:
         y = torch.empty((N, H), dtype=dt, device=dev)
     _need(y, "y", (N, H), dt, dev)
@@ -83,7 +88,7 @@ def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
     if nbytes == 0:
         B.check(B.ERR_BAD_SHAPE, "ffn_swiglu_fwd")
     ws = _workspace(nbytes, dev, workspace)
-    st = B.raw_ffn_swiglu_fwd(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(y), N, H, I, code,
+    st = B.raw_ffn_swiglu_fwd(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), _ptr(y), N, H, I, code,
                               _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
                               stage_events.ptr if stage_events is not None else None)
     B.check(st, "ffn_swiglu_fwd")
@@ -102,6 +107,7 @@ class MoeOutput:
 
 def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
                 Wd: torch.Tensor, k: int, aux_coef: float, *,
+                residual: Optional[torch.Tensor] = None, norm_topk_prob: bool = True,
                 y: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
                 alpha: Optional[torch.Tensor] = None, aux_loss: Optional[torch.Tensor] = None,
                 expert_offsets: Optional[torch.Tensor] = None,
@@ -110,7 +116,9 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
                 stage_events: Optional[B.StageEvents] = None) -> MoeOutput:
     """Top-k MoE FFN forward.  x [..., H]; Wr [E, H] float32; Wg, Wu [E, I, H];
     Wd [E, H, I].  Returns y (x's shape), topk_idx / alpha [N, k], aux_loss [1]
-    and, when ``return_lists``, expert_offsets [E+1] and sorted_token_ids [N*k]."""
+    and, when ``return_lists``, expert_offsets [E+1] and sorted_token_ids [N*k].
+    ``residual`` (x's shape and dtype, may be y itself) is added to y;
+    ``norm_topk_prob`` False keeps the raw top-k probabilities as alpha."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -131,6 +139,9 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
         expert_offsets = new((E + 1,), torch.int32) if expert_offsets is None else expert_offsets
         sorted_token_ids = new((N * k,), torch.int32) if sorted_token_ids is None else sorted_token_ids
     _need(y, "y", (N, H), dt, dev)
+    rf = None if residual is None else residual.reshape(-1, H)
+    if rf is not None:
+        _need(rf, "residual", (N, H), dt, dev)
     _need(topk_idx, "topk_idx", (N, k), torch.int32, dev)
     _need(alpha, "alpha", (N, k), torch.float32, dev)
     _need(aux_loss, "aux_loss", (1,), torch.float32, dev)
@@ -143,8 +154,9 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     if nbytes == 0:
         B.check(B.ERR_BAD_SHAPE, "moe_ffn_fwd")
     ws = _workspace(nbytes, dev, workspace)
-    st = B.raw_moe_ffn_fwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), N, H, I, E, k,
-                           float(aux_coef), code, _ptr(y), _ptr(topk_idx), _ptr(alpha),
+    flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
+    st = B.raw_moe_ffn_fwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), N, H, I, E,
+                           k, float(aux_coef), flags, code, _ptr(y), _ptr(topk_idx), _ptr(alpha),
                            _ptr(aux_loss), _ptr(expert_offsets), _ptr(sorted_token_ids),
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
                            stage_events.ptr if stage_events is not None else None)
