@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the MiniMind FFN / top-k MoE forward pass.
+"""fp64 CPU oracle for the MiniMind FFN / top-k MoE forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run anything in this package.
@@ -22,6 +22,9 @@ from .ffn_moe import (
     moe_route,
     moe_ffn,
     dense_ffn,
+    silu_grad,
+    swiglu_ffn_bwd,
+    moe_ffn_bwd,
 )
 
 __all__ = [
@@ -35,4 +38,7 @@ __all__ = [
     "moe_route",
     "moe_ffn",
     "dense_ffn",
+    "silu_grad",
+    "swiglu_ffn_bwd",
+    "moe_ffn_bwd",
 ]

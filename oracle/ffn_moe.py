@@ -1,4 +1,5 @@
-"""Plain float64 definition of the MiniMind FFN sub-layer forward pass.
+"""Plain float64 definition of the MiniMind FFN sub-layer forward pass and its
+gradients.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and obvious on
 purpose: library matmuls are used as steps, nothing is blocked, fused or
@@ -211,3 +212,101 @@ def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None, residual=None,
     res["y"] = y
     res["rows"] = rows
     return res
+
+
+# ----------------------------------------------------------------- backward
+# Gradients of the forward above with respect to its inputs and weights, the
+# ones autograd gives: the top-k selection and the per-expert counts are
+# discrete and carry no gradient; the selected weights (from the softmax) and
+# the mean probabilities in aux carry it back to the router ([NOTES] section 7
+# "how the router is trained"; [MM4] 4.4: f_i is not differentiable, P_i is).
+def silu_grad(z):
+    """d SiLU / dz = sigma(z) * (1 + z * (1 - sigma(z)))  (derivative of the
+    [MM4] 4.2 definition z * sigmoid(z)); overflow-safe sigma."""
+    z = np.asarray(z, dtype=np.float64)
+    s = np.empty_like(z)
+    pos = z >= 0
+    s[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    s[~pos] = ez / (1.0 + ez)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def swiglu_ffn_bwd(x, Wg, Wu, Wd, dy):
+    """Backward of ``swiglu_ffn`` for upstream dy [T, H]: returns dx [T, H],
+    dWg [I, H], dWu [I, H], dWd [H, I].
+
+    Chain rule through g = Wg x, u = Wu x, h = SiLU(g) u, y = Wd h.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    Wg, Wu, Wd = (np.asarray(a, dtype=np.float64) for a in (Wg, Wu, Wd))
+    g = x @ Wg.T
+    u = x @ Wu.T
+    s = silu(g)
+    h = s * u
+    dWd = dy.T @ h                    # [H, I]
+    dh = dy @ Wd                      # [T, I]
+    dg = dh * u * silu_grad(g)
+    du = dh * s
+    dWg = dg.T @ x                    # [I, H]
+    dWu = du.T @ x
+    dx = dg @ Wg + du @ Wu            # [T, H]
+    return dx, dWg, dWu, dWd
+
+
+def moe_ffn_bwd(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True):
+    """Backward of ``moe_ffn`` (with its aux_loss) for upstream dy [N, H] and
+    daux (the gradient reaching aux_loss; 1 when it is added to the loss).
+
+    Returns dict dx [N, H], dWr [E, H], dWg / dWu [E, I, H], dWd [E, H, I] and
+    the forward's routing.  Per expert e and token t with e in S_t:
+      o = Expert_e(x_t), y_t += alpha_{t,e} o   =>  d alpha_{t,e} = dy_t . o,
+      the expert's own backward with upstream alpha_{t,e} dy_t;
+    then through alpha = p_S / (sum p_S + 1e-20) (or alpha = p_S), the aux term
+    coef * E * sum_e c_e * (sum_t p_te) / N^2 (counts constant), the softmax
+    and the router logits r = Wr x.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    Wr = np.asarray(Wr, dtype=np.float64)
+    N, H = x.shape
+    E = Wr.shape[0]
+    r = moe_route(x, Wr, k, coef, norm_topk_prob)
+    p, idx, alpha, counts = r["p"], r["topk_idx"], r["alpha"], r["counts"]
+    dx = np.zeros_like(x)
+    dWg = np.zeros(np.shape(Wg))
+    dWu = np.zeros(np.shape(Wu))
+    dWd = np.zeros(np.shape(Wd))
+    dalpha = np.zeros(alpha.shape)
+    for e in range(E):
+        mask = idx == e
+        tok = np.nonzero(mask.any(axis=1))[0]
+        if tok.size == 0:
+            continue
+        slot = np.argmax(mask[tok], axis=1)               # which of the k slots holds e
+        w = alpha[tok, slot]
+        o = swiglu_ffn(x[tok], Wg[e], Wu[e], Wd[e])
+        dalpha[tok, slot] = (dy[tok] * o).sum(axis=1)
+        gx, gWg, gWu, gWd = swiglu_ffn_bwd(x[tok], Wg[e], Wu[e], Wd[e], w[:, None] * dy[tok])
+        dx[tok] += gx
+        dWg[e] += gWg
+        dWu[e] += gWu
+        dWd[e] += gWd
+    # selected weights -> probabilities
+    ps = np.take_along_axis(p, idx, axis=1)
+    dp = np.zeros_like(p)
+    if norm_topk_prob:
+        Z = ps.sum(axis=1, keepdims=True) + EPS_RENORM
+        dps = dalpha / Z - (dalpha * ps).sum(axis=1, keepdims=True) / Z ** 2
+    else:
+        dps = dalpha
+    np.put_along_axis(dp, idx, dps, axis=1)
+    # aux = coef * E * sum_e c_e * sum_t p_te / N^2  (c_e constant)
+    if coef != 0.0:
+        dp += daux * coef * E * counts[None, :] / float(N) ** 2
+    # softmax and router logits
+    dr = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dWr = dr.T @ x
+    dx += dr @ Wr
+    return {"dx": dx, "dWr": dWr, "dWg": dWg, "dWu": dWu, "dWd": dWd, "route": r}
