@@ -11,6 +11,11 @@
  *   MoE output     y = sum_{e in S} alpha_e * Expert_e(x), each expert a dense FFN
  *   aux loss       aux = E * coef * sum_e load_e * prob_e,
  *                  load_e = (tokens that selected e) / N,  prob_e = mean_t p_{t,e}
+ *   backward       the gradients of these with respect to x and every weight:
+ *                  the top-k choice and the counts load_e are discrete and
+ *                  carry no gradient; the softmax probabilities carry it back
+ *                  through alpha and prob_e (minimind3 chapter 4, section
+ *                  4.4; MiniMind study notes, section 7 on router training)
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
@@ -63,7 +68,7 @@ extern "C" {
 #define TOPMOE_ERR_UNSUPPORTED_DTYPE    -3  /* dtype not FP32 / BF16                  */
 #define TOPMOE_ERR_WORKSPACE_TOO_SMALL  -4  /* workspace_bytes < *_workspace_bytes()  */
 #define TOPMOE_ERR_HIP                  -5  /* a HIP runtime call or launch failed    */
-#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef negative / not finite, unknown flag bits,
+#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef negative / not finite, aux_grad not finite, unknown flag bits,
                                                misaligned pointer */
 
 /* ---- dtypes ------------------------------------------------------------ */
@@ -75,6 +80,14 @@ extern "C" {
 #define TOPMOE_MOE_STAGES 5  /* 0 router, 1 expert offsets + aux + token scatter,
                                 2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
                                 + alpha, 4 combine of the k slots (empty when k == 1)   */
+#define TOPMOE_FFN_BWD_STAGES 6  /* 0 weight transposes, 1 x / dy transposes,
+                                    2 fused g, u, dh GEMM, 3 dx GEMM, 4 dWg + dWu GEMM,
+                                    5 dWd GEMM                                          */
+#define TOPMOE_MOE_BWD_STAGES 11 /* 0 router, 1 offsets + scatter (the forward's routing),
+                                    2 weight transposes, 3 grouped x / alpha*dy
+                                    transposes, 4 grouped fused g, u, dh GEMM + d alpha,
+                                    5 grouped dx GEMM, 6 router backward, 7 dx combine,
+                                    8 dW_router, 9 grouped dWg + dWu, 10 grouped dWd   */
 
 /* ---- moe_ffn_fwd flags -------------------------------------------------- */
 /* The config's norm_topk_prob = False (lesson 13, walkthrough steps 1 and 5;
@@ -146,6 +159,73 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
                 int E, int k, float aux_coef, int flags, int dtype,
                 void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
                 int32_t* expert_offsets, int32_t* sorted_token_ids,
+                void* workspace, size_t workspace_bytes,
+                void* stream, void* const* stage_events);
+
+/* ---- backward ------------------------------------------------------------
+ * Gradients of the forward above (same shapes, dtypes and flags).  The
+ * forward's intermediate activations are not needed: the backward recomputes
+ * them (and, for the MoE, the routing: same kernels, same choices).
+ * Gradient outputs are overwritten, not accumulated; weight gradients have
+ * the weights' dtype and layout, dW_router is float32.  The gradient with
+ * respect to the residual stream of the forward is dy itself (nothing to
+ * compute).  In bf16, [dg | du], dg, du, h and alpha*dy are rounded to bf16
+ * before the GEMMs that consume them; all accumulation is fp32. */
+
+/* Workspace needed by ffn_swiglu_bwd: transposed weights [H, 2I] and [I, H],
+ * transposed x and dy [H, round64(N)], [dg | du] [N, 2I] and dg^T, du^T, h^T
+ * [I, round64(N)] (dtype-sized elements).  Returns 0 for invalid shapes. */
+size_t ffn_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype);
+
+/* Dense SwiGLU FFN backward.  With g = x Wg^T, u = x Wu^T, h = SiLU(g) * u,
+ * y = h Wd^T and the upstream gradient dy [N, H]:
+ *   dWd = dy^T h,  dh = dy Wd,  dg = dh * u * SiLU'(g),  du = dh * SiLU(g),
+ *   dWg = dg^T x,  dWu = du^T x,  dx = dg Wg + du Wu,
+ *   SiLU'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z))).
+ *   x, Wg, Wu, Wd   as for ffn_swiglu_fwd;  dy [N, H] (dtype)
+ *   dx [N, H], dWg [I, H], dWu [I, H], dWd [H, I]   outputs (dtype); N == 0
+ *                   gives zero weight gradients (x, dy, dx may then be NULL)
+ *   workspace       at least ffn_bwd_workspace_bytes(N, H, I, dtype) bytes,
+ *                   256-byte aligned; contents on entry ignored.
+ * Outputs must not alias inputs or each other; tensor pointers 16-byte
+ * aligned.  Shape limits as for the forward, plus [N, 2I], [H, 2I] and
+ * [I, round64(N)] operands below 4 GiB each. */
+int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                   const void* dy, void* dx, void* dWg, void* dWu, void* dWd,
+                   int64_t N, int64_t H, int64_t I, int dtype,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream, void* const* stage_events);
+
+/* Workspace needed by moe_ffn_bwd: the routing buffers, transposed expert
+ * weights [E, H, 2I] and [E, I, H], the per-entry intermediates and
+ * gradients, and float32 router buffers.  Returns 0 for invalid shapes. */
+size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype);
+
+/* Top-k MoE FFN backward.  The routing of moe_ffn_fwd(x, Wr, ..., k,
+ * aux_coef, flags) is recomputed; for each token t and selected expert e
+ * (weight alpha_{t,e}, expert output o = Expert_e(x_t)):
+ *   the expert's own backward (as ffn_swiglu_bwd) with upstream alpha * dy_t;
+ *   d alpha_{t,e} = dy_t . o;
+ *   then dp through alpha = p_S / (sum p_S + 1e-20) (or alpha = p_S with
+ *   TOPMOE_MOE_RAW_TOPK_WEIGHTS), plus aux_grad * aux_coef * E * c_e / N^2 on
+ *   every p_{t,e} (c_e = tokens routed to e); dr = p * (dp - sum(p * dp));
+ *   dW_router = dr^T x and dx_t += W_router^T dr_t.
+ *   x, Wr, Wg, Wu, Wd, N, H, I, E, k, aux_coef, flags, dtype
+ *                   as for moe_ffn_fwd
+ *   dy [N, H]       upstream gradient of y (dtype)
+ *   aux_grad        upstream gradient of aux_loss (1 when it is added to the
+ *                   loss as is); finite
+ *   dx [N, H] (dtype), dWr [E, H] (float32), dWg, dWu [E, I, H], dWd [E, H, I]
+ *                   (dtype) outputs; experts no token selected get zero
+ *                   gradients.  N == 0 gives all-zero weight gradients.
+ *   workspace       at least moe_bwd_workspace_bytes(N, H, I, E, k, dtype)
+ *                   bytes, 256-byte aligned; contents on entry ignored.
+ * Outputs must not alias inputs or each other; tensor pointers 16-byte
+ * aligned. */
+int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
+                const void* Wd, const void* dy, float aux_grad,
+                int64_t N, int64_t H, int64_t I, int E, int k, float aux_coef, int flags,
+                int dtype, void* dx, float* dWr, void* dWg, void* dWu, void* dWd,
                 void* workspace, size_t workspace_bytes,
                 void* stream, void* const* stage_events);
 

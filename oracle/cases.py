@@ -14,7 +14,7 @@ import numpy as np
 import workloads
 from workloads import Workload, make_inputs, redraw_token_rows, to_f64
 
-from .ffn_moe import router_probs, moe_ffn, dense_ffn, moe_route
+from .ffn_moe import router_probs, moe_ffn, dense_ffn, moe_route, swiglu_ffn_bwd, moe_ffn_bwd
 
 MARGIN = 1e-3
 MAX_REDRAWS = 64
@@ -87,6 +87,18 @@ def expected_route(w: Workload, inputs: dict) -> dict:
     return moe_route(f["x"], f["Wr"], w.k, w.coef, w.norm_topk_prob)
 
 
+def expected_bwd(w: Workload, inputs: dict, dy, daux: float = 1.0) -> dict:
+    """Oracle gradients for ``inputs`` and the upstream gradient ``dy``
+    (storage dtype): dx, dWg, dWu, dWd (+ dWr and the routing for MoE)."""
+    f = widen(inputs)
+    dy64 = to_f64(dy, inputs["dtype"])
+    if w.kind == "dense":
+        dx, dWg, dWu, dWd = swiglu_ffn_bwd(f["x"], f["Wg"], f["Wu"], f["Wd"], dy64)
+        return {"dx": dx, "dWg": dWg, "dWu": dWu, "dWd": dWd}
+    return moe_ffn_bwd(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], w.k, w.coef, dy64, daux,
+                       w.norm_topk_prob)
+
+
 def custom_workload(**kw) -> Workload:
     """Ad-hoc workload for edge-case tests (random small shapes)."""
     base = dict(name="custom", kind="moe", N=16, H=64, I=64, E=4, k=1, coef=0.01, dtype="bf16")
@@ -96,5 +108,5 @@ def custom_workload(**kw) -> Workload:
 
 __all__ = [
     "MARGIN", "widen", "small_margin_rows", "enforce_margin", "make_case",
-    "expected", "expected_route", "custom_workload", "workloads",
+    "expected", "expected_route", "expected_bwd", "custom_workload", "workloads",
 ]

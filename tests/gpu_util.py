@@ -102,3 +102,32 @@ def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
     edge = edge[(edge >= 0) & (edge < N)]
     rest = rng.choice(N, size=n - len(edge), replace=False)
     return np.unique(np.concatenate([edge, rest]))
+
+
+TOL_GRAD = {"fp32": 1e-5, "bf16": 2e-2}   # relative L2 of each gradient (per token / per matrix)
+TOL_DWR = 1e-4                           # router-weight gradient, relative L2 per expert row
+
+
+def arr_to_dev(a, dt: str, dev):
+    """A storage-dtype numpy array (bf16 bit patterns or float32) on the device."""
+    import torch
+
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def rel_l2_per_matrix(got: np.ndarray, ref: np.ndarray) -> float:
+    """Max over the leading (expert) axis of the Frobenius relative error; a
+    matrix whose reference is zero must come out zero."""
+    got = got.reshape((-1,) + got.shape[-2:]) if got.ndim >= 2 else got[None]
+    ref = ref.reshape(got.shape)
+    worst = 0.0
+    for g, r in zip(got, ref):
+        d = np.linalg.norm(r)
+        if d == 0.0:
+            if np.abs(g).max(initial=0.0) != 0.0:
+                return float("inf")
+            continue
+        worst = max(worst, float(np.linalg.norm(g - r) / d))
+    return worst

@@ -35,7 +35,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.topmoe_version() == 110
+    assert L.topmoe_version() == 120
 
 
 def test_strerror_covers_codes(L):
@@ -131,6 +131,71 @@ def test_ffn_validation_codes(L):
     need = B.raw_ffn_workspace_bytes(8, 64, 64, B.DTYPE_BF16)
     assert ffn_call(ws_bytes=need, Wd=FAKE + 4) == B.ERR_BAD_ARG
     assert ffn_call(ws_bytes=need, residual=FAKE + 4) == B.ERR_BAD_ARG
+
+
+def ffn_bwd_call(**over):
+    a = dict(x=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, dx=FAKE, dWg=FAKE, dWu=FAKE, dWd=FAKE,
+             N=8, H=64, I=64, dtype=B.DTYPE_BF16, ws=FAKE, ws_bytes=0, stream=None, events=None)
+    a.update(over)
+    return B.raw_ffn_swiglu_bwd(*a.values())
+
+
+def moe_bwd_call(**over):
+    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, aux_grad=1.0, N=8, H=64, I=64,
+             E=4, k=2, coef=0.01, flags=0, dtype=B.DTYPE_BF16, dx=FAKE, dWr=FAKE, dWg=FAKE,
+             dWu=FAKE, dWd=FAKE, ws=FAKE, ws_bytes=0, stream=None, events=None)
+    a.update(over)
+    return B.raw_moe_ffn_bwd(*a.values())
+
+
+def test_bwd_workspace_sizes(L):
+    # dense: [Wg|Wu]^T, Wd^T, x^T and dy^T [H, round64(N)], [dg|du], dg^T / du^T / h^T
+    N, H, I = 100, 128, 192
+    w = B.raw_ffn_bwd_workspace_bytes(N, H, I, B.DTYPE_BF16)
+    Np = 128
+    floor = 2 * (3 * H * I + 2 * H * Np + 2 * N * I + 3 * I * Np)
+    assert floor <= w < floor + 16 * 256
+    assert B.raw_ffn_bwd_workspace_bytes(N, H, I, B.DTYPE_FP32) >= 2 * floor
+    assert B.raw_ffn_bwd_workspace_bytes(0, H, I, B.DTYPE_BF16) > 0
+    assert B.raw_ffn_bwd_workspace_bytes(N, 96, I, B.DTYPE_BF16) == 0
+    # moe: at least the forward's routing plus the per-entry buffers
+    N, H, I, E, k = 300, 128, 128, 8, 2
+    wm = B.raw_moe_bwd_workspace_bytes(N, H, I, E, k, B.DTYPE_BF16)
+    rows = N * k
+    assert wm >= 2 * (3 * E * H * I + rows * 2 * I + rows * H) + 4 * N * E * 2
+    assert B.raw_moe_bwd_workspace_bytes(0, H, I, E, k, B.DTYPE_BF16) > 0
+    assert B.raw_moe_bwd_workspace_bytes(N, H, I, E, E + 1, B.DTYPE_BF16) == 0
+    assert B.raw_moe_bwd_workspace_bytes(N, H, I, 65, 1, B.DTYPE_BF16) == 0
+
+
+def test_bwd_validation_codes(L):
+    assert ffn_bwd_call(dy=None) == B.ERR_NULL_ARG
+    assert ffn_bwd_call(dWd=None) == B.ERR_NULL_ARG
+    assert ffn_bwd_call(N=0, x=None, dy=None, dx=None) == B.ERR_WORKSPACE_TOO_SMALL
+    assert ffn_bwd_call(N=0, dWg=None) == B.ERR_NULL_ARG
+    assert ffn_bwd_call(I=100) == B.ERR_BAD_SHAPE
+    assert ffn_bwd_call(N=1 << 20, I=1024) == B.ERR_BAD_SHAPE      # [dg|du] = 4 GiB bf16
+    assert ffn_bwd_call(dtype=5) == B.ERR_UNSUPPORTED_DTYPE
+    assert ffn_bwd_call() == B.ERR_WORKSPACE_TOO_SMALL
+    need = B.raw_ffn_bwd_workspace_bytes(8, 64, 64, B.DTYPE_BF16)
+    assert ffn_bwd_call(ws_bytes=need - 1) == B.ERR_WORKSPACE_TOO_SMALL
+    assert ffn_bwd_call(ws_bytes=need, dy=FAKE + 8) == B.ERR_BAD_ARG
+    assert ffn_bwd_call(ws_bytes=need, dWu=FAKE + 2) == B.ERR_BAD_ARG
+
+    assert moe_bwd_call(dWr=None) == B.ERR_NULL_ARG
+    assert moe_bwd_call(dy=None) == B.ERR_NULL_ARG
+    assert moe_bwd_call(N=0, x=None, dy=None, dx=None) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_bwd_call(k=5) == B.ERR_BAD_SHAPE
+    assert moe_bwd_call(N=1 << 20, I=1024) == B.ERR_BAD_SHAPE      # [dg|du] = 8 GiB bf16
+    assert moe_bwd_call(coef=-1.0) == B.ERR_BAD_ARG
+    assert moe_bwd_call(aux_grad=float("nan")) == B.ERR_BAD_ARG
+    assert moe_bwd_call(aux_grad=float("inf")) == B.ERR_BAD_ARG
+    assert moe_bwd_call(flags=4) == B.ERR_BAD_ARG
+    assert moe_bwd_call() == B.ERR_WORKSPACE_TOO_SMALL
+    need = B.raw_moe_bwd_workspace_bytes(8, 64, 64, 4, 2, B.DTYPE_BF16)
+    assert moe_bwd_call(ws_bytes=need - 1) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_bwd_call(ws_bytes=need, dWr=FAKE + 4) == B.ERR_BAD_ARG
+    assert moe_bwd_call(ws_bytes=need, ws=FAKE + 16) == B.ERR_BAD_ARG
 
 
 def test_torch_front_end_rejects_bad_tensors():

@@ -25,9 +25,15 @@ DTYPE_BF16 = 1
 MOE_RAW_TOPK_WEIGHTS = 1
 FFN_STAGES = 2
 MOE_STAGES = 5
+FFN_BWD_STAGES = 6
+MOE_BWD_STAGES = 11
 
 FFN_STAGE_NAMES = ["gateup_gemm", "down_gemm"]
 MOE_STAGE_NAMES = ["router", "permute", "gateup_gemm", "down_gemm", "combine"]
+FFN_BWD_STAGE_NAMES = ["transpose_w", "transpose_act", "bwd_h_gemm", "dx_gemm", "dwgu_gemm",
+                       "dwd_gemm"]
+MOE_BWD_STAGE_NAMES = ["router", "permute", "transpose_w", "transpose_act", "bwd_h_gemm",
+                       "dx_gemm", "router_bwd", "dx_combine", "dwr", "dwgu_gemm", "dwd_gemm"]
 
 # Every function include/topmoe.h declares, with its ctypes signature.
 _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
@@ -38,6 +44,12 @@ SIGNATURES = {
     "moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
     "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _i32,
                            _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "ffn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "ffn_swiglu_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
+                              _vp, _sz, _vp, _vp]),
+    "moe_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+    "moe_ffn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, _i32, _i32, _f32,
+                           _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "topmoe_strerror": (ctypes.c_char_p, [_i32]),
     "topmoe_version": (_i32, []),
     "topmoe_events_create": (_i32, [_i32, _vp]),
@@ -101,6 +113,26 @@ def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, flags, dty
     return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, flags, dtype,
                                  y, topk_idx, alpha, aux, offsets, sorted_ids, ws, ws_bytes,
                                  stream, events))
+
+
+def raw_ffn_bwd_workspace_bytes(N, H, I, dtype) -> int:
+    return int(lib().ffn_bwd_workspace_bytes(N, H, I, dtype))
+
+
+def raw_moe_bwd_workspace_bytes(N, H, I, E, k, dtype) -> int:
+    return int(lib().moe_bwd_workspace_bytes(N, H, I, E, k, dtype))
+
+
+def raw_ffn_swiglu_bwd(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws, ws_bytes, stream,
+                       events) -> int:
+    return int(lib().ffn_swiglu_bwd(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws,
+                                    ws_bytes, stream, events))
+
+
+def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, N, H, I, E, k, coef, flags, dtype, dx, dWr,
+                    dWg, dWu, dWd, ws, ws_bytes, stream, events) -> int:
+    return int(lib().moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, N, H, I, E, k, coef, flags,
+                                 dtype, dx, dWr, dWg, dWu, dWd, ws, ws_bytes, stream, events))
 
 
 class StageEvents:

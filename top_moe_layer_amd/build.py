@@ -22,7 +22,8 @@ LIB = os.path.join(LIBDIR, "libtopmoe.so")
 ARCH = os.environ.get("TOPMOE_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["plan.cpp", "api.hip", "router.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+SOURCES = ["plan.cpp", "api.hip", "router.hip", "permute.hip", "backward.hip", "gemm_bf16.hip",
+           "gemm_f32.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 # Device code: no packed fp32 instructions (they are generated from plain float

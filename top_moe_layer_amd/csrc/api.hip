@@ -58,7 +58,7 @@ struct Stages {
 
 extern "C" {
 
-int topmoe_version(void) { return 110; }
+int topmoe_version(void) { return 120; }
 
 const char* topmoe_strerror(int status) {
   switch (status) {
@@ -71,8 +71,8 @@ const char* topmoe_strerror(int status) {
     case TOPMOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_bytes() size";
     case TOPMOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case TOPMOE_ERR_BAD_ARG:
-      return "invalid argument (aux_coef negative or not finite, unknown flag bits, or a "
-             "misaligned pointer)";
+      return "invalid argument (aux_coef negative or not finite, aux_grad not finite, unknown "
+             "flag bits, or a misaligned pointer)";
   }
   return "unknown status";
 }
@@ -172,7 +172,7 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   const Launch l0 = st.at(0);
   TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, renorm, pl.tb, pl.nblk,
-                           pl.router_mode, topk_idx, alpha, count_part, psum_part, l0));
+                           pl.router_mode, topk_idx, alpha, nullptr, count_part, psum_part, l0));
   TOPMOE_TRY(st.close(l0));
   // 1: expert offsets, aux loss, stable scatter of entries into expert groups
   const Launch l1 = st.at(1);
@@ -202,6 +202,252 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   const Launch l4 = st.at(4);
   if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, residual, N, int(H), k, dtype, y, l4));
   TOPMOE_TRY(st.close(l4));
+  return TOPMOE_OK;
+}
+
+size_t ffn_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype) {
+  FfnBwdPlan pl;
+  return plan_ffn_bwd(N, H, I, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
+}
+
+size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype) {
+  MoeBwdPlan pl;
+  return plan_moe_bwd(N, H, I, E, k, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
+}
+
+int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd, const void* dy,
+                   void* dx, void* dWg, void* dWu, void* dWd, int64_t N, int64_t H, int64_t I,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                   void* const* stage_events) {
+  FfnBwdPlan pl;
+  const int status = plan_ffn_bwd(N, H, I, dtype, &pl);
+  if (status != TOPMOE_OK) return status;
+  if (!Wg || !Wu || !Wd || !dWg || !dWu || !dWd || !workspace || (N > 0 && (!x || !dy || !dx)))
+    return TOPMOE_ERR_NULL_ARG;
+  if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(x, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) || !aligned(Wd, 16) ||
+      !aligned(dy, 16) || !aligned(dx, 16) || !aligned(dWg, 16) || !aligned(dWu, 16) ||
+      !aligned(dWd, 16) || !aligned(workspace, 256))
+    return TOPMOE_ERR_BAD_ARG;
+
+  const Stages st{stage_events, static_cast<hipStream_t>(stream)};
+  char* ws = static_cast<char*>(workspace);
+  void* wgT = ws + pl.off_wgT;
+  void* wdT = ws + pl.off_wdT;
+  void* xT = ws + pl.off_xT;
+  void* dyT = ws + pl.off_dyT;
+  void* dgdu = ws + pl.off_dgdu;
+  void* dgT = ws + pl.off_dgT;
+  void* duT = ws + pl.off_duT;
+  void* hT = ws + pl.off_hT;
+  const int iH = int(H), iI = int(I);
+
+  // 0: weight transposes: [Wg | Wu]^T [H, 2I] and Wd^T [I, H]
+  const Launch l0 = st.at(0);
+  {
+    TransposeJobs tj{};
+    tj.job[0] = TransposeJob{Wg, wgT, iI, iH, 1, 0, 2 * I, 0, 0};
+    tj.job[1] = TransposeJob{Wu, wgT, iI, iH, 1, iI, 2 * I, 0, 0};
+    tj.job[2] = TransposeJob{Wd, wdT, iH, iI, 1, 0, H, 0, 0};
+    tj.n = 3;
+    TOPMOE_TRY(launch_transpose(dtype, tj, int((I / 64) * (H / 64)), 1, l0));
+  }
+  TOPMOE_TRY(st.close(l0));
+  // 1: activation transposes x^T, dy^T [H, ldk] (zero columns past N)
+  const Launch l1 = st.at(1);
+  {
+    GatherTransposeJobs gj{};
+    gj.job[0] = GatherTransposeJob{x, xT, nullptr};
+    gj.job[1] = GatherTransposeJob{dy, dyT, nullptr};
+    gj.n = 2;
+    gj.offsets = nullptr; gj.entries = nullptr;
+    gj.E = 1; gj.k = 1; gj.C = iH; gj.rows = N; gj.ldo = pl.ldk;
+    TOPMOE_TRY(launch_gather_transpose(dtype, gj, pl.ldk, l1));
+  }
+  TOPMOE_TRY(st.close(l1));
+  // 2: g, u, dh in one GEMM: [dg | du], dg^T, du^T, h^T
+  const Launch l2 = st.at(2);
+  if (N > 0) {
+    GemmParams g{};
+    g.A = x; g.A1 = dy; g.B0 = Wg; g.B1 = Wu; g.B2 = wdT;
+    g.out = dgdu; g.out1 = dgT; g.out2 = duT; g.out3 = hT;
+    g.M = N; g.ldk = pl.ldk; g.E = 1; g.k = 1; g.Nout = iI; g.K = iH;
+    TOPMOE_TRY(launch_gemm(KIND_BWD_H, dtype, pl.bwdh, g, (N + pl.bwdh.bm - 1) / pl.bwdh.bm, l2));
+  }
+  TOPMOE_TRY(st.close(l2));
+  // 3: dx = [dg | du] [Wg | Wu]
+  const Launch l3 = st.at(3);
+  if (N > 0) {
+    GemmParams g{};
+    g.A = dgdu; g.B0 = wgT; g.out = dx;
+    g.M = N; g.E = 1; g.k = 1; g.Nout = iH; g.K = 2 * iI;
+    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.dx, g, (N + pl.dx.bm - 1) / pl.dx.bm, l3));
+  }
+  TOPMOE_TRY(st.close(l3));
+  // 4: dWg = dg^T x, dWu = du^T x (contraction over tokens)
+  const Launch l4 = st.at(4);
+  {
+    GemmParams g{};
+    g.A = dgT; g.A1 = duT; g.B0 = xT; g.out = dWg; g.out1 = dWu;
+    g.M = I; g.ldk = pl.ldk; g.kcount = N; g.E = 1; g.k = 1; g.Nout = iH; g.K = int(pl.ldk);
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD2, dtype, pl.wgu, g, 0, l4));
+  }
+  TOPMOE_TRY(st.close(l4));
+  // 5: dWd = dy^T h
+  const Launch l5 = st.at(5);
+  {
+    GemmParams g{};
+    g.A = dyT; g.B0 = hT; g.out = dWd;
+    g.M = H; g.ldk = pl.ldk; g.kcount = N; g.E = 1; g.k = 1; g.Nout = iI; g.K = int(pl.ldk);
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD1, dtype, pl.wd, g, 0, l5));
+  }
+  TOPMOE_TRY(st.close(l5));
+  return TOPMOE_OK;
+}
+
+int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
+                const void* dy, float aux_grad, int64_t N, int64_t H, int64_t I, int E, int k,
+                float aux_coef, int flags, int dtype, void* dx, float* dWr, void* dWg,
+                void* dWu, void* dWd, void* workspace, size_t workspace_bytes, void* stream,
+                void* const* stage_events) {
+  MoeBwdPlan pl;
+  const int status = plan_moe_bwd(N, H, I, E, k, dtype, &pl);
+  if (status != TOPMOE_OK) return status;
+  if (!Wr || !Wg || !Wu || !Wd || !dWr || !dWg || !dWu || !dWd || !workspace ||
+      (N > 0 && (!x || !dy || !dx)))
+    return TOPMOE_ERR_NULL_ARG;
+  if (!(aux_coef >= 0.0f) || isinf(aux_coef) || !isfinite(aux_grad)) return TOPMOE_ERR_BAD_ARG;
+  if (flags & ~TOPMOE_MOE_RAW_TOPK_WEIGHTS) return TOPMOE_ERR_BAD_ARG;
+  const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
+  if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
+      !aligned(Wd, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(dWr, 16) ||
+      !aligned(dWg, 16) || !aligned(dWu, 16) || !aligned(dWd, 16) || !aligned(workspace, 256))
+    return TOPMOE_ERR_BAD_ARG;
+
+  const MoePlan& rp = pl.route;
+  const Stages st{stage_events, static_cast<hipStream_t>(stream)};
+  char* ws = static_cast<char*>(workspace);
+  int32_t* count_part = reinterpret_cast<int32_t*>(ws + rp.off_count_part);
+  float* psum_part = reinterpret_cast<float*>(ws + rp.off_psum_part);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + rp.off_offsets);
+  int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + rp.off_sorted);
+  float* alpha_g = reinterpret_cast<float*>(ws + rp.off_alpha_g);
+  float* probs = reinterpret_cast<float*>(ws + pl.off_probs);
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + pl.off_topk);
+  float* alpha = reinterpret_cast<float*>(ws + pl.off_alpha);
+  float* aux = reinterpret_cast<float*>(ws + pl.off_aux);
+  void* wgT = ws + pl.off_wgT;
+  void* wdT = ws + pl.off_wdT;
+  void* xT = ws + pl.off_xT;
+  void* dyT = ws + pl.off_dyT;
+  void* dgdu = ws + pl.off_dgdu;
+  void* dgT = ws + pl.off_dgT;
+  void* duT = ws + pl.off_duT;
+  void* hT = ws + pl.off_hT;
+  float* dal = reinterpret_cast<float*>(ws + pl.off_dal);
+  void* slots = ws + pl.off_slots;
+  float* dr = reinterpret_cast<float*>(ws + pl.off_dr);
+  float* dwr_part = reinterpret_cast<float*>(ws + pl.off_dwr);
+  const int iH = int(H), iI = int(I);
+  const int64_t rows = rp.rows;
+
+  // 0, 1: the forward's routing (probabilities kept for the softmax backward)
+  const Launch l0 = st.at(0);
+  if (N > 0)
+    TOPMOE_TRY(launch_router(x, Wr, dtype, N, iH, E, k, renorm, rp.tb, rp.nblk, rp.router_mode,
+                             topk_idx, alpha, probs, count_part, psum_part, l0));
+  TOPMOE_TRY(st.close(l0));
+  const Launch l1 = st.at(1);
+  if (N > 0)
+    TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, alpha, rp.nblk, E, k, rp.tb, N,
+                              aux_coef, offsets, aux, sorted_entry, alpha_g, nullptr, l1));
+  else
+    TOPMOE_TRY(launch_empty_route(E, offsets, aux, l1));
+  TOPMOE_TRY(st.close(l1));
+  // 2: per-expert weight transposes: [Wg | Wu]^T [E, H, 2I], Wd^T [E, I, H]
+  const Launch l2 = st.at(2);
+  {
+    TransposeJobs tj{};
+    const int64_t ih = I * H;
+    tj.job[0] = TransposeJob{Wg, wgT, iI, iH, E, 0, 2 * I, ih, 2 * ih};
+    tj.job[1] = TransposeJob{Wu, wgT, iI, iH, E, iI, 2 * I, ih, 2 * ih};
+    tj.job[2] = TransposeJob{Wd, wdT, iH, iI, E, 0, H, ih, ih};
+    tj.n = 3;
+    TOPMOE_TRY(launch_transpose(dtype, tj, int((I / 64) * (H / 64)), E, l2));
+  }
+  TOPMOE_TRY(st.close(l2));
+  // 3: x^T and (alpha dy)^T in expert-grouped padded columns
+  const Launch l3 = st.at(3);
+  {
+    GatherTransposeJobs gj{};
+    gj.job[0] = GatherTransposeJob{x, xT, nullptr};
+    gj.job[1] = GatherTransposeJob{dy, dyT, alpha_g};
+    gj.n = N > 0 ? 2 : 0;
+    gj.offsets = offsets; gj.entries = sorted_entry;
+    gj.E = E; gj.k = k; gj.C = iH; gj.rows = rows; gj.ldo = pl.ldk;
+    TOPMOE_TRY(launch_gather_transpose(dtype, gj, pl.ldk, l3));
+  }
+  TOPMOE_TRY(st.close(l3));
+  // 4: per expert g, u, dh = alpha dy Wd: [dg | du], dg^T, du^T, h^T, d alpha partials
+  const Launch l4 = st.at(4);
+  if (N > 0) {
+    GemmParams g{};
+    g.A = x; g.A1 = dy; g.B0 = Wg; g.B1 = Wu; g.B2 = wdT;
+    g.out = dgdu; g.out1 = dgT; g.out2 = duT; g.out3 = hT; g.dalpha_part = dal;
+    g.entries = sorted_entry; g.offsets = offsets; g.alpha = alpha_g;
+    g.M = rows; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iI; g.K = iH;
+    TOPMOE_TRY(launch_gemm(KIND_BWD_H, dtype, pl.bwdh, g, pl.bwdh_mtiles, l4));
+  }
+  TOPMOE_TRY(st.close(l4));
+  // 5: per entry dx term [dg | du] [Wg_e | Wu_e] into its slot
+  const Launch l5 = st.at(5);
+  if (N > 0) {
+    GemmParams g{};
+    g.A = dgdu; g.B0 = wgT; g.out = slots;
+    g.entries = sorted_entry; g.offsets = offsets; g.alpha = nullptr;
+    g.M = rows; g.E = E; g.k = k; g.Nout = iH; g.K = 2 * iI;
+    TOPMOE_TRY(launch_gemm(KIND_DOWN_SLOTS, dtype, pl.dx, g, pl.dx_mtiles, l5));
+  }
+  TOPMOE_TRY(st.close(l5));
+  // 6: router backward: d alpha -> dp (renormalisation, aux) -> softmax -> dr
+  const Launch l6 = st.at(6);
+  {
+    const double scale = N > 0 ? double(aux_grad) * double(aux_coef) * double(E) /
+                                     (double(N) * double(N))
+                               : 0.0;
+    TOPMOE_TRY(launch_router_bwd(probs, topk_idx, dal, pl.nt_h, offsets, N, E, k, renorm,
+                                 float(scale), dr, l6));
+  }
+  TOPMOE_TRY(st.close(l6));
+  // 7: dx = sum of the slots (ascending expert) + W_r^T dr
+  const Launch l7 = st.at(7);
+  TOPMOE_TRY(launch_combine_bwd(slots, topk_idx, dr, Wr, N, iH, E, k, dtype, dx, l7));
+  TOPMOE_TRY(st.close(l7));
+  // 8: dW_r = dr^T x
+  const Launch l8 = st.at(8);
+  TOPMOE_TRY(launch_dwr(x, dr, N, iH, E, dtype, dwr_part, dWr, l8));
+  TOPMOE_TRY(st.close(l8));
+  // 9: dWg_e = dg_e^T x_e, dWu_e = du_e^T x_e over each expert's rows
+  const Launch l9 = st.at(9);
+  {
+    GemmParams g{};
+    g.A = dgT; g.A1 = duT; g.B0 = xT; g.out = dWg; g.out1 = dWu;
+    g.offsets = offsets;
+    g.M = I; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iH; g.K = int(pl.ldk);
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD2, dtype, pl.wgu, g, 0, l9));
+  }
+  TOPMOE_TRY(st.close(l9));
+  // 10: dWd_e = (alpha dy)_e^T h_e
+  const Launch l10 = st.at(10);
+  {
+    GemmParams g{};
+    g.A = dyT; g.B0 = hT; g.out = dWd;
+    g.offsets = offsets;
+    g.M = H; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iI; g.K = int(pl.ldk);
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD1, dtype, pl.wd, g, 0, l10));
+  }
+  TOPMOE_TRY(st.close(l10));
   return TOPMOE_OK;
 }
 

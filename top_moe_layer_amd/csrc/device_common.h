@@ -36,6 +36,21 @@ __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
+// Four consecutive values in the dtype (8 bytes of bf16, 16 of fp32).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&v)[4]);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float (&v)[4]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const uint32_t a = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+  const uint32_t b = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+  *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
+}
+
 // SiLU(g) * u = g * u / (1 + e^-g) (SwiGLU, lesson 13, section 1.2), as
 // g * u / (1 + 2^(-g log2 e)) with v_exp_f32 and v_rcp_f32 (about 1 ulp each).
 __device__ __forceinline__ float silu_mul(float g, float u) {

@@ -122,28 +122,103 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Operands and products of each kind: NA A matrices and NB B matrices share
+// one LDS slice (A0, A1, B0, B1, B2 in that order); product p multiplies
+// A pa(p) by B pb(p) into accumulator p.
+template <int KIND>
+struct KindTraits {  // the down projections
+  static constexpr int NA = 1, NB = 1, NP = 1;
+  static constexpr bool META = true, KGROUP = false, GATHER = false;
+  __host__ __device__ static constexpr int pa(int) { return 0; }
+  __host__ __device__ static constexpr int pb(int) { return 0; }
+};
+template <>
+struct KindTraits<KIND_GATEUP> {  // x against Wg and Wu
+  static constexpr int NA = 1, NB = 2, NP = 2;
+  static constexpr bool META = false, KGROUP = false, GATHER = true;
+  __host__ __device__ static constexpr int pa(int) { return 0; }
+  __host__ __device__ static constexpr int pb(int q) { return q; }
+};
+template <>
+struct KindTraits<KIND_BWD_H> {  // x against Wg and Wu, dy against Wd^T
+  static constexpr int NA = 2, NB = 3, NP = 3;
+  static constexpr bool META = true, KGROUP = false, GATHER = true;
+  __host__ __device__ static constexpr int pa(int q) { return q == 2 ? 1 : 0; }
+  __host__ __device__ static constexpr int pb(int q) { return q; }
+};
+template <>
+struct KindTraits<KIND_WGRAD2> {  // dg^T and du^T against x^T
+  static constexpr int NA = 2, NB = 1, NP = 2;
+  static constexpr bool META = false, KGROUP = true, GATHER = false;
+  __host__ __device__ static constexpr int pa(int q) { return q; }
+  __host__ __device__ static constexpr int pb(int) { return 0; }
+};
+template <>
+struct KindTraits<KIND_WGRAD1> {  // (alpha dy)^T against h^T
+  static constexpr int NA = 1, NB = 1, NP = 1;
+  static constexpr bool META = false, KGROUP = true, GATHER = false;
+  __host__ __device__ static constexpr int pa(int) { return 0; }
+  __host__ __device__ static constexpr int pb(int) { return 0; }
+};
+
+// Sum of each of V per-lane values over the 32 lanes of a half-wavefront
+// (the MFMA column lanes fr = 0..31): halving exchanges (lane bit set keeps
+// the upper half), then plain butterflies once one value is left.  Lane fr
+// ends with cnt = max(V / 32, 1) sums, for value indices
+// (fr >> (5 - steps)) * cnt + w, steps = min(5, log2 V).
+template <int V>
+struct HalfWaveTransposeSum {
+  static constexpr int steps = V >= 32 ? 5 : (V == 16 ? 4 : V == 8 ? 3 : V == 4 ? 2 : V == 2 ? 1 : 0);
+  static constexpr int cnt = V >> steps;
+  template <int C, int MASK>
+  __device__ static __forceinline__ void halve(float* v, int fr) {
+    if constexpr (C > cnt) {
+      constexpr int half = C / 2;
+      const bool upper = (fr & MASK) != 0;
+#pragma unroll
+      for (int n = 0; n < half; ++n) {
+        const float send = upper ? v[n] : v[n + half];
+        const float keep = upper ? v[n + half] : v[n];
+        v[n] = keep + __shfl_xor(send, MASK, 64);
+      }
+      halve<half, MASK / 2>(v, fr);
+    } else if constexpr (MASK >= 1) {
+#pragma unroll
+      for (int n = 0; n < C; ++n) v[n] += __shfl_xor(v[n], MASK, 64);
+      halve<C, MASK / 2>(v, fr);
+    }
+  }
+  __device__ static __forceinline__ void run(float* v, int fr) { halve<V, 16>(v, fr); }
+};
+
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
-  constexpr int NB = KIND == KIND_GATEUP ? 2 : 1;
+  using KT_ = KindTraits<KIND>;
+  constexpr int NA = KT_::NA, NB = KT_::NB, NP = KT_::NP;
+  constexpr bool META = KT_::META;      // per-row entry / alpha in the epilogue
+  constexpr bool KGROUP = KT_::KGROUP;  // groups along K (weight gradients)
+  constexpr bool PAD = KGROUP || KIND == KIND_BWD_H;  // padded group columns
   constexpr int NW = WM * WN;                // wavefronts: WM along rows x WN along columns
   constexpr int NTHR = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wavefront and matrix
-  constexpr int R = BM + NB * BN;            // LDS rows per slice: A, then B0 (, B1)
-  constexpr int A_BYTES = BM * RB, B_BYTES = BN * RB;
+  constexpr int R = NA * BM + NB * BN;       // LDS rows per slice: A0 (, A1), B0 (, B1, B2)
+  constexpr int A_BYTES = NA * BM * RB, B_BYTES = BN * RB;
   constexpr int STAGE = R * RB;
   constexpr int CH = RB / 16;                // 16-byte chunks per LDS row
   constexpr int RPW = 256 / RB;              // rows per 256-byte bank window
   constexpr int RPI = 1024 / RB;             // rows per 1 KB direct-to-LDS load
   constexpr int LPW = R / RPI / NW;          // direct-to-LDS loads per wavefront per slice
   constexpr int QS = RB / 32;                // MFMA sub-steps per slice
-  constexpr bool META = KIND != KIND_GATEUP;  // down epilogue needs per-row entry / alpha
+  constexpr int EPS = RB / int(sizeof(T));   // K elements per slice
   static_assert(RB == 64 || RB == 128, "row bytes");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
   static_assert((R / RPI) % NW == 0 && LPW >= 1, "slice rows must split evenly over wavefronts");
-  static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring exceeds 160 KB");
+  static_assert(BM % RPI == 0 && BN % RPI == 0, "a load stays in one operand");
+  static_assert(S >= 2 && S * STAGE <= 156 * 1024, "LDS ring exceeds 156 KB");
   static_assert((S - 1) * LPW < 64, "vmcnt range");
   static_assert(BM <= NTHR, "one thread per tile row for the epilogue metadata");
+  static_assert(!PAD || BM % 64 == 0, "padded groups end inside a group's last row tile");
   // One __shared__ object per ring slot: the compiler then sees that LDS reads
   // of one slot never alias direct-to-LDS loads into another and does not
   // drain the load queue before each read.
@@ -153,81 +228,126 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) char ring3[S > 3 ? STAGE : 16];
   __shared__ int s_scan[64];
   __shared__ int s_off[65];
+  __shared__ int s_poff[PAD ? 64 : 1];
   __shared__ int s_ment[META ? BM : 1];
   __shared__ float s_malpha[META ? BM : 1];
+  __shared__ float s_dal[KIND == KIND_BWD_H ? WN * BM : 1];
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nt_count = (p.Nout + BN - 1) / BN;
-  const int KT = p.K / (RB / int(sizeof(T)));
+  const int KTu = KGROUP ? 0 : p.K / EPS;  // K slices of every tile (row-grouped kinds)
+  const int64_t rowbytes = int64_t(p.K) * int64_t(sizeof(T));  // A and B row pitch
 
-  // ---- real M tiles: per-group tile counts from the device-side offsets
-  // (grouped) or ceil(M / BM) (single group); offsets cached in LDS.
-  int total_mt;
-  if (p.offsets == nullptr) {
-    total_mt = int((p.M + BM - 1) / BM);
-  } else {
+  // ---- groups: per-group row offsets and tile counts from the device-side
+  // offsets (or one group), and with PAD the padded offsets: each group's
+  // rows rounded up to 64, which is where they sit in the transposed
+  // (K-major) activations of the weight gradients.  Cached in LDS.
+  const int G = p.offsets != nullptr ? p.E : 1;
+  if (p.offsets != nullptr || PAD) {
     if (tid < 64) {
       int c = 0;
-      if (lane < p.E) {
-        const int o0 = p.offsets[lane], o1 = p.offsets[lane + 1];
+      if (lane < G) {
+        const int dense_rows = KGROUP ? int(p.kcount) : int(p.M);
+        const int o0 = p.offsets != nullptr ? p.offsets[lane] : 0;
+        const int o1 = p.offsets != nullptr ? p.offsets[lane + 1] : dense_rows;
         c = o1 - o0;
         s_off[lane] = o0;
-        if (lane == p.E - 1) s_off[p.E] = o1;
+        if (lane == G - 1) s_off[G] = o1;
       }
       const int tiles = (c + BM - 1) / BM;
       s_scan[lane] = wave_inclusive_scan(tiles, lane);
+      if constexpr (PAD) {
+        const int kp = (c + 63) & ~63;
+        const int incl = wave_inclusive_scan(kp, lane);
+        if (lane < G) s_poff[lane] = incl - kp;
+      }
     }
     __syncthreads();
-    total_mt = __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
   }
 
-  // ---- persistent, XCD-aware work list.  Blocks are dispatched to the 8
-  // XCDs round robin (block b runs on XCD b % 8), each XCD with its own L2.
-  // XCD x owns the contiguous range [x*per, (x+1)*per) of the real tiles,
-  // ordered in groups of GM M-tiles (column by column inside a group), so
-  // co-resident blocks share A rows and weight panels in that L2; its
-  // gridDim/8 blocks take the range round robin.
-  constexpr int GM = 8;
-  const int total = total_mt * nt_count;
-  const int per = (total + 7) >> 3;
-  const int nbx = int(gridDim.x >> 3);
-  const int lb = int(blockIdx.x >> 3);
-  const int xbase = int(blockIdx.x & 7) * per;
-  int n_my = 0;
-  for (int l = lb; l < per && xbase + l < total; l += nbx) ++n_my;
-  if (n_my == 0) return;
-
   struct Tile {
-    int e, rows, n0;
+    int e, rows, n0, kt, koff;
     int64_t row0;
   };
+  // ---- work list.
+  // Row-grouped kinds: persistent and XCD-aware.  Blocks are dispatched to
+  // the 8 XCDs round robin (block b runs on XCD b % 8), each XCD with its own
+  // L2.  XCD x owns the contiguous range [x*per, (x+1)*per) of the real
+  // tiles, ordered in groups of GM M-tiles (column by column inside a group),
+  // so co-resident blocks share A rows and weight panels in that L2; its
+  // gridDim/8 blocks take the range round robin.
+  // K-grouped kinds: one tile per block.  Every group has the same output
+  // tiles; XCD x takes the x-th eighth of each group's tiles (so groups of
+  // very different K spread evenly over the XCDs), groups in order.
+  constexpr int GM = 8;
+  int total_mt = 0, total = 0, per = 0, nbx = 1, lb = 0, xbase = 0, n_my = 0;
+  int kg_e = 0, kg_idx = 0, kg_mt = 0;
+  if constexpr (KGROUP) {
+    kg_mt = int((p.M + BM - 1) / BM);
+    const int te = kg_mt * nt_count;
+    const int c = (te + 7) >> 3;
+    const int j = int(blockIdx.x >> 3);
+    kg_e = j / c;
+    kg_idx = int(blockIdx.x & 7) * c + (j - kg_e * c);
+    n_my = (kg_e < G && kg_idx < te) ? 1 : 0;
+  } else {
+    total_mt = p.offsets == nullptr ? int((p.M + BM - 1) / BM)
+                                    : __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
+    total = total_mt * nt_count;
+    per = (total + 7) >> 3;
+    nbx = int(gridDim.x >> 3);
+    lb = int(blockIdx.x >> 3);
+    xbase = int(blockIdx.x & 7) * per;
+    for (int l = lb; l < per && xbase + l < total; l += nbx) ++n_my;
+  }
+  if (n_my == 0) return;
+
   auto decode = [&](int j) -> Tile {
-    const int L = xbase + lb + j * nbx;
-    const int first_m = (L / (GM * nt_count)) * GM;
-    const int gsz = min(total_mt - first_m, GM);
-    const int in_group = L - first_m * nt_count;
-    const int mt = first_m + in_group % gsz;
     Tile t;
-    t.n0 = (in_group / gsz) * BN;
-    if (p.offsets == nullptr) {
-      t.e = 0;
+    if constexpr (KGROUP) {
+      const int first_m = (kg_idx / (GM * nt_count)) * GM;
+      const int gsz = min(kg_mt - first_m, GM);
+      const int in_group = kg_idx - first_m * nt_count;
+      const int mt = first_m + in_group % gsz;
+      t.n0 = (in_group / gsz) * BN;
+      t.e = kg_e;
       t.row0 = int64_t(mt) * BM;
       const int64_t left = p.M - t.row0;
       t.rows = left < BM ? int(left) : BM;
+      const int c = s_off[kg_e + 1] - s_off[kg_e];
+      t.kt = ((c + 63) & ~63) / EPS;
+      t.koff = s_poff[kg_e];
     } else {
-      int ge = 0;  // expert = number of groups whose tiles all precede mt
-      for (int g = 0; g < p.E; ++g) ge += (s_scan[g] <= mt) ? 1 : 0;
-      const int local_t = mt - (ge > 0 ? s_scan[ge - 1] : 0);
-      t.e = ge;
-      t.row0 = s_off[ge] + int64_t(local_t) * BM;
-      const int left = s_off[ge + 1] - int(t.row0);
-      t.rows = left < BM ? left : BM;
+      const int L = xbase + lb + j * nbx;
+      const int first_m = (L / (GM * nt_count)) * GM;
+      const int gsz = min(total_mt - first_m, GM);
+      const int in_group = L - first_m * nt_count;
+      const int mt = first_m + in_group % gsz;
+      t.n0 = (in_group / gsz) * BN;
+      t.kt = KTu;
+      t.koff = 0;
+      if (p.offsets == nullptr) {
+        t.e = 0;
+        t.row0 = int64_t(mt) * BM;
+        const int64_t left = p.M - t.row0;
+        t.rows = left < BM ? int(left) : BM;
+      } else {
+        int ge = 0;  // group = number of groups whose tiles all precede mt
+        for (int g = 0; g < p.E; ++g) ge += (s_scan[g] <= mt) ? 1 : 0;
+        const int local_t = mt - (ge > 0 ? s_scan[ge - 1] : 0);
+        t.e = ge;
+        t.row0 = s_off[ge] + int64_t(local_t) * BM;
+        const int left = s_off[ge + 1] - int(t.row0);
+        t.rows = left < BM ? left : BM;
+      }
     }
     // uniform over the block: keep the tile in scalar registers
     t.e = __builtin_amdgcn_readfirstlane(t.e);
     t.rows = __builtin_amdgcn_readfirstlane(t.rows);
     t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.kt = __builtin_amdgcn_readfirstlane(t.kt);
+    t.koff = __builtin_amdgcn_readfirstlane(t.koff);
     t.row0 = __builtin_amdgcn_readfirstlane(int(t.row0));
     return t;
   };
@@ -243,36 +363,42 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int r = (wid * LPW + j) * RPI + lane / CH;
-      int gr = int(t.row0) + (r < t.rows ? r : t.rows - 1);
-      if (r >= BM) gr = 0;
-      rid[j] = (KIND == KIND_GATEUP && p.entries != nullptr && r < BM) ? p.entries[gr] / p.k : gr;
+      const bool is_a = r < NA * BM;
+      const int lr = (NA == 2 && r >= BM) ? r - BM : r;
+      int gr = int(t.row0) + (lr < t.rows ? lr : t.rows - 1);
+      if (!is_a) gr = 0;
+      rid[j] = (KT_::GATHER && p.entries != nullptr && is_a) ? p.entries[gr] / p.k : gr;
     }
   };
   int32_t rid[LPW];          // A-row indices of the next tile
   const char* sbase[LPW];    // per-load base pointers (uniform) of the tile being issued
   uint32_t voff[LPW];        // per-lane byte offsets from them
   // Load j of a wavefront covers RPI consecutive LDS rows, all in one of the
-  // A, B0, B1 regions (BM, BN are multiples of 32), so its base pointer is
-  // uniform (scalar registers) and each lane keeps only a 32-bit byte offset
-  // (the global_load_lds saddr + voffset form).  Operand matrices are below
-  // 4 GiB (x and h as a whole, each expert's weight matrix on its own).
+  // A0, A1, B0, B1, B2 regions (BM, BN are multiples of RPI), so its base
+  // pointer is uniform (scalar registers) and each lane keeps only a 32-bit
+  // byte offset (the global_load_lds saddr + voffset form).  Operand
+  // matrices are below 4 GiB (activations as a whole, each expert's weight
+  // matrix on its own).
   auto make_src = [&](const Tile& t, const int32_t(&rid)[LPW]) {
+    const int64_t kbytes = int64_t(t.koff) * int64_t(sizeof(T));  // K-grouped: the group's columns
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int r0 = (wid * LPW + j) * RPI;  // first row of the load (uniform)
       const int r = r0 + lane / CH;
       const int chunk = (lane % CH) ^ ((r / RPW) % CH);
-      if (r0 < BM) {
-        sbase[j] = static_cast<const char*>(p.A);
-        voff[j] = uint32_t(rid[j]) * uint32_t(p.K * int(sizeof(T))) + uint32_t(chunk * 16);
+      if (r0 < NA * BM) {
+        const char* a = static_cast<const char*>((NA == 2 && r0 >= BM) ? p.A1 : p.A);
+        sbase[j] = a + kbytes;
+        voff[j] = uint32_t(rid[j]) * uint32_t(rowbytes) + uint32_t(chunk * 16);
       } else {
-        const int rb = r - BM;
-        const int which = (r0 - BM) >= BN ? 1 : 0;
+        const int rb = r - NA * BM;
+        const int which = (r0 - NA * BM) / BN;  // uniform
         int n = t.n0 + rb - which * BN;
         n = n < p.Nout ? n : p.Nout - 1;
-        sbase[j] = static_cast<const char*>(which ? p.B1 : p.B0) +
-                   int64_t(t.e) * p.Nout * p.K * int64_t(sizeof(T));
-        voff[j] = uint32_t(n) * uint32_t(p.K * int(sizeof(T))) + uint32_t(chunk * 16);
+        const void* b = which == 0 ? p.B0 : (NB > 1 && which == 1) ? p.B1 : p.B2;
+        sbase[j] = static_cast<const char*>(b) +
+                   (KGROUP ? kbytes : int64_t(t.e) * p.Nout * rowbytes);
+        voff[j] = uint32_t(n) * uint32_t(rowbytes) + uint32_t(chunk * 16);
       }
     }
   };
@@ -287,10 +413,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       lds_dma16(uniform_ptr(sbase[j]) + uint64_t(voff[j] + ko), dst + j * 1024);
   };
 
-  f32x16 acc[NB][TM][TN];
+  f32x16 acc[NP][TM][TN];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NP; ++b)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -305,12 +431,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 
   // MFMA operand fragments, double-buffered in registers: the fragments of
   // sub-step q + 1 are read from LDS while the MFMAs of sub-step q run.
-  u32x4 fa0[TM], fb0[NB][TN], fa1[TM], fb1[NB][TN];
-  auto frag_load = [&](const char* sb, int q, u32x4(&fa)[TM], u32x4(&fb)[NB][TN]) {
+  u32x4 fa0[NA][TM], fb0[NB][TN], fa1[NA][TM], fb1[NB][TN];
+  auto frag_load = [&](const char* sb, int q, u32x4(&fa)[NA][TM], u32x4(&fb)[NB][TN]) {
     const int rd = ((2 * q + fg) ^ sw) << 4;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      fa[i] = *reinterpret_cast<const u32x4*>(sb + (wm + 32 * i + fr) * RB + rd);
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[a][i] = *reinterpret_cast<const u32x4*>(sb + (a * BM + wm + 32 * i + fr) * RB + rd);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -318,17 +446,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
         fb[b][j] = *reinterpret_cast<const u32x4*>(sb + A_BYTES + b * B_BYTES +
                                                    (wn + 32 * j + fr) * RB + rd);
   };
-  auto mma_all = [&](const u32x4(&fa)[TM], const u32x4(&fb)[NB][TN]) {
+  auto mma_all = [&](const u32x4(&fa)[NA][TM], const u32x4(&fb)[NB][TN]) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int q = 0; q < NP; ++q)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) Mfma<T>::mma(acc[b][i][j], fa[i], fb[b][j]);
+        for (int j = 0; j < TN; ++j)
+          Mfma<T>::mma(acc[q][i][j], fa[KT_::pa(q)][i], fb[KT_::pb(q)][j]);
   };
 
-  constexpr int MF = NB * TM * TN * (sizeof(T) == 4 ? 4 : 1);  // MFMAs per sub-step
-  constexpr int DSR = TM + NB * TN;                            // LDS reads per sub-step
+  constexpr int MF = NP * TM * TN * (sizeof(T) == 4 ? 4 : 1);  // MFMAs per sub-step
+  constexpr int DSR = NA * TM + NB * TN;                       // LDS reads per sub-step
 
   // One K slice (QS MFMA sub-steps of 16 k), reading slot `cur`:
   //   LDS reads of sub-step q+1 | MFMAs of sub-step q   (q < QS - 1)
@@ -388,18 +517,107 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     asm volatile("" : "+v"(rl), "+v"(cl));
     const int rows_left = t.rows - rl;            // valid: 32 i + 8 (v / 4) + v % 4 < rows_left
     const int cols_left = p.Nout - (t.n0 + cl);   // valid: 32 j < cols_left
+    if constexpr (KIND == KIND_BWD_H) {
+      // Per element (column i of the intermediate, row t): g, u and
+      // dh_raw = (dy Wd)_{t,i}; with s = sigma(g), SiLU(g) = g s and
+      // SiLU'(g) = s (1 + g (1 - s)):
+      //   h = SiLU(g) u,  dh = alpha dh_raw,  dg = dh u SiLU'(g),  du = dh SiLU(g),
+      // and d alpha gets dh_raw . h summed over the row.  [dg | du] go out
+      // row-major (the dx GEMM's A operand), dg, du, h transposed into the
+      // group's padded columns (the weight-gradient GEMMs' operands), with
+      // zeros in the padding rows of the group.
+      const int lr0 = int(t.row0) - s_off[t.e];  // tile start within its group
+      const int64_t pcol = int64_t(s_poff[t.e]) + lr0 + rl;
+      const int pad_left = (((s_off[t.e + 1] - s_off[t.e]) + 63) & ~63) - lr0 - rl;
+      const int64_t ldk = p.ldk;
+      float dal[TM * 16];
+#pragma unroll
+      for (int n = 0; n < TM * 16; ++n) dal[n] = 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const int ro0 = 32 * i + 8 * vq;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const bool col_ok = 32 * j < cols_left;
+            const int col = t.n0 + cl + 32 * j;
+            float tg[4], tu[4], th[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const int v = 4 * vq + w;
+              const int ro = ro0 + w;
+              const float g = acc[0][i][j][v], u = acc[1][i][j][v], d = acc[2][i][j][v];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+              const float si = g * sg;
+              const float h = si * u;
+              const float dh = d * s_malpha[rl + ro];
+              const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
+              const float du = dh * si;
+              const bool ok = ro < rows_left && col_ok;
+              dal[16 * i + v] += col_ok ? d * h : 0.f;
+              tg[w] = ok ? dg : 0.f;
+              tu[w] = ok ? du : 0.f;
+              th[w] = ok ? h : 0.f;
+              if (ok) {
+                T* o = static_cast<T*>(p.out) + (t.row0 + rl + ro) * (2 * int64_t(p.Nout)) + col;
+                o[0] = from_f32<T>(dg);
+                o[p.Nout] = from_f32<T>(du);
+              }
+            }
+            if (col_ok && ro0 < pad_left) {
+              const int64_t o = int64_t(col) * ldk + pcol + ro0;
+              store4<T>(static_cast<T*>(p.out1) + o, tg);
+              store4<T>(static_cast<T*>(p.out2) + o, tu);
+              store4<T>(static_cast<T*>(p.out3) + o, th);
+            }
+          }
+        }
+      }
+      if (p.dalpha_part != nullptr) {
+        // row sums over the wavefront's columns, then over the WN wavefronts
+        using Red = HalfWaveTransposeSum<TM * 16>;
+        Red::run(dal, fr);
+        constexpr int sh = 5 - Red::steps;
+        if ((fr & ((1 << sh) - 1)) == 0) {
+#pragma unroll
+          for (int w = 0; w < Red::cnt; ++w) {
+            const int n = (fr >> sh) * Red::cnt + w;
+            const int row = wm + 32 * (n >> 4) + 8 * ((n & 15) >> 2) + 4 * fg + (n & 3);
+            s_dal[(wid % WN) * BM + row] = dal[w];
+          }
+        }
+        lds_barrier();
+        if (tid < t.rows) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) sum += s_dal[w * BM + tid];
+          p.dalpha_part[int64_t(s_ment[tid]) * nt_count + t.n0 / BN] = sum;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int ro = 32 * i + 8 * (v >> 2) + (v & 3);
         if (ro >= rows_left) continue;
-        if constexpr (KIND == KIND_GATEUP) {
+        if constexpr (KGROUP) {
+          const int64_t o = (int64_t(t.e) * p.M + t.row0 + rl + ro) * p.Nout + t.n0 + cl;
+#pragma unroll
+          for (int q = 0; q < NP; ++q) {
+            T* out = static_cast<T*>(q == 0 ? p.out : p.out1) + o;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[q][i][j][v]);
+          }
+        } else if constexpr (KIND == KIND_GATEUP) {
           T* out = static_cast<T*>(p.out) + (t.row0 + rl + ro) * p.Nout + t.n0 + cl;
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             if (32 * j < cols_left)
-              out[32 * j] = from_f32<T>(silu_mul(acc[0][i][j][v], acc[NB - 1][i][j][v]));
+              out[32 * j] = from_f32<T>(silu_mul(acc[0][i][j][v], acc[NP - 1][i][j][v]));
         } else {
           const int64_t ent = s_ment[rl + ro];
           const float a = s_malpha[rl + ro];
@@ -428,7 +646,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   // starts in slot 0 and the ring streams straight on into the next tile
   // (its first S slices are issued during this tile's last S steps);
   // otherwise each tile fills and drains the ring on its own.
-  const bool stream = (KT % S) == 0;
+  const bool stream = !KGROUP && (KTu % S) == 0;
   Tile cur = decode(0);
   load_rows(cur, rid);
   make_src(cur, rid);
@@ -441,6 +659,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   for (int cj = 0; cj < n_my; ++cj) {
     const bool has_next = cj + 1 < n_my;
     const bool xnext = stream && has_next;
+    const int KT = cur.kt;
     zero_acc();
     if (cj == 0 || !stream) {
       // fill the ring with the tile's first slices, wait for slice 0
@@ -526,27 +745,39 @@ int resident_blocks(K kernel, int threads) {
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, const Launch& s) {
   const int64_t nt = (p.Nout + BN - 1) / BN;
-  if (mtiles * nt <= 0) return hipSuccess;
-  // persistent grid: at most the blocks resident at once, in whole rounds of
-  // the 8 XCDs (blocks beyond the real tile count exit at once)
   auto kernel = gemm_kernel<T, BM, BN, WM, WN, RB, S, KIND>;
-  const int64_t cap = resident_blocks(kernel, 64 * WM * WN) / 8 * 8;
-  int64_t grid = (mtiles * nt + 7) / 8 * 8;
-  if (grid > cap && cap >= 8) grid = cap;
-  return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
+  if constexpr (KindTraits<KIND>::KGROUP) {
+    // one block per tile: eight per-XCD shares of every group's tiles
+    const int64_t te = ((p.M + BM - 1) / BM) * nt;
+    const int64_t groups = p.offsets != nullptr ? p.E : 1;
+    const int64_t grid = 8 * groups * ((te + 7) / 8);
+    if (te <= 0 || grid > 0x7fffffff) return te <= 0 ? hipSuccess : hipErrorInvalidValue;
+    return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
+  } else {
+    if (mtiles * nt <= 0) return hipSuccess;
+    // persistent grid: at most the blocks resident at once, in whole rounds of
+    // the 8 XCDs (blocks beyond the real tile count exit at once)
+    const int64_t cap = resident_blocks(kernel, 64 * WM * WN) / 8 * 8;
+    int64_t grid = (mtiles * nt + 7) / 8 * 8;
+    if (grid > cap && cap >= 8) grid = cap;
+    return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
+  }
 }
 
-// Launches a shape only when it is valid for the projection (LDS ring fits in
-// 160 KB, slice rows split evenly over the wavefronts).  A plain
+// Launches a shape only when it is valid for the kind (LDS ring within 156 KB,
+// leaving room for the epilogue's tables; slice rows split evenly over the
+// wavefronts; padded-group kinds need BM a multiple of 64).  A plain
 // specialisation rather than if-constexpr, so every kernel that can be
 // launched is instantiated at namespace scope with its host stub.
 template <int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 constexpr bool shape_ok() {
-  constexpr int NB = KIND == KIND_GATEUP ? 2 : 1;
-  constexpr int R = BM + NB * BN;
+  constexpr int R = KindTraits<KIND>::NA * BM + KindTraits<KIND>::NB * BN;
   constexpr int NW = WM * WN;
-  return S * R * RB <= 160 * 1024 && (R / (1024 / RB)) % NW == 0 &&
-         (S - 1) * (R / (1024 / RB) / NW) < 64 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0;
+  constexpr int RPI = 1024 / RB;
+  constexpr bool pad = KindTraits<KIND>::KGROUP || KIND == KIND_BWD_H;
+  return S * R * RB <= 156 * 1024 && (R / RPI) % NW == 0 && BM % RPI == 0 && BN % RPI == 0 &&
+         (S - 1) * (R / RPI / NW) < 64 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0 &&
+         (!pad || BM % 64 == 0) && BM <= 64 * NW;
 }
 
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND,
@@ -563,6 +794,7 @@ struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
 
 // The instantiated launch shapes: (BM, BN, WM, WN, RB, S) = block tile, wave
 // grid, LDS row bytes (K slice of RB / sizeof(T) elements), ring depth.
+// Forward projections:
 #define TOPMOE_GEMM_SHAPES_BF16(X)                                                        \
   X(128, 64, 2, 2, 128, 2) X(128, 64, 2, 2, 128, 3) X(128, 64, 2, 2, 64, 4)               \
   X(128, 128, 2, 2, 128, 2) X(128, 128, 2, 2, 128, 3) X(128, 128, 2, 2, 64, 4)            \
@@ -571,6 +803,17 @@ struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
   X(128, 128, 2, 4, 64, 4) X(256, 128, 4, 2, 128, 2) X(128, 128, 2, 4, 128, 3)            \
   X(128, 128, 2, 4, 128, 4) X(256, 64, 4, 2, 128, 3) X(256, 128, 4, 2, 128, 3)
 #define TOPMOE_GEMM_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
+// The fused backward projection (five operands per slice):
+// (4-wavefront 128-row tiles would hold three accumulator sets of 64 x 64 per
+// wavefront and spill.)
+#define TOPMOE_BWDH_SHAPES_BF16(X)                                                        \
+  X(128, 64, 4, 2, 128, 2) X(64, 128, 2, 4, 128, 2) X(128, 128, 2, 4, 64, 3)
+#define TOPMOE_BWDH_SHAPES_F32(X) X(64, 64, 2, 2, 128, 3)
+// Weight gradients:
+#define TOPMOE_WGRAD_SHAPES_BF16(X)                                                       \
+  X(128, 256, 2, 4, 128, 2) X(128, 128, 2, 4, 128, 3) X(256, 128, 4, 2, 128, 3)           \
+  X(128, 128, 2, 2, 128, 3) X(64, 64, 2, 2, 128, 3)
+#define TOPMOE_WGRAD_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
 
 template <typename T, int KIND>
 hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, const Launch& s) {
@@ -578,10 +821,24 @@ hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, 
   if (sh.bm == (BM_) && sh.bn == (BN_) && sh.wm == (WM_) && sh.wn == (WN_) &&            \
       sh.rb == (RB_) && sh.stages == (S_))                                               \
     return ShapeLauncher<T, BM_, BN_, WM_, WN_, RB_, S_, KIND>::run(p, mtiles, s);
-  if constexpr (sizeof(T) == 2) {
-    TOPMOE_GEMM_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+  if constexpr (KIND == KIND_BWD_H) {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_BWDH_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+    } else {
+      TOPMOE_BWDH_SHAPES_F32(TOPMOE_TRY_SHAPE)
+    }
+  } else if constexpr (KindTraits<KIND>::KGROUP) {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_WGRAD_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+    } else {
+      TOPMOE_WGRAD_SHAPES_F32(TOPMOE_TRY_SHAPE)
+    }
   } else {
-    TOPMOE_GEMM_SHAPES_F32(TOPMOE_TRY_SHAPE)
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_GEMM_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+    } else {
+      TOPMOE_GEMM_SHAPES_F32(TOPMOE_TRY_SHAPE)
+    }
   }
 #undef TOPMOE_TRY_SHAPE
   return hipErrorInvalidValue;
@@ -594,6 +851,9 @@ hipError_t launch_gemm_dtype(int kind, GemmShape sh, const GemmParams& p, int64_
     case KIND_GATEUP: return launch_gemm_tiles<T, KIND_GATEUP>(sh, p, mtiles, s);
     case KIND_DOWN_Y: return launch_gemm_tiles<T, KIND_DOWN_Y>(sh, p, mtiles, s);
     case KIND_DOWN_SLOTS: return launch_gemm_tiles<T, KIND_DOWN_SLOTS>(sh, p, mtiles, s);
+    case KIND_BWD_H: return launch_gemm_tiles<T, KIND_BWD_H>(sh, p, mtiles, s);
+    case KIND_WGRAD2: return launch_gemm_tiles<T, KIND_WGRAD2>(sh, p, mtiles, s);
+    case KIND_WGRAD1: return launch_gemm_tiles<T, KIND_WGRAD1>(sh, p, mtiles, s);
   }
   return hipErrorInvalidValue;
 }

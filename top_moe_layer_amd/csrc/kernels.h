@@ -43,18 +43,36 @@ enum GemmKind {
   KIND_GATEUP = 0,      // h = SiLU(A Wg^T) * (A Wu^T), rows gathered from x
   KIND_DOWN_Y = 1,      // y[token] = alpha * (h Wd^T), written in the output dtype
   KIND_DOWN_SLOTS = 2,  // slot[entry] = alpha * (h Wd^T), in the operand dtype
+  // backward
+  KIND_BWD_H = 3,       // g, u = x Wg^T, x Wu^T and dh = dy Wd (rows gathered from x, dy):
+                        // writes [dg | du] row-major, dg^T / du^T / h^T in padded group
+                        // columns, and per-row partial sums of dh . h (d alpha)
+  KIND_WGRAD2 = 4,      // out0 = A0 B^T, out1 = A1 B^T per group, K = the group's padded rows
+  KIND_WGRAD1 = 5,      // out0 = A0 B^T per group, K = the group's padded rows
 };
 
 struct GemmParams {
-  const void* A;           // gate/up: x [N, K]; down: h [rows, K] (grouped row order)
-  const void* B0;          // gate/up: Wg [E, Nout, K]; down: Wd [E, Nout, K]
-  const void* B1;          // gate/up: Wu [E, Nout, K]; down: unused
-  void* out;               // gate/up: h [rows, Nout]; down: y [N, Nout] or slots [rows, Nout]
+  const void* A;           // gate/up, bwd h: x [N, K]; down: h or [dg|du] [rows, K];
+                           // wgrad: [M, ldk] transposed activations (padded group columns)
+  const void* A1;          // bwd h: dy [N, K]; wgrad pair: second A [M, ldk]
+  const void* B0;          // gate/up, bwd h: Wg [E, Nout, K]; down: Wd or [Wg|Wu]^T [E, Nout, K];
+                           // wgrad: [Nout, ldk]
+  const void* B1;          // gate/up, bwd h: Wu [E, Nout, K]
+  const void* B2;          // bwd h: Wd^T [E, Nout, K]
+  void* out;               // gate/up: h [rows, Nout]; down: y [N, Nout] or slots [rows, Nout];
+                           // bwd h: [dg | du] [rows, 2 Nout]; wgrad: [groups, M, Nout]
+  void* out1;              // bwd h: dg^T [Nout, ldk]; wgrad pair: second [groups, M, Nout]
+  void* out2;              // bwd h: du^T [Nout, ldk]
+  void* out3;              // bwd h: h^T [Nout, ldk]
+  float* dalpha_part;      // bwd h: [entries, ceil(Nout / BN)] partial dh . h; NULL = skip
   const int32_t* entries;  // grouped row -> entry id t*k + j; NULL = identity (dense)
   const int32_t* offsets;  // [E+1] group row offsets; NULL = one group of M rows
-  const float* alpha;      // [rows] weight of each grouped row (down); NULL = 1
+                           // (wgrad: of kcount rows)
+  const float* alpha;      // [rows] weight of each grouped row (down, bwd h); NULL = 1
   const void* residual;    // down into y: [N, Nout] added before rounding; NULL = none
-  int64_t M;               // rows when offsets == NULL
+  int64_t M;               // rows when offsets == NULL (wgrad: output rows per group)
+  int64_t ldk;             // bwd h / wgrad: row length of the padded-column matrices
+  int64_t kcount;          // wgrad with offsets == NULL: rows of the single group
   int E, k;
   int Nout, K;
 };
@@ -66,7 +84,7 @@ enum RouterMode {
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
                          int k, bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                         float* alpha,
+                         float* alpha, float* probs,
                          int32_t* count_part, float* psum_part, const Launch& s);
 
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
@@ -82,5 +100,47 @@ hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch&
 
 hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
                        int64_t mtiles, const Launch& s);
+
+// ---- backward
+// out[b][c][col0 + r] = src[b][r][c]; R, C multiples of 64.
+struct TransposeJob {
+  const void* src;
+  void* dst;
+  int R, C, batch, col0;
+  int64_t ldo, src_bs, dst_bs;  // out row pitch; per-batch element strides
+};
+struct TransposeJobs {
+  TransposeJob job[3];
+  int n;
+};
+// Gathered transpose into padded group columns (see backward.hip).
+struct GatherTransposeJob {
+  const void* src;      // [*, C]
+  void* dst;            // [C, ldo]
+  const float* scale;   // per grouped row, or NULL
+};
+struct GatherTransposeJobs {
+  GatherTransposeJob job[2];
+  int n;
+  const int32_t* offsets;  // [E+1] group offsets, or NULL: one group of `rows`
+  const int32_t* entries;  // grouped row -> entry id (source row entries / k), or NULL
+  int E, k, C;
+  int64_t rows, ldo;
+};
+
+hipError_t launch_transpose(int dtype, const TransposeJobs& jobs, int max_tiles, int max_batch,
+                            const Launch& s);
+hipError_t launch_gather_transpose(int dtype, const GatherTransposeJobs& jobs, int64_t ldo,
+                                   const Launch& s);
+hipError_t launch_router_bwd(const float* probs, const int32_t* topk_idx,
+                             const float* dalpha_part, int nt, const int32_t* offsets, int64_t N,
+                             int E, int k, bool renorm, float aux_scale, float* dr,
+                             const Launch& s);
+hipError_t launch_combine_bwd(const void* slots, const int32_t* topk_idx, const float* dr,
+                              const float* Wr, int64_t N, int H, int E, int k, int dtype,
+                              void* dx, const Launch& s);
+int dwr_chunks(int64_t N);
+hipError_t launch_dwr(const void* x, const float* dr, int64_t N, int H, int E, int dtype,
+                      float* part, float* dWr, const Launch& s);
 
 }  // namespace topmoe

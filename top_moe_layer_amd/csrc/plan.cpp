@@ -121,6 +121,27 @@ GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int d
   return sh;
 }
 
+// ---- backward launch shapes (bf16 candidates measured on MI355X; fp32 the
+// register-light tiles).  Environment overrides as for the forward.
+GemmShape bwd_shape(const char* env, GemmShape bf16, GemmShape f32, int dtype) {
+  GemmShape sh = dtype == TOPMOE_DTYPE_FP32 ? f32 : bf16;
+  env_shape(env, &sh);
+  return sh;
+}
+
+GemmShape bwdh_tile(int dtype) {
+  return bwd_shape("TOPMOE_BWDH_TILE", GemmShape{128, 64, 4, 2, 128, 2},
+                   GemmShape{64, 64, 2, 2, 128, 3}, dtype);
+}
+GemmShape wgu_tile(int dtype) {
+  return bwd_shape("TOPMOE_WGU_TILE", GemmShape{128, 256, 2, 4, 128, 2},
+                   GemmShape{128, 64, 2, 2, 128, 2}, dtype);
+}
+GemmShape wd_tile(int dtype) {
+  return bwd_shape("TOPMOE_WD_TILE", GemmShape{256, 128, 4, 2, 128, 3},
+                   GemmShape{128, 64, 2, 2, 128, 2}, dtype);
+}
+
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
   if (!dtype_ok(dtype)) return TOPMOE_ERR_UNSUPPORTED_DTYPE;
   if (N < 0 || H < 64 || I < 64 || H % 64 || I % 64) return TOPMOE_ERR_BAD_SHAPE;
@@ -183,6 +204,81 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_slots = o;
   if (k >= 2) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
   q.total = o == 0 ? kAlign : o;
+  *p = q;
+  return TOPMOE_OK;
+}
+
+int plan_ffn_bwd(int64_t N, int64_t H, int64_t I, int dtype, FfnBwdPlan* p) {
+  FfnPlan f;
+  const int st = plan_ffn(N, H, I, dtype, &f);
+  if (st != TOPMOE_OK) return st;
+  const int el = f.elem;
+  FfnBwdPlan q;
+  q.N = N; q.H = H; q.I = I; q.dtype = dtype; q.elem = el;
+  q.ldk = (N + 63) / 64 * 64;
+  if (!operand_ok(N, 2 * I, el) || !operand_ok(H, 2 * I, el) || !operand_ok(I, q.ldk, el) ||
+      !operand_ok(H, q.ldk, el))
+    return TOPMOE_ERR_BAD_SHAPE;
+  q.bwdh = bwdh_tile(dtype);
+  q.dx = choose_down_tile(N, H, 2 * I, 1, dtype);
+  q.wgu = wgu_tile(dtype);
+  q.wd = wd_tile(dtype);
+  const size_t e = size_t(el);
+  size_t o = 0;
+  q.off_wgT = o;  o = align_up(o + size_t(H) * size_t(2 * I) * e);
+  q.off_wdT = o;  o = align_up(o + size_t(I) * size_t(H) * e);
+  q.off_xT = o;   o = align_up(o + size_t(H) * size_t(q.ldk) * e);
+  q.off_dyT = o;  o = align_up(o + size_t(H) * size_t(q.ldk) * e);
+  q.off_dgdu = o; o = align_up(o + size_t(N) * size_t(2 * I) * e);
+  q.off_dgT = o;  o = align_up(o + size_t(I) * size_t(q.ldk) * e);
+  q.off_duT = o;  o = align_up(o + size_t(I) * size_t(q.ldk) * e);
+  q.off_hT = o;   o = align_up(o + size_t(I) * size_t(q.ldk) * e);
+  q.total = o;
+  *p = q;
+  return TOPMOE_OK;
+}
+
+int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBwdPlan* p) {
+  MoePlan r;
+  const int st = plan_moe(N, H, I, E, k, dtype, &r);
+  if (st != TOPMOE_OK) return st;
+  const int el = r.elem;
+  const int64_t rows = r.rows;
+  MoeBwdPlan q;
+  q.route = r;
+  // every group's rows rounded up to 64: at most 63 extra per group
+  q.ldk = (rows + 63) / 64 * 64 + 64 * int64_t(E);
+  if (!operand_ok(rows, 2 * I, el) || !operand_ok(H, 2 * I, el) || !operand_ok(I, q.ldk, el) ||
+      !operand_ok(H, q.ldk, el) || q.ldk > kMaxRows)
+    return TOPMOE_ERR_BAD_SHAPE;
+  q.bwdh = bwdh_tile(dtype);
+  q.dx = choose_down_tile(rows, H, 2 * I, E, dtype);
+  q.wgu = wgu_tile(dtype);
+  q.wd = wd_tile(dtype);
+  q.bwdh_mtiles = grouped_mtiles_bound(rows, E, q.bwdh.bm);
+  q.dx_mtiles = grouped_mtiles_bound(rows, E, q.dx.bm);
+  q.nt_h = int((I + q.bwdh.bn - 1) / q.bwdh.bn);
+  q.nchunk = int((N + kDwrChunk - 1) / kDwrChunk);
+  const size_t e = size_t(el);
+  // routing buffers first (the forward's own layout), then the backward's
+  size_t o = r.off_h;
+  q.off_probs = o; o = align_up(o + size_t(N) * size_t(E) * 4);
+  q.off_topk = o;  o = align_up(o + size_t(rows) * 4);
+  q.off_alpha = o; o = align_up(o + size_t(rows) * 4);
+  q.off_aux = o;   o = align_up(o + 4);
+  q.off_wgT = o;   o = align_up(o + size_t(E) * size_t(H) * size_t(2 * I) * e);
+  q.off_wdT = o;   o = align_up(o + size_t(E) * size_t(I) * size_t(H) * e);
+  q.off_xT = o;    o = align_up(o + size_t(H) * size_t(q.ldk) * e);
+  q.off_dyT = o;   o = align_up(o + size_t(H) * size_t(q.ldk) * e);
+  q.off_dgdu = o;  o = align_up(o + size_t(rows) * size_t(2 * I) * e);
+  q.off_dgT = o;   o = align_up(o + size_t(I) * size_t(q.ldk) * e);
+  q.off_duT = o;   o = align_up(o + size_t(I) * size_t(q.ldk) * e);
+  q.off_hT = o;    o = align_up(o + size_t(I) * size_t(q.ldk) * e);
+  q.off_dal = o;   o = align_up(o + size_t(rows) * size_t(q.nt_h) * 4);
+  q.off_slots = o; o = align_up(o + size_t(rows) * size_t(H) * e);
+  q.off_dr = o;    o = align_up(o + size_t(N) * size_t(E) * 4);
+  q.off_dwr = o;   o = align_up(o + size_t(q.nchunk) * size_t(E) * size_t(H) * 4);
+  q.total = o;
   *p = q;
   return TOPMOE_OK;
 }

@@ -9,6 +9,7 @@
 namespace topmoe {
 
 constexpr size_t kAlign = 256;
+constexpr int kDwrChunk = 128;  // tokens per partial of the router-weight gradient
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
@@ -52,9 +53,60 @@ struct MoePlan {
   size_t total = 0;
 };
 
+// Backward of the dense FFN.  Transposed activations keep tokens along
+// their rows, padded to ldk = round64(N) columns (zeros past N), so the
+// weight gradients contract over whole 64-token slices.
+struct FfnBwdPlan {
+  int64_t N = 0, H = 0, I = 0;
+  int dtype = 0, elem = 0;
+  int64_t ldk = 0;
+  GemmShape bwdh, dx, wgu, wd;  // fused g/u/dh, dx, dWg+dWu, dWd GEMMs
+  size_t off_wgT = 0;    // [H, 2I]  [Wg | Wu]^T
+  size_t off_wdT = 0;    // [I, H]   Wd^T
+  size_t off_xT = 0;     // [H, ldk] x^T
+  size_t off_dyT = 0;    // [H, ldk] dy^T
+  size_t off_dgdu = 0;   // [N, 2I]  [dg | du]
+  size_t off_dgT = 0;    // [I, ldk] dg^T
+  size_t off_duT = 0;    // [I, ldk] du^T
+  size_t off_hT = 0;     // [I, ldk] h^T
+  size_t total = 0;
+};
+
+// Backward of the MoE FFN: the forward's routing is recomputed (same kernels,
+// so the same choices), then the expert GEMMs run on expert-grouped rows.
+// Transposed activations hold each expert's rows in columns padded to a
+// multiple of 64 (zeros in between); ldk bounds their total width.
+struct MoeBwdPlan {
+  MoePlan route;          // router / permutation parameters and buffers
+  int64_t ldk = 0;
+  GemmShape bwdh, dx, wgu, wd;
+  int64_t bwdh_mtiles = 0, dx_mtiles = 0;
+  int nt_h = 0;           // column tiles of the fused GEMM: d alpha partials per entry
+  int nchunk = 0;         // token chunks of the router-weight gradient
+  size_t off_probs = 0;   // f32 [N, E] softmax
+  size_t off_topk = 0;    // i32 [N, k]
+  size_t off_alpha = 0;   // f32 [N, k]
+  size_t off_aux = 0;     // f32 [1] (forward value, unused)
+  size_t off_wgT = 0;     // [E, H, 2I]
+  size_t off_wdT = 0;     // [E, I, H]
+  size_t off_xT = 0;      // [H, ldk]
+  size_t off_dyT = 0;     // [H, ldk] (alpha * dy)^T
+  size_t off_dgdu = 0;    // [N*k, 2I]
+  size_t off_dgT = 0;     // [I, ldk]
+  size_t off_duT = 0;     // [I, ldk]
+  size_t off_hT = 0;      // [I, ldk]
+  size_t off_dal = 0;     // f32 [N*k, nt_h]
+  size_t off_slots = 0;   // [N*k, H] per-entry dx terms
+  size_t off_dr = 0;      // f32 [N, E] router-logit gradients
+  size_t off_dwr = 0;     // f32 [nchunk, E, H] partial router-weight gradients
+  size_t total = 0;
+};
+
 // Returns TOPMOE_OK or a negative status; fills `plan` on success.
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* plan);
 int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* plan);
+int plan_ffn_bwd(int64_t N, int64_t H, int64_t I, int dtype, FfnBwdPlan* plan);
+int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBwdPlan* plan);
 
 // Launch shape for an M x Nout x K GEMM with `groups` row groups (experts).
 GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype);

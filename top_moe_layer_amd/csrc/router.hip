@@ -107,7 +107,8 @@ template <int EP, int TPW>
 __device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, int E, int k,
                                              bool renorm, int64_t t_first, int64_t t_end,
                                              int32_t* __restrict__ topk_idx,
-                                             float* __restrict__ alpha, int* s_cnt,
+                                             float* __restrict__ alpha,
+                                             float* __restrict__ probs, int* s_cnt,
                                              float& psum) {
   const bool expert_lane = lane < E;
   float p[TPW];
@@ -119,7 +120,10 @@ __device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, in
     const float ex = expert_lane ? expf(ru - m) : 0.f;
     const float sum = group_sum<EP>(ex);
     p[u] = expert_lane ? ex / sum : 0.f;  // (lanes past EP see an all-zero group)
-    if (t_first + u < t_end) psum += p[u];
+    if (t_first + u < t_end) {
+      psum += p[u];
+      if (probs != nullptr && expert_lane) probs[(t_first + u) * E + lane] = p[u];
+    }
     key[u] = expert_lane ? ((uint64_t(__float_as_uint(p[u])) << 32) | uint32_t(64 - lane)) : 0ull;
   }
   int my_e[TPW];
@@ -199,7 +203,7 @@ template <typename T, int EP>
 __global__ __launch_bounds__(64) void router_lds_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
     bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
-    int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
+    float* __restrict__ probs, int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
   constexpr int VE = 16 / int(sizeof(T));  // elements per 16-byte load
   constexpr int CI = 8;                    // loads per lane in flight per chunk
   extern __shared__ __attribute__((aligned(1024))) f32x4 s_w4[];  // [EP, H / 4], 1 KB-rounded
@@ -333,6 +337,11 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
 #pragma unroll
       for (int e = 0; e < EP; ++e) s_pt[tok][e] = valid ? acc[e] : 0.f;
     }
+    if (probs != nullptr && valid) {  // the softmax for the backward pass (lane part: e = part mod 4)
+#pragma unroll
+      for (int e = 0; e < EP; ++e)
+        if (e < E && (e & 3) == part) probs[t * E + e] = acc[e];
+    }
     __syncthreads();
     if (lane < E) {
       for (int u = 0; u < 16; ++u) psum += s_pt[u][lane];
@@ -357,7 +366,7 @@ template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_split_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
     bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
-    int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
+    float* __restrict__ probs, int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
   constexpr int CG = EP <= 16 ? 2 : 1;   // groups of 256 elements in flight per wavefront
   constexpr int EC = EP < 16 ? EP : 16;  // experts' W_router columns held at once
   __shared__ int s_cnt[64];
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(
     __syncthreads();
     if (wave == 0) {
       const float r[1] = {(s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane])};
-      route_tokens<EP, 1>(r, lane, E, k, renorm, t, t1, topk_idx, alpha, s_cnt, psum);
+      route_tokens<EP, 1>(r, lane, E, k, renorm, t, t1, topk_idx, alpha, probs, s_cnt, psum);
     }
   }
   s_ps[wave][lane] = psum;  // only wave 0 routed: the other rows are zero
@@ -426,25 +435,25 @@ __global__ __launch_bounds__(256) void router_split_kernel(
 template <typename T, int EP>
 hipError_t launch_router_ep(const T* x, const float* Wr, int64_t N, int H, int E, int k,
                             bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                            float* alpha,
+                            float* alpha, float* probs,
                             int32_t* count_part, float* psum_part, const Launch& s) {
   if (mode == ROUTER_MODE_SPLIT)
     return launch_kernel(router_split_kernel<T, EP>, dim3(nblk), dim3(256), 0, s, x, Wr, N, H,
-                         E, k, renorm, tb, topk_idx, alpha, count_part, psum_part);
+                         E, k, renorm, tb, topk_idx, alpha, probs, count_part, psum_part);
   // W_router rounded up to whole 1 KB direct-to-LDS loads
   const unsigned lds = (unsigned(EP) * unsigned(H) * sizeof(float) + 1023u) & ~1023u;
   return launch_kernel(router_lds_kernel<T, EP>, dim3(nblk), dim3(64), lds, s, x, Wr, N, H, E, k,
-                       renorm, tb, topk_idx, alpha, count_part, psum_part);
+                       renorm, tb, topk_idx, alpha, probs, count_part, psum_part);
 }
 
 template <typename T>
 hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E, int k,
                            bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                           float* alpha,
+                           float* alpha, float* probs,
                            int32_t* count_part, float* psum_part, const Launch& s) {
 #define TOPMOE_ROUTER(EPV)                                                                 \
   return launch_router_ep<T, EPV>(x, Wr, N, H, E, k, renorm, tb, nblk, mode, topk_idx,    \
-                                  alpha, count_part, psum_part, s)
+                                  alpha, probs, count_part, psum_part, s)
   if (E <= 1) TOPMOE_ROUTER(1);
   if (E <= 2) TOPMOE_ROUTER(2);
   if (E <= 4) TOPMOE_ROUTER(4);
@@ -459,14 +468,14 @@ hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E,
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
                          int k, bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                         float* alpha,
+                         float* alpha, float* probs,
                          int32_t* count_part, float* psum_part, const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (dtype == TOPMOE_DTYPE_FP32)
     return launch_router_t(static_cast<const float*>(x), Wr, N, H, E, k, renorm, tb, nblk, mode,
-                           topk_idx, alpha, count_part, psum_part, s);
+                           topk_idx, alpha, probs, count_part, psum_part, s);
   return launch_router_t(static_cast<const bf16_t*>(x), Wr, N, H, E, k, renorm, tb, nblk, mode,
-                         topk_idx, alpha, count_part, psum_part, s);
+                         topk_idx, alpha, probs, count_part, psum_part, s);
 }
 
 }  // namespace topmoe

@@ -162,3 +162,99 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
                            stage_events.ptr if stage_events is not None else None)
     B.check(st, "moe_ffn_fwd")
     return MoeOutput(y.view(x.shape), topk_idx, alpha, aux_loss, expert_offsets, sorted_token_ids)
+
+
+def ffn_bwd_workspace_bytes(N: int, H: int, I: int, dtype: torch.dtype) -> int:
+    return B.raw_ffn_bwd_workspace_bytes(N, H, I, _dtype_code(dtype))
+
+
+def moe_bwd_workspace_bytes(N: int, H: int, I: int, E: int, k: int, dtype: torch.dtype) -> int:
+    return B.raw_moe_bwd_workspace_bytes(N, H, I, E, k, _dtype_code(dtype))
+
+
+@dataclass
+class FfnGrads:
+    dx: torch.Tensor
+    dWg: torch.Tensor
+    dWu: torch.Tensor
+    dWd: torch.Tensor
+
+
+@dataclass
+class MoeGrads:
+    dx: torch.Tensor
+    dWr: torch.Tensor
+    dWg: torch.Tensor
+    dWu: torch.Tensor
+    dWd: torch.Tensor
+
+
+def ffn_swiglu_bwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
+                   dy: torch.Tensor, *, workspace: Optional[torch.Tensor] = None, stream=None,
+                   stage_events: Optional[B.StageEvents] = None) -> FfnGrads:
+    """Gradients of the dense SwiGLU FFN for the upstream gradient dy (x's
+    shape and dtype): dx (x's shape), dWg, dWu [I, H], dWd [H, I]."""
+    dev = x.device
+    H = x.shape[-1]
+    I = Wg.shape[0]
+    xf = x.reshape(-1, H)
+    N = xf.shape[0]
+    dt = x.dtype
+    dyf = dy.reshape(-1, H)
+    _need(xf, "x", (N, H), dt, dev)
+    _need(Wg, "Wg", (I, H), dt, dev)
+    _need(Wu, "Wu", (I, H), dt, dev)
+    _need(Wd, "Wd", (H, I), dt, dev)
+    _need(dyf, "dy", (N, H), dt, dev)
+    new = lambda shape: torch.empty(shape, dtype=dt, device=dev)
+    dx, dWg, dWu, dWd = new((N, H)), new((I, H)), new((I, H)), new((H, I))
+    code = _dtype_code(dt)
+    nbytes = B.raw_ffn_bwd_workspace_bytes(N, H, I, code)
+    if nbytes == 0:
+        B.check(B.ERR_BAD_SHAPE, "ffn_swiglu_bwd")
+    ws = _workspace(nbytes, dev, workspace)
+    st = B.raw_ffn_swiglu_bwd(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf), _ptr(dx),
+                              _ptr(dWg), _ptr(dWu), _ptr(dWd), N, H, I, code, _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(dev, stream),
+                              stage_events.ptr if stage_events is not None else None)
+    B.check(st, "ffn_swiglu_bwd")
+    return FfnGrads(dx.view(x.shape), dWg, dWu, dWd)
+
+
+def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
+                Wd: torch.Tensor, dy: torch.Tensor, k: int, aux_coef: float, *,
+                aux_grad: float = 1.0, norm_topk_prob: bool = True,
+                workspace: Optional[torch.Tensor] = None, stream=None,
+                stage_events: Optional[B.StageEvents] = None) -> MoeGrads:
+    """Gradients of the top-k MoE FFN (and of ``aux_grad`` * aux_loss) for the
+    upstream gradient dy: dx (x's shape), dWr [E, H] float32, dWg, dWu
+    [E, I, H], dWd [E, H, I].  The routing is recomputed from x and Wr."""
+    dev = x.device
+    H = x.shape[-1]
+    E, I = Wg.shape[0], Wg.shape[1]
+    xf = x.reshape(-1, H)
+    N = xf.shape[0]
+    dt = x.dtype
+    dyf = dy.reshape(-1, H)
+    _need(xf, "x", (N, H), dt, dev)
+    _need(Wr, "Wr", (E, H), torch.float32, dev)
+    _need(Wg, "Wg", (E, I, H), dt, dev)
+    _need(Wu, "Wu", (E, I, H), dt, dev)
+    _need(Wd, "Wd", (E, H, I), dt, dev)
+    _need(dyf, "dy", (N, H), dt, dev)
+    new = lambda shape, d=dt: torch.empty(shape, dtype=d, device=dev)
+    dx, dWr = new((N, H)), new((E, H), torch.float32)
+    dWg, dWu, dWd = new((E, I, H)), new((E, I, H)), new((E, H, I))
+    code = _dtype_code(dt)
+    nbytes = B.raw_moe_bwd_workspace_bytes(N, H, I, E, k, code)
+    if nbytes == 0:
+        B.check(B.ERR_BAD_SHAPE, "moe_ffn_bwd")
+    ws = _workspace(nbytes, dev, workspace)
+    flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
+    st = B.raw_moe_ffn_bwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf),
+                           float(aux_grad), N, H, I, E, k, float(aux_coef), flags, code,
+                           _ptr(dx), _ptr(dWr), _ptr(dWg), _ptr(dWu), _ptr(dWd), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(dev, stream),
+                           stage_events.ptr if stage_events is not None else None)
+    B.check(st, "moe_ffn_bwd")
+    return MoeGrads(dx.view(x.shape), dWr, dWg, dWu, dWd)

@@ -1,4 +1,4 @@
-"""Seeded synthetic workloads for the MiniMind FFN / top-k MoE forward pass.
+"""Seeded synthetic workloads for the MiniMind FFN / top-k MoE forward and backward passes.
 
 This package only *draws* inputs: shapes, seeds, distributions and storage
 rounding.  It holds none of the method's arithmetic (no projection, softmax,
@@ -8,6 +8,7 @@ bytes without sharing any computation.
 from .registry import WORKLOADS, Workload, get, intermediate_size
 from .gen import (
     make_inputs,
+    make_upstream,
     redraw_token_rows,
     to_f64,
     bf16_bits_from_f64,
@@ -20,6 +21,7 @@ __all__ = [
     "get",
     "intermediate_size",
     "make_inputs",
+    "make_upstream",
     "redraw_token_rows",
     "to_f64",
     "bf16_bits_from_f64",

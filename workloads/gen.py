@@ -10,6 +10,8 @@ once to the storage dtype with round-to-nearest-even):
 * Skewed routing: the router is bias-free, so a per-expert logit offset b is
   realised as one shared mean shift of the tokens, m = Wr^T (Wr Wr^T)^-1 b,
   x = round(z + m), which gives logits Wr z + b.  b = bias_scale * N(0, bias_std).
+* Upstream gradient for the backward (make_upstream): dy ~ N(0, 1), shape
+  [N, H], in the storage dtype.
 * Every tensor has its own random stream: SeedSequence(seed, spawn_key=(crc32(name),)).
   A token row that must be redrawn uses the stream keyed (crc32("x_redraw"), t, attempt).
 
@@ -118,6 +120,13 @@ def make_inputs(w: Workload, seed: int | None = None, N: int | None = None) -> d
     if w.residual:
         out["residual"] = round_to(_rng(seed, "residual").standard_normal((N, H)), dt)
     return out
+
+
+def make_upstream(inputs: dict, seed: int | None = None) -> np.ndarray:
+    """The upstream gradient dy [N, H] (storage dtype) for ``inputs``."""
+    seed = inputs["seed"] if seed is None else seed
+    N, H = inputs["x"].shape
+    return round_to(_rng(seed, "dy").standard_normal((N, H)), inputs["dtype"])
 
 
 def redraw_token_rows(inputs: dict, rows, attempt: int) -> None:
