@@ -1,6 +1,7 @@
-"""Benchmark of the MiniMind FFN / top-k MoE forward on one MI355X.
+"""Benchmark of the MiniMind FFN / top-k MoE forward (or backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cold | --warm]
+                    [--pass fwd | bwd]
 
 A step is one full forward (every kernel of the path) over one batch of
 synthetic inputs already resident in device memory.  W untimed steps, then
@@ -13,6 +14,10 @@ competes with the step), and ``value`` comes from those events.  A second pass o
 stage on the library's stream to get per-kernel durations, from which the
 dominant kernel's roofline fraction is computed.  The fp64 CPU oracle is then
 timed on a bounded sample of the same workload (rank 0, one GPU only).
+
+With ``--pass bwd`` a step is one backward instead (routing and gate/up
+activations recomputed, then every gradient); its line carries its own metric
+and the same roofline / cpu_baseline objects.
 
 Prints ONE JSON line.
 """
@@ -29,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "FFN/MoE fwd tokens/s + TFLOP/s (% bf16 MFMA peak) / GB/s (% HBM) on 1 GPU"
+METRIC_BWD = "FFN/MoE bwd tokens/s + TFLOP/s (% bf16 MFMA peak) on 1 GPU"
 DEFAULT_WORKLOAD = "moe_top1_n4096_h768_e4"
 
 # MI355X published peaks
@@ -87,6 +93,91 @@ def stage_units(w):
         "gateup_gemm": (4.0 * rows * H * I, N * H * el + 2 * touched * I * H * el + rows * I * el),
         "down_gemm": (2.0 * rows * H * I, rows * I * el + touched * H * I * el + N * H * el),
         "combine": (0.0, (rows * H * 4 + N * H * el) if k > 1 else 0.0),
+    }
+
+
+def stage_units_bwd(w, touched=None):
+    """Algorithmic work of each stage of one backward: (flops, bytes).  GEMM
+    stages are credited with the contraction flops they execute (including the
+    recomputed gate and up projections); memory stages
+    with each tensor they must read or write once."""
+    el = w.elem_bytes()
+    N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
+    rows = N * k
+    ex = 1 if w.kind == "dense" else (touched if touched is not None else min(E, rows))
+    Ew = 1 if w.kind == "dense" else E
+    u = {
+        "transpose_w": (0.0, 2 * 3 * Ew * H * I * el),
+        "transpose_act": (0.0, 2 * 2 * rows * H * el),
+        "gu_gemm": (4.0 * rows * H * I, N * H * el + 2 * ex * H * I * el + 3 * rows * I * el),
+        "dh_gemm": (2.0 * rows * H * I, N * H * el + ex * H * I * el + 6 * rows * I * el),
+        "dx_gemm": (4.0 * rows * H * I, 2 * rows * I * el + 2 * ex * H * I * el + rows * H * el),
+        "dwgu_gemm": (4.0 * rows * H * I, 2 * rows * I * el + rows * H * el + 2 * Ew * H * I * el),
+        "dwd_gemm": (2.0 * rows * H * I, rows * I * el + rows * H * el + Ew * H * I * el),
+    }
+    if w.kind == "moe":
+        u.update({
+            "router": (2.0 * N * H * E, N * H * el + E * H * 4 + N * k * 8 + N * E * 4),
+            "permute": (0.0, N * k * 4 * 2),
+            "router_bwd": (0.0, N * E * 8 + N * k * 8),
+            "dx_combine": (2.0 * N * H * E, rows * H * el + N * H * el + N * E * 4),
+            "dwr": (2.0 * N * H * E, N * H * el + N * E * 4 + E * H * 4),
+        })
+    return u
+
+
+def flops_bwd(w):
+    """Algorithmic FLOPs of one backward given the forward's activations:
+    12 * N*k * H * I for the three projections' input and weight gradients
+    (the recomputation of g and u is not credited), plus 4 * N * H * E for
+    the router's."""
+    f = 12.0 * w.N * w.k * w.H * w.I
+    if w.kind == "moe":
+        f += 4.0 * w.N * w.H * w.E
+    return f
+
+
+def cpu_baseline_bwd(w, inputs, dy, budget_s=10.0):
+    """Time the fp64 oracle's backward (as it stands) on a bounded sample: the
+    first n tokens as a batch of their own (n grown by 4x until one pass takes
+    a quarter of the budget, at most all N), repeated until the budget is spent."""
+    from oracle.cases import widen
+    from oracle import swiglu_ffn_bwd, moe_ffn_bwd
+    from workloads import to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    f = widen(inputs)
+    g = to_f64(dy, w.dtype)
+
+    def run(n):
+        t0 = time.perf_counter()
+        if w.kind == "dense":
+            swiglu_ffn_bwd(f["x"][:n], f["Wg"], f["Wu"], f["Wd"], g[:n])
+        else:
+            moe_ffn_bwd(f["x"][:n], f["Wr"], f["Wg"], f["Wu"], f["Wd"], w.k, w.coef, g[:n], 1.0,
+                        w.norm_topk_prob)
+        return time.perf_counter() - t0
+
+    n = min(w.N, 64)
+    dt = run(n)
+    while n < w.N and dt < budget_s / 4:
+        n = min(w.N, n * 4)
+        dt = run(n)
+    reps, total = 1, dt
+    while total < budget_s:
+        total += run(n)
+        reps += 1
+    return {
+        "value": n * reps / total,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle backward, first {n} of {w.N} tokens of {w.name} as one "
+                  f"batch, {reps} passes, {total:.1f} s",
     }
 
 
@@ -152,6 +243,8 @@ def main():
     cache.add_argument("--warm", action="store_const", const="warm", dest="cache",
                        help="back-to-back steps with warm caches (default otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -165,7 +258,7 @@ def main():
     import torch
 
     import top_moe_layer_amd as tm
-    from workloads import get, make_inputs
+    from workloads import get, make_inputs, make_upstream
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -180,7 +273,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 5}), flush=True)
         return
     w = get(args.workload)
-    log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype}")
+    bwd = args.which == "bwd"
+    log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype} {args.which}")
     decode_like = w.kind == "moe" and w.N * w.k <= 256
     # Decode-sized steps stream their weights; with warm caches part of them
     # would come from the 256 MB Infinity Cache, so they are timed cold.
@@ -198,8 +292,30 @@ def main():
     tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
     stream = torch.cuda.current_stream(dev)
+    dy_host = make_upstream(inputs) if bwd else None
 
-    if w.kind == "dense":
+    if bwd:
+        dyd = dev_t(dy_host)
+        new = lambda shape, dt_=tdt: torch.empty(shape, dtype=dt_, device=dev)
+        if w.kind == "dense":
+            ws = torch.empty(tm.ffn_bwd_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
+            names = tm.FFN_BWD_STAGE_NAMES
+            make_events = lambda: tm.StageEvents(tm.FFN_BWD_STAGES)
+
+            def step(ev=None):
+                tm.ffn_swiglu_bwd(d["x"], d["Wg"], d["Wu"], d["Wd"], dyd, workspace=ws,
+                                  stream=stream, stage_events=ev)
+        else:
+            ws = torch.empty(tm.moe_bwd_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8,
+                             device=dev)
+            names = tm.MOE_BWD_STAGE_NAMES
+            make_events = lambda: tm.StageEvents(tm.MOE_BWD_STAGES)
+
+            def step(ev=None):
+                tm.moe_ffn_bwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], dyd, k, w.coef,
+                               norm_topk_prob=w.norm_topk_prob, workspace=ws, stream=stream,
+                               stage_events=ev)
+    elif w.kind == "dense":
         ws = torch.empty(tm.ffn_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
         y = torch.empty((N, H), dtype=tdt, device=dev)
         names = tm.FFN_STAGE_NAMES
@@ -277,7 +393,9 @@ def main():
 
     units = stage_units(w)
     touched = None
-    if w.kind == "moe":
+    if bwd:
+        units = stage_units_bwd(w)
+    elif w.kind == "moe":
         cnt = np.diff(offs.cpu().numpy())
         touched = int((cnt > 0).sum())
         units = {**units}
@@ -286,14 +404,17 @@ def main():
         units["gateup_gemm"] = (4.0 * rows * H * I, N * H * el + 2 * touched * I * H * el + rows * I * el)
         units["down_gemm"] = (2.0 * rows * H * I, rows * I * el + touched * H * I * el + N * H * el)
 
-    total_flops = w.flops()
+    total_flops = flops_bwd(w) if bwd else w.flops()
     tflops = total_flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     dom = "gateup_gemm"
+    if bwd:  # the longest GEMM stage
+        dom = max(("gu_gemm", "dh_gemm", "dx_gemm", "dwgu_gemm", "dwd_gemm"),
+                  key=lambda n: stages_ms[n])
     dom_ms = stages_ms[dom]
     dom_pct = pct(per_step[:, names.index(dom)])
     dflops, dbytes = units[dom]
-    if decode_like:
+    if decode_like and not bwd:
         achieved = dbytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -307,7 +428,7 @@ def main():
                 "algorithmic_flops": dflops, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(N / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -327,11 +448,13 @@ def main():
         "stages_ms": stages_ms,
         "kernel_ms_per_step": pct(per_step.sum(axis=1)),
         "experts_touched": touched,
+        "pass": args.which,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(w, inputs)
+        result["cpu_baseline"] = (cpu_baseline_bwd(w, inputs, dy_host) if bwd
+                                  else cpu_baseline(w, inputs))
     print(json.dumps(result), flush=True)
 
 

@@ -80,14 +80,15 @@ extern "C" {
 #define TOPMOE_MOE_STAGES 5  /* 0 router, 1 expert offsets + aux + token scatter,
                                 2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
                                 + alpha, 4 combine of the k slots (empty when k == 1)   */
-#define TOPMOE_FFN_BWD_STAGES 6  /* 0 weight transposes, 1 x / dy transposes,
-                                    2 fused g, u, dh GEMM, 3 dx GEMM, 4 dWg + dWu GEMM,
-                                    5 dWd GEMM                                          */
-#define TOPMOE_MOE_BWD_STAGES 11 /* 0 router, 1 offsets + scatter (the forward's routing),
+#define TOPMOE_FFN_BWD_STAGES 7  /* 0 weight transposes, 1 x / dy transposes,
+                                    2 g, u GEMM (recomputed), 3 dh GEMM + dg, du,
+                                    4 dx GEMM, 5 dWg + dWu GEMM, 6 dWd GEMM             */
+#define TOPMOE_MOE_BWD_STAGES 12 /* 0 router, 1 offsets + scatter (the forward's routing),
                                     2 weight transposes, 3 grouped x / alpha*dy
-                                    transposes, 4 grouped fused g, u, dh GEMM + d alpha,
-                                    5 grouped dx GEMM, 6 router backward, 7 dx combine,
-                                    8 dW_router, 9 grouped dWg + dWu, 10 grouped dWd   */
+                                    transposes, 4 grouped g, u GEMM (recomputed),
+                                    5 grouped dh GEMM + dg, du, d alpha, 6 grouped dx GEMM,
+                                    7 router backward, 8 dx combine, 9 dW_router,
+                                    10 grouped dWg + dWu, 11 grouped dWd               */
 
 /* ---- moe_ffn_fwd flags -------------------------------------------------- */
 /* The config's norm_topk_prob = False (lesson 13, walkthrough steps 1 and 5;
@@ -169,12 +170,14 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
  * Gradient outputs are overwritten, not accumulated; weight gradients have
  * the weights' dtype and layout, dW_router is float32.  The gradient with
  * respect to the residual stream of the forward is dy itself (nothing to
- * compute).  In bf16, [dg | du], dg, du, h and alpha*dy are rounded to bf16
- * before the GEMMs that consume them; all accumulation is fp32. */
+ * compute).  In bf16, the recomputed g and u, [dg | du], dg, du, h and
+ * alpha*dy are rounded to bf16 before the arithmetic or GEMMs that consume
+ * them; all accumulation is fp32. */
 
 /* Workspace needed by ffn_swiglu_bwd: transposed weights [H, 2I] and [I, H],
- * transposed x and dy [H, round64(N)], [dg | du] [N, 2I] and dg^T, du^T, h^T
- * [I, round64(N)] (dtype-sized elements).  Returns 0 for invalid shapes. */
+ * transposed x and dy [H, round64(N)], the pairs (g, u) [N, I], [dg | du]
+ * [N, 2I] and dg^T, du^T, h^T [I, round64(N)] (dtype-sized elements).
+ * Returns 0 for invalid shapes. */
 size_t ffn_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype);
 
 /* Dense SwiGLU FFN backward.  With g = x Wg^T, u = x Wu^T, h = SiLU(g) * u,

@@ -105,7 +105,11 @@ def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
 
 
 TOL_GRAD = {"fp32": 1e-5, "bf16": 2e-2}   # relative L2 of each gradient (per token / per matrix)
-TOL_DWR = 1e-4                           # router-weight gradient, relative L2 per expert row
+# router-weight gradient, relative L2 per expert row: fp32 sums over up to 2^14
+# tokens (~sqrt(N) * 2^-24) times the softmax backward's cancellation; in bf16
+# the recomputed g and u are stored in bf16, so d alpha (and dr) carry
+# bf16-level error like every other bf16 gradient
+TOL_DWR = {"fp32": 1e-4, "bf16": 2e-2}
 
 
 def arr_to_dev(a, dt: str, dev):

@@ -6,7 +6,8 @@ notes): dx within a max per-token relative L2 error of 1e-5 (fp32) or 2e-2
 (bf16 operands, fp32 accumulation); each weight gradient within the same bound
 as a relative Frobenius error per expert (an expert with a zero reference
 gradient must come out exactly zero); the router-weight gradient (fp32 in both
-dtypes) within 1e-4 per expert row.  Inputs keep the top-k margin of 1e-3, so
+dtypes) within 1e-4 per expert row on the fp32 path and 2e-2 on the bf16 path
+(where the recomputed g, u feeding d alpha are bf16).  Inputs keep the top-k margin of 1e-3, so
 the routing the backward recomputes is the oracle's.
 """
 import numpy as np
@@ -44,7 +45,7 @@ def check_weight_grads(g, ref, dt, names=("dWg", "dWu", "dWd")):
         assert err <= TOL_GRAD[dt], (n, err)
 
 
-def check_dwr(got, ref):
+def check_dwr(got, ref, dt):
     got = got.detach().double().cpu().numpy()
     for e in range(ref.shape[0]):
         d = np.linalg.norm(ref[e])
@@ -52,7 +53,7 @@ def check_dwr(got, ref):
             assert np.abs(got[e]).max() <= 1e-9, (e, np.abs(got[e]).max())
         else:
             err = np.linalg.norm(got[e] - ref[e]) / d
-            assert err <= TOL_DWR, (e, err)
+            assert err <= TOL_DWR[dt], (e, err)
 
 
 # ------------------------------------------------------------------ dense
@@ -118,7 +119,7 @@ def test_moe_bwd(env, N, H, I, E, k, coef, norm, dt):
     err = rel_l2_per_token(y_to_f64(g.dx), ref["dx"])
     assert err <= TOL_GRAD[dt], ("dx", err)
     check_weight_grads(g, ref, dt)
-    check_dwr(g.dWr, ref["dWr"])
+    check_dwr(g.dWr, ref["dWr"], dt)
 
 
 def test_moe_bwd_empty_experts(env):
@@ -142,7 +143,7 @@ def test_moe_bwd_empty_experts(env):
     err = rel_l2_per_token(y_to_f64(g.dx), ref["dx"])
     assert err <= TOL_GRAD["bf16"], ("dx", err)
     check_weight_grads(g, ref, "bf16")
-    check_dwr(g.dWr, ref["dWr"])
+    check_dwr(g.dWr, ref["dWr"], "bf16")
 
 
 def test_moe_bwd_empty_batch(env):

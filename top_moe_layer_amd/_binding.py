@@ -25,14 +25,14 @@ DTYPE_BF16 = 1
 MOE_RAW_TOPK_WEIGHTS = 1
 FFN_STAGES = 2
 MOE_STAGES = 5
-FFN_BWD_STAGES = 6
-MOE_BWD_STAGES = 11
+FFN_BWD_STAGES = 7
+MOE_BWD_STAGES = 12
 
 FFN_STAGE_NAMES = ["gateup_gemm", "down_gemm"]
 MOE_STAGE_NAMES = ["router", "permute", "gateup_gemm", "down_gemm", "combine"]
-FFN_BWD_STAGE_NAMES = ["transpose_w", "transpose_act", "bwd_h_gemm", "dx_gemm", "dwgu_gemm",
-                       "dwd_gemm"]
-MOE_BWD_STAGE_NAMES = ["router", "permute", "transpose_w", "transpose_act", "bwd_h_gemm",
+FFN_BWD_STAGE_NAMES = ["transpose_w", "transpose_act", "gu_gemm", "dh_gemm", "dx_gemm",
+                       "dwgu_gemm", "dwd_gemm"]
+MOE_BWD_STAGE_NAMES = ["router", "permute", "transpose_w", "transpose_act", "gu_gemm", "dh_gemm",
                        "dx_gemm", "router_bwd", "dx_combine", "dwr", "dwgu_gemm", "dwd_gemm"]
 
 # Every function include/topmoe.h declares, with its ctypes signature.

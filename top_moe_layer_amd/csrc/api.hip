@@ -236,6 +236,7 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   void* wdT = ws + pl.off_wdT;
   void* xT = ws + pl.off_xT;
   void* dyT = ws + pl.off_dyT;
+  void* gu = ws + pl.off_gu;
   void* dgdu = ws + pl.off_dgdu;
   void* dgT = ws + pl.off_dgT;
   void* duT = ws + pl.off_duT;
@@ -265,43 +266,51 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
     TOPMOE_TRY(launch_gather_transpose(dtype, gj, pl.ldk, l1));
   }
   TOPMOE_TRY(st.close(l1));
-  // 2: g, u, dh in one GEMM: [dg | du], dg^T, du^T, h^T
+  // 2: g, u recomputed: the pairs (g, u) and h^T
   const Launch l2 = st.at(2);
   if (N > 0) {
     GemmParams g{};
-    g.A = x; g.A1 = dy; g.B0 = Wg; g.B1 = Wu; g.B2 = wdT;
-    g.out = dgdu; g.out1 = dgT; g.out2 = duT; g.out3 = hT;
+    g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = gu; g.out1 = hT;
     g.M = N; g.ldk = pl.ldk; g.E = 1; g.k = 1; g.Nout = iI; g.K = iH;
-    TOPMOE_TRY(launch_gemm(KIND_BWD_H, dtype, pl.bwdh, g, (N + pl.bwdh.bm - 1) / pl.bwdh.bm, l2));
+    TOPMOE_TRY(launch_gemm(KIND_BWD_GU, dtype, pl.gu, g, (N + pl.gu.bm - 1) / pl.gu.bm, l2));
   }
   TOPMOE_TRY(st.close(l2));
-  // 3: dx = [dg | du] [Wg | Wu]
+  // 3: dh = dy Wd, then [dg | du], dg^T, du^T
   const Launch l3 = st.at(3);
+  if (N > 0) {
+    GemmParams g{};
+    g.A = dy; g.B0 = wdT; g.gu = gu; g.out = dgdu; g.out1 = dgT; g.out2 = duT;
+    g.M = N; g.ldk = pl.ldk; g.E = 1; g.k = 1; g.Nout = iI; g.K = iH;
+    TOPMOE_TRY(launch_gemm(KIND_BWD_DH, dtype, pl.dh, g, (N + pl.dh.bm - 1) / pl.dh.bm, l3));
+  }
+  TOPMOE_TRY(st.close(l3));
+  // 4: dx = [dg | du] [Wg | Wu]
+  const Launch l4 = st.at(4);
   if (N > 0) {
     GemmParams g{};
     g.A = dgdu; g.B0 = wgT; g.out = dx;
     g.M = N; g.E = 1; g.k = 1; g.Nout = iH; g.K = 2 * iI;
-    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.dx, g, (N + pl.dx.bm - 1) / pl.dx.bm, l3));
+    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.dx, g, (N + pl.dx.bm - 1) / pl.dx.bm, l4));
   }
-  TOPMOE_TRY(st.close(l3));
-  // 4: dWg = dg^T x, dWu = du^T x (contraction over tokens)
-  const Launch l4 = st.at(4);
+  TOPMOE_TRY(st.close(l4));
+  // 5: dWg = dg^T x, dWu = du^T x (contraction over tokens)
+  const Launch l5 = st.at(5);
   {
     GemmParams g{};
     g.A = dgT; g.A1 = duT; g.B0 = xT; g.out = dWg; g.out1 = dWu;
     g.M = I; g.ldk = pl.ldk; g.kcount = N; g.E = 1; g.k = 1; g.Nout = iH; g.K = int(pl.ldk);
-    TOPMOE_TRY(launch_gemm(KIND_WGRAD2, dtype, pl.wgu, g, 0, l4));
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD2, dtype, pl.wgu, g, 0, l5));
   }
-  TOPMOE_TRY(st.close(l4));
-  // 5: dWd = dy^T h
-  const Launch l5 = st.at(5);
+  TOPMOE_TRY(st.close(l5));
+  // 6: dWd = dy^T h
+  const Launch l6 = st.at(6);
   {
     GemmParams g{};
     g.A = dyT; g.B0 = hT; g.out = dWd;
     g.M = H; g.ldk = pl.ldk; g.kcount = N; g.E = 1; g.k = 1; g.Nout = iI; g.K = int(pl.ldk);
-    TOPMOE_TRY(launch_gemm(KIND_WGRAD1, dtype, pl.wd, g, 0, l5));
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD1, dtype, pl.wd, g, 0, l6));
   }
-  TOPMOE_TRY(st.close(l5));
+  TOPMOE_TRY(st.close(l6));
   return TOPMOE_OK;
 }
 
@@ -341,6 +350,7 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   void* wdT = ws + pl.off_wdT;
   void* xT = ws + pl.off_xT;
   void* dyT = ws + pl.off_dyT;
+  void* gu = ws + pl.off_gu;
   void* dgdu = ws + pl.off_dgdu;
   void* dgT = ws + pl.off_dgT;
   void* duT = ws + pl.off_duT;
@@ -389,65 +399,75 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
     TOPMOE_TRY(launch_gather_transpose(dtype, gj, pl.ldk, l3));
   }
   TOPMOE_TRY(st.close(l3));
-  // 4: per expert g, u, dh = alpha dy Wd: [dg | du], dg^T, du^T, h^T, d alpha partials
+  // 4: per expert g, u recomputed: the pairs (g, u) and h^T
   const Launch l4 = st.at(4);
   if (N > 0) {
     GemmParams g{};
-    g.A = x; g.A1 = dy; g.B0 = Wg; g.B1 = Wu; g.B2 = wdT;
-    g.out = dgdu; g.out1 = dgT; g.out2 = duT; g.out3 = hT; g.dalpha_part = dal;
-    g.entries = sorted_entry; g.offsets = offsets; g.alpha = alpha_g;
+    g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = gu; g.out1 = hT;
+    g.entries = sorted_entry; g.offsets = offsets;
     g.M = rows; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iI; g.K = iH;
-    TOPMOE_TRY(launch_gemm(KIND_BWD_H, dtype, pl.bwdh, g, pl.bwdh_mtiles, l4));
+    TOPMOE_TRY(launch_gemm(KIND_BWD_GU, dtype, pl.gu, g, pl.gu_mtiles, l4));
   }
   TOPMOE_TRY(st.close(l4));
-  // 5: per entry dx term [dg | du] [Wg_e | Wu_e] into its slot
+  // 5: per expert dh = alpha dy Wd: [dg | du], dg^T, du^T, d alpha partials
   const Launch l5 = st.at(5);
+  if (N > 0) {
+    GemmParams g{};
+    g.A = dy; g.B0 = wdT; g.gu = gu;
+    g.out = dgdu; g.out1 = dgT; g.out2 = duT; g.dalpha_part = dal;
+    g.entries = sorted_entry; g.offsets = offsets; g.alpha = alpha_g;
+    g.M = rows; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iI; g.K = iH;
+    TOPMOE_TRY(launch_gemm(KIND_BWD_DH, dtype, pl.dh, g, pl.dh_mtiles, l5));
+  }
+  TOPMOE_TRY(st.close(l5));
+  // 6: per entry dx term [dg | du] [Wg_e | Wu_e] into its slot
+  const Launch l6 = st.at(6);
   if (N > 0) {
     GemmParams g{};
     g.A = dgdu; g.B0 = wgT; g.out = slots;
     g.entries = sorted_entry; g.offsets = offsets; g.alpha = nullptr;
     g.M = rows; g.E = E; g.k = k; g.Nout = iH; g.K = 2 * iI;
-    TOPMOE_TRY(launch_gemm(KIND_DOWN_SLOTS, dtype, pl.dx, g, pl.dx_mtiles, l5));
+    TOPMOE_TRY(launch_gemm(KIND_DOWN_SLOTS, dtype, pl.dx, g, pl.dx_mtiles, l6));
   }
-  TOPMOE_TRY(st.close(l5));
-  // 6: router backward: d alpha -> dp (renormalisation, aux) -> softmax -> dr
-  const Launch l6 = st.at(6);
+  TOPMOE_TRY(st.close(l6));
+  // 7: router backward: d alpha -> dp (renormalisation, aux) -> softmax -> dr
+  const Launch l7 = st.at(7);
   {
     const double scale = N > 0 ? double(aux_grad) * double(aux_coef) * double(E) /
                                      (double(N) * double(N))
                                : 0.0;
     TOPMOE_TRY(launch_router_bwd(probs, topk_idx, dal, pl.nt_h, offsets, N, E, k, renorm,
-                                 float(scale), dr, l6));
+                                 float(scale), dr, l7));
   }
-  TOPMOE_TRY(st.close(l6));
-  // 7: dx = sum of the slots (ascending expert) + W_r^T dr
-  const Launch l7 = st.at(7);
-  TOPMOE_TRY(launch_combine_bwd(slots, topk_idx, dr, Wr, N, iH, E, k, dtype, dx, l7));
   TOPMOE_TRY(st.close(l7));
-  // 8: dW_r = dr^T x
+  // 8: dx = sum of the slots (ascending expert) + W_r^T dr
   const Launch l8 = st.at(8);
-  TOPMOE_TRY(launch_dwr(x, dr, N, iH, E, dtype, dwr_part, dWr, l8));
+  TOPMOE_TRY(launch_combine_bwd(slots, topk_idx, dr, Wr, N, iH, E, k, dtype, dx, l8));
   TOPMOE_TRY(st.close(l8));
-  // 9: dWg_e = dg_e^T x_e, dWu_e = du_e^T x_e over each expert's rows
+  // 9: dW_r = dr^T x
   const Launch l9 = st.at(9);
+  TOPMOE_TRY(launch_dwr(x, dr, N, iH, E, dtype, dwr_part, dWr, l9));
+  TOPMOE_TRY(st.close(l9));
+  // 10: dWg_e = dg_e^T x_e, dWu_e = du_e^T x_e over each expert's rows
+  const Launch l10 = st.at(10);
   {
     GemmParams g{};
     g.A = dgT; g.A1 = duT; g.B0 = xT; g.out = dWg; g.out1 = dWu;
     g.offsets = offsets;
     g.M = I; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iH; g.K = int(pl.ldk);
-    TOPMOE_TRY(launch_gemm(KIND_WGRAD2, dtype, pl.wgu, g, 0, l9));
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD2, dtype, pl.wgu, g, 0, l10));
   }
-  TOPMOE_TRY(st.close(l9));
-  // 10: dWd_e = (alpha dy)_e^T h_e
-  const Launch l10 = st.at(10);
+  TOPMOE_TRY(st.close(l10));
+  // 11: dWd_e = (alpha dy)_e^T h_e
+  const Launch l11 = st.at(11);
   {
     GemmParams g{};
     g.A = dyT; g.B0 = hT; g.out = dWd;
     g.offsets = offsets;
     g.M = H; g.ldk = pl.ldk; g.E = E; g.k = k; g.Nout = iI; g.K = int(pl.ldk);
-    TOPMOE_TRY(launch_gemm(KIND_WGRAD1, dtype, pl.wd, g, 0, l10));
+    TOPMOE_TRY(launch_gemm(KIND_WGRAD1, dtype, pl.wd, g, 0, l11));
   }
-  TOPMOE_TRY(st.close(l10));
+  TOPMOE_TRY(st.close(l11));
   return TOPMOE_OK;
 }
 

@@ -283,64 +283,127 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 }
 
 // ------------------------------------------------------- router weight grad
-// dW_r[e][h] = sum_t dr[t][e] x[t][h]: block (column block of 512, token
-// chunk of kDwrChunk) writes per-chunk partials; a second kernel sums the
-// chunks in order.  Lane: 8 consecutive columns; experts 8 at a time.
+// dW_r[e][h] = sum_t dr[t][e] x[t][h], split over token chunks of kDwrChunk
+// (256): block (512-column block, chunk) has four wavefronts of 64 tokens
+// each; a lane owns 8 consecutive columns and 8 experts at a time.  The four
+// wavefronts' sums meet in LDS in a fixed order and the block writes one
+// partial per chunk; a second kernel sums the chunks (again in a fixed order).
+constexpr int kDwrWaves = 4;
+static_assert(kDwrChunk == 64 * kDwrWaves, "a wavefront per 64 tokens of a chunk");
+
 template <typename T>
-__global__ __launch_bounds__(64) void dwr_partial_kernel(const T* __restrict__ x,
-                                                         const float* __restrict__ dr,
-                                                         int64_t N, int H, int E,
-                                                         float* __restrict__ part) {
-  __shared__ float s_dr[kDwrChunk * 64];
-  const int lane = int(threadIdx.x);
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    ld16<T>(p, v);
+  } else {
+    float a[4], b[4];
+    ld16<T>(p, a);
+    ld16<T>(p + 4, b);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { v[w] = a[w]; v[w + 4] = b[w]; }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ x,
+                                                          const float* __restrict__ dr,
+                                                          int64_t N, int H, int E,
+                                                          float* __restrict__ part) {
+  __shared__ float s_dr[kDwrChunk * 8];                 // this expert chunk's dr rows
+  __shared__ float s_acc[kDwrWaves - 1][8][8 * 64 + 4];  // waves 1..3: 8 experts x 512 columns
+  const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
   const int h = int(blockIdx.x) * 512 + lane * 8;
+  const bool hok = h < H;
   const int64_t t0 = int64_t(blockIdx.y) * kDwrChunk;
   const int nt = int(N - t0 < kDwrChunk ? N - t0 : kDwrChunk);
-  for (int i = lane; i < nt * E; i += 64) s_dr[i] = dr[t0 * E + i];
-  __syncthreads();
-  if (h >= H) return;
+  const int tw0 = wave * 64;                                  // this wave's tokens in the chunk
+  const int ntw = nt - tw0 < 0 ? 0 : (nt - tw0 < 64 ? nt - tw0 : 64);
   for (int e0 = 0; e0 < E; e0 += 8) {
+    __syncthreads();  // the previous expert chunk's LDS reads are done
+    for (int i = tid; i < kDwrChunk * 8; i += 256) {
+      const int t = i >> 3, e = e0 + (i & 7);
+      s_dr[i] = (t < nt && e < E) ? dr[(t0 + t) * E + e] : 0.f;
+    }
+    __syncthreads();
     float acc[8][8];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
-    for (int i = 0; i < nt; ++i) {
-      float xv[8];
-      if constexpr (sizeof(T) == 2) {
-        ld16<T>(x + (t0 + i) * H + h, xv);
-      } else {
-        float a4[4], b4[4];
-        ld16<T>(x + (t0 + i) * H + h, a4);
-        ld16<T>(x + (t0 + i) * H + h + 4, b4);
+    if (hok) {
+      int i = 0;
+      for (; i + 4 <= ntw; i += 4) {  // four rows in flight
+        float xv[4][8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) { xv[w] = a4[w]; xv[w + 4] = b4[w]; }
+        for (int r = 0; r < 4; ++r) load8<T>(x + (t0 + tw0 + i + r) * H + h, xv[r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int a = 0; a < 8; ++a) {
+            const float d = s_dr[(tw0 + i + r) * 8 + a];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(d, xv[r][b], acc[a][b]);
+          }
       }
+      for (; i < ntw; ++i) {
+        float xv[8];
+        load8<T>(x + (t0 + tw0 + i) * H + h, xv);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const float d = (e0 + a < E) ? s_dr[i * E + e0 + a] : 0.f;
+        for (int a = 0; a < 8; ++a) {
+          const float d = s_dr[(tw0 + i) * 8 + a];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(d, xv[b], acc[a][b]);
+          for (int b = 0; b < 8; ++b) acc[a][b] = fmaf(d, xv[b], acc[a][b]);
+        }
       }
     }
+    if (wave > 0) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      if (e0 + a >= E) break;
-      float* o = part + (int64_t(blockIdx.y) * E + e0 + a) * H + h;
-      *reinterpret_cast<f32x4*>(o) = f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
-      *reinterpret_cast<f32x4*>(o + 4) = f32x4{acc[a][4], acc[a][5], acc[a][6], acc[a][7]};
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) s_acc[wave - 1][a][lane * 8 + b] = acc[a][b];
+    }
+    __syncthreads();
+    if (wave == 0 && hok) {
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        if (e0 + a >= E) break;
+        float v[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          float sum = acc[a][b];
+#pragma unroll
+          for (int w = 0; w < kDwrWaves - 1; ++w) sum += s_acc[w][a][lane * 8 + b];
+          v[b] = sum;
+        }
+        float* o = part + (int64_t(blockIdx.y) * E + e0 + a) * H + h;
+        *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
     }
   }
 }
 
+// dW_r[i] = sum over chunks c (ascending) of part[c][i]: 64 outputs per block,
+// four threads per output take every fourth chunk, then meet in LDS in order.
 __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict__ part,
                                                          int nchunk, int64_t EH,
                                                          float* __restrict__ dWr) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= EH) return;
+  __shared__ float s_sum[4][64];
+  const int tid = int(threadIdx.x), o = tid & 63, q = tid >> 6;
+  const int64_t i = int64_t(blockIdx.x) * 64 + o;
   float s = 0.f;
-  for (int c = 0; c < nchunk; ++c) s += part[int64_t(c) * EH + i];
-  dWr[i] = s;
+  if (i < EH) {
+    int c = q;
+    for (; c + 12 < nchunk; c += 16) {  // four loads in flight
+      const float a = part[int64_t(c) * EH + i], b = part[int64_t(c + 4) * EH + i];
+      const float d = part[int64_t(c + 8) * EH + i], e = part[int64_t(c + 12) * EH + i];
+      s += a; s += b; s += d; s += e;
+    }
+    for (; c < nchunk; c += 4) s += part[int64_t(c) * EH + i];
+  }
+  s_sum[q][o] = s;
+  __syncthreads();
+  if (q == 0 && i < EH) dWr[i] = (s_sum[0][o] + s_sum[1][o]) + (s_sum[2][o] + s_sum[3][o]);
 }
 
 template <int EP>
@@ -418,16 +481,16 @@ hipError_t launch_dwr(const void* x, const float* dr, int64_t N, int H, int E, i
     const dim3 grid(unsigned((H + 511) / 512), unsigned(nchunk));
     const hipError_t err =
         dtype == TOPMOE_DTYPE_FP32
-            ? launch_kernel(dwr_partial_kernel<float>, grid, dim3(64), 0, first,
+            ? launch_kernel(dwr_partial_kernel<float>, grid, dim3(256), 0, first,
                             static_cast<const float*>(x), dr, N, H, E, part)
-            : launch_kernel(dwr_partial_kernel<bf16_t>, grid, dim3(64), 0, first,
+            : launch_kernel(dwr_partial_kernel<bf16_t>, grid, dim3(256), 0, first,
                             static_cast<const bf16_t*>(x), dr, N, H, E, part);
     if (err != hipSuccess) return err;
   } else {
     second.start = s.start;
   }
   const int64_t EH = int64_t(E) * H;
-  const hipError_t err = launch_kernel(dwr_reduce_kernel, dim3(unsigned((EH + 255) / 256)),
+  const hipError_t err = launch_kernel(dwr_reduce_kernel, dim3(unsigned((EH + 63) / 64)),
                                        dim3(256), 0, second, part, nchunk, EH, dWr);
   s.launched = true;
   return err;

@@ -51,6 +51,101 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float (&v)[4]) {
   *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
 }
 
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float (&v)[4]);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float (&v)[4]) {
+  const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+template <>
+__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&v)[4]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 q = *reinterpret_cast<const u32x2*>(p);
+  v[0] = __uint_as_float(q.x << 16);
+  v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16);
+  v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+
+// 4 x 4 transpose inside each quad of lanes (q = lane & 3) with two DPP
+// quad permutations: on entry lane q holds rows 0..3 of column q, on exit
+// row q of columns 0..3.  Step m (m = 1, 2) pairs index r (bit m clear) with
+// r ^ m and lane q with q ^ m: the lane whose bit m is clear keeps b[r] and
+// sends b[r ^ m], its partner keeps b[r ^ m] and sends b[r]; each puts what it
+// receives where its sent value was.  An element (row, col) thus moves only
+// when its row and column bits differ, flipping both, which after both steps
+// puts it at lane row, index col.  Every lane of the quad must execute it.
+template <int M, int CTRL>
+__device__ __forceinline__ void quad_exchange(float& lo, float& hi, bool upper) {
+  const float send = upper ? lo : hi;
+  const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xF, 0xF, false));
+  if (upper) lo = recv;
+  else hi = recv;
+}
+__device__ __forceinline__ void quad_transpose(float (&b)[4], int q) {
+  const bool u1 = (q & 1) != 0, u2 = (q & 2) != 0;
+  quad_exchange<1, 0xB1>(b[0], b[1], u1);  // lane ^ 1
+  quad_exchange<1, 0xB1>(b[2], b[3], u1);
+  quad_exchange<2, 0x4E>(b[0], b[2], u2);  // lane ^ 2
+  quad_exchange<2, 0x4E>(b[1], b[3], u2);
+}
+
+// Two values of the dtype stored together (the (g, u) pairs of the backward):
+// one 4-byte word for bf16 (first value in the low half), 8 bytes for fp32.
+template <typename T>
+__device__ __forceinline__ void store_pair(void* base, int64_t i, float a, float b);
+template <>
+__device__ __forceinline__ void store_pair<bf16_t>(void* base, int64_t i, float a, float b) {
+  static_cast<uint32_t*>(base)[i] = uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16);
+}
+template <>
+__device__ __forceinline__ void store_pair<float>(void* base, int64_t i, float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  static_cast<f32x2*>(base)[i] = f32x2{a, b};
+}
+// Pairs i .. i+3 (first values a[], second values b[]) in one or two 16-byte stores.
+template <typename T>
+__device__ __forceinline__ void store_pairs4(void* base, int64_t i, const float (&a)[4],
+                                             const float (&b)[4]);
+template <>
+__device__ __forceinline__ void store_pairs4<bf16_t>(void* base, int64_t i, const float (&a)[4],
+                                                     const float (&b)[4]) {
+  u32x4 q;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    q[w] = uint32_t(f32_to_bf16(a[w])) | (uint32_t(f32_to_bf16(b[w])) << 16);
+  *reinterpret_cast<u32x4*>(static_cast<uint32_t*>(base) + i) = q;
+}
+template <>
+__device__ __forceinline__ void store_pairs4<float>(void* base, int64_t i, const float (&a)[4],
+                                                    const float (&b)[4]) {
+  f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(base) + 2 * i);
+  o[0] = f32x4{a[0], b[0], a[1], b[1]};
+  o[1] = f32x4{a[2], b[2], a[3], b[3]};
+}
+// The word holding one pair, for loads kept in registers before use.
+template <typename T>
+struct PairWord;
+template <>
+struct PairWord<bf16_t> {
+  typedef uint32_t type;
+  __device__ static __forceinline__ type zero() { return 0u; }
+  __device__ static __forceinline__ void unpack(type v, float& a, float& b) {
+    a = __uint_as_float(v << 16);
+    b = __uint_as_float(v & 0xffff0000u);
+  }
+};
+template <>
+struct PairWord<float> {
+  typedef float type __attribute__((ext_vector_type(2)));
+  __device__ static __forceinline__ type zero() { return type{0.f, 0.f}; }
+  __device__ static __forceinline__ void unpack(type v, float& a, float& b) {
+    a = v.x;
+    b = v.y;
+  }
+};
+
 // SiLU(g) * u = g * u / (1 + e^-g) (SwiGLU, lesson 13, section 1.2), as
 // g * u / (1 + 2^(-g log2 e)) with v_exp_f32 and v_rcp_f32 (about 1 ulp each).
 __device__ __forceinline__ float silu_mul(float g, float u) {

@@ -140,11 +140,18 @@ struct KindTraits<KIND_GATEUP> {  // x against Wg and Wu
   __host__ __device__ static constexpr int pb(int q) { return q; }
 };
 template <>
-struct KindTraits<KIND_BWD_H> {  // x against Wg and Wu, dy against Wd^T
-  static constexpr int NA = 2, NB = 3, NP = 3;
-  static constexpr bool META = true, KGROUP = false, GATHER = true;
-  __host__ __device__ static constexpr int pa(int q) { return q == 2 ? 1 : 0; }
+struct KindTraits<KIND_BWD_GU> {  // x against Wg and Wu (recomputed for the backward)
+  static constexpr int NA = 1, NB = 2, NP = 2;
+  static constexpr bool META = false, KGROUP = false, GATHER = true;
+  __host__ __device__ static constexpr int pa(int) { return 0; }
   __host__ __device__ static constexpr int pb(int q) { return q; }
+};
+template <>
+struct KindTraits<KIND_BWD_DH> {  // dy against Wd^T
+  static constexpr int NA = 1, NB = 1, NP = 1;
+  static constexpr bool META = true, KGROUP = false, GATHER = true;
+  __host__ __device__ static constexpr int pa(int) { return 0; }
+  __host__ __device__ static constexpr int pb(int) { return 0; }
 };
 template <>
 struct KindTraits<KIND_WGRAD2> {  // dg^T and du^T against x^T
@@ -161,43 +168,13 @@ struct KindTraits<KIND_WGRAD1> {  // (alpha dy)^T against h^T
   __host__ __device__ static constexpr int pb(int) { return 0; }
 };
 
-// Sum of each of V per-lane values over the 32 lanes of a half-wavefront
-// (the MFMA column lanes fr = 0..31): halving exchanges (lane bit set keeps
-// the upper half), then plain butterflies once one value is left.  Lane fr
-// ends with cnt = max(V / 32, 1) sums, for value indices
-// (fr >> (5 - steps)) * cnt + w, steps = min(5, log2 V).
-template <int V>
-struct HalfWaveTransposeSum {
-  static constexpr int steps = V >= 32 ? 5 : (V == 16 ? 4 : V == 8 ? 3 : V == 4 ? 2 : V == 2 ? 1 : 0);
-  static constexpr int cnt = V >> steps;
-  template <int C, int MASK>
-  __device__ static __forceinline__ void halve(float* v, int fr) {
-    if constexpr (C > cnt) {
-      constexpr int half = C / 2;
-      const bool upper = (fr & MASK) != 0;
-#pragma unroll
-      for (int n = 0; n < half; ++n) {
-        const float send = upper ? v[n] : v[n + half];
-        const float keep = upper ? v[n + half] : v[n];
-        v[n] = keep + __shfl_xor(send, MASK, 64);
-      }
-      halve<half, MASK / 2>(v, fr);
-    } else if constexpr (MASK >= 1) {
-#pragma unroll
-      for (int n = 0; n < C; ++n) v[n] += __shfl_xor(v[n], MASK, 64);
-      halve<C, MASK / 2>(v, fr);
-    }
-  }
-  __device__ static __forceinline__ void run(float* v, int fr) { halve<V, 16>(v, fr); }
-};
-
 template <typename T, int BM, int BN, int WM, int WN, int RB, int S, int KIND>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   using KT_ = KindTraits<KIND>;
   constexpr int NA = KT_::NA, NB = KT_::NB, NP = KT_::NP;
   constexpr bool META = KT_::META;      // per-row entry / alpha in the epilogue
   constexpr bool KGROUP = KT_::KGROUP;  // groups along K (weight gradients)
-  constexpr bool PAD = KGROUP || KIND == KIND_BWD_H;  // padded group columns
+  constexpr bool PAD = KGROUP || KIND == KIND_BWD_GU || KIND == KIND_BWD_DH;  // padded group columns
   constexpr int NW = WM * WN;                // wavefronts: WM along rows x WN along columns
   constexpr int NTHR = 64 * NW;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -216,6 +193,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   static_assert((R / RPI) % NW == 0 && LPW >= 1, "slice rows must split evenly over wavefronts");
   static_assert(BM % RPI == 0 && BN % RPI == 0, "a load stays in one operand");
   static_assert(S >= 2 && S * STAGE <= 156 * 1024, "LDS ring exceeds 156 KB");
+  static_assert(BM % (16 / int(sizeof(T))) == 0, "staged rows split into 16-byte pieces");
   static_assert((S - 1) * LPW < 64, "vmcnt range");
   static_assert(BM <= NTHR, "one thread per tile row for the epilogue metadata");
   static_assert(!PAD || BM % 64 == 0, "padded groups end inside a group's last row tile");
@@ -231,7 +209,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   __shared__ int s_poff[PAD ? 64 : 1];
   __shared__ int s_ment[META ? BM : 1];
   __shared__ float s_malpha[META ? BM : 1];
-  __shared__ float s_dal[KIND == KIND_BWD_H ? WN * BM : 1];
+  __shared__ float s_dal[KIND == KIND_BWD_DH ? WN * BM : 1];
+  // backward: a transposed output tile [BN][BM + 16 bytes] on its way out,
+  // where it fits beside the ring (else the transposed stores go direct)
+  constexpr int LDST = BM + 16 / int(sizeof(T));
+  constexpr bool STAGE_T = (KIND == KIND_BWD_GU || KIND == KIND_BWD_DH) &&
+                           S * STAGE + BN * LDST * int(sizeof(T)) <= 156 * 1024;
+  __shared__ __attribute__((aligned(16))) T s_stage[STAGE_T ? BN * LDST : 1];
+  // Row-major outputs go out four columns per store after a transpose inside
+  // each lane quad -- except from gate/up tiles whose two accumulator sets
+  // already hold half of a wavefront's 256 registers at two wavefronts per
+  // SIMD: there the transpose's temporaries would spill, so they store
+  // element by element.
+  constexpr bool QT =
+      !((KIND == KIND_GATEUP || KIND == KIND_BWD_GU) && NP * TM * TN * 16 >= 128 && NW == 8);
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -502,6 +493,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       m_alpha = p.alpha != nullptr ? p.alpha[g] : 1.f;
     }
   };
+  // dh kind: the tile's (g, u) pairs, fetched with the metadata so that their
+  // latency hides behind the tile's last K steps (zeros outside the tile).
+  constexpr bool DHK = KIND == KIND_BWD_DH;
+  typedef typename PairWord<T>::type pair_t;
+  pair_t gu_pre[DHK ? TM : 1][DHK ? 16 : 1][DHK ? TN : 1];
+  auto load_gu = [&](const Tile& t) {
+    if constexpr (DHK) {
+      int rl = wm + 4 * fg, cl = wn + fr;
+      asm volatile("" : "+v"(rl), "+v"(cl));
+      const int rows_left = t.rows - rl;
+      const int cols_left = p.Nout - (t.n0 + cl);
+      const pair_t* src = static_cast<const pair_t*>(p.gu);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int ro = 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const bool ok = ro < rows_left && 32 * j < cols_left;
+            const int64_t e_idx = (t.row0 + rl + ro) * int64_t(p.Nout) + t.n0 + cl + 32 * j;
+            gu_pre[i][v][j] = ok ? src[e_idx] : PairWord<T>::zero();
+          }
+        }
+    }
+  };
   auto epilogue = [&](const Tile& t) {
     if constexpr (META) {
       // The previous tile's reads of s_ment / s_malpha finished before the
@@ -517,125 +534,253 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     asm volatile("" : "+v"(rl), "+v"(cl));
     const int rows_left = t.rows - rl;            // valid: 32 i + 8 (v / 4) + v % 4 < rows_left
     const int cols_left = p.Nout - (t.n0 + cl);   // valid: 32 j < cols_left
-    if constexpr (KIND == KIND_BWD_H) {
-      // Per element (column i of the intermediate, row t): g, u and
-      // dh_raw = (dy Wd)_{t,i}; with s = sigma(g), SiLU(g) = g s and
-      // SiLU'(g) = s (1 + g (1 - s)):
-      //   h = SiLU(g) u,  dh = alpha dh_raw,  dg = dh u SiLU'(g),  du = dh SiLU(g),
-      // and d alpha gets dh_raw . h summed over the row.  [dg | du] go out
-      // row-major (the dx GEMM's A operand), dg, du, h transposed into the
-      // group's padded columns (the weight-gradient GEMMs' operands), with
-      // zeros in the padding rows of the group.
+    if constexpr (KIND == KIND_BWD_GU || KIND == KIND_BWD_DH) {
+      // Backward epilogues, per element (column i of the intermediate, row t):
+      //   gu: g, u (the accumulators) go out as a pair in the dtype, row-major;
+      //       h = SiLU(g) u transposed into the group's padded columns.
+      //   dh: with g, u read back, s = sigma(g), SiLU(g) = g s and
+      //       SiLU'(g) = s (1 + g (1 - s)):  dh = alpha dh_raw,
+      //       dg = dh u SiLU'(g),  du = dh SiLU(g);  [dg | du] row-major (the dx
+      //       GEMM's A operand), dg and du transposed (the weight-gradient
+      //       GEMMs' operands); d alpha gets dh_raw . h summed over the row.
+      // Transposed outputs hold zeros in the group's padding rows.
+      constexpr bool DH = KIND == KIND_BWD_DH;
       const int lr0 = int(t.row0) - s_off[t.e];  // tile start within its group
-      const int64_t pcol = int64_t(s_poff[t.e]) + lr0 + rl;
-      const int pad_left = (((s_off[t.e + 1] - s_off[t.e]) + 63) & ~63) - lr0 - rl;
+      const int64_t pcol0 = int64_t(s_poff[t.e]) + lr0;  // its first padded column
+      const int kpad = ((s_off[t.e + 1] - s_off[t.e]) + 63) & ~63;
+      const int pad_rows = kpad - lr0 < BM ? kpad - lr0 : BM;  // tile rows inside the padded group
+      const int pad_left = pad_rows - rl;
       const int64_t ldk = p.ldk;
-      float dal[TM * 16];
+      // Transposed outputs: staged in LDS where it fits (each lane writes its
+      // four consecutive rows of a column as one 8-byte word, then the block
+      // copies whole 16-byte row pieces of consecutive tokens out); else
+      // written directly, four rows per lane.
+      auto copy_out = [&](T* dst) {
+        constexpr int V = 16 / int(sizeof(T));
+        constexpr int CPR = BM / V;
+        for (int idx = tid; idx < BN * CPR; idx += NTHR) {
+          const int c = idx / CPR, r = (idx - c * CPR) * V;
+          if (t.n0 + c < p.Nout && r < pad_rows)
+            *reinterpret_cast<u32x4*>(dst + int64_t(t.n0 + c) * ldk + pcol0 + r) =
+                *reinterpret_cast<const u32x4*>(s_stage + c * LDST + r);
+        }
+      };
+      auto put_t = [&](T* dst, int i, int vq, int j, const float (&v)[4]) {
+        const int ro0 = 32 * i + 8 * vq;
+        if constexpr (STAGE_T) {
+          store4<T>(s_stage + (cl + 32 * j) * LDST + rl + ro0, v);
+        } else {
+          if (32 * j < cols_left && ro0 < pad_left)
+            store4<T>(dst + int64_t(t.n0 + cl + 32 * j) * ldk + pcol0 + rl + ro0, v);
+        }
+      };
+      const int q4 = fr & 3;
+      const int cq = t.n0 + (cl & ~3);  // first column of the lane's quad
+      float dal[DH ? TM * 16 : 1];
+      float dus[DH ? TM : 1][DH ? 4 : 1][DH ? TN : 1][4];
 #pragma unroll
-      for (int n = 0; n < TM * 16; ++n) dal[n] = 0.f;
+      for (int n = 0; n < (DH ? TM * 16 : 1); ++n) dal[n] = 0.f;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int vq = 0; vq < 4; ++vq) {
           const int ro0 = 32 * i + 8 * vq;
+          const bool row_ok_t = ro0 + q4 < rows_left;  // the lane's row after the transpose
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const bool col_ok = 32 * j < cols_left;
-            const int col = t.n0 + cl + 32 * j;
-            float tg[4], tu[4], th[4];
+            const bool col_ok = 32 * j < cols_left;   // the same for the whole quad
+            const int64_t rowbase = (t.row0 + rl + ro0 + q4) * int64_t(p.Nout) + cq + 32 * j;
+            float t0[4];
+            if constexpr (!DH) {
+              float g4[4], u4[4];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const int v = 4 * vq + w;
-              const int ro = ro0 + w;
-              const float g = acc[0][i][j][v], u = acc[1][i][j][v], d = acc[2][i][j][v];
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
-              const float si = g * sg;
-              const float h = si * u;
-              const float dh = d * s_malpha[rl + ro];
-              const float dg = dh * u * (sg * (1.0f + g * (1.0f - sg)));
-              const float du = dh * si;
-              const bool ok = ro < rows_left && col_ok;
-              dal[16 * i + v] += col_ok ? d * h : 0.f;
-              tg[w] = ok ? dg : 0.f;
-              tu[w] = ok ? du : 0.f;
-              th[w] = ok ? h : 0.f;
-              if (ok) {
-                T* o = static_cast<T*>(p.out) + (t.row0 + rl + ro) * (2 * int64_t(p.Nout)) + col;
-                o[0] = from_f32<T>(dg);
-                o[p.Nout] = from_f32<T>(du);
+              for (int w = 0; w < 4; ++w) {
+                const int v = 4 * vq + w;
+                const bool ok = ro0 + w < rows_left && col_ok;
+                g4[w] = acc[0][i][j][v];
+                u4[w] = acc[1][i][j][v];
+                t0[w] = ok ? silu_mul(g4[w], u4[w]) : 0.f;
+              }
+              if constexpr (QT) {
+                quad_transpose(g4, q4);
+                quad_transpose(u4, q4);
+                if (row_ok_t && col_ok) store_pairs4<T>(p.out, rowbase, g4, u4);
+              } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                  if (ro0 + w < rows_left && col_ok)
+                    store_pair<T>(p.out, (t.row0 + rl + ro0 + w) * int64_t(p.Nout) + t.n0 + cl + 32 * j,
+                                  g4[w], u4[w]);
+              }
+            } else {
+              float dg4[4], du4[4];
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const int v = 4 * vq + w;
+                const bool ok = ro0 + w < rows_left && col_ok;
+                float g, u;
+                PairWord<T>::unpack(gu_pre[i][v][j], g, u);
+                const float d = acc[0][i][j][v];
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+                const float si = g * sg;
+                const float dh = d * s_malpha[rl + ro0 + w];
+                dg4[w] = dh * u * (sg * (1.0f + g * (1.0f - sg)));
+                du4[w] = dh * si;
+                dal[16 * i + v] += d * (si * u);  // zero where not ok (g = u = 0)
+                t0[w] = ok ? dg4[w] : 0.f;
+                dus[i][vq][j][w] = ok ? du4[w] : 0.f;
+              }
+              quad_transpose(dg4, q4);
+              quad_transpose(du4, q4);
+              if (row_ok_t && col_ok) {
+                T* o = static_cast<T*>(p.out) + (t.row0 + rl + ro0 + q4) * (2 * int64_t(p.Nout)) +
+                       cq + 32 * j;
+                store4<T>(o, dg4);
+                store4<T>(o + p.Nout, du4);
               }
             }
-            if (col_ok && ro0 < pad_left) {
-              const int64_t o = int64_t(col) * ldk + pcol + ro0;
-              store4<T>(static_cast<T*>(p.out1) + o, tg);
-              store4<T>(static_cast<T*>(p.out2) + o, tu);
-              store4<T>(static_cast<T*>(p.out3) + o, th);
-            }
+            put_t(static_cast<T*>(p.out1), i, vq, j, t0);
           }
         }
       }
-      if (p.dalpha_part != nullptr) {
-        // row sums over the wavefront's columns, then over the WN wavefronts
-        using Red = HalfWaveTransposeSum<TM * 16>;
-        Red::run(dal, fr);
-        constexpr int sh = 5 - Red::steps;
-        if ((fr & ((1 << sh) - 1)) == 0) {
-#pragma unroll
-          for (int w = 0; w < Red::cnt; ++w) {
-            const int n = (fr >> sh) * Red::cnt + w;
-            const int row = wm + 32 * (n >> 4) + 8 * ((n & 15) >> 2) + 4 * fg + (n & 3);
-            s_dal[(wid % WN) * BM + row] = dal[w];
-          }
-        }
+      if constexpr (STAGE_T) {
         lds_barrier();
-        if (tid < t.rows) {
-          float sum = 0.f;
+        copy_out(static_cast<T*>(p.out1));
+      }
+      if constexpr (DH) {
+        if constexpr (STAGE_T) lds_barrier();  // every piece of dg^T has been read
 #pragma unroll
-          for (int w = 0; w < WN; ++w) sum += s_dal[w * BM + tid];
-          p.dalpha_part[int64_t(s_ment[tid]) * nt_count + t.n0 / BN] = sum;
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int vq = 0; vq < 4; ++vq)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) put_t(static_cast<T*>(p.out2), i, vq, j, dus[i][vq][j]);
+        if constexpr (STAGE_T) {
+          lds_barrier();
+          copy_out(static_cast<T*>(p.out2));
+        }
+      }
+      if constexpr (DH) {
+        if (p.dalpha_part != nullptr) {
+          // Row sums over the wavefront's columns (the 32 lanes fr of each
+          // half-wavefront), then over the WN wavefronts.  Halving exchanges:
+          // at mask m a lane with (fr & m) keeps the upper half of its values
+          // and adds its partner's; once one value is left, plain butterflies.
+          // Lane fr ends with the sum for value index fr >> (5 - STEPS).
+          constexpr int V = TM * 16;
+          constexpr int STEPS = V >= 32 ? 5 : 4;  // TM >= 1: V is 16, 32 or more
+          constexpr int CNT = V >> STEPS;
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st) {
+            const int mask = 16 >> st;
+            const int half = V >> (st + 1);
+            const bool upper = (fr & mask) != 0;
+#pragma unroll
+            for (int n = 0; n < half; ++n) {
+              const float send = upper ? dal[n] : dal[n + half];
+              const float keep = upper ? dal[n + half] : dal[n];
+              dal[n] = keep + __shfl_xor(send, mask, 64);
+            }
+          }
+          if constexpr (STEPS < 5) dal[0] += __shfl_xor(dal[0], 1, 64);
+          constexpr int sh = 5 - STEPS;
+          if ((fr & ((1 << sh) - 1)) == 0) {
+#pragma unroll
+            for (int w = 0; w < CNT; ++w) {
+              const int n = (fr >> sh) * CNT + w;
+              const int row = wm + 32 * (n >> 4) + 8 * ((n & 15) >> 2) + 4 * fg + (n & 3);
+              s_dal[(wid % WN) * BM + row] = dal[w];
+            }
+          }
+          lds_barrier();
+          if (tid < t.rows) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) sum += s_dal[w * BM + tid];
+            p.dalpha_part[int64_t(s_ment[tid]) * nt_count + t.n0 / BN] = sum;
+          }
         }
       }
       return;
     }
+    // Row-major outputs: each group of four rows of a column (the lane's
+    // registers 4 vq .. 4 vq + 3) is transposed inside the lane quad, so a lane
+    // stores four consecutive columns of one row in a single 8-byte (bf16) or
+    // 16-byte (fp32) store.  Row scales (alpha) apply before the transpose.
+    if constexpr (!QT) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int ro = 32 * i + 8 * (v >> 2) + (v & 3);
-        if (ro >= rows_left) continue;
-        if constexpr (KGROUP) {
-          const int64_t o = (int64_t(t.e) * p.M + t.row0 + rl + ro) * p.Nout + t.n0 + cl;
-#pragma unroll
-          for (int q = 0; q < NP; ++q) {
-            T* out = static_cast<T*>(q == 0 ? p.out : p.out1) + o;
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[q][i][j][v]);
-          }
-        } else if constexpr (KIND == KIND_GATEUP) {
+        for (int v = 0; v < 16; ++v) {
+          const int ro = 32 * i + 8 * (v >> 2) + (v & 3);
+          if (ro >= rows_left) continue;
           T* out = static_cast<T*>(p.out) + (t.row0 + rl + ro) * p.Nout + t.n0 + cl;
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            if (32 * j < cols_left)
-              out[32 * j] = from_f32<T>(silu_mul(acc[0][i][j][v], acc[NP - 1][i][j][v]));
-        } else {
-          const int64_t ent = s_ment[rl + ro];
-          const float a = s_malpha[rl + ro];
-          if constexpr (KIND == KIND_DOWN_Y) {
-            const int64_t o = (ent / p.k) * p.Nout + t.n0 + cl;
-            T* out = static_cast<T*>(p.out) + o;
-            const T* res = p.residual != nullptr ? static_cast<const T*>(p.residual) + o : nullptr;
+            if (32 * j < cols_left) {
+              if constexpr (KIND == KIND_GATEUP)
+                out[32 * j] = from_f32<T>(silu_mul(acc[0][i][j][v], acc[NP - 1][i][j][v]));
+            }
+        }
+      }
+      return;
+    }
+    const int q4 = fr & 3;
+    const int cq = t.n0 + (cl & ~3);  // first column of the lane's quad
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              if (32 * j < cols_left) {
-                const float r = res != nullptr ? to_f32<T>(res[32 * j]) : 0.f;
-                out[32 * j] = from_f32<T>(r + acc[0][i][j][v] * a);
-              }
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        const int ro0 = 32 * i + 8 * vq;
+        const int ro = ro0 + q4;  // the lane's row after the transpose
+        const bool row_ok = ro < rows_left;
+        float a4[4] = {1.f, 1.f, 1.f, 1.f};
+        int64_t ent = 0;
+        if constexpr (META) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) a4[w] = s_malpha[rl + ro0 + w];
+          ent = s_ment[rl + ro];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const bool ok = row_ok && 32 * j < cols_left;  // columns: the same for the quad
+          const int col = cq + 32 * j;
+          if constexpr (KGROUP) {
+            const int64_t o = (int64_t(t.e) * p.M + t.row0 + rl + ro) * p.Nout + col;
+#pragma unroll
+            for (int q = 0; q < NP; ++q) {
+              float b[4];
+#pragma unroll
+              for (int w = 0; w < 4; ++w) b[w] = acc[q][i][j][4 * vq + w];
+              quad_transpose(b, q4);
+              if (ok) store4<T>(static_cast<T*>(q == 0 ? p.out : p.out1) + o, b);
+            }
+          } else if constexpr (KIND == KIND_GATEUP) {
+            float b[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              b[w] = silu_mul(acc[0][i][j][4 * vq + w], acc[NP - 1][i][j][4 * vq + w]);
+            quad_transpose(b, q4);
+            if (ok) store4<T>(static_cast<T*>(p.out) + (t.row0 + rl + ro) * p.Nout + col, b);
           } else {
-            T* out = static_cast<T*>(p.out) + ent * p.Nout + t.n0 + cl;
+            float b[4];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              if (32 * j < cols_left) out[32 * j] = from_f32<T>(acc[0][i][j][v] * a);
+            for (int w = 0; w < 4; ++w) b[w] = acc[0][i][j][4 * vq + w] * a4[w];
+            quad_transpose(b, q4);
+            if constexpr (KIND == KIND_DOWN_Y) {
+              const int64_t o = (ent / p.k) * p.Nout + col;
+              if (ok) {
+                if (p.residual != nullptr) {
+                  float r[4];
+                  load4<T>(static_cast<const T*>(p.residual) + o, r);
+#pragma unroll
+                  for (int w = 0; w < 4; ++w) b[w] = r[w] + b[w];
+                }
+                store4<T>(static_cast<T*>(p.out) + o, b);
+              }
+            } else {
+              if (ok) store4<T>(static_cast<T*>(p.out) + ent * p.Nout + col, b);
+            }
           }
         }
       }
@@ -680,6 +825,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
         // this tile's slices are all issued: the sources move on to the next tile
         if (xnext) make_src(nxt, rid);
         load_meta(cur);
+        load_gu(cur);
       }
       // the very last slices of the block: nothing left to fetch, drain
       const bool tail = last_group && !xnext;
@@ -701,6 +847,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     // slots; in the last S - 1 of them there is nothing left to fetch.
     if (!stream) {
       load_meta(cur);
+      load_gu(cur);
       for (; kt < KT; ++kt) {
         const int sl = kt % S;
         const bool more = kt + S < KT;
@@ -774,7 +921,7 @@ constexpr bool shape_ok() {
   constexpr int R = KindTraits<KIND>::NA * BM + KindTraits<KIND>::NB * BN;
   constexpr int NW = WM * WN;
   constexpr int RPI = 1024 / RB;
-  constexpr bool pad = KindTraits<KIND>::KGROUP || KIND == KIND_BWD_H;
+  constexpr bool pad = KindTraits<KIND>::KGROUP || KIND == KIND_BWD_GU || KIND == KIND_BWD_DH;
   return S * R * RB <= 156 * 1024 && (R / RPI) % NW == 0 && BM % RPI == 0 && BN % RPI == 0 &&
          (S - 1) * (R / RPI / NW) < 64 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0 &&
          (!pad || BM % 64 == 0) && BM <= 64 * NW;
@@ -803,12 +950,13 @@ struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
   X(128, 128, 2, 4, 64, 4) X(256, 128, 4, 2, 128, 2) X(128, 128, 2, 4, 128, 3)            \
   X(128, 128, 2, 4, 128, 4) X(256, 64, 4, 2, 128, 3) X(256, 128, 4, 2, 128, 3)
 #define TOPMOE_GEMM_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
-// The fused backward projection (five operands per slice):
-// (4-wavefront 128-row tiles would hold three accumulator sets of 64 x 64 per
-// wavefront and spill.)
-#define TOPMOE_BWDH_SHAPES_BF16(X)                                                        \
-  X(128, 64, 4, 2, 128, 2) X(64, 128, 2, 4, 128, 2) X(128, 128, 2, 4, 64, 3)
-#define TOPMOE_BWDH_SHAPES_F32(X) X(64, 64, 2, 2, 128, 3)
+// The backward's recomputed gate/up projection and its dh projection (their
+// LDS also holds one staged transposed output tile where it fits; the dh
+// epilogue's (g, u) words and du values make 256-row tiles spill):
+#define TOPMOE_BWDGU_SHAPES_BF16(X)                                                       \
+  X(256, 128, 4, 2, 128, 2) X(128, 128, 2, 4, 128, 2) X(256, 64, 4, 2, 128, 2)
+#define TOPMOE_BWDDH_SHAPES_BF16(X) X(128, 128, 2, 4, 128, 3) X(128, 128, 2, 4, 128, 2)
+#define TOPMOE_BWD_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
 // Weight gradients:
 #define TOPMOE_WGRAD_SHAPES_BF16(X)                                                       \
   X(128, 256, 2, 4, 128, 2) X(128, 128, 2, 4, 128, 3) X(256, 128, 4, 2, 128, 3)           \
@@ -821,11 +969,17 @@ hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, 
   if (sh.bm == (BM_) && sh.bn == (BN_) && sh.wm == (WM_) && sh.wn == (WN_) &&            \
       sh.rb == (RB_) && sh.stages == (S_))                                               \
     return ShapeLauncher<T, BM_, BN_, WM_, WN_, RB_, S_, KIND>::run(p, mtiles, s);
-  if constexpr (KIND == KIND_BWD_H) {
+  if constexpr (KIND == KIND_BWD_GU) {
     if constexpr (sizeof(T) == 2) {
-      TOPMOE_BWDH_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+      TOPMOE_BWDGU_SHAPES_BF16(TOPMOE_TRY_SHAPE)
     } else {
-      TOPMOE_BWDH_SHAPES_F32(TOPMOE_TRY_SHAPE)
+      TOPMOE_BWD_SHAPES_F32(TOPMOE_TRY_SHAPE)
+    }
+  } else if constexpr (KIND == KIND_BWD_DH) {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_BWDDH_SHAPES_BF16(TOPMOE_TRY_SHAPE)
+    } else {
+      TOPMOE_BWD_SHAPES_F32(TOPMOE_TRY_SHAPE)
     }
   } else if constexpr (KindTraits<KIND>::KGROUP) {
     if constexpr (sizeof(T) == 2) {
@@ -851,7 +1005,8 @@ hipError_t launch_gemm_dtype(int kind, GemmShape sh, const GemmParams& p, int64_
     case KIND_GATEUP: return launch_gemm_tiles<T, KIND_GATEUP>(sh, p, mtiles, s);
     case KIND_DOWN_Y: return launch_gemm_tiles<T, KIND_DOWN_Y>(sh, p, mtiles, s);
     case KIND_DOWN_SLOTS: return launch_gemm_tiles<T, KIND_DOWN_SLOTS>(sh, p, mtiles, s);
-    case KIND_BWD_H: return launch_gemm_tiles<T, KIND_BWD_H>(sh, p, mtiles, s);
+    case KIND_BWD_GU: return launch_gemm_tiles<T, KIND_BWD_GU>(sh, p, mtiles, s);
+    case KIND_BWD_DH: return launch_gemm_tiles<T, KIND_BWD_DH>(sh, p, mtiles, s);
     case KIND_WGRAD2: return launch_gemm_tiles<T, KIND_WGRAD2>(sh, p, mtiles, s);
     case KIND_WGRAD1: return launch_gemm_tiles<T, KIND_WGRAD1>(sh, p, mtiles, s);
   }

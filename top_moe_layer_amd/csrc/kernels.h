@@ -44,27 +44,33 @@ enum GemmKind {
   KIND_DOWN_Y = 1,      // y[token] = alpha * (h Wd^T), written in the output dtype
   KIND_DOWN_SLOTS = 2,  // slot[entry] = alpha * (h Wd^T), in the operand dtype
   // backward
-  KIND_BWD_H = 3,       // g, u = x Wg^T, x Wu^T and dh = dy Wd (rows gathered from x, dy):
-                        // writes [dg | du] row-major, dg^T / du^T / h^T in padded group
-                        // columns, and per-row partial sums of dh . h (d alpha)
+  KIND_BWD_GU = 3,      // g, u = x Wg^T, x Wu^T (rows gathered from x): writes the pairs
+                        // (g, u) row-major and h^T in padded group columns
   KIND_WGRAD2 = 4,      // out0 = A0 B^T, out1 = A1 B^T per group, K = the group's padded rows
   KIND_WGRAD1 = 5,      // out0 = A0 B^T per group, K = the group's padded rows
+  KIND_BWD_DH = 6,      // dh = alpha * dy Wd (rows gathered from dy), with the pairs (g, u):
+                        // writes [dg | du] row-major, dg^T / du^T in padded group columns and
+                        // per-row partial sums of dh_raw . h (d alpha)
 };
 
 struct GemmParams {
-  const void* A;           // gate/up, bwd h: x [N, K]; down: h or [dg|du] [rows, K];
+  const void* A;           // gate/up, bwd gu: x [N, K]; bwd dh: dy [N, K];
+                           // down: h or [dg|du] [rows, K];
                            // wgrad: [M, ldk] transposed activations (padded group columns)
-  const void* A1;          // bwd h: dy [N, K]; wgrad pair: second A [M, ldk]
-  const void* B0;          // gate/up, bwd h: Wg [E, Nout, K]; down: Wd or [Wg|Wu]^T [E, Nout, K];
-                           // wgrad: [Nout, ldk]
-  const void* B1;          // gate/up, bwd h: Wu [E, Nout, K]
-  const void* B2;          // bwd h: Wd^T [E, Nout, K]
+  const void* A1;          // wgrad pair: second A [M, ldk]
+  const void* B0;          // gate/up, bwd gu: Wg [E, Nout, K]; bwd dh: Wd^T [E, Nout, K];
+                           // down: Wd or [Wg|Wu]^T [E, Nout, K]; wgrad: [Nout, ldk]
+  const void* B1;          // gate/up, bwd gu: Wu [E, Nout, K]
+  const void* B2;          // (a third B operand; unused by the current kinds)
+  const void* gu;          // bwd dh: the pairs (g, u) [rows, Nout] written by bwd gu
   void* out;               // gate/up: h [rows, Nout]; down: y [N, Nout] or slots [rows, Nout];
-                           // bwd h: [dg | du] [rows, 2 Nout]; wgrad: [groups, M, Nout]
-  void* out1;              // bwd h: dg^T [Nout, ldk]; wgrad pair: second [groups, M, Nout]
-  void* out2;              // bwd h: du^T [Nout, ldk]
-  void* out3;              // bwd h: h^T [Nout, ldk]
-  float* dalpha_part;      // bwd h: [entries, ceil(Nout / BN)] partial dh . h; NULL = skip
+                           // bwd gu: pairs (g, u) [rows, Nout]; bwd dh: [dg | du] [rows, 2 Nout];
+                           // wgrad: [groups, M, Nout]
+  void* out1;              // bwd gu: h^T; bwd dh: dg^T [Nout, ldk];
+                           // wgrad pair: second [groups, M, Nout]
+  void* out2;              // bwd dh: du^T [Nout, ldk]
+  void* out3;              // (unused)
+  float* dalpha_part;      // bwd dh: [entries, ceil(Nout / BN)] partial dh_raw . h; NULL = skip
   const int32_t* entries;  // grouped row -> entry id t*k + j; NULL = identity (dense)
   const int32_t* offsets;  // [E+1] group row offsets; NULL = one group of M rows
                            // (wgrad: of kcount rows)

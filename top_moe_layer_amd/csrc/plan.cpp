@@ -129,8 +129,12 @@ GemmShape bwd_shape(const char* env, GemmShape bf16, GemmShape f32, int dtype) {
   return sh;
 }
 
-GemmShape bwdh_tile(int dtype) {
-  return bwd_shape("TOPMOE_BWDH_TILE", GemmShape{128, 64, 4, 2, 128, 2},
+GemmShape gu_tile(int dtype) {
+  return bwd_shape("TOPMOE_BWDGU_TILE", GemmShape{256, 128, 4, 2, 128, 2},
+                   GemmShape{128, 64, 2, 2, 128, 2}, dtype);
+}
+GemmShape dh_tile(int dtype) {
+  return bwd_shape("TOPMOE_BWDDH_TILE", GemmShape{128, 128, 2, 4, 128, 3},
                    GemmShape{64, 64, 2, 2, 128, 3}, dtype);
 }
 GemmShape wgu_tile(int dtype) {
@@ -219,7 +223,8 @@ int plan_ffn_bwd(int64_t N, int64_t H, int64_t I, int dtype, FfnBwdPlan* p) {
   if (!operand_ok(N, 2 * I, el) || !operand_ok(H, 2 * I, el) || !operand_ok(I, q.ldk, el) ||
       !operand_ok(H, q.ldk, el))
     return TOPMOE_ERR_BAD_SHAPE;
-  q.bwdh = bwdh_tile(dtype);
+  q.gu = gu_tile(dtype);
+  q.dh = dh_tile(dtype);
   q.dx = choose_down_tile(N, H, 2 * I, 1, dtype);
   q.wgu = wgu_tile(dtype);
   q.wd = wd_tile(dtype);
@@ -229,6 +234,7 @@ int plan_ffn_bwd(int64_t N, int64_t H, int64_t I, int dtype, FfnBwdPlan* p) {
   q.off_wdT = o;  o = align_up(o + size_t(I) * size_t(H) * e);
   q.off_xT = o;   o = align_up(o + size_t(H) * size_t(q.ldk) * e);
   q.off_dyT = o;  o = align_up(o + size_t(H) * size_t(q.ldk) * e);
+  q.off_gu = o;   o = align_up(o + size_t(N) * size_t(I) * 2 * e);
   q.off_dgdu = o; o = align_up(o + size_t(N) * size_t(2 * I) * e);
   q.off_dgT = o;  o = align_up(o + size_t(I) * size_t(q.ldk) * e);
   q.off_duT = o;  o = align_up(o + size_t(I) * size_t(q.ldk) * e);
@@ -251,13 +257,15 @@ int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBw
   if (!operand_ok(rows, 2 * I, el) || !operand_ok(H, 2 * I, el) || !operand_ok(I, q.ldk, el) ||
       !operand_ok(H, q.ldk, el) || q.ldk > kMaxRows)
     return TOPMOE_ERR_BAD_SHAPE;
-  q.bwdh = bwdh_tile(dtype);
+  q.gu = gu_tile(dtype);
+  q.dh = dh_tile(dtype);
   q.dx = choose_down_tile(rows, H, 2 * I, E, dtype);
   q.wgu = wgu_tile(dtype);
   q.wd = wd_tile(dtype);
-  q.bwdh_mtiles = grouped_mtiles_bound(rows, E, q.bwdh.bm);
+  q.gu_mtiles = grouped_mtiles_bound(rows, E, q.gu.bm);
+  q.dh_mtiles = grouped_mtiles_bound(rows, E, q.dh.bm);
   q.dx_mtiles = grouped_mtiles_bound(rows, E, q.dx.bm);
-  q.nt_h = int((I + q.bwdh.bn - 1) / q.bwdh.bn);
+  q.nt_h = int((I + q.dh.bn - 1) / q.dh.bn);
   q.nchunk = int((N + kDwrChunk - 1) / kDwrChunk);
   const size_t e = size_t(el);
   // routing buffers first (the forward's own layout), then the backward's
@@ -270,6 +278,7 @@ int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBw
   q.off_wdT = o;   o = align_up(o + size_t(E) * size_t(I) * size_t(H) * e);
   q.off_xT = o;    o = align_up(o + size_t(H) * size_t(q.ldk) * e);
   q.off_dyT = o;   o = align_up(o + size_t(H) * size_t(q.ldk) * e);
+  q.off_gu = o;    o = align_up(o + size_t(rows) * size_t(I) * 2 * e);
   q.off_dgdu = o;  o = align_up(o + size_t(rows) * size_t(2 * I) * e);
   q.off_dgT = o;   o = align_up(o + size_t(I) * size_t(q.ldk) * e);
   q.off_duT = o;   o = align_up(o + size_t(I) * size_t(q.ldk) * e);

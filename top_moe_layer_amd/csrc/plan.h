@@ -9,7 +9,7 @@
 namespace topmoe {
 
 constexpr size_t kAlign = 256;
-constexpr int kDwrChunk = 128;  // tokens per partial of the router-weight gradient
+constexpr int kDwrChunk = 256;  // tokens per partial of the router-weight gradient
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
@@ -60,11 +60,12 @@ struct FfnBwdPlan {
   int64_t N = 0, H = 0, I = 0;
   int dtype = 0, elem = 0;
   int64_t ldk = 0;
-  GemmShape bwdh, dx, wgu, wd;  // fused g/u/dh, dx, dWg+dWu, dWd GEMMs
+  GemmShape gu, dh, dx, wgu, wd;  // g/u, dh, dx, dWg+dWu, dWd GEMMs
   size_t off_wgT = 0;    // [H, 2I]  [Wg | Wu]^T
   size_t off_wdT = 0;    // [I, H]   Wd^T
   size_t off_xT = 0;     // [H, ldk] x^T
   size_t off_dyT = 0;    // [H, ldk] dy^T
+  size_t off_gu = 0;     // [N, I]   pairs (g, u)
   size_t off_dgdu = 0;   // [N, 2I]  [dg | du]
   size_t off_dgT = 0;    // [I, ldk] dg^T
   size_t off_duT = 0;    // [I, ldk] du^T
@@ -79,9 +80,9 @@ struct FfnBwdPlan {
 struct MoeBwdPlan {
   MoePlan route;          // router / permutation parameters and buffers
   int64_t ldk = 0;
-  GemmShape bwdh, dx, wgu, wd;
-  int64_t bwdh_mtiles = 0, dx_mtiles = 0;
-  int nt_h = 0;           // column tiles of the fused GEMM: d alpha partials per entry
+  GemmShape gu, dh, dx, wgu, wd;
+  int64_t gu_mtiles = 0, dh_mtiles = 0, dx_mtiles = 0;
+  int nt_h = 0;           // column tiles of the dh GEMM: d alpha partials per entry
   int nchunk = 0;         // token chunks of the router-weight gradient
   size_t off_probs = 0;   // f32 [N, E] softmax
   size_t off_topk = 0;    // i32 [N, k]
@@ -91,6 +92,7 @@ struct MoeBwdPlan {
   size_t off_wdT = 0;     // [E, I, H]
   size_t off_xT = 0;      // [H, ldk]
   size_t off_dyT = 0;     // [H, ldk] (alpha * dy)^T
+  size_t off_gu = 0;      // [N*k, I] pairs (g, u)
   size_t off_dgdu = 0;    // [N*k, 2I]
   size_t off_dgT = 0;     // [I, ldk]
   size_t off_duT = 0;     // [I, ldk]
