@@ -149,11 +149,12 @@ def moe_bwd_call(**over):
 
 
 def test_bwd_workspace_sizes(L):
-    # dense: [Wg|Wu]^T, Wd^T, x^T and dy^T [H, round64(N)], [dg|du], dg^T / du^T / h^T
+    # dense: [Wg|Wu]^T, Wd^T, x^T and dy^T [H, round64(N)], the (g, u) pairs [N, I],
+    # [dg|du], dg^T / du^T / h^T
     N, H, I = 100, 128, 192
     w = B.raw_ffn_bwd_workspace_bytes(N, H, I, B.DTYPE_BF16)
     Np = 128
-    floor = 2 * (3 * H * I + 2 * H * Np + 2 * N * I + 3 * I * Np)
+    floor = 2 * (3 * H * I + 2 * H * Np + 2 * N * I + 2 * N * I + 3 * I * Np)
     assert floor <= w < floor + 16 * 256
     assert B.raw_ffn_bwd_workspace_bytes(N, H, I, B.DTYPE_FP32) >= 2 * floor
     assert B.raw_ffn_bwd_workspace_bytes(0, H, I, B.DTYPE_BF16) > 0
