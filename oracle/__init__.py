@@ -25,6 +25,7 @@ from .ffn_moe import (
     silu_grad,
     swiglu_ffn_bwd,
     moe_ffn_bwd,
+    moe_ffn_bwd_sampled,
 )
 
 __all__ = [
@@ -41,4 +42,5 @@ __all__ = [
     "silu_grad",
     "swiglu_ffn_bwd",
     "moe_ffn_bwd",
+    "moe_ffn_bwd_sampled",
 ]

@@ -310,3 +310,75 @@ def moe_ffn_bwd(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True):
     dWr = dr.T @ x
     dx += dr @ Wr
     return {"dx": dx, "dWr": dWr, "dWg": dWg, "dWu": dWu, "dWd": dWd, "route": r}
+
+
+def moe_ffn_bwd_sampled(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True,
+                        rows=None, units=None):
+    """Exact parts of ``moe_ffn_bwd`` at a fraction of its cost, for checks at
+    full size.
+
+    * dx[rows]: each token's input gradient needs only its own selected
+      experts (their outputs for that token give d alpha), the routing counts
+      (aux term) and the router weights, so it is computed row by row.
+    * dWg[e][units], dWu[e][units], dWd[e][:, units]: the FFN is a sum over its
+      intermediate units, and a unit's weight gradients involve only that
+      unit's g, u and down column, so the expert backward restricted to those
+      units (upstream alpha * dy over all the expert's tokens) gives them
+      exactly.
+
+    * dW_r (only when every row is taken): the sum of dr_t x_t^T over them.
+
+    Returns dict dx_rows [len(rows), H], rows, units, dWg_u / dWu_u
+    [E, len(units), H], dWd_u [E, H, len(units)], dWr (or None) and the routing.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    Wr = np.asarray(Wr, dtype=np.float64)
+    N, H = x.shape
+    E = Wr.shape[0]
+    r = moe_route(x, Wr, k, coef, norm_topk_prob)
+    p, idx, alpha, counts = r["p"], r["topk_idx"], r["alpha"], r["counts"]
+    all_rows = rows is None
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    units = np.arange(np.shape(Wg)[1]) if units is None else np.asarray(units, dtype=np.int64)
+    # dx for the sampled rows
+    dx = np.zeros((len(rows), H))
+    drs = np.zeros((len(rows), E))
+    for n, t in enumerate(rows):
+        dalpha = np.zeros(k)
+        for j in range(k):
+            e = idx[t, j]
+            xt = x[t:t + 1]
+            o = swiglu_ffn(xt, Wg[e], Wu[e], Wd[e])[0]
+            dalpha[j] = dy[t] @ o
+            gx = swiglu_ffn_bwd(xt, Wg[e], Wu[e], Wd[e], alpha[t, j] * dy[t:t + 1])[0]
+            dx[n] += gx[0]
+        ps = p[t, idx[t]]
+        if norm_topk_prob:
+            Z = ps.sum() + EPS_RENORM
+            dps = dalpha / Z - (dalpha * ps).sum() / Z ** 2
+        else:
+            dps = dalpha
+        dp = np.zeros(E)
+        dp[idx[t]] = dps
+        if coef != 0.0:
+            dp += daux * coef * E * counts / float(N) ** 2
+        dr = p[t] * (dp - (p[t] * dp).sum())
+        drs[n] = dr
+        dx[n] += dr @ Wr
+    # weight gradients of the sampled units
+    dWg_u = np.zeros((E, len(units), H))
+    dWu_u = np.zeros((E, len(units), H))
+    dWd_u = np.zeros((E, H, len(units)))
+    for e in range(E):
+        mask = idx == e
+        tok = np.nonzero(mask.any(axis=1))[0]
+        if tok.size == 0:
+            continue
+        slot = np.argmax(mask[tok], axis=1)
+        w = alpha[tok, slot]
+        _, gWg, gWu, gWd = swiglu_ffn_bwd(x[tok], np.asarray(Wg[e])[units], np.asarray(Wu[e])[units],
+                                          np.asarray(Wd[e])[:, units], w[:, None] * dy[tok])
+        dWg_u[e], dWu_u[e], dWd_u[e] = gWg, gWu, gWd
+    return {"dx_rows": dx, "rows": rows, "units": units, "dWg_u": dWg_u, "dWu_u": dWu_u,
+            "dWd_u": dWd_u, "dWr": drs.T @ x if all_rows else None, "route": r}

@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 from oracle import (
-    silu, silu_grad, swiglu_ffn, swiglu_ffn_bwd, moe_ffn, moe_ffn_bwd,
+    silu, silu_grad, swiglu_ffn, swiglu_ffn_bwd, moe_ffn, moe_ffn_bwd, moe_ffn_bwd_sampled,
     router_probs, topk_canonical,
 )
 
@@ -217,3 +217,33 @@ def test_moe_bwd_linearity_and_zero():
     c = moe_ffn_bwd(*args, d1 + 0.5 * d2, 2.0, True)
     for key in ("dx", "dWr", "dWg", "dWu", "dWd"):
         np.testing.assert_allclose(c[key], a[key] + 0.5 * b[key], rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("k,coef,norm", [(1, 0.01, True), (2, 0.05, False), (3, 0.02, True)])
+def test_moe_bwd_sampled_matches_full(k, coef, norm):
+    """The sampled entry point (dx row by row, weight gradients of a subset of
+    intermediate units) reproduces the corresponding parts of the full backward."""
+    N, H, I, E = 40, 6, 7, 5
+    P = _moe_params(N, H, I, E, 700 + k)
+    dy = rnd((N, H), 17)
+    args = (P["x"], P["Wr"], P["Wg"], P["Wu"], P["Wd"], k, coef, dy, 1.3, norm)
+    full = moe_ffn_bwd(*args)
+    rows = np.array([0, 3, 17, 39])
+    units = np.array([1, 4, 6])
+    s = moe_ffn_bwd_sampled(*args, rows=rows, units=units)
+    np.testing.assert_allclose(s["dx_rows"], full["dx"][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s["dWg_u"], full["dWg"][:, units], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s["dWu_u"], full["dWu"][:, units], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s["dWd_u"], full["dWd"][:, :, units], rtol=1e-12, atol=1e-13)
+
+
+def test_moe_bwd_sampled_all_rows_gives_dwr():
+    N, H, I, E = 30, 5, 6, 4
+    P = _moe_params(N, H, I, E, 800)
+    dy = rnd((N, H), 18)
+    args = (P["x"], P["Wr"], P["Wg"], P["Wu"], P["Wd"], 2, 0.03, dy, 0.7, True)
+    full = moe_ffn_bwd(*args)
+    s = moe_ffn_bwd_sampled(*args, units=np.array([0, 5]))
+    np.testing.assert_allclose(s["dWr"], full["dWr"], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s["dx_rows"], full["dx"], rtol=1e-12, atol=1e-13)
+    assert moe_ffn_bwd_sampled(*args, rows=[1, 2])["dWr"] is None
