@@ -26,6 +26,10 @@ from .ffn_moe import (
     swiglu_ffn_bwd,
     moe_ffn_bwd,
     moe_ffn_bwd_sampled,
+    logsumexp_rows,
+    router_z_loss,
+    expert_capacity,
+    kept_entries,
 )
 
 __all__ = [
@@ -43,4 +47,8 @@ __all__ = [
     "swiglu_ffn_bwd",
     "moe_ffn_bwd",
     "moe_ffn_bwd_sampled",
+    "logsumexp_rows",
+    "router_z_loss",
+    "expert_capacity",
+    "kept_entries",
 ]

@@ -148,16 +148,73 @@ def aux_loss(p, idx, E, coef):
     return float((load * prob[None, :]).sum() * E * coef)
 
 
+# ------------------------------------------------- z-loss and capacity
+# The study notes' section 10 table names both (z-loss keeps the router
+# logits from growing; capacity limits how many tokens one expert takes) and
+# lesson 13 section 4 lists capacity / token dropping as not required; no
+# page defines them.  These follow the standard published forms (readings,
+# listed with the design notes):
+#   z-loss    z_coef * mean_t (logsumexp_e r_te)^2
+#   capacity  C = ceil(capacity_factor * N * k / E) (capacity_factor 0: no
+#             limit); expert e keeps the first C of its tokens in the
+#             dispatch order (ascending token id) and drops the rest; a
+#             dropped (token, expert) pair adds nothing to y; alpha is not
+#             renormalised; aux uses the router's choices before dropping.
+def logsumexp_rows(r):
+    """log sum_e exp(r_te) per row, shifted by the row maximum (no overflow)."""
+    r = np.asarray(r, dtype=np.float64)
+    m = r.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(r - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def router_z_loss(x, Wr, z_coef):
+    """z_coef * mean over tokens of logsumexp(W_r x_t)^2 (0 when z_coef is 0)."""
+    if z_coef == 0.0:
+        return 0.0
+    r = np.asarray(x, dtype=np.float64) @ np.asarray(Wr, dtype=np.float64).T
+    return float(z_coef * np.mean(logsumexp_rows(r) ** 2))
+
+
+def expert_capacity(N, k, E, capacity_factor):
+    """C = ceil(capacity_factor * N * k / E); None for capacity_factor 0 (no limit)."""
+    if capacity_factor == 0.0:
+        return None
+    return int(np.ceil(capacity_factor * N * k / E))
+
+
+def kept_entries(idx, E, C):
+    """keep [N, k]: True where (token, slot) is among the first C tokens of its
+    expert in ascending token order (all True when C is None)."""
+    idx = np.asarray(idx)
+    keep = np.ones(idx.shape, dtype=bool)
+    if C is None:
+        return keep
+    for e in range(E):
+        t, j = np.nonzero(idx == e)          # row-major: ascending token
+        keep[t[C:], j[C:]] = False
+    return keep
+
+
 # --------------------------------------------------------------------- MoE
-def moe_route(x, Wr, k, coef, norm_topk_prob=True):
+def moe_route(x, Wr, k, coef, norm_topk_prob=True, z_coef=0.0, capacity_factor=0.0):
     """Routing half of the MoE forward: probabilities, top-k, renormalised
     (or, with norm_topk_prob False, raw) weights, per-expert lists and
-    aux_loss ([L13] section 3 steps 4-6)."""
+    aux_loss ([L13] section 3 steps 4-6); with the readings above also the
+    z-loss and, under a capacity, the kept entries, their per-expert counts,
+    offsets and token lists (the plain lists and aux stay pre-drop)."""
     p = router_probs(x, Wr)
     E = p.shape[1]
+    N = p.shape[0]
     idx = topk_canonical(p, k)
     alpha = renorm_weights(p, idx, normalize=norm_topk_prob)
     counts, offsets, sorted_ids = expert_lists(idx, E)
+    C = expert_capacity(N, k, E, capacity_factor)
+    keep = kept_entries(idx, E, C)
+    kept_counts = np.array([int(keep[idx == e].sum()) for e in range(E)], dtype=np.int64)
+    kept_offsets = np.zeros(E + 1, dtype=np.int64)
+    kept_offsets[1:] = np.cumsum(kept_counts)
+    kept_ids = [np.nonzero(((idx == e) & keep).any(axis=1))[0] for e in range(E)]
+    kept_sorted = np.concatenate(kept_ids) if kept_ids else np.zeros(0, np.int64)
     return {
         "p": p,
         "topk_idx": idx,
@@ -166,11 +223,17 @@ def moe_route(x, Wr, k, coef, norm_topk_prob=True):
         "offsets": offsets,
         "sorted_token_ids": sorted_ids,
         "aux": aux_loss(p, idx, E, coef),
+        "z_loss": router_z_loss(x, Wr, z_coef),
+        "capacity": C,
+        "keep": keep,
+        "kept_counts": kept_counts,
+        "kept_offsets": kept_offsets,
+        "kept_sorted_token_ids": kept_sorted.astype(np.int64),
     }
 
 
 def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None, residual=None,
-            norm_topk_prob=True):
+            norm_topk_prob=True, z_coef=0.0, capacity_factor=0.0):
     """MoE FFN forward ([L13] section 0 MoE equations, section 3 steps 4-6;
     [MM4] 4.3 steps 1-3):
 
@@ -182,13 +245,16 @@ def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None, residual=None,
     x [N, H]; Wr [E, H]; Wg, Wu [E, I, H]; Wd [E, H, I].  ``rows`` (sorted or
     not) restricts y to those tokens; routing statistics always use all N.
     ``residual`` [N, H] (optional) starts y from the residual stream instead of
-    zeros ([L13] section 1.3 and 1.4: hidden_states + mlp(...)).
+    zeros ([L13] section 1.3 and 1.4: hidden_states + mlp(...)).  Under a
+    capacity only the kept (token, expert) pairs contribute.
     Returns the routing dict plus ``y`` ([len(rows), H] or [N, H]).
     """
     x = np.asarray(x, dtype=np.float64)
     N = x.shape[0]
-    r = moe_route(x, Wr, k, coef, norm_topk_prob) if route is None else route
+    r = (moe_route(x, Wr, k, coef, norm_topk_prob, z_coef, capacity_factor) if route is None
+         else route)
     idx, alpha = r["topk_idx"], r["alpha"]
+    keep = r.get("keep", np.ones(np.shape(idx), dtype=bool))
     E = r["p"].shape[1]
     if rows is None:
         rows = np.arange(N)
@@ -200,8 +266,8 @@ def moe_ffn(x, Wr, Wg, Wu, Wd, k, coef, rows=None, route=None, residual=None,
     else:
         y = np.asarray(residual, dtype=np.float64)[rows].copy()
     for e in range(E):
-        mask = idx == e                                  # [N, k]
-        tok = np.nonzero(mask.any(axis=1))[0]            # ascending tokens that chose e
+        mask = (idx == e) & keep                         # [N, k]
+        tok = np.nonzero(mask.any(axis=1))[0]            # ascending kept tokens that chose e
         tok = tok[where[tok] >= 0]
         if tok.size == 0:
             continue
@@ -255,7 +321,8 @@ def swiglu_ffn_bwd(x, Wg, Wu, Wd, dy):
     return dx, dWg, dWu, dWd
 
 
-def moe_ffn_bwd(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True):
+def moe_ffn_bwd(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True,
+                z_coef=0.0, dz=1.0, capacity_factor=0.0):
     """Backward of ``moe_ffn`` (with its aux_loss) for upstream dy [N, H] and
     daux (the gradient reaching aux_loss; 1 when it is added to the loss).
 
@@ -265,22 +332,25 @@ def moe_ffn_bwd(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True):
       the expert's own backward with upstream alpha_{t,e} dy_t;
     then through alpha = p_S / (sum p_S + 1e-20) (or alpha = p_S), the aux term
     coef * E * sum_e c_e * (sum_t p_te) / N^2 (counts constant), the softmax
-    and the router logits r = Wr x.
+    and the router logits r = Wr x.  The z-loss z_coef * mean_t lse_t^2 (with
+    upstream dz) adds z_coef * dz * 2 lse_t p_te / N to d r_te (d lse / d r = p);
+    a pair dropped by the capacity passes nothing (no expert gradient, d alpha 0).
     """
     x = np.asarray(x, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
     Wr = np.asarray(Wr, dtype=np.float64)
     N, H = x.shape
     E = Wr.shape[0]
-    r = moe_route(x, Wr, k, coef, norm_topk_prob)
+    r = moe_route(x, Wr, k, coef, norm_topk_prob, z_coef, capacity_factor)
     p, idx, alpha, counts = r["p"], r["topk_idx"], r["alpha"], r["counts"]
+    keep = r["keep"]
     dx = np.zeros_like(x)
     dWg = np.zeros(np.shape(Wg))
     dWu = np.zeros(np.shape(Wu))
     dWd = np.zeros(np.shape(Wd))
     dalpha = np.zeros(alpha.shape)
     for e in range(E):
-        mask = idx == e
+        mask = (idx == e) & keep
         tok = np.nonzero(mask.any(axis=1))[0]
         if tok.size == 0:
             continue
@@ -307,13 +377,16 @@ def moe_ffn_bwd(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True):
         dp += daux * coef * E * counts[None, :] / float(N) ** 2
     # softmax and router logits
     dr = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    if z_coef != 0.0:
+        lse = logsumexp_rows(x @ Wr.T)
+        dr += (z_coef * dz * 2.0 / N) * lse[:, None] * p
     dWr = dr.T @ x
     dx += dr @ Wr
     return {"dx": dx, "dWr": dWr, "dWg": dWg, "dWu": dWu, "dWd": dWd, "route": r}
 
 
 def moe_ffn_bwd_sampled(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob=True,
-                        rows=None, units=None):
+                        rows=None, units=None, z_coef=0.0, dz=1.0, capacity_factor=0.0):
     """Exact parts of ``moe_ffn_bwd`` at a fraction of its cost, for checks at
     full size.
 
@@ -336,8 +409,10 @@ def moe_ffn_bwd_sampled(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob
     Wr = np.asarray(Wr, dtype=np.float64)
     N, H = x.shape
     E = Wr.shape[0]
-    r = moe_route(x, Wr, k, coef, norm_topk_prob)
+    r = moe_route(x, Wr, k, coef, norm_topk_prob, z_coef, capacity_factor)
     p, idx, alpha, counts = r["p"], r["topk_idx"], r["alpha"], r["counts"]
+    keep = r["keep"]
+    lse = logsumexp_rows(x @ Wr.T) if z_coef != 0.0 else None
     all_rows = rows is None
     rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     units = np.arange(np.shape(Wg)[1]) if units is None else np.asarray(units, dtype=np.int64)
@@ -347,6 +422,8 @@ def moe_ffn_bwd_sampled(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob
     for n, t in enumerate(rows):
         dalpha = np.zeros(k)
         for j in range(k):
+            if not keep[t, j]:
+                continue
             e = idx[t, j]
             xt = x[t:t + 1]
             o = swiglu_ffn(xt, Wg[e], Wu[e], Wd[e])[0]
@@ -364,6 +441,8 @@ def moe_ffn_bwd_sampled(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob
         if coef != 0.0:
             dp += daux * coef * E * counts / float(N) ** 2
         dr = p[t] * (dp - (p[t] * dp).sum())
+        if lse is not None:
+            dr = dr + (z_coef * dz * 2.0 / N) * lse[t] * p[t]
         drs[n] = dr
         dx[n] += dr @ Wr
     # weight gradients of the sampled units
@@ -371,7 +450,7 @@ def moe_ffn_bwd_sampled(x, Wr, Wg, Wu, Wd, k, coef, dy, daux=1.0, norm_topk_prob
     dWu_u = np.zeros((E, len(units), H))
     dWd_u = np.zeros((E, H, len(units)))
     for e in range(E):
-        mask = idx == e
+        mask = (idx == e) & keep
         tok = np.nonzero(mask.any(axis=1))[0]
         if tok.size == 0:
             continue
