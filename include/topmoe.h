@@ -11,6 +11,14 @@
  *   MoE output     y = sum_{e in S} alpha_e * Expert_e(x), each expert a dense FFN
  *   aux loss       aux = E * coef * sum_e load_e * prob_e,
  *                  load_e = (tokens that selected e) / N,  prob_e = mean_t p_{t,e}
+ *   z-loss         z_coef * mean_t logsumexp_e(r_te)^2 (router logits r = W_router x)
+ *   capacity       each expert takes at most C = ceil(capacity_factor * N * k / E)
+ *                  tokens: the first C of its tokens in ascending token order
+ *                  (the dispatch order); the others' (token, expert) pairs are
+ *                  dropped and add nothing to y
+ *                  (the MiniMind study notes' section 10 table names router
+ *                  z-loss and expert capacity without defining them; these are
+ *                  the standard forms)
  *   backward       the gradients of these with respect to x and every weight:
  *                  the top-k choice and the counts load_e are discrete and
  *                  carry no gradient; the softmax probabilities carry it back
@@ -68,8 +76,9 @@ extern "C" {
 #define TOPMOE_ERR_UNSUPPORTED_DTYPE    -3  /* dtype not FP32 / BF16                  */
 #define TOPMOE_ERR_WORKSPACE_TOO_SMALL  -4  /* workspace_bytes < *_workspace_bytes()  */
 #define TOPMOE_ERR_HIP                  -5  /* a HIP runtime call or launch failed    */
-#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef negative / not finite, aux_grad not finite, unknown flag bits,
-                                               misaligned pointer */
+#define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef, z_coef or capacity_factor negative or not
+                                               finite; aux_grad or z_grad not finite; unknown
+                                               flag bits; misaligned pointer */
 
 /* ---- dtypes ------------------------------------------------------------ */
 #define TOPMOE_DTYPE_FP32 0
@@ -79,7 +88,8 @@ extern "C" {
 #define TOPMOE_FFN_STAGES 2  /* 0 gate/up GEMM + SiLU*up, 1 down GEMM                   */
 #define TOPMOE_MOE_STAGES 5  /* 0 router, 1 expert offsets + aux + token scatter,
                                 2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
-                                + alpha, 4 combine of the k slots (empty when k == 1)   */
+                                + alpha, 4 combine of the k slots (empty when k == 1
+                                and there is no capacity)                               */
 #define TOPMOE_FFN_BWD_STAGES 7  /* 0 weight transposes, 1 x / dy transposes,
                                     2 g, u GEMM (recomputed), 3 dh GEMM + dg, du,
                                     4 dx GEMM, 5 dWg + dWu GEMM, 6 dWd GEMM             */
@@ -119,8 +129,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
                    void* stream, void* const* stage_events);
 
 /* Workspace needed by moe_ffn_fwd (routing partials, permutation, the
- * SiLU(g)*u intermediate [N*k, I] and, for k >= 2, the k-slots [N*k, H] of
- * alpha-scaled expert outputs in the dtype).
+ * SiLU(g)*u intermediate [N*k, I] and the k-slots [N*k, H] of alpha-scaled
+ * expert outputs in the dtype).
  * Returns 0 for invalid shapes. */
 size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype);
 
@@ -135,31 +145,39 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
  *                        sections 1.3-1.4).  May alias y.
  *   aux_coef             router_aux_loss_coef (>= 0); 0 gives aux = 0 exactly,
  *                        which is also the module's value outside training
+ *   z_coef               router z-loss coefficient (>= 0); 0 gives z_loss = 0
+ *   capacity_factor      expert capacity factor (>= 0); 0 = no capacity (dropless,
+ *                        the pages' module); a capacity of N or more drops nothing
  *   flags                0 or TOPMOE_MOE_RAW_TOPK_WEIGHTS
  *   y        [N, H]      output (dtype): y_t = residual_t (or 0) + the sum over
- *                        the selected experts in ascending expert id of
- *                        alpha * Expert_e(x_t); with k >= 2 each expert term
- *                        is first rounded to the dtype (the terms the pages'
- *                        index_add_ adds); the sum is taken in fp32 and
- *                        rounded once
+ *                        the selected (and kept) experts in ascending expert id
+ *                        of alpha * Expert_e(x_t); with k >= 2 (or a capacity)
+ *                        each expert term is first rounded to the dtype (the
+ *                        terms the pages' index_add_ adds); the sum is taken in
+ *                        fp32 and rounded once
  *   topk_idx [N, k]      int32 selected experts, slot order = probability
  *                        descending, equal probabilities by ascending id
+ *                        (dropped pairs included: the router's choice)
  *   alpha    [N, k]      float32 weights in the same slot order: renormalised
- *                        to sum 1 (default) or the raw probabilities (flag)
- *   aux_loss [1]         float32 load-balancing loss (training-mode value)
+ *                        to sum 1 (default) or the raw probabilities (flag);
+ *                        not renormalised after drops
+ *   aux_loss [1]         float32 load-balancing loss (training-mode value; counts
+ *                        every selection, kept or dropped)
+ *   z_loss   [1]         optional (NULL = not returned) float32 router z-loss
  *   expert_offsets [E+1] optional (NULL = not returned) int32 exclusive prefix
- *                        sum of per-expert token counts
+ *                        sum of per-expert token counts (of the kept tokens)
  *   sorted_token_ids [N*k] optional int32: tokens grouped by expert, ascending
- *                        expert id, ascending token id within an expert
+ *                        expert id, ascending token id within an expert (kept
+ *                        tokens; the remaining positions hold -1)
  *   workspace            at least moe_workspace_bytes(N, H, I, E, k, dtype)
  *                        bytes, 256-byte aligned; contents on entry ignored.
  * Outputs must not alias inputs or each other.  Tensor pointers must be
  * 16-byte aligned (int32/float32 outputs: 4-byte aligned). */
 int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
                 const void* Wd, const void* residual, int64_t N, int64_t H, int64_t I,
-                int E, int k, float aux_coef, int flags, int dtype,
-                void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
-                int32_t* expert_offsets, int32_t* sorted_token_ids,
+                int E, int k, float aux_coef, float z_coef, float capacity_factor, int flags,
+                int dtype, void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
+                float* z_loss, int32_t* expert_offsets, int32_t* sorted_token_ids,
                 void* workspace, size_t workspace_bytes,
                 void* stream, void* const* stage_events);
 
@@ -211,13 +229,16 @@ size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, in
  *   d alpha_{t,e} = dy_t . o;
  *   then dp through alpha = p_S / (sum p_S + 1e-20) (or alpha = p_S with
  *   TOPMOE_MOE_RAW_TOPK_WEIGHTS), plus aux_grad * aux_coef * E * c_e / N^2 on
- *   every p_{t,e} (c_e = tokens routed to e); dr = p * (dp - sum(p * dp));
- *   dW_router = dr^T x and dx_t += W_router^T dr_t.
- *   x, Wr, Wg, Wu, Wd, N, H, I, E, k, aux_coef, flags, dtype
- *                   as for moe_ffn_fwd
+ *   every p_{t,e} (c_e = tokens routed to e); dr = p * (dp - sum(p * dp))
+ *   + z_grad * z_coef * 2 * logsumexp(r_t) * p / N; dW_router = dr^T x and
+ *   dx_t += W_router^T dr_t.  A pair dropped by the capacity contributes
+ *   neither an expert gradient nor d alpha.
+ *   x, Wr, Wg, Wu, Wd, N, H, I, E, k, aux_coef, z_coef, capacity_factor,
+ *   flags, dtype    as for moe_ffn_fwd
  *   dy [N, H]       upstream gradient of y (dtype)
  *   aux_grad        upstream gradient of aux_loss (1 when it is added to the
  *                   loss as is); finite
+ *   z_grad          upstream gradient of z_loss; finite
  *   dx [N, H] (dtype), dWr [E, H] (float32), dWg, dWu [E, I, H], dWd [E, H, I]
  *                   (dtype) outputs; experts no token selected get zero
  *                   gradients.  N == 0 gives all-zero weight gradients.
@@ -226,9 +247,10 @@ size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, in
  * Outputs must not alias inputs or each other; tensor pointers 16-byte
  * aligned. */
 int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
-                const void* Wd, const void* dy, float aux_grad,
-                int64_t N, int64_t H, int64_t I, int E, int k, float aux_coef, int flags,
-                int dtype, void* dx, float* dWr, void* dWg, void* dWu, void* dWd,
+                const void* Wd, const void* dy, float aux_grad, float z_grad,
+                int64_t N, int64_t H, int64_t I, int E, int k, float aux_coef, float z_coef,
+                float capacity_factor, int flags, int dtype,
+                void* dx, float* dWr, void* dWg, void* dWu, void* dWd,
                 void* workspace, size_t workspace_bytes,
                 void* stream, void* const* stage_events);
 

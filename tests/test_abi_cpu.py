@@ -35,7 +35,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.topmoe_version() == 120
+    assert L.topmoe_version() == 130
 
 
 def test_strerror_covers_codes(L):
@@ -50,8 +50,9 @@ def test_workspace_sizes(L):
     assert B.raw_ffn_workspace_bytes(100, 768, 2432, B.DTYPE_FP32) >= 100 * 2432 * 4
     assert B.raw_ffn_workspace_bytes(16384, 2048, 6464, B.DTYPE_BF16) >= 16384 * 6464 * 2
     # moe: intermediate [N*k, I] plus the k-slots [N*k, H] (dtype) when k >= 2
+    # (the slots exist for k = 1 too: an expert capacity routes k = 1 through them)
     w1 = B.raw_moe_workspace_bytes(4096, 768, 2432, 4, 1, B.DTYPE_BF16)
-    assert 4096 * 2432 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 768 * 2
+    assert 4096 * 2432 * 2 + 4096 * 768 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 768 * 2 + 4096 * 8 + 65536
     w2 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_BF16)
     assert w2 >= 32768 * 2432 * 2 + 32768 * 768 * 2
     w3 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_FP32)
@@ -69,8 +70,8 @@ FAKE = 1 << 20  # 256-byte aligned, never dereferenced: validation fails first
 
 def moe_call(**over):
     a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, residual=None, N=8, H=64, I=64, E=4, k=2,
-             coef=0.01, flags=0, dtype=B.DTYPE_BF16, y=FAKE, topk_idx=FAKE, alpha=FAKE, aux=FAKE,
-             offsets=None,
+             coef=0.01, z_coef=0.0, capacity_factor=0.0, flags=0, dtype=B.DTYPE_BF16, y=FAKE,
+             topk_idx=FAKE, alpha=FAKE, aux=FAKE, z_loss=None, offsets=None,
              sorted_ids=None, ws=FAKE, ws_bytes=0, stream=None, events=None)
     a.update(over)
     return B.raw_moe_ffn_fwd(*a.values())
@@ -117,6 +118,11 @@ def test_moe_validation_codes(L):
     assert moe_call(ws_bytes=need, residual=FAKE + 8) == B.ERR_BAD_ARG
     assert moe_call(ws_bytes=need, flags=2) == B.ERR_BAD_ARG
     assert moe_call(ws_bytes=need, flags=-1) == B.ERR_BAD_ARG
+    assert moe_call(z_coef=-0.1) == B.ERR_BAD_ARG
+    assert moe_call(z_coef=float("inf")) == B.ERR_BAD_ARG
+    assert moe_call(capacity_factor=-1.0) == B.ERR_BAD_ARG
+    assert moe_call(capacity_factor=float("nan")) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, z_loss=FAKE + 2) == B.ERR_BAD_ARG
 
 
 def test_ffn_validation_codes(L):
@@ -141,9 +147,10 @@ def ffn_bwd_call(**over):
 
 
 def moe_bwd_call(**over):
-    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, aux_grad=1.0, N=8, H=64, I=64,
-             E=4, k=2, coef=0.01, flags=0, dtype=B.DTYPE_BF16, dx=FAKE, dWr=FAKE, dWg=FAKE,
-             dWu=FAKE, dWd=FAKE, ws=FAKE, ws_bytes=0, stream=None, events=None)
+    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, aux_grad=1.0, z_grad=1.0, N=8,
+             H=64, I=64, E=4, k=2, coef=0.01, z_coef=0.0, capacity_factor=0.0, flags=0,
+             dtype=B.DTYPE_BF16, dx=FAKE, dWr=FAKE, dWg=FAKE, dWu=FAKE, dWd=FAKE, ws=FAKE,
+             ws_bytes=0, stream=None, events=None)
     a.update(over)
     return B.raw_moe_ffn_bwd(*a.values())
 
@@ -192,6 +199,9 @@ def test_bwd_validation_codes(L):
     assert moe_bwd_call(aux_grad=float("nan")) == B.ERR_BAD_ARG
     assert moe_bwd_call(aux_grad=float("inf")) == B.ERR_BAD_ARG
     assert moe_bwd_call(flags=4) == B.ERR_BAD_ARG
+    assert moe_bwd_call(z_grad=float("nan")) == B.ERR_BAD_ARG
+    assert moe_bwd_call(z_coef=-1.0) == B.ERR_BAD_ARG
+    assert moe_bwd_call(capacity_factor=float("inf")) == B.ERR_BAD_ARG
     assert moe_bwd_call() == B.ERR_WORKSPACE_TOO_SMALL
     need = B.raw_moe_bwd_workspace_bytes(8, 64, 64, 4, 2, B.DTYPE_BF16)
     assert moe_bwd_call(ws_bytes=need - 1) == B.ERR_WORKSPACE_TOO_SMALL

@@ -42,14 +42,16 @@ SIGNATURES = {
     "ffn_swiglu_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp,
                               _vp]),
     "moe_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
-    "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _i32,
-                           _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _f32,
+                           _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                           _vp]),
     "ffn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "ffn_swiglu_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
                               _vp, _sz, _vp, _vp]),
     "moe_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
-    "moe_ffn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _i64, _i64, _i64, _i32, _i32, _f32,
-                           _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "moe_ffn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, _i64, _i32, _i32,
+                           _f32, _f32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                           _vp]),
     "topmoe_strerror": (ctypes.c_char_p, [_i32]),
     "topmoe_version": (_i32, []),
     "topmoe_events_create": (_i32, [_i32, _vp]),
@@ -108,11 +110,12 @@ def raw_ffn_swiglu_fwd(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, ws, ws_bytes,
                                     stream, events))
 
 
-def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, flags, dtype, y, topk_idx,
-                    alpha, aux, offsets, sorted_ids, ws, ws_bytes, stream, events) -> int:
-    return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, flags, dtype,
-                                 y, topk_idx, alpha, aux, offsets, sorted_ids, ws, ws_bytes,
-                                 stream, events))
+def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef, capacity_factor,
+                    flags, dtype, y, topk_idx, alpha, aux, z_loss, offsets, sorted_ids, ws,
+                    ws_bytes, stream, events) -> int:
+    return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef,
+                                 capacity_factor, flags, dtype, y, topk_idx, alpha, aux, z_loss,
+                                 offsets, sorted_ids, ws, ws_bytes, stream, events))
 
 
 def raw_ffn_bwd_workspace_bytes(N, H, I, dtype) -> int:
@@ -129,10 +132,12 @@ def raw_ffn_swiglu_bwd(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws,
                                     ws_bytes, stream, events))
 
 
-def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, N, H, I, E, k, coef, flags, dtype, dx, dWr,
-                    dWg, dWu, dWd, ws, ws_bytes, stream, events) -> int:
-    return int(lib().moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, N, H, I, E, k, coef, flags,
-                                 dtype, dx, dWr, dWg, dWu, dWd, ws, ws_bytes, stream, events))
+def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, N, H, I, E, k, coef, z_coef,
+                    capacity_factor, flags, dtype, dx, dWr, dWg, dWu, dWd, ws, ws_bytes, stream,
+                    events) -> int:
+    return int(lib().moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, N, H, I, E, k, coef,
+                                 z_coef, capacity_factor, flags, dtype, dx, dWr, dWg, dWu, dWd, ws,
+                                 ws_bytes, stream, events))
 
 
 class StageEvents:

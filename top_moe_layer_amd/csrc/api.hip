@@ -49,6 +49,16 @@ struct Stages {
   }
 };
 
+// Expert capacity ceil(capacity_factor * N * k / E); 0 = no capacity (also
+// when it could not be reached).
+int capacity_of(double capacity_factor, int64_t N, int k, int E) {
+  if (capacity_factor <= 0.0) return 0;
+  const double c = ceil(capacity_factor * double(N) * double(k) / double(E));
+  return c >= double(N) ? 0 : int(c);
+}
+
+bool nonneg_finite(float v) { return v >= 0.0f && !isinf(v); }
+
 #define TOPMOE_TRY(expr)                              \
   do {                                                \
     if ((expr) != hipSuccess) return TOPMOE_ERR_HIP;  \
@@ -58,7 +68,7 @@ struct Stages {
 
 extern "C" {
 
-int topmoe_version(void) { return 120; }
+int topmoe_version(void) { return 130; }
 
 const char* topmoe_strerror(int status) {
   switch (status) {
@@ -71,8 +81,8 @@ const char* topmoe_strerror(int status) {
     case TOPMOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_bytes() size";
     case TOPMOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case TOPMOE_ERR_BAD_ARG:
-      return "invalid argument (aux_coef negative or not finite, aux_grad not finite, unknown "
-             "flag bits, or a misaligned pointer)";
+      return "invalid argument (aux_coef, z_coef or capacity_factor negative or not finite, "
+             "aux_grad or z_grad not finite, unknown flag bits, or a misaligned pointer)";
   }
   return "unknown status";
 }
@@ -128,8 +138,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
 
 int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
                 const void* residual, int64_t N, int64_t H, int64_t I, int E, int k,
-                float aux_coef, int flags, int dtype,
-                void* y, int32_t* topk_idx, float* alpha, float* aux_loss,
+                float aux_coef, float z_coef, float capacity_factor, int flags, int dtype,
+                void* y, int32_t* topk_idx, float* alpha, float* aux_loss, float* z_loss,
                 int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
                 size_t workspace_bytes, void* stream, void* const* stage_events) {
   MoePlan pl;
@@ -139,16 +149,17 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   if (!Wr || !Wg || !Wu || !Wd || !aux_loss || !workspace ||
       (N > 0 && (!x || !y || !topk_idx || !alpha)))
     return TOPMOE_ERR_NULL_ARG;
-  if (!(aux_coef >= 0.0f) || isinf(aux_coef)) return TOPMOE_ERR_BAD_ARG;
+  if (!nonneg_finite(aux_coef) || !nonneg_finite(z_coef) || !nonneg_finite(capacity_factor))
+    return TOPMOE_ERR_BAD_ARG;
   if (flags & ~TOPMOE_MOE_RAW_TOPK_WEIGHTS) return TOPMOE_ERR_BAD_ARG;
   const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
       !aligned(Wd, 16) || !aligned(residual, 16) || !aligned(y, 16) || !aligned(topk_idx, 4) ||
-      !aligned(alpha, 4) ||
-      !aligned(aux_loss, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_token_ids, 4) ||
-      !aligned(workspace, 256))
+      !aligned(alpha, 4) || !aligned(aux_loss, 4) || !aligned(z_loss, 4) ||
+      !aligned(expert_offsets, 4) || !aligned(sorted_token_ids, 4) || !aligned(workspace, 256))
     return TOPMOE_ERR_BAD_ARG;
+  const int cap = capacity_of(capacity_factor, N, k, E);
 
   const Stages st{stage_events, static_cast<hipStream_t>(stream)};
   char* ws = static_cast<char*>(workspace);
@@ -157,13 +168,15 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(ws + pl.off_offsets);
   int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
   float* alpha_g = reinterpret_cast<float*>(ws + pl.off_alpha_g);
+  float* z_part = reinterpret_cast<float*>(ws + pl.off_zpart);
+  uint8_t* keep = cap > 0 ? reinterpret_cast<uint8_t*>(ws + pl.off_keep) : nullptr;
   void* h = ws + pl.off_h;
   void* slots = ws + pl.off_slots;
 
   if (N == 0) {
     for (int i = 0; i < TOPMOE_MOE_STAGES; ++i) {
       const Launch L = st.at(i);
-      if (i == 1) TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, L));
+      if (i == 1) TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, z_loss, L));
       TOPMOE_TRY(st.close(L));
     }
     return TOPMOE_OK;
@@ -172,13 +185,15 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   const Launch l0 = st.at(0);
   TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, renorm, pl.tb, pl.nblk,
-                           pl.router_mode, topk_idx, alpha, nullptr, count_part, psum_part, l0));
+                           pl.router_mode, topk_idx, alpha, nullptr, nullptr, count_part,
+                           psum_part, z_part, l0));
   TOPMOE_TRY(st.close(l0));
-  // 1: expert offsets, aux loss, stable scatter of entries into expert groups
+  // 1: expert offsets, aux (and z) loss, stable scatter of entries into expert
+  // groups (under a capacity: of the kept entries)
   const Launch l1 = st.at(1);
-  TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, alpha, pl.nblk, E, k, pl.tb, N,
-                            aux_coef, offsets, aux_loss, sorted_entry, alpha_g,
-                            sorted_token_ids, l1));
+  TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k, pl.tb,
+                            N, aux_coef, z_coef, cap, offsets, nullptr, aux_loss, z_loss,
+                            sorted_entry, alpha_g, sorted_token_ids, keep, l1));
   TOPMOE_TRY(st.close(l1));
   // 2: grouped gate/up GEMM + SiLU * up
   const Launch l2 = st.at(2);
@@ -188,19 +203,21 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
   TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
   TOPMOE_TRY(st.close(l2));
-  // 3: grouped down GEMM, alpha-scaled, into y (k == 1) or the k slots
+  // 3: grouped down GEMM, alpha-scaled, into y (k == 1, no capacity) or the slots
+  const bool direct = k == 1 && cap == 0;
   const Launch l3 = st.at(3);
   GemmParams dn{};
-  dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = k == 1 ? y : slots;
-  dn.residual = k == 1 ? residual : nullptr;  // k >= 2: added by the combine
+  dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = direct ? y : slots;
+  dn.residual = direct ? residual : nullptr;  // otherwise added by the combine
   dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha_g;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
-  TOPMOE_TRY(launch_gemm(k == 1 ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
+  TOPMOE_TRY(launch_gemm(direct ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
                          pl.down_mtiles, l3));
   TOPMOE_TRY(st.close(l3));
-  // 4: fixed-order combine of the k slots
+  // 4: fixed-order combine of the kept slots
   const Launch l4 = st.at(4);
-  if (k >= 2) TOPMOE_TRY(launch_combine(slots, topk_idx, residual, N, int(H), k, dtype, y, l4));
+  if (!direct)
+    TOPMOE_TRY(launch_combine(slots, topk_idx, keep, residual, N, int(H), k, dtype, y, l4));
   TOPMOE_TRY(st.close(l4));
   return TOPMOE_OK;
 }
@@ -315,18 +332,21 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
 }
 
 int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
-                const void* dy, float aux_grad, int64_t N, int64_t H, int64_t I, int E, int k,
-                float aux_coef, int flags, int dtype, void* dx, float* dWr, void* dWg,
-                void* dWu, void* dWd, void* workspace, size_t workspace_bytes, void* stream,
-                void* const* stage_events) {
+                const void* dy, float aux_grad, float z_grad, int64_t N, int64_t H, int64_t I,
+                int E, int k, float aux_coef, float z_coef, float capacity_factor, int flags,
+                int dtype, void* dx, float* dWr, void* dWg, void* dWu, void* dWd, void* workspace,
+                size_t workspace_bytes, void* stream, void* const* stage_events) {
   MoeBwdPlan pl;
   const int status = plan_moe_bwd(N, H, I, E, k, dtype, &pl);
   if (status != TOPMOE_OK) return status;
   if (!Wr || !Wg || !Wu || !Wd || !dWr || !dWg || !dWu || !dWd || !workspace ||
       (N > 0 && (!x || !dy || !dx)))
     return TOPMOE_ERR_NULL_ARG;
-  if (!(aux_coef >= 0.0f) || isinf(aux_coef) || !isfinite(aux_grad)) return TOPMOE_ERR_BAD_ARG;
+  if (!nonneg_finite(aux_coef) || !nonneg_finite(z_coef) || !nonneg_finite(capacity_factor) ||
+      !isfinite(aux_grad) || !isfinite(z_grad))
+    return TOPMOE_ERR_BAD_ARG;
   if (flags & ~TOPMOE_MOE_RAW_TOPK_WEIGHTS) return TOPMOE_ERR_BAD_ARG;
+  const int cap = capacity_of(capacity_factor, N, k, E);
   const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
@@ -343,6 +363,10 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + rp.off_sorted);
   float* alpha_g = reinterpret_cast<float*>(ws + rp.off_alpha_g);
   float* probs = reinterpret_cast<float*>(ws + pl.off_probs);
+  float* lse = reinterpret_cast<float*>(ws + pl.off_lse);
+  float* z_part = reinterpret_cast<float*>(ws + rp.off_zpart);
+  int32_t* counts_off = reinterpret_cast<int32_t*>(ws + rp.off_counts_off);
+  uint8_t* keep = cap > 0 ? reinterpret_cast<uint8_t*>(ws + rp.off_keep) : nullptr;
   int32_t* topk_idx = reinterpret_cast<int32_t*>(ws + pl.off_topk);
   float* alpha = reinterpret_cast<float*>(ws + pl.off_alpha);
   float* aux = reinterpret_cast<float*>(ws + pl.off_aux);
@@ -366,14 +390,16 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   const Launch l0 = st.at(0);
   if (N > 0)
     TOPMOE_TRY(launch_router(x, Wr, dtype, N, iH, E, k, renorm, rp.tb, rp.nblk, rp.router_mode,
-                             topk_idx, alpha, probs, count_part, psum_part, l0));
+                             topk_idx, alpha, probs, z_coef != 0.f ? lse : nullptr, count_part,
+                             psum_part, z_part, l0));
   TOPMOE_TRY(st.close(l0));
   const Launch l1 = st.at(1);
   if (N > 0)
-    TOPMOE_TRY(launch_permute(count_part, psum_part, topk_idx, alpha, rp.nblk, E, k, rp.tb, N,
-                              aux_coef, offsets, aux, sorted_entry, alpha_g, nullptr, l1));
+    TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, rp.nblk, E, k,
+                              rp.tb, N, aux_coef, z_coef, cap, offsets, counts_off, aux, nullptr,
+                              sorted_entry, alpha_g, nullptr, keep, l1));
   else
-    TOPMOE_TRY(launch_empty_route(E, offsets, aux, l1));
+    TOPMOE_TRY(launch_empty_route(E, offsets, aux, nullptr, l1));
   TOPMOE_TRY(st.close(l1));
   // 2: per-expert weight transposes: [Wg | Wu]^T [E, H, 2I], Wd^T [E, I, H]
   const Launch l2 = st.at(2);
@@ -436,13 +462,15 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
     const double scale = N > 0 ? double(aux_grad) * double(aux_coef) * double(E) /
                                      (double(N) * double(N))
                                : 0.0;
-    TOPMOE_TRY(launch_router_bwd(probs, topk_idx, dal, pl.nt_h, offsets, N, E, k, renorm,
-                                 float(scale), dr, l7));
+    const double zscale = N > 0 ? double(z_grad) * double(z_coef) * 2.0 / double(N) : 0.0;
+    TOPMOE_TRY(launch_router_bwd(probs, topk_idx, dal, pl.nt_h, counts_off, keep,
+                                 z_coef != 0.f ? lse : nullptr, N, E, k, renorm, float(scale),
+                                 float(zscale), dr, l7));
   }
   TOPMOE_TRY(st.close(l7));
   // 8: dx = sum of the slots (ascending expert) + W_r^T dr
   const Launch l8 = st.at(8);
-  TOPMOE_TRY(launch_combine_bwd(slots, topk_idx, dr, Wr, N, iH, E, k, dtype, dx, l8));
+  TOPMOE_TRY(launch_combine_bwd(slots, topk_idx, keep, dr, Wr, N, iH, E, k, dtype, dx, l8));
   TOPMOE_TRY(st.close(l8));
   // 9: dW_r = dr^T x
   const Launch l9 = st.at(9);

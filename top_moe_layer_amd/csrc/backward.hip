@@ -12,6 +12,8 @@
 //   (alpha = p_S when the weights are not renormalised: dp_{S_j} = d alpha_j)
 //   aux = coef E sum_e c_e (sum_t p_{t,e}) / N^2:  dp_{t,e} += daux coef E c_e / N^2
 //   softmax:  dr_e = p_e (dp_e - sum_e' p_e' dp_e');  dx_t += W_r^T dr_t;  dW_r += dr_t x_t^T.
+//   router z-loss z_coef * mean_t lse_t^2 (upstream dz):  dr_e += z_coef dz 2 lse_t p_e / N
+//   (d lse / d r = p); an entry dropped by an expert capacity passes no d alpha.
 // Every float reduction runs in a fixed order, so results repeat bit for bit.
 #include "device_common.h"
 #include "kernels.h"
@@ -191,8 +193,9 @@ __device__ __forceinline__ float group_sum(float v) {
 template <int EP>
 __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ dalpha_part, int nt, const int32_t* __restrict__ offsets,
-    int64_t N, int E, int k, bool renorm, float aux_scale, float* __restrict__ dr) {
+    const float* __restrict__ dalpha_part, int nt, const int32_t* __restrict__ counts_off,
+    const uint8_t* __restrict__ keep, const float* __restrict__ lse, int64_t N, int E, int k,
+    bool renorm, float aux_scale, float z_scale, float* __restrict__ dr) {
   constexpr int TPW = 64 / EP;
   const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6;
   const int u = lane / EP, e = lane - u * EP, base = u * EP;
@@ -206,8 +209,10 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
   float dal = 0.f;
   if (valid && e < k) {
     ej = topk_idx[t * k + e];
-    const float* dp = dalpha_part + (t * k + e) * int64_t(nt);
-    for (int c = 0; c < nt; ++c) dal += dp[c];
+    if (keep == nullptr || keep[t * k + e] != 0) {  // a dropped entry's output was not used
+      const float* dp = dalpha_part + (t * k + e) * int64_t(nt);
+      for (int c = 0; c < nt; ++c) dal += dp[c];
+    }
   }
   const float pj = __shfl(p, base + ej, 64);
   const bool slot = valid && e < k;
@@ -229,9 +234,11 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float v = __shfl(dps, base + j, 64);
     if (ex == e) dp = v;
   }
-  if (el && aux_scale != 0.f) dp += aux_scale * float(offsets[e + 1] - offsets[e]);
+  if (el && aux_scale != 0.f) dp += aux_scale * float(counts_off[e + 1] - counts_off[e]);
   const float dot = group_sum<EP>(el ? p * dp : 0.f);
-  if (el) dr[t * E + e] = p * (dp - dot);
+  float g = p * (dp - dot);
+  if (lse != nullptr && el) g = fmaf(z_scale * lse[t], p, g);
+  if (el) dr[t * E + e] = g;
 }
 
 // ------------------------------------------------------------------- combine
@@ -241,8 +248,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 template <typename T>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ slots, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ dr, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
-    T* __restrict__ dx) {
+    const uint8_t* __restrict__ keep, const float* __restrict__ dr,
+    const float* __restrict__ Wr, int64_t N, int H, int E, int k, T* __restrict__ dx) {
   constexpr int V = Pack<T>::n;
   const int hv = H / V;
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -261,6 +268,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       if (e > prev && e < best_e) { best_e = e; best_j = j; }
     }
     prev = best_e;
+    if (keep != nullptr && keep[t * k + best_j] == 0) continue;  // dropped: no expert term
     float v[V];
     ld16<T>(slots + (t * k + best_j) * H + h, v);
 #pragma unroll
@@ -408,13 +416,15 @@ __global__ __launch_bounds__(256) void dwr_reduce_kernel(const float* __restrict
 
 template <int EP>
 hipError_t launch_router_bwd_ep(const float* probs, const int32_t* topk_idx,
-                                const float* dalpha_part, int nt, const int32_t* offsets,
-                                int64_t N, int E, int k, bool renorm, float aux_scale, float* dr,
+                                const float* dalpha_part, int nt, const int32_t* counts_off,
+                                const uint8_t* keep, const float* lse, int64_t N, int E, int k,
+                                bool renorm, float aux_scale, float z_scale, float* dr,
                                 const Launch& s) {
   constexpr int TPB = 4 * (64 / EP);  // tokens per block
   const int64_t grid = (N + TPB - 1) / TPB;
   return launch_kernel(router_bwd_kernel<EP>, dim3(unsigned(grid)), dim3(256), 0, s, probs,
-                       topk_idx, dalpha_part, nt, offsets, N, E, k, renorm, aux_scale, dr);
+                       topk_idx, dalpha_part, nt, counts_off, keep, lse, N, E, k, renorm,
+                       aux_scale, z_scale, dr);
 }
 
 }  // namespace
@@ -438,12 +448,14 @@ hipError_t launch_gather_transpose(int dtype, const GatherTransposeJobs& jobs, i
 }
 
 hipError_t launch_router_bwd(const float* probs, const int32_t* topk_idx,
-                             const float* dalpha_part, int nt, const int32_t* offsets, int64_t N,
-                             int E, int k, bool renorm, float aux_scale, float* dr,
+                             const float* dalpha_part, int nt, const int32_t* counts_off,
+                             const uint8_t* keep, const float* lse, int64_t N, int E, int k,
+                             bool renorm, float aux_scale, float z_scale, float* dr,
                              const Launch& s) {
   if (N <= 0) return hipSuccess;
-#define TOPMOE_RB(EPV) \
-  return launch_router_bwd_ep<EPV>(probs, topk_idx, dalpha_part, nt, offsets, N, E, k, renorm, aux_scale, dr, s)
+#define TOPMOE_RB(EPV)                                                                       \
+  return launch_router_bwd_ep<EPV>(probs, topk_idx, dalpha_part, nt, counts_off, keep, lse, N, \
+                                   E, k, renorm, aux_scale, z_scale, dr, s)
   if (E <= 1) TOPMOE_RB(1);
   if (E <= 2) TOPMOE_RB(2);
   if (E <= 4) TOPMOE_RB(4);
@@ -454,18 +466,18 @@ hipError_t launch_router_bwd(const float* probs, const int32_t* topk_idx,
 #undef TOPMOE_RB
 }
 
-hipError_t launch_combine_bwd(const void* slots, const int32_t* topk_idx, const float* dr,
-                              const float* Wr, int64_t N, int H, int E, int k, int dtype,
-                              void* dx, const Launch& s) {
+hipError_t launch_combine_bwd(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
+                              const float* dr, const float* Wr, int64_t N, int H, int E, int k,
+                              int dtype, void* dx, const Launch& s) {
   const int64_t work = N * (H / (dtype == TOPMOE_DTYPE_FP32 ? 4 : 8));
   if (work <= 0) return hipSuccess;
   const int64_t grid = (work + 255) / 256;
   if (dtype == TOPMOE_DTYPE_FP32)
     return launch_kernel(combine_bwd_kernel<float>, dim3(unsigned(grid)), dim3(256), 0, s,
-                         static_cast<const float*>(slots), topk_idx, dr, Wr, N, H, E, k,
+                         static_cast<const float*>(slots), topk_idx, keep, dr, Wr, N, H, E, k,
                          static_cast<float*>(dx));
   return launch_kernel(combine_bwd_kernel<bf16_t>, dim3(unsigned(grid)), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(slots), topk_idx, dr, Wr, N, H, E, k,
+                       static_cast<const bf16_t*>(slots), topk_idx, keep, dr, Wr, N, H, E, k,
                        static_cast<bf16_t*>(dx));
 }
 

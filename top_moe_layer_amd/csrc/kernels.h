@@ -88,21 +88,28 @@ enum RouterMode {
   ROUTER_MODE_SPLIT = 1,  // one token per block, H split over the wavefronts
 };
 
+// probs [N, E] and lse [N] (logsumexp of the logits) are optional outputs for
+// the backward; z_part [blocks] always receives each block's sum of lse^2.
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
                          int k, bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                         float* alpha, float* probs,
-                         int32_t* count_part, float* psum_part, const Launch& s);
+                         float* alpha, float* probs, float* lse,
+                         int32_t* count_part, float* psum_part, float* z_part, const Launch& s);
 
+// cap <= 0: no expert capacity.  offsets: of the kept entries; counts_off
+// (optional): of every selection.  keep [N*k] (optional): 1 where the entry is kept.
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
-                          const int32_t* topk_idx, const float* alpha, int nblk, int E, int k,
-                          int tb, int64_t N, float coef, int32_t* offsets, float* aux,
-                          int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
+                          const float* z_part, const int32_t* topk_idx, const float* alpha,
+                          int nblk, int E, int k, int tb, int64_t N, float coef, float z_coef,
+                          int cap, int32_t* offsets, int32_t* counts_off, float* aux,
+                          float* z_loss, int32_t* sorted_entry, float* alpha_g,
+                          int32_t* sorted_tok, uint8_t* keep, const Launch& s);
+
+hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
+                          const void* residual, int64_t N, int H, int k, int dtype, void* y,
                           const Launch& s);
 
-hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const void* residual,
-                          int64_t N, int H, int k, int dtype, void* y, const Launch& s);
-
-hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s);
+hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, float* z_loss,
+                              const Launch& s);
 
 hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
                        int64_t mtiles, const Launch& s);
@@ -138,13 +145,16 @@ hipError_t launch_transpose(int dtype, const TransposeJobs& jobs, int max_tiles,
                             const Launch& s);
 hipError_t launch_gather_transpose(int dtype, const GatherTransposeJobs& jobs, int64_t ldo,
                                    const Launch& s);
+// counts_off [E+1]: exclusive prefix sums of every expert's selections (before
+// any capacity); keep / lse as from the routing (NULL: all kept / no z-loss).
 hipError_t launch_router_bwd(const float* probs, const int32_t* topk_idx,
-                             const float* dalpha_part, int nt, const int32_t* offsets, int64_t N,
-                             int E, int k, bool renorm, float aux_scale, float* dr,
+                             const float* dalpha_part, int nt, const int32_t* counts_off,
+                             const uint8_t* keep, const float* lse, int64_t N, int E, int k,
+                             bool renorm, float aux_scale, float z_scale, float* dr,
                              const Launch& s);
-hipError_t launch_combine_bwd(const void* slots, const int32_t* topk_idx, const float* dr,
-                              const float* Wr, int64_t N, int H, int E, int k, int dtype,
-                              void* dx, const Launch& s);
+hipError_t launch_combine_bwd(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
+                              const float* dr, const float* Wr, int64_t N, int H, int E, int k,
+                              int dtype, void* dx, const Launch& s);
 int dwr_chunks(int64_t N);
 hipError_t launch_dwr(const void* x, const float* dr, int64_t N, int H, int E, int dtype,
                       float* part, float* dWr, const Launch& s);

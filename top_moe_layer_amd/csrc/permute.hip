@@ -13,6 +13,14 @@
 //     copied beside it for the down projection's epilogue);
 //   * combine: y_t = sum of the k alpha-scaled expert rows (each in the output
 //     dtype) in ascending expert id, accumulated in fp32 and rounded once.
+// With an expert capacity C (the study notes' section 10 names it; the
+// standard form is a reading: each expert keeps the first C of its entries in
+// the dispatch order, i.e. ascending token), the scatter keeps an entry only
+// if its rank within its expert is below C: the expert groups, the offsets and
+// the token lists hold the kept entries (the lists end in -1), a flag per
+// entry records the choice for the combine, and aux still counts every
+// selection.  Block 0 also finishes the router z-loss from the router
+// blocks' partial sums.
 // All integer work is exact; the only float reductions run in a fixed order.
 #include "device_common.h"
 #include "kernels.h"
@@ -40,14 +48,18 @@ constexpr int kScanMax = 8192;
 
 __global__ __launch_bounds__(256) void permute_kernel(
     const int32_t* __restrict__ count_part, const float* __restrict__ psum_part,
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ alpha, int nblk, int G,
-    int E, int k, int tb, int64_t N, float coef, int32_t* __restrict__ offsets,
-    float* __restrict__ aux, int32_t* __restrict__ sorted_entry, float* __restrict__ alpha_g,
-    int32_t* __restrict__ sorted_tok) {
+    const float* __restrict__ z_part, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ alpha, int nblk, int G, int E, int k, int tb, int64_t N,
+    float coef, float z_coef, int cap, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ counts_off, float* __restrict__ aux, float* __restrict__ z_loss,
+    int32_t* __restrict__ sorted_entry, float* __restrict__ alpha_g,
+    int32_t* __restrict__ sorted_tok, uint8_t* __restrict__ keep) {
   __shared__ int s_c[kScanMax];
   __shared__ float s_p[kScanMax];  // block 0 only
   __shared__ int s_tot[64];
-  __shared__ int s_base[64];
+  __shared__ int s_base[64];   // the block's first rank within each expert
+  __shared__ int s_koff[64];   // kept-entry offset of each expert
+  __shared__ int s_ktot;
   __shared__ double s_ps[64];
   __shared__ int run[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -105,12 +117,20 @@ __global__ __launch_bounds__(256) void permute_kernel(
 
   if (wave == 0) {
     const int c = lane < E ? s_tot[lane] : 0;
-    const int incl = wave_inclusive_scan(c, lane);
-    if (lane < E) s_base[lane] += incl - c;  // expert offset + entries of earlier blocks
+    const int kc = (cap > 0 && c > cap) ? cap : c;  // entries the expert keeps
+    const int kincl = wave_inclusive_scan(kc, lane);
+    if (lane < E) s_koff[lane] = kincl - kc;
+    if (lane == E - 1) s_ktot = kincl;
     if (first) {
-      if (lane < E) offsets[lane] = incl - c;
-      if (lane == E - 1) offsets[E] = incl;
-      // aux = E * coef * sum_e c_e * (sum_t p_{t,e}) / N^2 (fixed summation order)
+      if (lane < E) offsets[lane] = kincl - kc;
+      if (lane == E - 1) offsets[E] = kincl;
+      if (counts_off != nullptr) {  // offsets of every selection (before any capacity)
+        const int incl = wave_inclusive_scan(c, lane);
+        if (lane < E) counts_off[lane] = incl - c;
+        if (lane == E - 1) counts_off[E] = incl;
+      }
+      // aux = E * coef * sum_e c_e * (sum_t p_{t,e}) / N^2 (fixed summation order;
+      // c_e counts every selection, kept or not)
       double term = lane < E ? double(c) * s_ps[lane] : 0.0;
       term = wave_sum(term);
       if (lane == 0) {
@@ -118,9 +138,19 @@ __global__ __launch_bounds__(256) void permute_kernel(
         if (coef != 0.f && N > 0) a = float(double(E) * double(coef) * term / (double(N) * double(N)));
         *aux = a;
       }
+      // z-loss = z_coef * (sum of the router blocks' logsumexp^2 sums) / N
+      if (z_loss != nullptr) {
+        double z = 0.0;
+        for (int b = lane; b < nblk; b += 64) z += double(z_part[b]);
+        z = wave_sum(z);
+        if (lane == 0) *z_loss = (z_coef != 0.f && N > 0) ? float(double(z_coef) * z / double(N)) : 0.f;
+      }
     }
   }
   __syncthreads();
+  if (first && sorted_tok != nullptr && cap > 0) {  // the lists end in -1 after the kept entries
+    for (int64_t i = s_ktot + tid; i < N * k; i += 256) sorted_tok[i] = -1;
+  }
 
   if (wave == 0) {
     const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -139,10 +169,15 @@ __global__ __launch_bounds__(256) void permute_kernel(
         todo &= ~m;
       }
       if (valid) {
-        const int dest = s_base[ex] + run[ex] + __popcll(peers & lt_mask);
-        sorted_entry[dest] = int32_t(ent);
-        alpha_g[dest] = al;
-        if (sorted_tok) sorted_tok[dest] = int32_t(ent / k);
+        const int rank = s_base[ex] + run[ex] + __popcll(peers & lt_mask);  // within expert ex
+        const bool kept = cap <= 0 || rank < cap;
+        if (kept) {
+          const int dest = s_koff[ex] + rank;
+          sorted_entry[dest] = int32_t(ent);
+          alpha_g[dest] = al;
+          if (sorted_tok) sorted_tok[dest] = int32_t(ent / k);
+        }
+        if (keep) keep[ent] = kept ? 1 : 0;
       }
       __builtin_amdgcn_wave_barrier();
       if (valid && (peers & lt_mask) == 0ull) run[ex] += __popcll(peers);
@@ -195,6 +230,7 @@ __device__ __forceinline__ void store16<bf16_t>(bf16_t* p, const float (&v)[8]) 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slots,
                                                       const int32_t* __restrict__ topk_idx,
+                                                      const uint8_t* __restrict__ keep,
                                                       const T* residual, int64_t N, int H, int k,
                                                       T* y) {
   constexpr int V = Vec16<T>::n;
@@ -219,6 +255,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
       if (e > prev && e < best_e) { best_e = e; best_j = j; }
     }
     prev = best_e;
+    if (keep != nullptr && keep[t * k + best_j] == 0) continue;  // dropped by the capacity
     float v[V];
     load16<T>(slots + (t * k + best_j) * H + h, v);
 #pragma unroll
@@ -227,44 +264,48 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
   store16<T>(y + t * H + h, acc);
 }
 
-__global__ void empty_route_kernel(int E, int32_t* offsets, float* aux) {
+__global__ void empty_route_kernel(int E, int32_t* offsets, float* aux, float* z_loss) {
   const int tid = threadIdx.x;
   if (tid <= E) offsets[tid] = 0;
   if (tid == 0) *aux = 0.f;
+  if (tid == 0 && z_loss != nullptr) *z_loss = 0.f;
 }
 
 }  // namespace
 
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
-                          const int32_t* topk_idx, const float* alpha, int nblk, int E, int k,
-                          int tb, int64_t N, float coef, int32_t* offsets, float* aux,
-                          int32_t* sorted_entry, float* alpha_g, int32_t* sorted_tok,
-                          const Launch& s) {
+                          const float* z_part, const int32_t* topk_idx, const float* alpha,
+                          int nblk, int E, int k, int tb, int64_t N, float coef, float z_coef,
+                          int cap, int32_t* offsets, int32_t* counts_off, float* aux,
+                          float* z_loss, int32_t* sorted_entry, float* alpha_g,
+                          int32_t* sorted_tok, uint8_t* keep, const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (int64_t(E) * nblk > kScanMax) return hipErrorInvalidValue;
   const int G = nblk > 256 ? (nblk + 255) / 256 : 1;  // router blocks per scatter block
   const int nsb = (nblk + G - 1) / G;
-  return launch_kernel(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part,
-                       topk_idx, alpha, nblk, G, E, k, tb, N, coef, offsets, aux, sorted_entry,
-                       alpha_g, sorted_tok);
+  return launch_kernel(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part, z_part,
+                       topk_idx, alpha, nblk, G, E, k, tb, N, coef, z_coef, cap, offsets,
+                       counts_off, aux, z_loss, sorted_entry, alpha_g, sorted_tok, keep);
 }
 
-hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const void* residual,
-                          int64_t N, int H, int k, int dtype, void* y, const Launch& s) {
+hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
+                          const void* residual, int64_t N, int H, int k, int dtype, void* y,
+                          const Launch& s) {
   const int64_t work = N * (H / (dtype == TOPMOE_DTYPE_FP32 ? 4 : 8));  // 16-byte pieces
   if (work <= 0) return hipSuccess;
   const int64_t grid = (work + 255) / 256;
   if (dtype == TOPMOE_DTYPE_FP32)
     return launch_kernel(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
-                         static_cast<const float*>(slots), topk_idx,
+                         static_cast<const float*>(slots), topk_idx, keep,
                          static_cast<const float*>(residual), N, H, k, static_cast<float*>(y));
   return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(slots), topk_idx,
+                       static_cast<const bf16_t*>(slots), topk_idx, keep,
                        static_cast<const bf16_t*>(residual), N, H, k, static_cast<bf16_t*>(y));
 }
 
-hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, const Launch& s) {
-  return launch_kernel(empty_route_kernel, dim3(1), dim3(128), 0, s, E, offsets, aux);
+hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, float* z_loss,
+                              const Launch& s) {
+  return launch_kernel(empty_route_kernel, dim3(1), dim3(128), 0, s, E, offsets, aux, z_loss);
 }
 
 }  // namespace topmoe

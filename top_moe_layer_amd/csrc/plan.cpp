@@ -202,11 +202,14 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_count_part = o; o = align_up(o + nbe * 4);
   q.off_psum_part = o;  o = align_up(o + nbe * 4);
   q.off_offsets = o;    o = align_up(o + size_t(E + 1) * 4);
+  q.off_counts_off = o; o = align_up(o + size_t(E + 1) * 4);
+  q.off_zpart = o;      o = align_up(o + size_t(q.nblk) * 4);
+  q.off_keep = o;       o = align_up(o + size_t(rows));
   q.off_sorted = o;     o = align_up(o + size_t(rows) * 4);
   q.off_alpha_g = o;    o = align_up(o + size_t(rows) * 4);
   q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);
-  q.off_slots = o;
-  if (k >= 2) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
+  q.off_slots = o;  // k-slots; also for k = 1 so that a capacity can drop rows
+  o = align_up(o + size_t(rows) * size_t(H) * q.elem);
   q.total = o == 0 ? kAlign : o;
   *p = q;
   return TOPMOE_OK;
@@ -271,6 +274,7 @@ int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBw
   // routing buffers first (the forward's own layout), then the backward's
   size_t o = r.off_h;
   q.off_probs = o; o = align_up(o + size_t(N) * size_t(E) * 4);
+  q.off_lse = o;   o = align_up(o + size_t(N) * 4);
   q.off_topk = o;  o = align_up(o + size_t(rows) * 4);
   q.off_alpha = o; o = align_up(o + size_t(rows) * 4);
   q.off_aux = o;   o = align_up(o + 4);

@@ -46,10 +46,14 @@ struct MoePlan {
   size_t off_count_part = 0;  // int32 [E, nblk] per-block expert counts
   size_t off_psum_part = 0;   // f32   [E, nblk] per-block sums of p
   size_t off_offsets = 0;     // int32 [E+1] expert offsets (when the caller passes none)
+  size_t off_counts_off = 0;  // int32 [E+1] offsets of every selection (before a capacity)
+  size_t off_zpart = 0;       // f32   [nblk] per-block sums of logsumexp^2 (z-loss)
+  size_t off_keep = 0;        // u8    [N*k] 1 where an entry survives the capacity
   size_t off_sorted = 0;      // int32 [N*k] entry ids (t*k + j) grouped by expert
   size_t off_alpha_g = 0;     // f32   [N*k] alpha of each grouped row
   size_t off_h = 0;           // elem  [N*k, I] SiLU(g)*u in grouped row order
-  size_t off_slots = 0;       // elem  [N*k, H] alpha-scaled expert outputs (k >= 2)
+  size_t off_slots = 0;       // elem  [N*k, H] alpha-scaled expert outputs (k >= 2, or
+                              // any k under an expert capacity)
   size_t total = 0;
 };
 
@@ -85,6 +89,7 @@ struct MoeBwdPlan {
   int nt_h = 0;           // column tiles of the dh GEMM: d alpha partials per entry
   int nchunk = 0;         // token chunks of the router-weight gradient
   size_t off_probs = 0;   // f32 [N, E] softmax
+  size_t off_lse = 0;     // f32 [N] logsumexp of the logits (z-loss backward)
   size_t off_topk = 0;    // i32 [N, k]
   size_t off_alpha = 0;   // f32 [N, k]
   size_t off_aux = 0;     // f32 [1] (forward value, unused)

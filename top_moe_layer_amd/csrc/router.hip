@@ -5,7 +5,9 @@
 // emits, for its tokens, the per-expert selection counts and the per-expert
 // sums of p that the offsets and load-balancing loss need (lesson 13, section
 // 1.6), stored expert-major ([E, blocks]) so the offset scan reads them
-// contiguously.
+// contiguously, and the sum over its tokens of logsumexp(r)^2 for the router
+// z-loss (named in the study notes' section 10 table; the squared
+// logsumexp is the standard form, a reading).
 //
 // Work layout: a lane owns x[h] for h = 4l + 256g (of the whole row or of one
 // quarter of it) and accumulates one partial dot product per expert; a
@@ -108,8 +110,9 @@ __device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, in
                                              bool renorm, int64_t t_first, int64_t t_end,
                                              int32_t* __restrict__ topk_idx,
                                              float* __restrict__ alpha,
-                                             float* __restrict__ probs, int* s_cnt,
-                                             float& psum) {
+                                             float* __restrict__ probs,
+                                             float* __restrict__ lse_out, int* s_cnt,
+                                             float& psum, float& zsum) {
   const bool expert_lane = lane < E;
   float p[TPW];
   uint64_t key[TPW];
@@ -119,6 +122,11 @@ __device__ __forceinline__ void route_tokens(const float (&r)[TPW], int lane, in
     const float m = group_max<EP>(ru);
     const float ex = expert_lane ? expf(ru - m) : 0.f;
     const float sum = group_sum<EP>(ex);
+    if (lane == 0 && t_first + u < t_end) {  // z-loss term: logsumexp of the logits, squared
+      const float lse = m + logf(sum);
+      zsum += lse * lse;
+      if (lse_out != nullptr) lse_out[t_first + u] = lse;
+    }
     p[u] = expert_lane ? ex / sum : 0.f;  // (lanes past EP see an all-zero group)
     if (t_first + u < t_end) {
       psum += p[u];
@@ -203,12 +211,14 @@ template <typename T, int EP>
 __global__ __launch_bounds__(64) void router_lds_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
     bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
-    float* __restrict__ probs, int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
+    float* __restrict__ probs, float* __restrict__ lse_out, int32_t* __restrict__ count_part,
+    float* __restrict__ psum_part, float* __restrict__ z_part) {
   constexpr int VE = 16 / int(sizeof(T));  // elements per 16-byte load
   constexpr int CI = 8;                    // loads per lane in flight per chunk
   extern __shared__ __attribute__((aligned(1024))) f32x4 s_w4[];  // [EP, H / 4], 1 KB-rounded
   __shared__ int s_cnt[64];
   __shared__ float s_pt[16][EP + 1];  // p of the pass's 16 tokens
+  __shared__ float s_z[16];           // their logsumexp^2 (z-loss)
   const int lane = threadIdx.x;
   const int part = lane & 3, tok = lane >> 2;
   const int h4 = H >> 2;
@@ -230,6 +240,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
   }
   s_cnt[lane] = 0;
   float psum = 0.f;  // lane e < E: sum of p_e over the block's tokens
+  float zsum = 0.f;  // lane 0: sum of logsumexp^2 over the block's tokens
   bool staged = false;
 
   for (int64_t tp = t0; tp < t1; tp += 16) {
@@ -301,6 +312,11 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
       acc[e] = e < E ? expf(acc[e] - m) : 0.f;
       s += acc[e];
     }
+    if (part == 0) {  // z-loss term: logsumexp of the logits, squared
+      const float lse = m + logf(s);
+      s_z[tok] = valid ? lse * lse : 0.f;
+      if (lse_out != nullptr && valid) lse_out[t] = lse;
+    }
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[e] = acc[e] / s;  // p (0 past E)
 
@@ -346,6 +362,9 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
     if (lane < E) {
       for (int u = 0; u < 16; ++u) psum += s_pt[u][lane];
     }
+    if (lane == 0) {
+      for (int u = 0; u < 16; ++u) zsum += s_z[u];
+    }
     __syncthreads();
   }
 
@@ -354,6 +373,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
     psum_part[o] = psum;
     count_part[o] = s_cnt[lane];
   }
+  if (lane == 0) z_part[blockIdx.x] = zsum;
 }
 
 // Mode split (large W_router, or few tokens): the four wavefronts of a block
@@ -366,7 +386,8 @@ template <typename T, int EP>
 __global__ __launch_bounds__(256) void router_split_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
     bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
-    float* __restrict__ probs, int32_t* __restrict__ count_part, float* __restrict__ psum_part) {
+    float* __restrict__ probs, float* __restrict__ lse_out, int32_t* __restrict__ count_part,
+    float* __restrict__ psum_part, float* __restrict__ z_part) {
   constexpr int CG = EP <= 16 ? 2 : 1;   // groups of 256 elements in flight per wavefront
   constexpr int EC = EP < 16 ? EP : 16;  // experts' W_router columns held at once
   __shared__ int s_cnt[64];
@@ -381,6 +402,7 @@ __global__ __launch_bounds__(256) void router_split_kernel(
   const f32x4* W4 = reinterpret_cast<const f32x4*>(Wr);
   const int h4 = H >> 2;
   float psum = 0.f;
+  float zsum = 0.f;  // thread 0: sum of logsumexp^2 over the block's tokens
   for (int64_t t = t0; t < t1; ++t) {
     float acc[EP];
 #pragma unroll
@@ -424,36 +446,42 @@ __global__ __launch_bounds__(256) void router_split_kernel(
     __syncthreads();
     if (wave == 0) {
       const float r[1] = {(s_part[0][lane] + s_part[1][lane]) + (s_part[2][lane] + s_part[3][lane])};
-      route_tokens<EP, 1>(r, lane, E, k, renorm, t, t1, topk_idx, alpha, probs, s_cnt, psum);
+      route_tokens<EP, 1>(r, lane, E, k, renorm, t, t1, topk_idx, alpha, probs, lse_out, s_cnt,
+                          psum, zsum);
     }
   }
   s_ps[wave][lane] = psum;  // only wave 0 routed: the other rows are zero
   __syncthreads();
   write_block_partials(tid, E, s_cnt, s_ps, count_part, psum_part);
+  if (tid == 0) z_part[blockIdx.x] = zsum;
 }
 
 template <typename T, int EP>
 hipError_t launch_router_ep(const T* x, const float* Wr, int64_t N, int H, int E, int k,
                             bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                            float* alpha, float* probs,
-                            int32_t* count_part, float* psum_part, const Launch& s) {
+                            float* alpha, float* probs, float* lse_out,
+                            int32_t* count_part, float* psum_part, float* z_part,
+                            const Launch& s) {
   if (mode == ROUTER_MODE_SPLIT)
     return launch_kernel(router_split_kernel<T, EP>, dim3(nblk), dim3(256), 0, s, x, Wr, N, H,
-                         E, k, renorm, tb, topk_idx, alpha, probs, count_part, psum_part);
+                         E, k, renorm, tb, topk_idx, alpha, probs, lse_out, count_part, psum_part,
+                         z_part);
   // W_router rounded up to whole 1 KB direct-to-LDS loads
   const unsigned lds = (unsigned(EP) * unsigned(H) * sizeof(float) + 1023u) & ~1023u;
   return launch_kernel(router_lds_kernel<T, EP>, dim3(nblk), dim3(64), lds, s, x, Wr, N, H, E, k,
-                       renorm, tb, topk_idx, alpha, probs, count_part, psum_part);
+                       renorm, tb, topk_idx, alpha, probs, lse_out, count_part, psum_part,
+                       z_part);
 }
 
 template <typename T>
 hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E, int k,
                            bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                           float* alpha, float* probs,
-                           int32_t* count_part, float* psum_part, const Launch& s) {
+                           float* alpha, float* probs, float* lse_out,
+                           int32_t* count_part, float* psum_part, float* z_part,
+                           const Launch& s) {
 #define TOPMOE_ROUTER(EPV)                                                                 \
   return launch_router_ep<T, EPV>(x, Wr, N, H, E, k, renorm, tb, nblk, mode, topk_idx,    \
-                                  alpha, probs, count_part, psum_part, s)
+                                  alpha, probs, lse_out, count_part, psum_part, z_part, s)
   if (E <= 1) TOPMOE_ROUTER(1);
   if (E <= 2) TOPMOE_ROUTER(2);
   if (E <= 4) TOPMOE_ROUTER(4);
@@ -468,14 +496,14 @@ hipError_t launch_router_t(const T* x, const float* Wr, int64_t N, int H, int E,
 
 hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, int H, int E,
                          int k, bool renorm, int tb, int nblk, int mode, int32_t* topk_idx,
-                         float* alpha, float* probs,
-                         int32_t* count_part, float* psum_part, const Launch& s) {
+                         float* alpha, float* probs, float* lse_out,
+                         int32_t* count_part, float* psum_part, float* z_part, const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (dtype == TOPMOE_DTYPE_FP32)
     return launch_router_t(static_cast<const float*>(x), Wr, N, H, E, k, renorm, tb, nblk, mode,
-                           topk_idx, alpha, probs, count_part, psum_part, s);
+                           topk_idx, alpha, probs, lse_out, count_part, psum_part, z_part, s);
   return launch_router_t(static_cast<const bf16_t*>(x), Wr, N, H, E, k, renorm, tb, nblk, mode,
-                         topk_idx, alpha, probs, count_part, psum_part, s);
+                         topk_idx, alpha, probs, lse_out, count_part, psum_part, z_part, s);
 }
 
 }  // namespace topmoe

@@ -103,11 +103,13 @@ class MoeOutput:
     aux_loss: torch.Tensor
     expert_offsets: Optional[torch.Tensor]
     sorted_token_ids: Optional[torch.Tensor]
+    z_loss: Optional[torch.Tensor] = None
 
 
 def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
                 Wd: torch.Tensor, k: int, aux_coef: float, *,
                 residual: Optional[torch.Tensor] = None, norm_topk_prob: bool = True,
+                z_coef: float = 0.0, capacity_factor: float = 0.0,
                 y: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
                 alpha: Optional[torch.Tensor] = None, aux_loss: Optional[torch.Tensor] = None,
                 expert_offsets: Optional[torch.Tensor] = None,
@@ -118,7 +120,10 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     Wd [E, H, I].  Returns y (x's shape), topk_idx / alpha [N, k], aux_loss [1]
     and, when ``return_lists``, expert_offsets [E+1] and sorted_token_ids [N*k].
     ``residual`` (x's shape and dtype, may be y itself) is added to y;
-    ``norm_topk_prob`` False keeps the raw top-k probabilities as alpha."""
+    ``norm_topk_prob`` False keeps the raw top-k probabilities as alpha;
+    ``z_coef`` > 0 also returns the router z-loss; ``capacity_factor`` > 0
+    caps each expert at ceil(factor * N * k / E) tokens (offsets and lists
+    then hold the kept tokens)."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -135,6 +140,7 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     topk_idx = new((N, k), torch.int32) if topk_idx is None else topk_idx
     alpha = new((N, k), torch.float32) if alpha is None else alpha
     aux_loss = new((1,), torch.float32) if aux_loss is None else aux_loss
+    z_loss = new((1,), torch.float32) if z_coef else None
     if return_lists:
         expert_offsets = new((E + 1,), torch.int32) if expert_offsets is None else expert_offsets
         sorted_token_ids = new((N * k,), torch.int32) if sorted_token_ids is None else sorted_token_ids
@@ -156,12 +162,14 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     ws = _workspace(nbytes, dev, workspace)
     flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
     st = B.raw_moe_ffn_fwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), N, H, I, E,
-                           k, float(aux_coef), flags, code, _ptr(y), _ptr(topk_idx), _ptr(alpha),
-                           _ptr(aux_loss), _ptr(expert_offsets), _ptr(sorted_token_ids),
+                           k, float(aux_coef), float(z_coef), float(capacity_factor), flags, code,
+                           _ptr(y), _ptr(topk_idx), _ptr(alpha), _ptr(aux_loss), _ptr(z_loss),
+                           _ptr(expert_offsets), _ptr(sorted_token_ids),
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
                            stage_events.ptr if stage_events is not None else None)
     B.check(st, "moe_ffn_fwd")
-    return MoeOutput(y.view(x.shape), topk_idx, alpha, aux_loss, expert_offsets, sorted_token_ids)
+    return MoeOutput(y.view(x.shape), topk_idx, alpha, aux_loss, expert_offsets, sorted_token_ids,
+                     z_loss)
 
 
 def ffn_bwd_workspace_bytes(N: int, H: int, I: int, dtype: torch.dtype) -> int:
@@ -223,12 +231,14 @@ def ffn_swiglu_bwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
 
 def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
                 Wd: torch.Tensor, dy: torch.Tensor, k: int, aux_coef: float, *,
-                aux_grad: float = 1.0, norm_topk_prob: bool = True,
+                aux_grad: float = 1.0, norm_topk_prob: bool = True, z_coef: float = 0.0,
+                z_grad: float = 1.0, capacity_factor: float = 0.0,
                 workspace: Optional[torch.Tensor] = None, stream=None,
                 stage_events: Optional[B.StageEvents] = None) -> MoeGrads:
-    """Gradients of the top-k MoE FFN (and of ``aux_grad`` * aux_loss) for the
-    upstream gradient dy: dx (x's shape), dWr [E, H] float32, dWg, dWu
-    [E, I, H], dWd [E, H, I].  The routing is recomputed from x and Wr."""
+    """Gradients of the top-k MoE FFN (and of ``aux_grad`` * aux_loss and
+    ``z_grad`` * z_loss) for the upstream gradient dy: dx (x's shape), dWr
+    [E, H] float32, dWg, dWu [E, I, H], dWd [E, H, I].  The routing (with the
+    same capacity) is recomputed from x and Wr."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -252,7 +262,8 @@ def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     ws = _workspace(nbytes, dev, workspace)
     flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
     st = B.raw_moe_ffn_bwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf),
-                           float(aux_grad), N, H, I, E, k, float(aux_coef), flags, code,
+                           float(aux_grad), float(z_grad), N, H, I, E, k, float(aux_coef),
+                           float(z_coef), float(capacity_factor), flags, code,
                            _ptr(dx), _ptr(dWr), _ptr(dWg), _ptr(dWu), _ptr(dWd), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(dev, stream),
                            stage_events.ptr if stage_events is not None else None)
