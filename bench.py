@@ -61,8 +61,9 @@ def gemm_source_hash():
 
 def recorded_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` measured with rocprofv3 counters and
-    stored in profiles/traffic.json; None if absent or if the GEMM sources
-    have changed since the counters were taken."""
+    stored in profiles/traffic.json (under "<workload>:bwd" for the backward);
+    None if absent or if the GEMM sources have changed since the counters were
+    taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
@@ -418,13 +419,13 @@ def main():
         achieved = dbytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(w.name, dom),
+                "traffic": recorded_traffic(w.name + (":bwd" if bwd else ""), dom),
                 "algorithmic_bytes": dbytes, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
     else:
         achieved = dflops / (dom_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": recorded_traffic(w.name, dom),
+                "traffic": recorded_traffic(w.name + (":bwd" if bwd else ""), dom),
                 "algorithmic_flops": dflops, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
 
     result = {
