@@ -17,6 +17,7 @@ BF16_SHAPES = [
     "256x128x4x2x64x4", "256x128x4x2x64x3", "256x256x4x2x64x4",
     "128x128x2x4x64x4", "256x128x4x2x128x2", "128x128x2x4x128x3",
     "128x128x2x4x128x4", "256x64x4x2x128x3", "256x128x4x2x128x3",
+    "64x128x2x4x128x3",
 ]
 # shapes whose LDS ring does not fit for the gate/up projection (two weight panels)
 GATEUP_TOO_BIG = {"128x128x2x2x128x3", "256x256x4x2x64x4", "128x128x2x4x128x4",
@@ -32,9 +33,13 @@ def env():
     return torch, dev, tm
 
 
+TILE_VARS = ("TOPMOE_GATEUP_TILE", "TOPMOE_DOWN_TILE", "TOPMOE_BWDGU_TILE", "TOPMOE_BWDDH_TILE",
+             "TOPMOE_WGU_TILE", "TOPMOE_WD_TILE")
+
+
 @pytest.fixture
 def shape_env():
-    saved = {k: os.environ.get(k) for k in ("TOPMOE_GATEUP_TILE", "TOPMOE_DOWN_TILE")}
+    saved = {k: os.environ.get(k) for k in TILE_VARS}
     yield
     for k, v in saved.items():
         if v is None:
@@ -67,3 +72,42 @@ def test_shape_dense_and_moe(env, shape_env, shape):
     torch.cuda.synchronize()
     check_routing(out, ref, w.k, w.E)
     assert rel_l2_per_token(y_to_f64(out.y), ref["y"]) <= TOL_Y["bf16"]
+
+
+# backward kinds: (override variable, shapes instantiated and valid for it)
+BWD_SHAPES = [("TOPMOE_BWDGU_TILE", s) for s in
+              ("256x128x4x2x128x2", "128x128x2x4x128x2", "256x64x4x2x128x2")] + \
+             [("TOPMOE_BWDDH_TILE", s) for s in ("128x128x2x4x128x3", "128x128x2x4x128x2")] + \
+             [("TOPMOE_WGU_TILE", s) for s in
+              ("128x256x2x4x128x2", "128x128x2x4x128x3", "128x128x2x2x128x3", "64x64x2x2x128x3")] + \
+             [("TOPMOE_WD_TILE", s) for s in
+              ("128x256x2x4x128x2", "128x128x2x4x128x3", "256x128x4x2x128x3", "128x128x2x2x128x3",
+               "64x64x2x2x128x3")]
+
+
+@pytest.mark.parametrize("var,shape", BWD_SHAPES)
+def test_bwd_shape(env, shape_env, var, shape):
+    """Each backward launch shape, forced through its override, on a MoE
+    backward with ragged tails against the oracle's gradients."""
+    import numpy as np
+
+    from oracle.cases import expected_bwd
+    from workloads import make_upstream
+    from gpu_util import TOL_GRAD, arr_to_dev, rel_l2_per_matrix
+
+    torch, dev, tm = env
+    os.environ[var] = shape
+    w = custom_workload(name="shape_bwd", N=700, H=192, I=320, E=5, k=2, coef=0.01, dtype="bf16",
+                        seed=13)
+    inp = make_case(w)
+    dy = make_upstream(inp)
+    ref = expected_bwd(w, inp, dy)
+    announce(f"moe_ffn_bwd {var}={shape} N=700 H=192 I=320 E=5 k=2")
+    d = to_dev(inp, dev)
+    g = tm.moe_ffn_bwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], arr_to_dev(dy, "bf16", dev),
+                       w.k, w.coef)
+    torch.cuda.synchronize()
+    assert rel_l2_per_token(y_to_f64(g.dx), ref["dx"]) <= TOL_GRAD["bf16"]
+    for n in ("dWg", "dWu", "dWd"):
+        err = rel_l2_per_matrix(getattr(g, n).double().cpu().numpy(), ref[n])
+        assert err <= TOL_GRAD["bf16"], (n, err)

@@ -98,16 +98,18 @@ const Cand kFp32[] = {
 
 // Few rows per group and long K: the projection streams weights from HBM.
 // MFMA work is then nearly free; what counts is the weight bytes in flight
-// per CU, which the 8-wavefront 128 x 128 tile with 128-byte rows maximises
-// (measured on the 32-token decode step: 30 us gate/up with a 3-deep ring and
-// 19 us down with a 4-deep ring, against 41 / 24 us with 64 x 64 tiles).
+// per CU.  The 8-wavefront tiles with 128-byte rows carry the most; with at
+// most 32 rows per expert a 64-row tile wastes less of each slice on clamped
+// duplicate x rows than a 128-row one (measured cold on the 32-token decode
+// step: gate/up 43.6 us against 45.3 us with 128 x 128; down 18.9 against
+// 22.4 us, the down tile's smaller LDS slice also fitting two blocks per CU).
 bool weight_streaming(int64_t M, int groups) { return M <= int64_t(groups) * 32; }
 
 }  // namespace
 
 GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 2);
-  GemmShape sh = weight_streaming(M, groups) ? GemmShape{128, 128, 2, 4, 128, 3}
+  GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
                                              : choose(kGateupBf16, 3, M, Nout, K, groups, 2);
   env_shape("TOPMOE_GATEUP_TILE", &sh);
   return sh;
@@ -115,7 +117,7 @@ GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int
 
 GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 1);
-  GemmShape sh = weight_streaming(M, groups) ? GemmShape{128, 128, 2, 4, 128, 4}
+  GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
                                              : choose(kDownBf16, 4, M, Nout, K, groups, 1);
   env_shape("TOPMOE_DOWN_TILE", &sh);
   return sh;
