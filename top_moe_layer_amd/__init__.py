@@ -32,4 +32,7 @@ def __getattr__(name):
                 "moe_bwd_workspace_bytes", "FfnGrads", "MoeGrads"):
         from . import ops
         return getattr(ops, name)
+    if name in ("swiglu_ffn", "moe_ffn"):
+        from . import autograd
+        return getattr(autograd, name)
     raise AttributeError(name)

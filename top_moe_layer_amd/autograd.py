@@ -1,0 +1,72 @@
+"""torch.autograd bindings: the forward and backward entry points of the C ABI
+as autograd Functions, so the FFN / MoE sub-layer trains inside a PyTorch
+graph.  Argument marshalling only: both passes run in the library's kernels
+(the backward recomputes the routing and the gate/up activations from the
+saved inputs)."""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import ops
+
+
+class _SwiGLUFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, Wg, Wu, Wd, residual):
+        ctx.save_for_backward(x, Wg, Wu, Wd)
+        ctx.has_residual = residual is not None
+        return ops.ffn_swiglu_fwd(x, Wg, Wu, Wd, residual=residual)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, Wg, Wu, Wd = ctx.saved_tensors
+        g = ops.ffn_swiglu_bwd(x, Wg, Wu, Wd, dy.contiguous())
+        return g.dx, g.dWg, g.dWu, g.dWd, (dy if ctx.has_residual else None)
+
+
+def swiglu_ffn(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
+               residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Differentiable dense SwiGLU FFN: y = residual + Wd (SiLU(Wg x) * Wu x)."""
+    return _SwiGLUFunction.apply(x, Wg, Wu, Wd, residual)
+
+
+class _MoEFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, Wr, Wg, Wu, Wd, residual, k, aux_coef, z_coef, capacity_factor,
+                norm_topk_prob):
+        out = ops.moe_ffn_fwd(x, Wr, Wg, Wu, Wd, k, aux_coef, residual=residual,
+                              norm_topk_prob=norm_topk_prob, z_coef=z_coef,
+                              capacity_factor=capacity_factor, return_lists=False)
+        ctx.save_for_backward(x, Wr, Wg, Wu, Wd)
+        ctx.cfg = (k, aux_coef, z_coef, capacity_factor, norm_topk_prob, residual is not None)
+        z = out.z_loss if out.z_loss is not None else torch.zeros(1, dtype=torch.float32,
+                                                                   device=x.device)
+        ctx.mark_non_differentiable(out.topk_idx, out.alpha)
+        return out.y, out.aux_loss, z, out.topk_idx, out.alpha
+
+    @staticmethod
+    def backward(ctx, dy, daux, dz, _didx, _dalpha):
+        x, Wr, Wg, Wu, Wd = ctx.saved_tensors
+        k, aux_coef, z_coef, capacity_factor, norm, has_res = ctx.cfg
+        if dy is None:
+            dy = torch.zeros_like(x)
+        # the C ABI takes the loss terms' upstream gradients as host scalars
+        aux_grad = float(daux.reshape(-1)[0]) if daux is not None else 0.0
+        z_grad = float(dz.reshape(-1)[0]) if dz is not None else 0.0
+        g = ops.moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy.contiguous(), k, aux_coef, aux_grad=aux_grad,
+                            norm_topk_prob=norm, z_coef=z_coef, z_grad=z_grad,
+                            capacity_factor=capacity_factor)
+        return (g.dx, g.dWr, g.dWg, g.dWu, g.dWd, (dy if has_res else None),
+                None, None, None, None, None)
+
+
+def moe_ffn(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
+            Wd: torch.Tensor, k: int, aux_coef: float, *, residual: Optional[torch.Tensor] = None,
+            z_coef: float = 0.0, capacity_factor: float = 0.0, norm_topk_prob: bool = True):
+    """Differentiable top-k MoE FFN.  Returns (y, aux_loss [1], z_loss [1],
+    topk_idx, alpha); y, aux_loss and z_loss carry gradients to x and every
+    weight (topk_idx and alpha are the router's choices, not differentiable)."""
+    return _MoEFunction.apply(x, Wr, Wg, Wu, Wd, residual, k, aux_coef, z_coef, capacity_factor,
+                              norm_topk_prob)
