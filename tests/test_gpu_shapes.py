@@ -17,11 +17,11 @@ BF16_SHAPES = [
     "256x128x4x2x64x4", "256x128x4x2x64x3", "256x256x4x2x64x4",
     "128x128x2x4x64x4", "256x128x4x2x128x2", "128x128x2x4x128x3",
     "128x128x2x4x128x4", "256x64x4x2x128x3", "256x128x4x2x128x3",
-    "64x128x2x4x128x3",
+    "64x128x2x4x128x3", "256x256x4x2x128x2",
 ]
 # shapes whose LDS ring does not fit for the gate/up projection (two weight panels)
 GATEUP_TOO_BIG = {"128x128x2x2x128x3", "256x256x4x2x64x4", "128x128x2x4x128x4",
-                  "256x128x4x2x128x3"}
+                  "256x128x4x2x128x3", "256x256x4x2x128x2"}
 
 
 @pytest.fixture(scope="module")

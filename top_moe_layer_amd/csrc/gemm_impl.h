@@ -949,7 +949,7 @@ struct ShapeLauncher<T, BM, BN, WM, WN, RB, S, KIND, true> {
   X(256, 128, 4, 2, 64, 4) X(256, 128, 4, 2, 64, 3) X(256, 256, 4, 2, 64, 4)              \
   X(128, 128, 2, 4, 64, 4) X(256, 128, 4, 2, 128, 2) X(128, 128, 2, 4, 128, 3)            \
   X(128, 128, 2, 4, 128, 4) X(256, 64, 4, 2, 128, 3) X(256, 128, 4, 2, 128, 3)            \
-  X(64, 128, 2, 4, 128, 3)
+  X(64, 128, 2, 4, 128, 3) X(256, 256, 4, 2, 128, 2)
 #define TOPMOE_GEMM_SHAPES_F32(X) X(128, 64, 2, 2, 128, 2) X(64, 64, 2, 2, 128, 3)
 // The backward's recomputed gate/up projection and its dh projection (their
 // LDS also holds one staged transposed output tile where it fits; the dh

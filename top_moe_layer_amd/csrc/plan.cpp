@@ -86,6 +86,7 @@ const Cand kGateupBf16[] = {
     {{256, 64, 4, 2, 128, 3}, 1033.0, 1},
 };
 const Cand kDownBf16[] = {
+    {{256, 256, 4, 2, 128, 2}, 1140.0, 1},
     {{256, 128, 4, 2, 128, 3}, 1093.0, 1},
     {{256, 256, 4, 2, 64, 4}, 1025.0, 1},
     {{128, 128, 2, 4, 128, 3}, 893.0, 1},
@@ -118,7 +119,7 @@ GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int
 GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 1);
   GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
-                                             : choose(kDownBf16, 4, M, Nout, K, groups, 1);
+                                             : choose(kDownBf16, 5, M, Nout, K, groups, 1);
   env_shape("TOPMOE_DOWN_TILE", &sh);
   return sh;
 }
