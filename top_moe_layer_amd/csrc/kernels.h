@@ -84,8 +84,9 @@ struct GemmParams {
 };
 
 enum RouterMode {
-  ROUTER_MODE_LDS = 0,    // W_router staged in LDS, one token per wavefront
+  ROUTER_MODE_LDS = 0,    // W_router staged in LDS, 16 tokens per wavefront pass
   ROUTER_MODE_SPLIT = 1,  // one token per block, H split over the wavefronts
+  ROUTER_MODE_LDS16 = 2,  // as LDS, 16 lanes per token: four wavefronts per block
 };
 
 // probs [N, E] and lse [N] (logsumexp of the logits) are optional outputs for

@@ -186,9 +186,13 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   int ep = 1;
   while (ep < E) ep *= 2;
   const bool lds_fits = int64_t(ep) * H * 4 <= 64 * 1024;
-  q.router_mode = (lds_fits && N >= 256) ? 0 : 1;
+  // With H a multiple of 16 loads (16 bytes each), 16 lanes per token in
+  // four-wavefront blocks (mode 2): four times the wavefronts for the same
+  // blocks.
+  const bool p16 = H % (16 * (16 / q.elem)) == 0;
+  q.router_mode = (lds_fits && N >= 256) ? (p16 ? 2 : 0) : 1;
   int64_t tb = 1;
-  if (q.router_mode == 0) {
+  if (q.router_mode != 1) {
     const int64_t passes = (N + 15) / 16;
     tb = 16 * ((passes + 1023) / 1024);
   }

@@ -38,7 +38,7 @@ struct MoePlan {
   int64_t rows = 0;        // N * k expert rows
   int tb = 0;              // router / scatter tokens per block
   int nblk = 0;            // router / scatter blocks
-  int router_mode = 0;     // 0: W_router in LDS, token per wavefront; 1: H split per token
+  int router_mode = 0;     // 0 / 2: W_router in LDS, 4 / 16 lanes per token; 1: H split per token
   GemmShape up, down;
   int64_t up_mtiles = 0;   // upper bound on grouped M tiles (gate/up)
   int64_t down_mtiles = 0; // upper bound on grouped M tiles (down)

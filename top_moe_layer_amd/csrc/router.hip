@@ -181,6 +181,20 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+// Sum over each group of P (4 or 16) consecutive lanes, the same value in
+// every lane of the group: the quad sum, then the two quads of each half row
+// (half-row mirror: lane i with 7 - i), then the two halves of the row (row
+// mirror: lane i with 15 - i).
+template <int P>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v = quad_sum(v);
+  if constexpr (P == 16) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  }
+  return v;
+}
+
 template <typename T>
 __device__ __forceinline__ void unpack16(const u32x4& q, float (&v)[16 / sizeof(T)]);
 template <>
@@ -197,18 +211,20 @@ __device__ __forceinline__ void unpack16<bf16_t>(const u32x4& q, float (&v)[8]) 
   }
 }
 
-// Mode LDS (EP * H * 4 <= 64 KB): one wavefront per block routes 16 tokens
-// per pass, four lanes per token.  W_router is copied into LDS once per block
-// with direct-to-LDS loads (all in flight together) and padded with zero rows
-// to EP experts.  Lane 4u + j of token u loads 16-byte pieces j, j + 4,
-// j + 8, ... of the token's row (the token's four lanes read 64 contiguous
-// bytes per load) and accumulates E partial logits against W_router columns
-// read from LDS (the 16 tokens share each read); a quad sum completes the
-// logits, and every lane of the quad then runs the softmax and the top-k of
-// its token on its own, with no cross-lane traffic.  The block owns tokens
-// [t0, t0 + tb).  Per-expert sums of p go through LDS in token order.
-template <typename T, int EP>
-__global__ __launch_bounds__(64) void router_lds_kernel(
+// Mode LDS (EP * H * 4 <= 64 KB): a block routes 16 tokens per pass with P
+// lanes per token: P = 4 (one wavefront), or P = 16 where H is a multiple of
+// 16 loads (four wavefronts, four tokens each: four times the lanes for the
+// same tokens).  W_router is copied into LDS once per block with
+// direct-to-LDS loads (all in flight together) and padded with zero rows to
+// EP experts.  Lane P u + j of token u loads 16-byte pieces j, j + P, j + 2P,
+// ... of the token's row (the token's lanes read 16 P contiguous bytes per
+// load) and accumulates E partial logits against W_router columns read from
+// LDS; a sum over the P lanes completes the logits, and every lane of the
+// group then runs the softmax and the top-k of its token on its own, with no
+// cross-lane traffic.  The block owns tokens [t0, t0 + tb).  Per-expert sums
+// of p go through LDS in token order.
+template <typename T, int EP, int P>
+__global__ __launch_bounds__(16 * P) void router_lds_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, int64_t N, int H, int E, int k,
     bool renorm, int tb, int32_t* __restrict__ topk_idx, float* __restrict__ alpha,
     float* __restrict__ probs, float* __restrict__ lse_out, int32_t* __restrict__ count_part,
@@ -219,10 +235,12 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
   __shared__ int s_cnt[64];
   __shared__ float s_pt[16][EP + 1];  // p of the pass's 16 tokens
   __shared__ float s_z[16];           // their logsumexp^2 (z-loss)
-  const int lane = threadIdx.x;
-  const int part = lane & 3, tok = lane >> 2;
+  constexpr int NT = 16 * P;  // threads: 16 tokens per pass
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int part = tid % P, tok = tid / P;
   const int h4 = H >> 2;
-  const int ni = H / (4 * VE);  // loads per lane per row (H is a multiple of 64)
+  const int ni = H / (P * VE);  // loads per lane per row (H is a multiple of P * VE)
   const int64_t t0 = int64_t(blockIdx.x) * tb;
   const int64_t t1 = (t0 + tb < N) ? t0 + tb : N;
 
@@ -231,16 +249,16 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
   const int nreal = E * h4, nall = EP * h4;
   {
     const f32x4* W4 = reinterpret_cast<const f32x4*>(Wr);
-    for (int c = 0; c * 64 < nreal; ++c) {
+    for (int c = wave; c * 64 < nreal; c += NT / 64) {
       const int i = c * 64 + lane;
       __builtin_amdgcn_global_load_lds(W4 + (i < nreal ? i : nreal - 1),
                                        (__attribute__((address_space(3))) void*)(s_w4 + c * 64),
                                        16, 0, 0);
     }
   }
-  s_cnt[lane] = 0;
-  float psum = 0.f;  // lane e < E: sum of p_e over the block's tokens
-  float zsum = 0.f;  // lane 0: sum of logsumexp^2 over the block's tokens
+  if (tid < 64) s_cnt[tid] = 0;
+  float psum = 0.f;  // thread e < E: sum of p_e over the block's tokens
+  float zsum = 0.f;  // thread 0: sum of logsumexp^2 over the block's tokens
   bool staged = false;
 
   for (int64_t tp = t0; tp < t1; tp += 16) {
@@ -256,7 +274,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
 #pragma unroll
       for (int c = 0; c < CI; ++c) {
         const int i = i0 + c < ni ? i0 + c : ni - 1;
-        xq[c] = *reinterpret_cast<const u32x4*>(xr + i * 4 * VE);
+        xq[c] = *reinterpret_cast<const u32x4*>(xr + i * P * VE);
       }
     };
     auto fma_chunk = [&](int i0, const u32x4(&xq)[CI]) {
@@ -265,7 +283,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
         if (i0 + c < ni) {  // wave-uniform
           float xv[VE];
           unpack16<T>(xq[c], xv);
-          const int q = (i0 + c) * VE + part * (VE / 4);  // f32x4 column of xv[0]
+          const int q = (i0 + c) * (P * VE / 4) + part * (VE / 4);  // f32x4 column of xv[0]
 #pragma unroll
           for (int e = 0; e < EP; ++e) {
 #pragma unroll
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
     if (CI < ni) load_chunk(CI, xb);
     if (!staged) {  // the first row loads are in flight: finish the W_router copy
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-      for (int i = nreal + lane; i < ((nall + 63) & ~63); i += 64)
+      for (int i = nreal + tid; i < ((nall + 63) & ~63); i += NT)
         s_w4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
       staged = true;
@@ -299,7 +317,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
       if (i0 + 3 * CI < ni) load_chunk(i0 + 3 * CI, xb);
     }
 #pragma unroll
-    for (int e = 0; e < EP; ++e) acc[e] = quad_sum(acc[e]);
+    for (int e = 0; e < EP; ++e) acc[e] = lane_group_sum<P>(acc[e]);
 
     // softmax over the E logits (fixed order), in the lane
     float m = -INFINITY;
@@ -342,7 +360,7 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
       for (int e = 0; e < EP; ++e)
         if (e < E && !((taken >> e) & 1ull) && acc[e] > bp) { bp = acc[e]; be = e; }
       taken |= 1ull << be;
-      if (valid && (r & 3) == part) {
+      if (valid && r % P == part) {
         topk_idx[t * k + r] = be;
         alpha[t * k + r] = renorm ? bp / (ssum + 1e-20f) : bp;
         atomicAdd(&s_cnt[be], 1);  // integer count: order-independent
@@ -353,27 +371,27 @@ __global__ __launch_bounds__(64) void router_lds_kernel(
 #pragma unroll
       for (int e = 0; e < EP; ++e) s_pt[tok][e] = valid ? acc[e] : 0.f;
     }
-    if (probs != nullptr && valid) {  // the softmax for the backward pass (lane part: e = part mod 4)
+    if (probs != nullptr && valid) {  // the softmax for the backward pass (lane part: e = part mod P)
 #pragma unroll
       for (int e = 0; e < EP; ++e)
-        if (e < E && (e & 3) == part) probs[t * E + e] = acc[e];
+        if (e < E && e % P == part) probs[t * E + e] = acc[e];
     }
     __syncthreads();
-    if (lane < E) {
-      for (int u = 0; u < 16; ++u) psum += s_pt[u][lane];
+    if (tid < E) {
+      for (int u = 0; u < 16; ++u) psum += s_pt[u][tid];
     }
-    if (lane == 0) {
+    if (tid == 0) {
       for (int u = 0; u < 16; ++u) zsum += s_z[u];
     }
     __syncthreads();
   }
 
-  if (lane < E) {
-    const int64_t o = int64_t(lane) * gridDim.x + blockIdx.x;
+  if (tid < E) {
+    const int64_t o = int64_t(tid) * gridDim.x + blockIdx.x;
     psum_part[o] = psum;
-    count_part[o] = s_cnt[lane];
+    count_part[o] = s_cnt[tid];
   }
-  if (lane == 0) z_part[blockIdx.x] = zsum;
+  if (tid == 0) z_part[blockIdx.x] = zsum;
 }
 
 // Mode split (large W_router, or few tokens): the four wavefronts of a block
@@ -468,8 +486,12 @@ hipError_t launch_router_ep(const T* x, const float* Wr, int64_t N, int H, int E
                          z_part);
   // W_router rounded up to whole 1 KB direct-to-LDS loads
   const unsigned lds = (unsigned(EP) * unsigned(H) * sizeof(float) + 1023u) & ~1023u;
-  return launch_kernel(router_lds_kernel<T, EP>, dim3(nblk), dim3(64), lds, s, x, Wr, N, H, E, k,
-                       renorm, tb, topk_idx, alpha, probs, lse_out, count_part, psum_part,
+  if (mode == ROUTER_MODE_LDS16)
+    return launch_kernel(router_lds_kernel<T, EP, 16>, dim3(nblk), dim3(256), lds, s, x, Wr, N, H,
+                         E, k, renorm, tb, topk_idx, alpha, probs, lse_out, count_part,
+                         psum_part, z_part);
+  return launch_kernel(router_lds_kernel<T, EP, 4>, dim3(nblk), dim3(64), lds, s, x, Wr, N, H, E,
+                       k, renorm, tb, topk_idx, alpha, probs, lse_out, count_part, psum_part,
                        z_part);
 }
 
