@@ -244,6 +244,8 @@ def main():
     cache.add_argument("--warm", action="store_const", const="warm", dest="cache",
                        help="back-to-back steps with warm caches (default otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timing (extra field graph_ms_per_step)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -303,27 +305,27 @@ def main():
             names = tm.FFN_BWD_STAGE_NAMES
             make_events = lambda: tm.StageEvents(tm.FFN_BWD_STAGES)
 
-            def step(ev=None):
+            def step(ev=None, st=stream):
                 tm.ffn_swiglu_bwd(d["x"], d["Wg"], d["Wu"], d["Wd"], dyd, workspace=ws,
-                                  stream=stream, stage_events=ev)
+                                  stream=st, stage_events=ev)
         else:
             ws = torch.empty(tm.moe_bwd_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8,
                              device=dev)
             names = tm.MOE_BWD_STAGE_NAMES
             make_events = lambda: tm.StageEvents(tm.MOE_BWD_STAGES)
 
-            def step(ev=None):
+            def step(ev=None, st=stream):
                 tm.moe_ffn_bwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], dyd, k, w.coef,
-                               norm_topk_prob=w.norm_topk_prob, workspace=ws, stream=stream,
+                               norm_topk_prob=w.norm_topk_prob, workspace=ws, stream=st,
                                stage_events=ev)
     elif w.kind == "dense":
         ws = torch.empty(tm.ffn_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
         y = torch.empty((N, H), dtype=tdt, device=dev)
         names = tm.FFN_STAGE_NAMES
 
-        def step(ev=None):
+        def step(ev=None, st=stream):
             tm.ffn_swiglu_fwd(d["x"], d["Wg"], d["Wu"], d["Wd"], y=y, workspace=ws,
-                              stream=stream, stage_events=ev)
+                              stream=st, stage_events=ev)
         make_events = lambda: tm.StageEvents(tm.FFN_STAGES)
     else:
         ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8, device=dev)
@@ -334,10 +336,10 @@ def main():
         offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         names = tm.MOE_STAGE_NAMES
 
-        def step(ev=None):
+        def step(ev=None, st=stream):
             tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef, y=y,
                            topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
-                           return_lists=False, workspace=ws, stream=stream, stage_events=ev)
+                           return_lists=False, workspace=ws, stream=st, stage_events=ev)
         make_events = lambda: tm.StageEvents(tm.MOE_STAGES)
 
     flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if cold else None
@@ -372,6 +374,24 @@ def main():
             tot += s0.elapsed_time(s1)
         ms_step = tot / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step")
+
+    # The same step captured once in a HIP graph and replayed K times (warm
+    # runs only): the launch overhead that a caller capturing its loop saves.
+    graph_ms = None
+    if not cold and not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(None, torch.cuda.current_stream(dev))
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del g
+        log(f"graph replays: {graph_ms:.4f} ms/step")
 
     # Per-kernel durations: the same K steps again, each with its own start /
     # stop events per stage, stamped by the kernel dispatches themselves
@@ -448,6 +468,7 @@ def main():
         "mfma_frac": round(tflops / peak, 4),
         "stages_ms": stages_ms,
         "kernel_ms_per_step": pct(per_step.sum(axis=1)),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "experts_touched": touched,
         "pass": args.which,
         "roofline": roof,
