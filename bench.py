@@ -244,6 +244,8 @@ def main():
     cache.add_argument("--warm", action="store_const", const="warm", dest="cache",
                        help="back-to-back steps with warm caches (default otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold-too", dest="cold_too", action="store_false",
+                    help="warm runs: skip the extra cold-cache timing (field cold_ms_per_step)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing (extra field graph_ms_per_step)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
@@ -342,7 +344,7 @@ def main():
                            return_lists=False, workspace=ws, stream=st, stage_events=ev)
         make_events = lambda: tm.StageEvents(tm.MOE_STAGES)
 
-    flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if cold else None
+    flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if cold or args.cold_too else None
 
     def flush():  # evict L2 and the Infinity Cache with clean lines
         flush_buf.sum()
@@ -374,6 +376,23 @@ def main():
             tot += s0.elapsed_time(s1)
         ms_step = tot / args.steps
     log(f"timed {args.steps} steps: {ms_step:.4f} ms/step")
+
+    # Warm workloads: the same K steps with L2 and the Infinity Cache flushed
+    # before each one (events around the step only), reported alongside.
+    cold_ms = None
+    if not cold and args.cold_too:
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for _ in range(args.steps):
+            flush()
+            s0.record(stream)
+            step()
+            s1.record(stream)
+            s1.synchronize()
+            tot += s0.elapsed_time(s1)
+        cold_ms = tot / args.steps
+        log(f"cold steps: {cold_ms:.4f} ms/step")
 
     # The same step captured once in a HIP graph and replayed K times (warm
     # runs only): the launch overhead that a caller capturing its loop saves.
@@ -469,6 +488,7 @@ def main():
         "stages_ms": stages_ms,
         "kernel_ms_per_step": pct(per_step.sum(axis=1)),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
         "experts_touched": touched,
         "pass": args.which,
         "roofline": roof,

@@ -292,12 +292,14 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 
 // ------------------------------------------------------- router weight grad
 // dW_r[e][h] = sum_t dr[t][e] x[t][h], split over token chunks of kDwrChunk
-// (256): block (512-column block, chunk) has four wavefronts of 64 tokens
-// each; a lane owns 8 consecutive columns and 8 experts at a time.  The four
-// wavefronts' sums meet in LDS in a fixed order and the block writes one
-// partial per chunk; a second kernel sums the chunks (again in a fixed order).
+// (64: enough blocks to fill the chip at a few thousand tokens): block
+// (512-column block, chunk) has four wavefronts of 16 tokens each; a lane
+// owns 8 consecutive columns and 8 experts at a time.  The four wavefronts'
+// sums meet in LDS in a fixed order and the block writes one partial per
+// chunk; a second kernel sums the chunks (again in a fixed order).
 constexpr int kDwrWaves = 4;
-static_assert(kDwrChunk == 64 * kDwrWaves, "a wavefront per 64 tokens of a chunk");
+constexpr int kDwrTpw = kDwrChunk / kDwrWaves;  // tokens per wavefront
+static_assert(kDwrTpw % 4 == 0, "whole groups of four rows per wavefront");
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
@@ -324,8 +326,8 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ 
   const bool hok = h < H;
   const int64_t t0 = int64_t(blockIdx.y) * kDwrChunk;
   const int nt = int(N - t0 < kDwrChunk ? N - t0 : kDwrChunk);
-  const int tw0 = wave * 64;                                  // this wave's tokens in the chunk
-  const int ntw = nt - tw0 < 0 ? 0 : (nt - tw0 < 64 ? nt - tw0 : 64);
+  const int tw0 = wave * kDwrTpw;  // this wave's tokens in the chunk
+  const int ntw = nt - tw0 < 0 ? 0 : (nt - tw0 < kDwrTpw ? nt - tw0 : kDwrTpw);
   for (int e0 = 0; e0 < E; e0 += 8) {
     __syncthreads();  // the previous expert chunk's LDS reads are done
     for (int i = tid; i < kDwrChunk * 8; i += 256) {

@@ -9,7 +9,7 @@
 namespace topmoe {
 
 constexpr size_t kAlign = 256;
-constexpr int kDwrChunk = 256;  // tokens per partial of the router-weight gradient
+constexpr int kDwrChunk = 64;   // tokens per partial of the router-weight gradient
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
