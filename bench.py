@@ -244,8 +244,9 @@ def main():
     cache.add_argument("--warm", action="store_const", const="warm", dest="cache",
                        help="back-to-back steps with warm caches (default otherwise)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-cold-too", dest="cold_too", action="store_false",
-                    help="warm runs: skip the extra cold-cache timing (field cold_ms_per_step)")
+    ap.add_argument("--cold-too", action="store_true",
+                    help="warm runs: also time the steps with cold caches (field cold_ms_per_step; "
+                         "off by default so that every kernel of a default run is a warm one)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing (extra field graph_ms_per_step)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
