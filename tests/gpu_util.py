@@ -135,3 +135,47 @@ def rel_l2_per_matrix(got: np.ndarray, ref: np.ndarray) -> float:
             continue
         worst = max(worst, float(np.linalg.norm(g - r) / d))
     return worst
+
+
+
+def bf16_of(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (nearest even) and widen them back."""
+    from workloads.gen import round_to, to_f64
+    return to_f64(round_to(np.asarray(a, dtype=np.float64), "bf16"), "bf16")
+
+
+def dwr_bf16_h_shift(f: dict, route: dict, dy64: np.ndarray, k: int,
+                     norm_topk_prob: bool) -> np.ndarray:
+    """The part of the bf16 path's router-weight gradient [E, H] that comes
+    from recomputing g and u in bf16: its d alpha_{t,j} is dh_raw . SiLU(g~) u~
+    with g~, u~ the bf16-rounded projections (the backward's stored pairs)
+    instead of dh_raw . SiLU(g) u.  That change passes linearly through the
+    renormalisation (d p_S = d alpha / Z - (d alpha . p_S) / Z^2), the softmax
+    (d r = p (d p - p . d p)) and d W_r = d r^T x, so the shift is exact given
+    the rounding.  Where d alpha cancels (few tokens per expert), this shift
+    dominates the difference to the fp64 oracle."""
+    p, idx = route["p"], route["topk_idx"]
+    keep = route.get("keep")
+    N, E = p.shape
+    ddal = np.zeros((N, k))
+    for t in range(N):
+        for j in range(k):
+            if keep is not None and not keep[t, j]:
+                continue
+            e = idx[t, j]
+            g = f["Wg"][e] @ f["x"][t]
+            u = f["Wu"][e] @ f["x"][t]
+            gb, ub = bf16_of(g), bf16_of(u)
+            silu = lambda z: z / (1.0 + np.exp(-z))
+            dh_raw = f["Wd"][e].T @ dy64[t]
+            ddal[t, j] = dh_raw @ (silu(gb) * ub - silu(g) * u)
+    ps = np.take_along_axis(p, idx, axis=1)
+    if norm_topk_prob:
+        Z = ps.sum(axis=1, keepdims=True) + 1e-20
+        dps = ddal / Z - (ddal * ps).sum(axis=1, keepdims=True) / Z ** 2
+    else:
+        dps = ddal
+    dp = np.zeros_like(p)
+    np.put_along_axis(dp, idx, dps, axis=1)
+    dr = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return dr.T @ f["x"]
