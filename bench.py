@@ -1,7 +1,7 @@
 """Benchmark of the MiniMind FFN / top-k MoE forward (or backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cold | --warm]
-                    [--pass fwd | bwd]
+                    [--pass fwd | bwd | train]
 
 A step is one full forward (every kernel of the path) over one batch of
 synthetic inputs already resident in device memory.  W untimed steps, then
@@ -17,7 +17,9 @@ timed on a bounded sample of the same workload (rank 0, one GPU only).
 
 With ``--pass bwd`` a step is one backward instead (routing and gate/up
 activations recomputed, then every gradient); its line carries its own metric
-and the same roofline / cpu_baseline objects.
+and the same roofline / cpu_baseline objects.  With ``--pass train`` a step
+is one training step: the training forward, which keeps g, u for the
+backward, then the backward that takes them instead of recomputing them.
 
 Prints ONE JSON line.
 """
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "FFN/MoE fwd tokens/s + TFLOP/s (% bf16 MFMA peak) / GB/s (% HBM) on 1 GPU"
 METRIC_BWD = "FFN/MoE bwd tokens/s + TFLOP/s (% bf16 MFMA peak) on 1 GPU"
+METRIC_TRAIN = "FFN/MoE train step (fwd + bwd) tokens/s + TFLOP/s (% bf16 MFMA peak) on 1 GPU"
 DEFAULT_WORKLOAD = "moe_top1_n4096_h768_e4"
 
 # MI355X published peaks
@@ -182,6 +185,20 @@ def cpu_baseline_bwd(w, inputs, dy, budget_s=10.0):
     }
 
 
+def cpu_baseline_train(w, inputs, dy):
+    """A training step of the oracle: its forward and its backward timed as in
+    the other passes (about 6 s each), the per-token times added."""
+    f = cpu_baseline(w, inputs, budget_s=6.0)
+    b = cpu_baseline_bwd(w, inputs, dy, budget_s=6.0)
+    return {
+        "value": 1.0 / (1.0 / f["value"] + 1.0 / b["value"]),
+        "unit": "tokens/s",
+        "cores": max(f["cores"], b["cores"]),
+        "kind": "oracle",
+        "sample": f"forward: {f['sample']}; backward: {b['sample']}; per-token times added",
+    }
+
+
 def cpu_baseline(w, inputs, budget_s=10.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
     the first n tokens (n grown by 4x until one pass takes a quarter of the
@@ -231,6 +248,20 @@ def cpu_baseline(w, inputs, budget_s=10.0):
     }
 
 
+class _EventPair:
+    """The forward's and the backward's stage events of one training step."""
+
+    def __init__(self, a, b):
+        self.a, self.b = a, b
+
+    def elapsed_ms(self):
+        return list(self.a.elapsed_ms()) + list(self.b.elapsed_ms())
+
+    def close(self):
+        self.a.close()
+        self.b.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,8 +280,9 @@ def main():
                          "off by default so that every kernel of a default run is a warm one)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing (extra field graph_ms_per_step)")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward (default) or the backward")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "train"), default="fwd",
+                    help="time the forward (default), the backward, or a training step (the "
+                         "forward keeping g, u + the backward taking them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -280,6 +312,7 @@ def main():
         return
     w = get(args.workload)
     bwd = args.which == "bwd"
+    train = args.which == "train"
     log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype} {args.which}")
     decode_like = w.kind == "moe" and w.N * w.k <= 256
     # Decode-sized steps stream their weights; with warm caches part of them
@@ -298,9 +331,46 @@ def main():
     tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
     stream = torch.cuda.current_stream(dev)
-    dy_host = make_upstream(inputs) if bwd else None
+    dy_host = make_upstream(inputs) if (bwd or train) else None
 
-    if bwd:
+    if train:
+        dyd = dev_t(dy_host)
+        y = torch.empty((N, H), dtype=tdt, device=dev)
+        if w.kind == "dense":
+            ws = torch.empty(tm.ffn_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
+            saved = torch.empty(tm.ffn_bwd_workspace_bytes(N, H, I, tdt), dtype=torch.uint8,
+                                device=dev)
+            fnames, bnames = tm.FFN_STAGE_NAMES, tm.FFN_BWD_STAGE_NAMES
+            nf, nb = tm.FFN_STAGES, tm.FFN_BWD_STAGES
+
+            def step(ev=None, st=stream):
+                tm.ffn_swiglu_fwd(d["x"], d["Wg"], d["Wu"], d["Wd"], y=y, workspace=ws,
+                                  saved=saved, stream=st, stage_events=ev and ev.a)
+                tm.ffn_swiglu_bwd(d["x"], d["Wg"], d["Wu"], d["Wd"], dyd, workspace=saved,
+                                  from_saved=True, stream=st, stage_events=ev and ev.b)
+        else:
+            ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8,
+                             device=dev)
+            saved = torch.empty(tm.moe_bwd_workspace_bytes(N, H, I, E, k, tdt),
+                                dtype=torch.uint8, device=dev)
+            idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+            alpha = torch.empty((N, k), dtype=torch.float32, device=dev)
+            aux = torch.empty((1,), dtype=torch.float32, device=dev)
+            offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+            fnames, bnames = tm.MOE_STAGE_NAMES, tm.MOE_BWD_STAGE_NAMES
+            nf, nb = tm.MOE_STAGES, tm.MOE_BWD_STAGES
+
+            def step(ev=None, st=stream):
+                tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef, y=y,
+                               topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
+                               norm_topk_prob=w.norm_topk_prob, return_lists=False,
+                               workspace=ws, saved=saved, stream=st, stage_events=ev and ev.a)
+                tm.moe_ffn_bwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], dyd, k, w.coef,
+                               norm_topk_prob=w.norm_topk_prob, workspace=saved,
+                               from_saved=True, stream=st, stage_events=ev and ev.b)
+        names = ["fwd:" + n for n in fnames] + ["bwd:" + n for n in bnames]
+        make_events = lambda: _EventPair(tm.StageEvents(nf), tm.StageEvents(nb))
+    elif bwd:
         dyd = dev_t(dy_host)
         new = lambda shape, dt_=tdt: torch.empty(shape, dtype=dt_, device=dev)
         if w.kind == "dense":
@@ -434,7 +504,17 @@ def main():
 
     units = stage_units(w)
     touched = None
-    if bwd:
+    if train:
+        units = {**{"fwd:" + n: v for n, v in stage_units(w).items()},
+                 **{"bwd:" + n: v for n, v in stage_units_bwd(w).items()}}
+        el = w.elem_bytes()
+        rows = N * k
+        ex = 1 if w.kind == "dense" else min(E, rows)
+        # the gate/up projection also writes g, u (kept) besides h
+        units["fwd:gateup_gemm"] = (4.0 * rows * H * I,
+                                    N * H * el + 2 * ex * I * H * el + 3 * rows * I * el)
+        units["bwd:gu_gemm"] = (0.0, 0.0)  # skipped: g, u come from the forward
+    elif bwd:
         units = stage_units_bwd(w)
     elif w.kind == "moe":
         cnt = np.diff(offs.cpu().numpy())
@@ -445,31 +525,39 @@ def main():
         units["gateup_gemm"] = (4.0 * rows * H * I, N * H * el + 2 * touched * I * H * el + rows * I * el)
         units["down_gemm"] = (2.0 * rows * H * I, rows * I * el + touched * H * I * el + N * H * el)
 
-    total_flops = flops_bwd(w) if bwd else w.flops()
+    total_flops = (w.flops() + flops_bwd(w)) if train else (flops_bwd(w) if bwd else w.flops())
     tflops = total_flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     dom = "gateup_gemm"
-    if bwd:  # the longest GEMM stage
+    if train:  # the longest GEMM stage of the step
+        dom = max((n for n in names if n.endswith("_gemm")), key=lambda n: stages_ms[n])
+    elif bwd:  # the longest GEMM stage
         dom = max(("gu_gemm", "dh_gemm", "dx_gemm", "dwgu_gemm", "dwd_gemm"),
                   key=lambda n: stages_ms[n])
     dom_ms = stages_ms[dom]
     dom_pct = pct(per_step[:, names.index(dom)])
     dflops, dbytes = units[dom]
-    if decode_like and not bwd:
+    if train:  # each stage is the same kernel as in the fwd / bwd passes but the gate/up one
+        tkey, tkern = ((w.name, dom[4:]) if dom.startswith("fwd:") and dom != "fwd:gateup_gemm"
+                       else (w.name + ":bwd", dom[4:]) if dom.startswith("bwd:") else (None, None))
+        traffic = recorded_traffic(tkey, tkern) if tkey else None
+    else:
+        traffic = recorded_traffic(w.name + (":bwd" if bwd else ""), dom)
+    if decode_like and not bwd and not train:
         achieved = dbytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": recorded_traffic(w.name + (":bwd" if bwd else ""), dom),
+                "traffic": traffic,
                 "algorithmic_bytes": dbytes, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
     else:
         achieved = dflops / (dom_ms * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": recorded_traffic(w.name + (":bwd" if bwd else ""), dom),
+                "traffic": traffic,
                 "algorithmic_flops": dflops, "avg_launch_ms": dom_ms, "launch_ms": dom_pct}
 
     result = {
-        "metric": METRIC_BWD if bwd else METRIC,
+        "metric": METRIC_TRAIN if train else (METRIC_BWD if bwd else METRIC),
         "value": round(N / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -496,8 +584,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
-        result["cpu_baseline"] = (cpu_baseline_bwd(w, inputs, dy_host) if bwd
-                                  else cpu_baseline(w, inputs))
+        if train:
+            result["cpu_baseline"] = cpu_baseline_train(w, inputs, dy_host)
+        else:
+            result["cpu_baseline"] = (cpu_baseline_bwd(w, inputs, dy_host) if bwd
+                                      else cpu_baseline(w, inputs))
     print(json.dumps(result), flush=True)
 
 

@@ -105,6 +105,10 @@ extern "C" {
  * minimind3 chapter 4, section 4.3 step 2): alpha is the selected
  * probabilities as they are, without renormalisation to sum 1. */
 #define TOPMOE_MOE_RAW_TOPK_WEIGHTS 1
+/* moe_ffn_bwd only: the workspace already holds the pairs (g, u) and h^T
+ * that moe_ffn_fwd_train wrote into it for the same inputs and arguments,
+ * so the grouped g, u GEMM (stage 4) is skipped. */
+#define TOPMOE_MOE_BWD_SAVED 2
 
 /* Workspace needed by ffn_swiglu_fwd: the SiLU(g)*u intermediate [N, I]
  * (dtype-sized elements), 256-byte aligned.  Returns 0 for invalid shapes. */
@@ -217,6 +221,40 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
                    void* workspace, size_t workspace_bytes,
                    void* stream, void* const* stage_events);
 
+/* ---- training: keep g, u for the backward ----------------------------- */
+/* The backward recomputes g = x Wg^T and u = x Wu^T (its stage "g, u GEMM")
+ * unless the forward kept them.  These forwards compute exactly what
+ * ffn_swiglu_fwd / moe_ffn_fwd compute (the same bits in every output) and
+ * in the same gate/up GEMM also write the pairs (g, u) and h^T into `saved`,
+ * a backward workspace: at least ffn_bwd_workspace_bytes(N, H, I, dtype) /
+ * moe_bwd_workspace_bytes(N, H, I, E, k, dtype) bytes, 256-byte aligned.
+ * Pass that same buffer, untouched in between, as the workspace of
+ * ffn_swiglu_bwd_saved / moe_ffn_bwd with TOPMOE_MOE_BWD_SAVED for the same
+ * inputs and arguments.  Costs the forward the pair and h^T stores (three
+ * times h's bytes), saves the backward its largest GEMM but one.  The other
+ * arguments, errors and stage events are those of the plain forwards; a
+ * NULL `saved` is TOPMOE_ERR_NULL_ARG. */
+int ffn_swiglu_fwd_train(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                         const void* residual, void* y, int64_t N, int64_t H, int64_t I,
+                         int dtype, void* workspace, size_t workspace_bytes,
+                         void* saved, size_t saved_bytes,
+                         void* stream, void* const* stage_events);
+int moe_ffn_fwd_train(const void* x, const float* Wr, const void* Wg, const void* Wu,
+                      const void* Wd, const void* residual, int64_t N, int64_t H, int64_t I,
+                      int E, int k, float aux_coef, float z_coef, float capacity_factor,
+                      int flags, int dtype, void* y, int32_t* topk_idx, float* alpha,
+                      float* aux_loss, float* z_loss, int32_t* expert_offsets,
+                      int32_t* sorted_token_ids, void* workspace, size_t workspace_bytes,
+                      void* saved, size_t saved_bytes,
+                      void* stream, void* const* stage_events);
+/* ffn_swiglu_bwd on a workspace that ffn_swiglu_fwd_train filled (stage 2
+ * skipped, its events zero-length). */
+int ffn_swiglu_bwd_saved(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                         const void* dy, void* dx, void* dWg, void* dWu, void* dWd,
+                         int64_t N, int64_t H, int64_t I, int dtype,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* stage_events);
+
 /* Workspace needed by moe_ffn_bwd: the routing buffers, transposed expert
  * weights [E, H, 2I] and [E, I, H], the per-entry intermediates and
  * gradients, and float32 router buffers.  Returns 0 for invalid shapes. */
@@ -234,7 +272,7 @@ size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, in
  *   dx_t += W_router^T dr_t.  A pair dropped by the capacity contributes
  *   neither an expert gradient nor d alpha.
  *   x, Wr, Wg, Wu, Wd, N, H, I, E, k, aux_coef, z_coef, capacity_factor,
- *   flags, dtype    as for moe_ffn_fwd
+ *   flags, dtype    as for moe_ffn_fwd; flags may add TOPMOE_MOE_BWD_SAVED
  *   dy [N, H]       upstream gradient of y (dtype)
  *   aux_grad        upstream gradient of aux_loss (1 when it is added to the
  *                   loss as is); finite

@@ -35,7 +35,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.topmoe_version() == 130
+    assert L.topmoe_version() == 140
 
 
 def test_strerror_covers_codes(L):
@@ -207,6 +207,60 @@ def test_bwd_validation_codes(L):
     assert moe_bwd_call(ws_bytes=need - 1) == B.ERR_WORKSPACE_TOO_SMALL
     assert moe_bwd_call(ws_bytes=need, dWr=FAKE + 4) == B.ERR_BAD_ARG
     assert moe_bwd_call(ws_bytes=need, ws=FAKE + 16) == B.ERR_BAD_ARG
+
+
+def ffn_train_call(**over):
+    a = dict(x=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, residual=None, y=FAKE, N=8, H=64, I=64,
+             dtype=B.DTYPE_BF16, ws=FAKE, ws_bytes=0, saved=FAKE, saved_bytes=0, stream=None,
+             events=None)
+    a.update(over)
+    return B.raw_ffn_swiglu_fwd_train(*a.values())
+
+
+def moe_train_call(**over):
+    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, residual=None, N=8, H=64, I=64, E=4, k=2,
+             coef=0.01, z_coef=0.0, capacity_factor=0.0, flags=0, dtype=B.DTYPE_BF16, y=FAKE,
+             topk_idx=FAKE, alpha=FAKE, aux=FAKE, z_loss=None, offsets=None,
+             sorted_ids=None, ws=FAKE, ws_bytes=0, saved=FAKE, saved_bytes=0, stream=None,
+             events=None)
+    a.update(over)
+    return B.raw_moe_ffn_fwd_train(*a.values())
+
+
+def test_train_forward_validation_codes(L):
+    # the saved buffer is a backward workspace: its size, presence and alignment are checked
+    # first, then everything the plain forward checks
+    nb = B.raw_ffn_bwd_workspace_bytes(8, 64, 64, B.DTYPE_BF16)
+    nf = B.raw_ffn_workspace_bytes(8, 64, 64, B.DTYPE_BF16)
+    assert ffn_train_call(saved=None, saved_bytes=nb) == B.ERR_NULL_ARG
+    assert ffn_train_call(saved_bytes=nb - 1) == B.ERR_WORKSPACE_TOO_SMALL
+    assert ffn_train_call(saved_bytes=nb, saved=FAKE + 128) == B.ERR_BAD_ARG
+    assert ffn_train_call(saved_bytes=nb) == B.ERR_WORKSPACE_TOO_SMALL
+    assert ffn_train_call(saved_bytes=nb, ws_bytes=nf, y=None) == B.ERR_NULL_ARG
+    assert ffn_train_call(saved_bytes=nb, ws_bytes=nf, Wd=FAKE + 4) == B.ERR_BAD_ARG
+    assert ffn_train_call(H=96, saved_bytes=nb) == B.ERR_BAD_SHAPE
+    assert ffn_train_call(dtype=3, saved_bytes=nb) == B.ERR_UNSUPPORTED_DTYPE
+
+    mb = B.raw_moe_bwd_workspace_bytes(8, 64, 64, 4, 2, B.DTYPE_BF16)
+    mf = B.raw_moe_workspace_bytes(8, 64, 64, 4, 2, B.DTYPE_BF16)
+    assert moe_train_call(saved=None, saved_bytes=mb) == B.ERR_NULL_ARG
+    assert moe_train_call(saved_bytes=mb - 1) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_train_call(saved_bytes=mb, saved=FAKE + 16) == B.ERR_BAD_ARG
+    assert moe_train_call(saved_bytes=mb) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_train_call(saved_bytes=mb, ws_bytes=mf, alpha=None) == B.ERR_NULL_ARG
+    assert moe_train_call(saved_bytes=mb, ws_bytes=mf, flags=B.MOE_BWD_SAVED) == B.ERR_BAD_ARG
+    assert moe_train_call(saved_bytes=mb, ws_bytes=mf, coef=-1.0) == B.ERR_BAD_ARG
+    assert moe_train_call(k=5, saved_bytes=mb) == B.ERR_BAD_SHAPE
+    # the backward from the saved buffer validates as the recomputing one does
+    fb = dict(x=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, dx=FAKE, dWg=FAKE, dWu=FAKE, dWd=FAKE,
+              N=8, H=64, I=64, dtype=B.DTYPE_BF16, ws=FAKE, ws_bytes=nb - 1, stream=None,
+              events=None)
+    assert B.raw_ffn_swiglu_bwd_saved(*fb.values()) == B.ERR_WORKSPACE_TOO_SMALL
+    fb.update(ws_bytes=nb, dy=None)
+    assert B.raw_ffn_swiglu_bwd_saved(*fb.values()) == B.ERR_NULL_ARG
+    assert moe_bwd_call(flags=B.MOE_BWD_SAVED) == B.ERR_WORKSPACE_TOO_SMALL
+    assert moe_bwd_call(flags=B.MOE_BWD_SAVED | B.MOE_RAW_TOPK_WEIGHTS, ws_bytes=mb,
+                        dWr=FAKE + 4) == B.ERR_BAD_ARG
 
 
 def test_torch_front_end_rejects_bad_tensors():

@@ -23,6 +23,7 @@ ERR_BAD_ARG = -6
 DTYPE_FP32 = 0
 DTYPE_BF16 = 1
 MOE_RAW_TOPK_WEIGHTS = 1
+MOE_BWD_SAVED = 2
 FFN_STAGES = 2
 MOE_STAGES = 5
 FFN_BWD_STAGES = 7
@@ -45,9 +46,16 @@ SIGNATURES = {
     "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _f32,
                            _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                            _vp]),
+    "ffn_swiglu_fwd_train": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
+                                    _vp, _sz, _vp, _vp]),
+    "moe_ffn_fwd_train": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
+                                 _f32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _sz, _vp, _sz, _vp, _vp]),
     "ffn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "ffn_swiglu_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32,
                               _vp, _sz, _vp, _vp]),
+    "ffn_swiglu_bwd_saved": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                    _i32, _vp, _sz, _vp, _vp]),
     "moe_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
     "moe_ffn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, _i64, _i32, _i32,
                            _f32, _f32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
@@ -118,6 +126,21 @@ def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef, ca
                                  offsets, sorted_ids, ws, ws_bytes, stream, events))
 
 
+def raw_ffn_swiglu_fwd_train(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, ws, ws_bytes, saved,
+                             saved_bytes, stream, events) -> int:
+    return int(lib().ffn_swiglu_fwd_train(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, ws, ws_bytes,
+                                          saved, saved_bytes, stream, events))
+
+
+def raw_moe_ffn_fwd_train(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef,
+                          capacity_factor, flags, dtype, y, topk_idx, alpha, aux, z_loss, offsets,
+                          sorted_ids, ws, ws_bytes, saved, saved_bytes, stream, events) -> int:
+    return int(lib().moe_ffn_fwd_train(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef,
+                                       capacity_factor, flags, dtype, y, topk_idx, alpha, aux,
+                                       z_loss, offsets, sorted_ids, ws, ws_bytes, saved,
+                                       saved_bytes, stream, events))
+
+
 def raw_ffn_bwd_workspace_bytes(N, H, I, dtype) -> int:
     return int(lib().ffn_bwd_workspace_bytes(N, H, I, dtype))
 
@@ -130,6 +153,12 @@ def raw_ffn_swiglu_bwd(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws,
                        events) -> int:
     return int(lib().ffn_swiglu_bwd(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws,
                                     ws_bytes, stream, events))
+
+
+def raw_ffn_swiglu_bwd_saved(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws, ws_bytes,
+                             stream, events) -> int:
+    return int(lib().ffn_swiglu_bwd_saved(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, ws,
+                                          ws_bytes, stream, events))
 
 
 def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, N, H, I, E, k, coef, z_coef,

@@ -68,7 +68,7 @@ bool nonneg_finite(float v) { return v >= 0.0f && !isinf(v); }
 
 extern "C" {
 
-int topmoe_version(void) { return 130; }
+int topmoe_version(void) { return 140; }
 
 const char* topmoe_strerror(int status) {
   switch (status) {
@@ -97,13 +97,28 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
   return plan_moe(N, H, I, E, k, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
 }
 
-int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
-                   const void* residual, void* y, int64_t N, int64_t H, int64_t I, int dtype,
-                   void* workspace, size_t workspace_bytes, void* stream,
-                   void* const* stage_events) {
+}  // extern "C"
+
+namespace {
+
+// The dense forward; with `saved` (a backward workspace) the gate/up
+// projection also keeps the pairs (g, u) and h^T there for
+// ffn_swiglu_bwd_saved.
+int ffn_fwd_impl(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                 const void* residual, void* y, int64_t N, int64_t H, int64_t I, int dtype,
+                 void* workspace, size_t workspace_bytes, void* saved, size_t saved_bytes,
+                 bool train, void* stream, void* const* stage_events) {
   FfnPlan pl;
   const int status = plan_ffn(N, H, I, dtype, &pl);
   if (status != TOPMOE_OK) return status;
+  FfnBwdPlan bpl;
+  if (train) {
+    const int bst = plan_ffn_bwd(N, H, I, dtype, &bpl);
+    if (bst != TOPMOE_OK) return bst;
+    if (!saved) return TOPMOE_ERR_NULL_ARG;
+    if (saved_bytes < bpl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(saved, 256)) return TOPMOE_ERR_BAD_ARG;
+  }
   // zero-size tensors (N == 0) are never touched and may be NULL
   if (!Wg || !Wu || !Wd || !workspace || (N > 0 && (!x || !y))) return TOPMOE_ERR_NULL_ARG;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
@@ -116,7 +131,14 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   void* h = ws + pl.off_h;
 
   const Launch l0 = st.at(0);
-  if (N > 0) {
+  if (N > 0 && train) {  // the backward's g, u projection, writing h row-major as well
+    char* sv = static_cast<char*>(saved);
+    GemmParams g{};
+    g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = sv + bpl.off_gu; g.out1 = sv + bpl.off_hT;
+    g.out2 = h;
+    g.M = N; g.ldk = bpl.ldk; g.E = 1; g.k = 1; g.Nout = int(I); g.K = int(H);
+    TOPMOE_TRY(launch_gemm(KIND_BWD_GU, dtype, bpl.gu, g, (N + bpl.gu.bm - 1) / bpl.gu.bm, l0));
+  } else if (N > 0) {
     GemmParams up{};
     up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
     up.entries = nullptr; up.offsets = nullptr; up.alpha = nullptr;
@@ -136,15 +158,25 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   return TOPMOE_OK;
 }
 
-int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
-                const void* residual, int64_t N, int64_t H, int64_t I, int E, int k,
-                float aux_coef, float z_coef, float capacity_factor, int flags, int dtype,
-                void* y, int32_t* topk_idx, float* alpha, float* aux_loss, float* z_loss,
-                int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
-                size_t workspace_bytes, void* stream, void* const* stage_events) {
+// The MoE forward; with `saved` (a backward workspace) as for the dense one.
+int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
+                 const void* residual, int64_t N, int64_t H, int64_t I, int E, int k,
+                 float aux_coef, float z_coef, float capacity_factor, int flags, int dtype,
+                 void* y, int32_t* topk_idx, float* alpha, float* aux_loss, float* z_loss,
+                 int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
+                 size_t workspace_bytes, void* saved, size_t saved_bytes, bool train,
+                 void* stream, void* const* stage_events) {
   MoePlan pl;
   const int status = plan_moe(N, H, I, E, k, dtype, &pl);
   if (status != TOPMOE_OK) return status;
+  MoeBwdPlan bpl;
+  if (train) {
+    const int bst = plan_moe_bwd(N, H, I, E, k, dtype, &bpl);
+    if (bst != TOPMOE_OK) return bst;
+    if (!saved) return TOPMOE_ERR_NULL_ARG;
+    if (saved_bytes < bpl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(saved, 256)) return TOPMOE_ERR_BAD_ARG;
+  }
   // zero-size tensors (N == 0) are never touched and may be NULL
   if (!Wr || !Wg || !Wu || !Wd || !aux_loss || !workspace ||
       (N > 0 && (!x || !y || !topk_idx || !alpha)))
@@ -195,13 +227,24 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
                             N, aux_coef, z_coef, cap, offsets, nullptr, aux_loss, z_loss,
                             sorted_entry, alpha_g, sorted_token_ids, keep, l1));
   TOPMOE_TRY(st.close(l1));
-  // 2: grouped gate/up GEMM + SiLU * up
+  // 2: grouped gate/up GEMM + SiLU * up (training: the backward's g, u
+  // projection, keeping the pairs and h^T in `saved`, h row-major as well)
   const Launch l2 = st.at(2);
-  GemmParams up{};
-  up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
-  up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
-  up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
-  TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
+  if (train) {
+    char* sv = static_cast<char*>(saved);
+    GemmParams g{};
+    g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = sv + bpl.off_gu; g.out1 = sv + bpl.off_hT;
+    g.out2 = h;
+    g.entries = sorted_entry; g.offsets = offsets;
+    g.M = pl.rows; g.ldk = bpl.ldk; g.E = E; g.k = k; g.Nout = int(I); g.K = int(H);
+    TOPMOE_TRY(launch_gemm(KIND_BWD_GU, dtype, bpl.gu, g, bpl.gu_mtiles, l2));
+  } else {
+    GemmParams up{};
+    up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
+    up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
+    up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
+    TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
+  }
   TOPMOE_TRY(st.close(l2));
   // 3: grouped down GEMM, alpha-scaled, into y (k == 1, no capacity) or the slots
   const bool direct = k == 1 && cap == 0;
@@ -222,6 +265,51 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   return TOPMOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                   const void* residual, void* y, int64_t N, int64_t H, int64_t I, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream,
+                   void* const* stage_events) {
+  return ffn_fwd_impl(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, workspace, workspace_bytes,
+                      nullptr, 0, false, stream, stage_events);
+}
+
+int ffn_swiglu_fwd_train(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                         const void* residual, void* y, int64_t N, int64_t H, int64_t I,
+                         int dtype, void* workspace, size_t workspace_bytes, void* saved,
+                         size_t saved_bytes, void* stream, void* const* stage_events) {
+  return ffn_fwd_impl(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, workspace, workspace_bytes,
+                      saved, saved_bytes, true, stream, stage_events);
+}
+
+int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
+                const void* residual, int64_t N, int64_t H, int64_t I, int E, int k,
+                float aux_coef, float z_coef, float capacity_factor, int flags, int dtype,
+                void* y, int32_t* topk_idx, float* alpha, float* aux_loss, float* z_loss,
+                int32_t* expert_offsets, int32_t* sorted_token_ids, void* workspace,
+                size_t workspace_bytes, void* stream, void* const* stage_events) {
+  return moe_fwd_impl(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, aux_coef, z_coef,
+                      capacity_factor, flags, dtype, y, topk_idx, alpha, aux_loss, z_loss,
+                      expert_offsets, sorted_token_ids, workspace, workspace_bytes, nullptr, 0,
+                      false, stream, stage_events);
+}
+
+int moe_ffn_fwd_train(const void* x, const float* Wr, const void* Wg, const void* Wu,
+                      const void* Wd, const void* residual, int64_t N, int64_t H, int64_t I,
+                      int E, int k, float aux_coef, float z_coef, float capacity_factor,
+                      int flags, int dtype, void* y, int32_t* topk_idx, float* alpha,
+                      float* aux_loss, float* z_loss, int32_t* expert_offsets,
+                      int32_t* sorted_token_ids, void* workspace, size_t workspace_bytes,
+                      void* saved, size_t saved_bytes, void* stream, void* const* stage_events) {
+  return moe_fwd_impl(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, aux_coef, z_coef,
+                      capacity_factor, flags, dtype, y, topk_idx, alpha, aux_loss, z_loss,
+                      expert_offsets, sorted_token_ids, workspace, workspace_bytes, saved,
+                      saved_bytes, true, stream, stage_events);
+}
+
 size_t ffn_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype) {
   FfnBwdPlan pl;
   return plan_ffn_bwd(N, H, I, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
@@ -232,10 +320,16 @@ size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, in
   return plan_moe_bwd(N, H, I, E, k, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
 }
 
-int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd, const void* dy,
-                   void* dx, void* dWg, void* dWu, void* dWd, int64_t N, int64_t H, int64_t I,
-                   int dtype, void* workspace, size_t workspace_bytes, void* stream,
-                   void* const* stage_events) {
+}  // extern "C"
+
+namespace {
+
+// The dense backward; `saved`: the workspace already holds the pairs (g, u)
+// and h^T from ffn_swiglu_fwd_train on the same inputs (stage 2 is skipped).
+int ffn_bwd_impl(const void* x, const void* Wg, const void* Wu, const void* Wd, const void* dy,
+                 void* dx, void* dWg, void* dWu, void* dWd, int64_t N, int64_t H, int64_t I,
+                 int dtype, void* workspace, size_t workspace_bytes, bool saved, void* stream,
+                 void* const* stage_events) {
   FfnBwdPlan pl;
   const int status = plan_ffn_bwd(N, H, I, dtype, &pl);
   if (status != TOPMOE_OK) return status;
@@ -283,9 +377,9 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
     TOPMOE_TRY(launch_gather_transpose(dtype, gj, pl.ldk, l1));
   }
   TOPMOE_TRY(st.close(l1));
-  // 2: g, u recomputed: the pairs (g, u) and h^T
+  // 2: g, u recomputed: the pairs (g, u) and h^T (kept by the training forward)
   const Launch l2 = st.at(2);
-  if (N > 0) {
+  if (N > 0 && !saved) {
     GemmParams g{};
     g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = gu; g.out1 = hT;
     g.M = N; g.ldk = pl.ldk; g.E = 1; g.k = 1; g.Nout = iI; g.K = iH;
@@ -331,6 +425,26 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
   return TOPMOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd, const void* dy,
+                   void* dx, void* dWg, void* dWu, void* dWd, int64_t N, int64_t H, int64_t I,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream,
+                   void* const* stage_events) {
+  return ffn_bwd_impl(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, workspace,
+                      workspace_bytes, false, stream, stage_events);
+}
+
+int ffn_swiglu_bwd_saved(const void* x, const void* Wg, const void* Wu, const void* Wd,
+                         const void* dy, void* dx, void* dWg, void* dWu, void* dWd, int64_t N,
+                         int64_t H, int64_t I, int dtype, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* stage_events) {
+  return ffn_bwd_impl(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtype, workspace,
+                      workspace_bytes, true, stream, stage_events);
+}
+
 int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
                 const void* dy, float aux_grad, float z_grad, int64_t N, int64_t H, int64_t I,
                 int E, int k, float aux_coef, float z_coef, float capacity_factor, int flags,
@@ -345,9 +459,10 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   if (!nonneg_finite(aux_coef) || !nonneg_finite(z_coef) || !nonneg_finite(capacity_factor) ||
       !isfinite(aux_grad) || !isfinite(z_grad))
     return TOPMOE_ERR_BAD_ARG;
-  if (flags & ~TOPMOE_MOE_RAW_TOPK_WEIGHTS) return TOPMOE_ERR_BAD_ARG;
+  if (flags & ~(TOPMOE_MOE_RAW_TOPK_WEIGHTS | TOPMOE_MOE_BWD_SAVED)) return TOPMOE_ERR_BAD_ARG;
   const int cap = capacity_of(capacity_factor, N, k, E);
   const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
+  const bool saved = (flags & TOPMOE_MOE_BWD_SAVED) != 0;
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
       !aligned(Wd, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(dWr, 16) ||
@@ -425,9 +540,10 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
     TOPMOE_TRY(launch_gather_transpose(dtype, gj, pl.ldk, l3));
   }
   TOPMOE_TRY(st.close(l3));
-  // 4: per expert g, u recomputed: the pairs (g, u) and h^T
+  // 4: per expert g, u recomputed: the pairs (g, u) and h^T (kept by the
+  // training forward)
   const Launch l4 = st.at(4);
-  if (N > 0) {
+  if (N > 0 && !saved) {
     GemmParams g{};
     g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = gu; g.out1 = hT;
     g.entries = sorted_entry; g.offsets = offsets;

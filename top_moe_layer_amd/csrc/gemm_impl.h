@@ -537,7 +537,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     if constexpr (KIND == KIND_BWD_GU || KIND == KIND_BWD_DH) {
       // Backward epilogues, per element (column i of the intermediate, row t):
       //   gu: g, u (the accumulators) go out as a pair in the dtype, row-major;
-      //       h = SiLU(g) u transposed into the group's padded columns.
+      //       h = SiLU(g) u transposed into the group's padded columns (and,
+      //       for the training forward, row-major into out2 as well).
       //   dh: with g, u read back, s = sigma(g), SiLU(g) = g s and
       //       SiLU'(g) = s (1 + g (1 - s)):  dh = alpha dh_raw,
       //       dg = dh u SiLU'(g),  du = dh SiLU(g);  [dg | du] row-major (the dx
@@ -605,12 +606,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
                 quad_transpose(g4, q4);
                 quad_transpose(u4, q4);
                 if (row_ok_t && col_ok) store_pairs4<T>(p.out, rowbase, g4, u4);
+                if (p.out2 != nullptr) {  // the forward's h as well, row-major
+                  float h4[4] = {t0[0], t0[1], t0[2], t0[3]};
+                  quad_transpose(h4, q4);
+                  if (row_ok_t && col_ok) store4<T>(static_cast<T*>(p.out2) + rowbase, h4);
+                }
               } else {
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                  if (ro0 + w < rows_left && col_ok)
-                    store_pair<T>(p.out, (t.row0 + rl + ro0 + w) * int64_t(p.Nout) + t.n0 + cl + 32 * j,
-                                  g4[w], u4[w]);
+                  if (ro0 + w < rows_left && col_ok) {
+                    const int64_t o = (t.row0 + rl + ro0 + w) * int64_t(p.Nout) + t.n0 + cl + 32 * j;
+                    store_pair<T>(p.out, o, g4[w], u4[w]);
+                    if (p.out2 != nullptr) static_cast<T*>(p.out2)[o] = from_f32<T>(t0[w]);
+                  }
               }
             } else {
               float dg4[4], du4[4];

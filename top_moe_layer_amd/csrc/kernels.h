@@ -68,7 +68,8 @@ struct GemmParams {
                            // wgrad: [groups, M, Nout]
   void* out1;              // bwd gu: h^T; bwd dh: dg^T [Nout, ldk];
                            // wgrad pair: second [groups, M, Nout]
-  void* out2;              // bwd dh: du^T [Nout, ldk]
+  void* out2;              // bwd dh: du^T [Nout, ldk]; bwd gu: NULL, or h [rows, Nout] row-major
+                           // (the training forward, which keeps g, u for the backward)
   void* out3;              // (unused)
   float* dalpha_part;      // bwd dh: [entries, ceil(Nout / BN)] partial dh_raw . h; NULL = skip
   const int32_t* entries;  // grouped row -> entry id t*k + j; NULL = identity (dense)

@@ -62,11 +62,15 @@ def moe_workspace_bytes(N: int, H: int, I: int, E: int, k: int, dtype: torch.dty
 
 def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, *,
                    residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   workspace: Optional[torch.Tensor] = None,
+                   saved: Optional[torch.Tensor] = None, stream=None,
                    stage_events: Optional[B.StageEvents] = None) -> torch.Tensor:
     """Dense SwiGLU FFN: y = residual + Wd (SiLU(Wg x) * Wu x) (residual
     optional, x's shape and dtype; it may be y itself).  x [..., H];
-    Wg, Wu [I, H]; Wd [H, I].  Returns y with x's shape and dtype."""
+    Wg, Wu [I, H]; Wd [H, I].  Returns y with x's shape and dtype.
+    ``saved`` (a backward workspace, ffn_bwd_workspace_bytes long): also keep
+    g, u and h there for ``ffn_swiglu_bwd(..., workspace=saved,
+    from_saved=True)``; y is the same either way."""
     dev = x.device
     H = x.shape[-1]
     I = Wg.shape[0]
@@ -88,9 +92,16 @@ def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
     if nbytes == 0:
         B.check(B.ERR_BAD_SHAPE, "ffn_swiglu_fwd")
     ws = _workspace(nbytes, dev, workspace)
+    evp = stage_events.ptr if stage_events is not None else None
+    if saved is not None:
+        st = B.raw_ffn_swiglu_fwd_train(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), _ptr(y),
+                                        N, H, I, code, _ptr(ws), ws.numel() * ws.element_size(),
+                                        _ptr(saved), saved.numel() * saved.element_size(),
+                                        _stream(dev, stream), evp)
+        B.check(st, "ffn_swiglu_fwd_train")
+        return y.view(x.shape)
     st = B.raw_ffn_swiglu_fwd(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), _ptr(y), N, H, I, code,
-                              _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
-                              stage_events.ptr if stage_events is not None else None)
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream), evp)
     B.check(st, "ffn_swiglu_fwd")
     return y.view(x.shape)
 
@@ -114,8 +125,8 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
                 alpha: Optional[torch.Tensor] = None, aux_loss: Optional[torch.Tensor] = None,
                 expert_offsets: Optional[torch.Tensor] = None,
                 sorted_token_ids: Optional[torch.Tensor] = None, return_lists: bool = True,
-                workspace: Optional[torch.Tensor] = None, stream=None,
-                stage_events: Optional[B.StageEvents] = None) -> MoeOutput:
+                workspace: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None,
+                stream=None, stage_events: Optional[B.StageEvents] = None) -> MoeOutput:
     """Top-k MoE FFN forward.  x [..., H]; Wr [E, H] float32; Wg, Wu [E, I, H];
     Wd [E, H, I].  Returns y (x's shape), topk_idx / alpha [N, k], aux_loss [1]
     and, when ``return_lists``, expert_offsets [E+1] and sorted_token_ids [N*k].
@@ -123,7 +134,10 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     ``norm_topk_prob`` False keeps the raw top-k probabilities as alpha;
     ``z_coef`` > 0 also returns the router z-loss; ``capacity_factor`` > 0
     caps each expert at ceil(factor * N * k / E) tokens (offsets and lists
-    then hold the kept tokens)."""
+    then hold the kept tokens).  ``saved`` (a backward workspace,
+    moe_bwd_workspace_bytes long): also keep g, u and h there for
+    ``moe_ffn_bwd(..., workspace=saved, from_saved=True)``; the outputs are
+    the same either way."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -161,13 +175,18 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
         B.check(B.ERR_BAD_SHAPE, "moe_ffn_fwd")
     ws = _workspace(nbytes, dev, workspace)
     flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
-    st = B.raw_moe_ffn_fwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), N, H, I, E,
-                           k, float(aux_coef), float(z_coef), float(capacity_factor), flags, code,
-                           _ptr(y), _ptr(topk_idx), _ptr(alpha), _ptr(aux_loss), _ptr(z_loss),
-                           _ptr(expert_offsets), _ptr(sorted_token_ids),
-                           _ptr(ws), ws.numel() * ws.element_size(), _stream(dev, stream),
-                           stage_events.ptr if stage_events is not None else None)
-    B.check(st, "moe_ffn_fwd")
+    args = (_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), N, H, I, E, k,
+            float(aux_coef), float(z_coef), float(capacity_factor), flags, code, _ptr(y),
+            _ptr(topk_idx), _ptr(alpha), _ptr(aux_loss), _ptr(z_loss), _ptr(expert_offsets),
+            _ptr(sorted_token_ids), _ptr(ws), ws.numel() * ws.element_size())
+    evp = stage_events.ptr if stage_events is not None else None
+    if saved is not None:
+        st = B.raw_moe_ffn_fwd_train(*args, _ptr(saved), saved.numel() * saved.element_size(),
+                                     _stream(dev, stream), evp)
+        B.check(st, "moe_ffn_fwd_train")
+    else:
+        st = B.raw_moe_ffn_fwd(*args, _stream(dev, stream), evp)
+        B.check(st, "moe_ffn_fwd")
     return MoeOutput(y.view(x.shape), topk_idx, alpha, aux_loss, expert_offsets, sorted_token_ids,
                      z_loss)
 
@@ -198,10 +217,13 @@ class MoeGrads:
 
 
 def ffn_swiglu_bwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
-                   dy: torch.Tensor, *, workspace: Optional[torch.Tensor] = None, stream=None,
+                   dy: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
+                   from_saved: bool = False, stream=None,
                    stage_events: Optional[B.StageEvents] = None) -> FfnGrads:
     """Gradients of the dense SwiGLU FFN for the upstream gradient dy (x's
-    shape and dtype): dx (x's shape), dWg, dWu [I, H], dWd [H, I]."""
+    shape and dtype): dx (x's shape), dWg, dWu [I, H], dWd [H, I].
+    ``from_saved``: ``workspace`` is the ``saved`` buffer of a training
+    forward on the same inputs, and g, u are not recomputed."""
     dev = x.device
     H = x.shape[-1]
     I = Wg.shape[0]
@@ -220,11 +242,14 @@ def ffn_swiglu_bwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
     nbytes = B.raw_ffn_bwd_workspace_bytes(N, H, I, code)
     if nbytes == 0:
         B.check(B.ERR_BAD_SHAPE, "ffn_swiglu_bwd")
+    if from_saved and workspace is None:
+        raise ValueError("from_saved needs the training forward's saved buffer as workspace")
     ws = _workspace(nbytes, dev, workspace)
-    st = B.raw_ffn_swiglu_bwd(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf), _ptr(dx),
-                              _ptr(dWg), _ptr(dWu), _ptr(dWd), N, H, I, code, _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(dev, stream),
-                              stage_events.ptr if stage_events is not None else None)
+    fn = B.raw_ffn_swiglu_bwd_saved if from_saved else B.raw_ffn_swiglu_bwd
+    st = fn(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf), _ptr(dx),
+            _ptr(dWg), _ptr(dWu), _ptr(dWd), N, H, I, code, _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(dev, stream),
+            stage_events.ptr if stage_events is not None else None)
     B.check(st, "ffn_swiglu_bwd")
     return FfnGrads(dx.view(x.shape), dWg, dWu, dWd)
 
@@ -233,12 +258,14 @@ def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
                 Wd: torch.Tensor, dy: torch.Tensor, k: int, aux_coef: float, *,
                 aux_grad: float = 1.0, norm_topk_prob: bool = True, z_coef: float = 0.0,
                 z_grad: float = 1.0, capacity_factor: float = 0.0,
-                workspace: Optional[torch.Tensor] = None, stream=None,
+                workspace: Optional[torch.Tensor] = None, from_saved: bool = False, stream=None,
                 stage_events: Optional[B.StageEvents] = None) -> MoeGrads:
     """Gradients of the top-k MoE FFN (and of ``aux_grad`` * aux_loss and
     ``z_grad`` * z_loss) for the upstream gradient dy: dx (x's shape), dWr
     [E, H] float32, dWg, dWu [E, I, H], dWd [E, H, I].  The routing (with the
-    same capacity) is recomputed from x and Wr."""
+    same capacity) is recomputed from x and Wr.  ``from_saved``: ``workspace``
+    is the ``saved`` buffer of a training forward on the same inputs and
+    arguments, and g, u are not recomputed."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -259,8 +286,10 @@ def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     nbytes = B.raw_moe_bwd_workspace_bytes(N, H, I, E, k, code)
     if nbytes == 0:
         B.check(B.ERR_BAD_SHAPE, "moe_ffn_bwd")
+    if from_saved and workspace is None:
+        raise ValueError("from_saved needs the training forward's saved buffer as workspace")
     ws = _workspace(nbytes, dev, workspace)
-    flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
+    flags = (0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS) | (B.MOE_BWD_SAVED if from_saved else 0)
     st = B.raw_moe_ffn_bwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf),
                            float(aux_grad), float(z_grad), N, H, I, E, k, float(aux_coef),
                            float(z_coef), float(capacity_factor), flags, code,
