@@ -815,6 +815,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     const int KT = cur.kt;
     zero_acc();
     if (cj == 0 || !stream) {
+      // A tile that fills the ring on its own waits here for its first slice
+      // anyway: its epilogue metadata and (dh) (g, u) pairs are fetched under
+      // that wait instead of stalling one of its last K steps.
+      if (!stream) {
+        load_meta(cur);
+        load_gu(cur);
+      }
       // fill the ring with the tile's first slices, wait for slice 0
       const int npro = KT < S ? KT : S;
       for (int sl = 0; sl < npro; ++sl) issue(sl, slot_ptr(sl));
@@ -854,8 +861,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     // Non-streaming tiles: the remaining steps (fewer than 2S) with run-time
     // slots; in the last S - 1 of them there is nothing left to fetch.
     if (!stream) {
-      load_meta(cur);
-      load_gu(cur);
       for (; kt < KT; ++kt) {
         const int sl = kt % S;
         const bool more = kt + S < KT;
