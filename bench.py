@@ -495,6 +495,15 @@ def main():
         step(ev_sets[i])
     torch.cuda.synchronize()
     per_step = np.array([e.elapsed_ms() for e in ev_sets])  # [steps, stages]
+    # Stages that enqueue no kernel here still get their two events, recorded
+    # back to back; they read a few microseconds of event overhead, not work.
+    empty = set()
+    if w.kind == "moe" and k == 1 and not bwd:
+        empty.add(("fwd:" if train else "") + "combine")  # y written by the down GEMM
+    if train:
+        empty.add("bwd:gu_gemm")  # g, u kept by the forward
+    for n in empty:
+        per_step[:, names.index(n)] = 0.0
     per = per_step.mean(axis=0)
     pct = lambda v: {q: round(float(np.percentile(v, p)), 5) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     for e in ev_sets:
