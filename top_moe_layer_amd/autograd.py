@@ -42,7 +42,8 @@ def swiglu_ffn(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Te
     ``keep_activations``: the forward keeps g, u for the backward (one backward
     workspace held from the forward to the backward) instead of the backward
     recomputing them; the results are the same bits either way."""
-    return _SwiGLUFunction.apply(x, Wg, Wu, Wd, residual, keep_activations)
+    keep = keep_activations and torch.is_grad_enabled()  # no backward under no_grad
+    return _SwiGLUFunction.apply(x, Wg, Wu, Wd, residual, keep)
 
 
 class _MoEFunction(torch.autograd.Function):
@@ -91,5 +92,6 @@ def moe_ffn(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tenso
     topk_idx, alpha); y, aux_loss and z_loss carry gradients to x and every
     weight (topk_idx and alpha are the router's choices, not differentiable).
     ``keep_activations`` as for swiglu_ffn."""
+    keep = keep_activations and torch.is_grad_enabled()  # no backward under no_grad
     return _MoEFunction.apply(x, Wr, Wg, Wu, Wd, residual, k, aux_coef, z_coef, capacity_factor,
-                              norm_topk_prob, keep_activations)
+                              norm_topk_prob, keep)
