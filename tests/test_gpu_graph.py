@@ -119,3 +119,42 @@ def test_graph_moe_backward(env):
     with torch.cuda.graph(g):
         captured = call(dy, torch.cuda.current_stream())  # the graph's own output tensors
     replay_checks(torch, dev, g, [getattr(captured, n) for n in names], want, lambda: call(dy2))
+
+
+def test_graph_moe_train_step(env):
+    """The training step (forward keeping g, u, then the backward taking them)
+    captured as one graph; the eager work between replays runs the same step on
+    other inputs through the same saved buffer."""
+    torch, dev, tm = env
+    w = custom_workload(name="graph_moe_train", N=400, H=128, I=192, E=8, k=2, coef=0.01,
+                        seed=35)
+    inp = make_case(w)
+    d = to_dev(inp, dev)
+    d2 = to_dev(make_case(custom_workload(name="graph_moe_train2", N=400, H=128, I=192, E=8,
+                                          k=2, coef=0.01, seed=36)), dev)
+    dy = arr_to_dev(make_upstream(inp), "bf16", dev)
+    N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
+    ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    saved = torch.empty(tm.moe_bwd_workspace_bytes(N, H, I, E, k, torch.bfloat16),
+                        dtype=torch.uint8, device=dev)
+    y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    names = ("dx", "dWr", "dWg", "dWu", "dWd")
+
+    def step(src, stream=None):
+        tm.moe_ffn_fwd(src["x"], src["Wr"], src["Wg"], src["Wu"], src["Wd"], k, w.coef, y=y,
+                       return_lists=False, workspace=ws, saved=saved, stream=stream)
+        return tm.moe_ffn_bwd(src["x"], src["Wr"], src["Wg"], src["Wu"], src["Wd"], dy, k,
+                              w.coef, workspace=saved, from_saved=True, stream=stream)
+
+    announce("graph capture of the training step N=400 E=8 k=2")
+    eager = step(d)
+    torch.cuda.synchronize()
+    want = {n: getattr(eager, n).clone() for n in names}
+    want["y"] = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = step(d, torch.cuda.current_stream())
+    outs = [getattr(captured, n) for n in names] + [y]
+    replay_checks(torch, dev, g, outs, {**{n: want[n] for n in names}, "y": want["y"]},
+                  lambda: step(d2))
