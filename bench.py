@@ -18,8 +18,9 @@ timed on a bounded sample of the same workload (rank 0, one GPU only).
 With ``--pass bwd`` a step is one backward instead (routing and gate/up
 activations recomputed, then every gradient); its line carries its own metric
 and the same roofline / cpu_baseline objects.  With ``--pass train`` a step
-is one training step: the training forward, which keeps g, u for the
-backward, then the backward that takes them instead of recomputing them.
+is one training step: the training forward, which keeps g, u (and the
+routing) for the backward, then the backward that takes them instead of
+recomputing them.
 
 Prints ONE JSON line.
 """
@@ -502,6 +503,8 @@ def main():
         empty.add(("fwd:" if train else "") + "combine")  # y written by the down GEMM
     if train:
         empty.add("bwd:gu_gemm")  # g, u kept by the forward
+        if w.kind == "moe":
+            empty.update(("bwd:router", "bwd:permute"))  # so is the routing
     for n in empty:
         per_step[:, names.index(n)] = 0.0
     per = per_step.mean(axis=0)

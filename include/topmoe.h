@@ -105,9 +105,10 @@ extern "C" {
  * minimind3 chapter 4, section 4.3 step 2): alpha is the selected
  * probabilities as they are, without renormalisation to sum 1. */
 #define TOPMOE_MOE_RAW_TOPK_WEIGHTS 1
-/* moe_ffn_bwd only: the workspace already holds the pairs (g, u) and h^T
- * that moe_ffn_fwd_train wrote into it for the same inputs and arguments,
- * so the grouped g, u GEMM (stage 4) is skipped. */
+/* moe_ffn_bwd only: the workspace already holds the routing, the pairs
+ * (g, u) and h^T that moe_ffn_fwd_train wrote into it for the same inputs
+ * and arguments, so the router, the permutation and the grouped g, u GEMM
+ * (stages 0, 1 and 4) are skipped. */
 #define TOPMOE_MOE_BWD_SAVED 2
 
 /* Workspace needed by ffn_swiglu_fwd: the SiLU(g)*u intermediate [N, I]
@@ -226,12 +227,14 @@ int ffn_swiglu_bwd(const void* x, const void* Wg, const void* Wu, const void* Wd
  * unless the forward kept them.  These forwards compute exactly what
  * ffn_swiglu_fwd / moe_ffn_fwd compute (the same bits in every output) and
  * in the same gate/up GEMM also write the pairs (g, u) and h^T into `saved`,
- * a backward workspace: at least ffn_bwd_workspace_bytes(N, H, I, dtype) /
+ * a backward workspace (the MoE forward keeps its routing there as well:
+ * selections, probabilities, offsets and the expert-grouped entry lists): at least ffn_bwd_workspace_bytes(N, H, I, dtype) /
  * moe_bwd_workspace_bytes(N, H, I, E, k, dtype) bytes, 256-byte aligned.
  * Pass that same buffer, untouched in between, as the workspace of
  * ffn_swiglu_bwd_saved / moe_ffn_bwd with TOPMOE_MOE_BWD_SAVED for the same
  * inputs and arguments.  Costs the forward the pair and h^T stores (three
- * times h's bytes), saves the backward its largest GEMM but one.  The other
+ * times h's bytes), saves the backward its largest GEMM but one (and, for
+ * the MoE, its routing kernels).  The other
  * arguments, errors and stage events are those of the plain forwards; a
  * NULL `saved` is TOPMOE_ERR_NULL_ARG. */
 int ffn_swiglu_fwd_train(const void* x, const void* Wg, const void* Wu, const void* Wd,

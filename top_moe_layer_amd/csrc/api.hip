@@ -195,20 +195,40 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
 
   const Stages st{stage_events, static_cast<hipStream_t>(stream)};
   char* ws = static_cast<char*>(workspace);
-  int32_t* count_part = reinterpret_cast<int32_t*>(ws + pl.off_count_part);
-  float* psum_part = reinterpret_cast<float*>(ws + pl.off_psum_part);
-  int32_t* offsets = expert_offsets ? expert_offsets : reinterpret_cast<int32_t*>(ws + pl.off_offsets);
-  int32_t* sorted_entry = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
-  float* alpha_g = reinterpret_cast<float*>(ws + pl.off_alpha_g);
-  float* z_part = reinterpret_cast<float*>(ws + pl.off_zpart);
-  uint8_t* keep = cap > 0 ? reinterpret_cast<uint8_t*>(ws + pl.off_keep) : nullptr;
+  char* sv = static_cast<char*>(saved);
+  // Training: the routing buffers are the backward workspace's own (the
+  // backward keeps them at its start in this same layout), plus the
+  // probabilities, logsumexps, selections and pre-capacity offsets the
+  // backward needs, so that it takes the routing from there.
+  char* rb = train ? sv : ws;
+  int32_t* count_part = reinterpret_cast<int32_t*>(rb + pl.off_count_part);
+  float* psum_part = reinterpret_cast<float*>(rb + pl.off_psum_part);
+  int32_t* offsets = (expert_offsets && !train) ? expert_offsets
+                                                : reinterpret_cast<int32_t*>(rb + pl.off_offsets);
+  int32_t* sorted_entry = reinterpret_cast<int32_t*>(rb + pl.off_sorted);
+  float* alpha_g = reinterpret_cast<float*>(rb + pl.off_alpha_g);
+  float* z_part = reinterpret_cast<float*>(rb + pl.off_zpart);
+  uint8_t* keep = cap > 0 ? reinterpret_cast<uint8_t*>(rb + pl.off_keep) : nullptr;
+  int32_t* counts_off = train ? reinterpret_cast<int32_t*>(rb + pl.off_counts_off) : nullptr;
+  float* probs = train ? reinterpret_cast<float*>(sv + bpl.off_probs) : nullptr;
+  float* lse = train && z_coef != 0.f ? reinterpret_cast<float*>(sv + bpl.off_lse) : nullptr;
+  int32_t* topk_keep = train ? reinterpret_cast<int32_t*>(sv + bpl.off_topk) : nullptr;
+  float* alpha_keep = train ? reinterpret_cast<float*>(sv + bpl.off_alpha) : nullptr;
+  int32_t* offsets_out = train ? expert_offsets : nullptr;  // the caller's copy
   void* h = ws + pl.off_h;
   void* slots = ws + pl.off_slots;
 
   if (N == 0) {
     for (int i = 0; i < TOPMOE_MOE_STAGES; ++i) {
       const Launch L = st.at(i);
-      if (i == 1) TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, z_loss, L));
+      if (i == 1) {
+        TOPMOE_TRY(launch_empty_route(E, offsets, aux_loss, z_loss, L));
+        if (offsets_out) {
+          Launch c = L;
+          c.start = c.stop = nullptr;
+          TOPMOE_TRY(launch_empty_route(E, offsets_out, aux_loss, z_loss, c));
+        }
+      }
       TOPMOE_TRY(st.close(L));
     }
     return TOPMOE_OK;
@@ -217,21 +237,21 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   const Launch l0 = st.at(0);
   TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, renorm, pl.tb, pl.nblk,
-                           pl.router_mode, topk_idx, alpha, nullptr, nullptr, count_part,
+                           pl.router_mode, topk_idx, alpha, probs, lse, count_part,
                            psum_part, z_part, l0));
   TOPMOE_TRY(st.close(l0));
   // 1: expert offsets, aux (and z) loss, stable scatter of entries into expert
   // groups (under a capacity: of the kept entries)
   const Launch l1 = st.at(1);
   TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k, pl.tb,
-                            N, aux_coef, z_coef, cap, offsets, nullptr, aux_loss, z_loss,
-                            sorted_entry, alpha_g, sorted_token_ids, keep, l1));
+                            N, aux_coef, z_coef, cap, offsets, counts_off, aux_loss, z_loss,
+                            sorted_entry, alpha_g, sorted_token_ids, keep, topk_keep, alpha_keep,
+                            offsets_out, l1));
   TOPMOE_TRY(st.close(l1));
   // 2: grouped gate/up GEMM + SiLU * up (training: the backward's g, u
   // projection, keeping the pairs and h^T in `saved`, h row-major as well)
   const Launch l2 = st.at(2);
   if (train) {
-    char* sv = static_cast<char*>(saved);
     GemmParams g{};
     g.A = x; g.B0 = Wg; g.B1 = Wu; g.out = sv + bpl.off_gu; g.out1 = sv + bpl.off_hT;
     g.out2 = h;
@@ -501,19 +521,21 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   const int iH = int(H), iI = int(I);
   const int64_t rows = rp.rows;
 
-  // 0, 1: the forward's routing (probabilities kept for the softmax backward)
+  // 0, 1: the forward's routing (probabilities kept for the softmax backward);
+  // with a saved workspace the training forward left it there
   const Launch l0 = st.at(0);
-  if (N > 0)
+  if (N > 0 && !saved)
     TOPMOE_TRY(launch_router(x, Wr, dtype, N, iH, E, k, renorm, rp.tb, rp.nblk, rp.router_mode,
                              topk_idx, alpha, probs, z_coef != 0.f ? lse : nullptr, count_part,
                              psum_part, z_part, l0));
   TOPMOE_TRY(st.close(l0));
   const Launch l1 = st.at(1);
-  if (N > 0)
+  if (N > 0 && !saved)
     TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, rp.nblk, E, k,
                               rp.tb, N, aux_coef, z_coef, cap, offsets, counts_off, aux, nullptr,
-                              sorted_entry, alpha_g, nullptr, keep, l1));
-  else
+                              sorted_entry, alpha_g, nullptr, keep, nullptr, nullptr, nullptr,
+                              l1));
+  else if (!saved)
     TOPMOE_TRY(launch_empty_route(E, offsets, aux, nullptr, l1));
   TOPMOE_TRY(st.close(l1));
   // 2: per-expert weight transposes: [Wg | Wu]^T [E, H, 2I], Wd^T [E, I, H]

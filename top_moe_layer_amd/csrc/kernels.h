@@ -99,12 +99,16 @@ hipError_t launch_router(const void* x, const float* Wr, int dtype, int64_t N, i
 
 // cap <= 0: no expert capacity.  offsets: of the kept entries; counts_off
 // (optional): of every selection.  keep [N*k] (optional): 1 where the entry is kept.
+// topk_copy / alpha_copy [N*k] and offsets_copy [E+1] (optional): second
+// copies of topk_idx, alpha and offsets (the training forward keeps the
+// routing for the backward besides the caller's outputs).
 hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                           const float* z_part, const int32_t* topk_idx, const float* alpha,
                           int nblk, int E, int k, int tb, int64_t N, float coef, float z_coef,
                           int cap, int32_t* offsets, int32_t* counts_off, float* aux,
                           float* z_loss, int32_t* sorted_entry, float* alpha_g,
-                          int32_t* sorted_tok, uint8_t* keep, const Launch& s);
+                          int32_t* sorted_tok, uint8_t* keep, int32_t* topk_copy,
+                          float* alpha_copy, int32_t* offsets_copy, const Launch& s);
 
 hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
                           const void* residual, int64_t N, int H, int k, int dtype, void* y,

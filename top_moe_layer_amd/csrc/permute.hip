@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256) void permute_kernel(
     float coef, float z_coef, int cap, int32_t* __restrict__ offsets,
     int32_t* __restrict__ counts_off, float* __restrict__ aux, float* __restrict__ z_loss,
     int32_t* __restrict__ sorted_entry, float* __restrict__ alpha_g,
-    int32_t* __restrict__ sorted_tok, uint8_t* __restrict__ keep) {
+    int32_t* __restrict__ sorted_tok, uint8_t* __restrict__ keep,
+    int32_t* __restrict__ topk_copy, float* __restrict__ alpha_copy,
+    int32_t* __restrict__ offsets_copy) {
   __shared__ int s_c[kScanMax];
   __shared__ float s_p[kScanMax];  // block 0 only
   __shared__ int s_tot[64];
@@ -124,6 +126,10 @@ __global__ __launch_bounds__(256) void permute_kernel(
     if (first) {
       if (lane < E) offsets[lane] = kincl - kc;
       if (lane == E - 1) offsets[E] = kincl;
+      if (offsets_copy != nullptr) {
+        if (lane < E) offsets_copy[lane] = kincl - kc;
+        if (lane == E - 1) offsets_copy[E] = kincl;
+      }
       if (counts_off != nullptr) {  // offsets of every selection (before any capacity)
         const int incl = wave_inclusive_scan(c, lane);
         if (lane < E) counts_off[lane] = incl - c;
@@ -167,6 +173,10 @@ __global__ __launch_bounds__(256) void permute_kernel(
         const uint64_t m = __ballot(valid && ex == le);
         if (valid && ex == le) peers = m;
         todo &= ~m;
+      }
+      if (valid && topk_copy != nullptr) {
+        topk_copy[ent] = ex;
+        alpha_copy[ent] = al;
       }
       if (valid) {
         const int rank = s_base[ex] + run[ex] + __popcll(peers & lt_mask);  // within expert ex
@@ -278,14 +288,16 @@ hipError_t launch_permute(const int32_t* count_part, const float* psum_part,
                           int nblk, int E, int k, int tb, int64_t N, float coef, float z_coef,
                           int cap, int32_t* offsets, int32_t* counts_off, float* aux,
                           float* z_loss, int32_t* sorted_entry, float* alpha_g,
-                          int32_t* sorted_tok, uint8_t* keep, const Launch& s) {
+                          int32_t* sorted_tok, uint8_t* keep, int32_t* topk_copy,
+                          float* alpha_copy, int32_t* offsets_copy, const Launch& s) {
   if (nblk <= 0) return hipSuccess;
   if (int64_t(E) * nblk > kScanMax) return hipErrorInvalidValue;
   const int G = nblk > 256 ? (nblk + 255) / 256 : 1;  // router blocks per scatter block
   const int nsb = (nblk + G - 1) / G;
   return launch_kernel(permute_kernel, dim3(nsb), dim3(256), 0, s, count_part, psum_part, z_part,
                        topk_idx, alpha, nblk, G, E, k, tb, N, coef, z_coef, cap, offsets,
-                       counts_off, aux, z_loss, sorted_entry, alpha_g, sorted_tok, keep);
+                       counts_off, aux, z_loss, sorted_entry, alpha_g, sorted_tok, keep,
+                       topk_copy, alpha_copy, offsets_copy);
 }
 
 hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
