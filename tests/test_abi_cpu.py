@@ -272,3 +272,18 @@ def test_torch_front_end_rejects_bad_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         tm.moe_ffn_fwd(x, torch.zeros(4, 64), torch.zeros(4, 64, 64), torch.zeros(4, 64, 64),
                        torch.zeros(4, 64, 64), 1, 0.01)
+
+
+def test_torch_front_end_checks_caller_buffers():
+    torch = pytest.importorskip("torch")
+    from top_moe_layer_amd import ops
+
+    cpu, gpu = torch.device("cpu"), torch.device("cuda:0")
+    with pytest.raises(ValueError, match="expected cuda:0"):
+        ops._buffer(torch.empty(64, dtype=torch.uint8), "saved", 16, gpu)
+    with pytest.raises(ValueError, match="needs 128"):
+        ops._buffer(torch.empty(64, dtype=torch.uint8), "workspace", 128, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        ops._buffer(torch.empty(64, 2, dtype=torch.uint8).t(), "saved", 16, cpu)
+    ok = torch.empty(32, dtype=torch.float32)
+    assert ops._buffer(ok, "saved", 128, cpu) is ok

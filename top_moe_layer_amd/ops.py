@@ -44,12 +44,23 @@ def _stream(device, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _buffer(t: torch.Tensor, name: str, nbytes: int, device) -> torch.Tensor:
+    """A caller-provided byte buffer: on the device, contiguous, large enough."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return t
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is None:
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-    if ws.numel() * ws.element_size() < nbytes:
-        raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
-    return ws
+    return _buffer(ws, "workspace", nbytes, device)
 
 
 def ffn_workspace_bytes(N: int, H: int, I: int, dtype: torch.dtype) -> int:
@@ -94,6 +105,7 @@ def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
     ws = _workspace(nbytes, dev, workspace)
     evp = stage_events.ptr if stage_events is not None else None
     if saved is not None:
+        _buffer(saved, "saved", B.raw_ffn_bwd_workspace_bytes(N, H, I, code), dev)
         st = B.raw_ffn_swiglu_fwd_train(_ptr(xf), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), _ptr(y),
                                         N, H, I, code, _ptr(ws), ws.numel() * ws.element_size(),
                                         _ptr(saved), saved.numel() * saved.element_size(),
@@ -135,9 +147,9 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     ``z_coef`` > 0 also returns the router z-loss; ``capacity_factor`` > 0
     caps each expert at ceil(factor * N * k / E) tokens (offsets and lists
     then hold the kept tokens).  ``saved`` (a backward workspace,
-    moe_bwd_workspace_bytes long): also keep g, u and h there for
-    ``moe_ffn_bwd(..., workspace=saved, from_saved=True)``; the outputs are
-    the same either way."""
+    moe_bwd_workspace_bytes long): also keep the routing, g, u and h there
+    for ``moe_ffn_bwd(..., workspace=saved, from_saved=True)``; the outputs
+    are the same either way."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -181,6 +193,7 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
             _ptr(sorted_token_ids), _ptr(ws), ws.numel() * ws.element_size())
     evp = stage_events.ptr if stage_events is not None else None
     if saved is not None:
+        _buffer(saved, "saved", B.raw_moe_bwd_workspace_bytes(N, H, I, E, k, code), dev)
         st = B.raw_moe_ffn_fwd_train(*args, _ptr(saved), saved.numel() * saved.element_size(),
                                      _stream(dev, stream), evp)
         B.check(st, "moe_ffn_fwd_train")
@@ -265,7 +278,7 @@ def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     [E, H] float32, dWg, dWu [E, I, H], dWd [E, H, I].  The routing (with the
     same capacity) is recomputed from x and Wr.  ``from_saved``: ``workspace``
     is the ``saved`` buffer of a training forward on the same inputs and
-    arguments, and g, u are not recomputed."""
+    arguments, and neither the routing nor g, u are recomputed."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
