@@ -1,8 +1,9 @@
 """GPU checks of the training path that keeps g, u for the backward: the
 training forwards (ffn_swiglu_fwd_train, moe_ffn_fwd_train) must give the
 same bits as the plain forwards in every output, and a backward that takes
-g, u from the saved buffer (ffn_swiglu_bwd_saved, moe_ffn_bwd with
-TOPMOE_MOE_BWD_SAVED) the same bits as the backward that recomputes them.
+g, u (and, for the MoE, the routing) from the saved buffer
+(ffn_swiglu_bwd_saved, moe_ffn_bwd with TOPMOE_MOE_BWD_SAVED) the same bits as
+the backward that recomputes them.
 The plain paths are checked against the oracle by the parity tests, so
 bit-equality carries their parity over.  The saved buffer starts filled with
 0xFF bytes (NaN in either dtype), so that any part of it the backward reads
