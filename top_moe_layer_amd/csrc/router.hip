@@ -230,6 +230,11 @@ __global__ __launch_bounds__(16 * P) void router_lds_kernel(
     float* __restrict__ probs, float* __restrict__ lse_out, int32_t* __restrict__ count_part,
     float* __restrict__ psum_part, float* __restrict__ z_part) {
   constexpr int VE = 16 / int(sizeof(T));  // elements per 16-byte load
+  // bf16 with 16 lanes per token: a lane's 8 x elements meet two consecutive
+  // 16-byte W_router pieces, so the 16 lanes of a read would stride 32 bytes
+  // (two-way LDS bank conflicts).  The copy into LDS then permutes each block
+  // of 32 pieces so that piece j of every lane's pair lies in one run of 16.
+  constexpr bool WPERM = P == 16 && VE == 8;
   constexpr int CI = 8;                    // loads per lane in flight per chunk
   extern __shared__ __attribute__((aligned(1024))) f32x4 s_w4[];  // [EP, H / 4], 1 KB-rounded
   __shared__ int s_cnt[64];
@@ -250,7 +255,11 @@ __global__ __launch_bounds__(16 * P) void router_lds_kernel(
   {
     const f32x4* W4 = reinterpret_cast<const f32x4*>(Wr);
     for (int c = wave; c * 64 < nreal; c += NT / 64) {
-      const int i = c * 64 + lane;
+      int i = c * 64 + lane;
+      if constexpr (WPERM) {  // slot 16 j + p of each 32-slot block holds piece 2 p + j
+        const int r = lane & 31;
+        i = c * 64 + (lane & 32) + 2 * (r & 15) + (r >> 4);
+      }
       __builtin_amdgcn_global_load_lds(W4 + (i < nreal ? i : nreal - 1),
                                        (__attribute__((address_space(3))) void*)(s_w4 + c * 64),
                                        16, 0, 0);
@@ -284,11 +293,12 @@ __global__ __launch_bounds__(16 * P) void router_lds_kernel(
           float xv[VE];
           unpack16<T>(xq[c], xv);
           const int q = (i0 + c) * (P * VE / 4) + part * (VE / 4);  // f32x4 column of xv[0]
+          const int qb = (i0 + c) * (P * VE / 4) + part;  // permuted: slot of piece j is qb + 16 j
 #pragma unroll
           for (int e = 0; e < EP; ++e) {
 #pragma unroll
             for (int j = 0; j < VE / 4; ++j) {
-              const f32x4 w = s_w4[e * h4 + q + j];
+              const f32x4 w = s_w4[e * h4 + (WPERM ? qb + 16 * j : q + j)];
               float a = acc[e];
               a = fmaf(xv[4 * j + 0], w.x, a);
               a = fmaf(xv[4 * j + 1], w.y, a);
