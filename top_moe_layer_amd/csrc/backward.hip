@@ -64,12 +64,19 @@ __device__ __forceinline__ void st16<bf16_t>(bf16_t* p, const float (&v)[8]) {
 // Tiles of 64 x 64 elements through LDS: 16-byte row-piece loads, 16-byte
 // column-piece stores.  The row stride of the LDS tile is 64 + 16 bytes worth
 // of elements so that 16-byte writes stay aligned.
+// bf16: the column pass reads 2-byte elements of rows 8 apart, which with the
+// padded stride alone put four of every eight lane groups on the same banks;
+// the 16-byte piece of row r sits at piece index p ^ ((r / 8) % 8) as well.
 template <typename T>
 struct TileT {
   static constexpr int V = 16 / int(sizeof(T));  // elements per 16 bytes
   static constexpr int LD = 64 + V;              // LDS row stride (elements)
   static constexpr int CPR = 64 / V;             // 16-byte pieces per 64-element row
   static constexpr int PER = 64 * CPR / 256;     // pieces per thread (256 threads)
+  __device__ static int sw(int r) { return sizeof(T) == 2 ? (r >> 3) & 7 : 0; }
+  // element (r, c) and 16-byte piece (r, p) of the tile
+  __device__ static int at(int r, int c) { return r * LD + (((c / V) ^ sw(r)) * V) + c % V; }
+  __device__ static int piece(int r, int p) { return r * LD + (p ^ sw(r)) * V; }
 };
 
 // out[b][c][col0 + r] = in[b][r][c] for up to three matrices (blockIdx.z),
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeJobs jobs) {
   for (int i = 0; i < TT::PER; ++i) {
     const int id = int(threadIdx.x) + 256 * i;
     const int r = id / TT::CPR, q = id - r * TT::CPR;
-    *reinterpret_cast<u32x4*>(&tile[r * TT::LD + q * TT::V]) =
+    *reinterpret_cast<u32x4*>(&tile[TT::piece(r, q)]) =
         *reinterpret_cast<const u32x4*>(src + int64_t(r0 + r) * jb.C + c0 + q * TT::V);
   }
   __syncthreads();
@@ -103,7 +110,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeJobs jobs) {
     const int c = id / TT::CPR, q = id - c * TT::CPR;
     float v[TT::V];
 #pragma unroll
-    for (int w = 0; w < TT::V; ++w) v[w] = to_f32<T>(tile[(q * TT::V + w) * TT::LD + c]);
+    for (int w = 0; w < TT::V; ++w) v[w] = to_f32<T>(tile[TT::at(q * TT::V + w, c)]);
     st16<T>(dst + int64_t(c0 + c) * jb.ldo + jb.col0 + r0 + q * TT::V, v);
   }
 }
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(GatherTransposeJo
 #pragma unroll
       for (int w = 0; w < TT::V; ++w) v[w] = 0.f;
     }
-    st16<T>(&tile[l * TT::LD + q * TT::V], v);
+    st16<T>(&tile[TT::piece(l, q)], v);
   }
   __syncthreads();
   T* dst = static_cast<T*>(jb.dst);
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(256) void gather_transpose_kernel(GatherTransposeJo
     const int h = id / TT::CPR, q = id - h * TT::CPR;
     float v[TT::V];
 #pragma unroll
-    for (int w = 0; w < TT::V; ++w) v[w] = to_f32<T>(tile[(q * TT::V + w) * TT::LD + h]);
+    for (int w = 0; w < TT::V; ++w) v[w] = to_f32<T>(tile[TT::at(q * TT::V + w, h)]);
     st16<T>(dst + int64_t(h0 + h) * jobs.ldo + pc0 + q * TT::V, v);
   }
 }
