@@ -321,6 +321,13 @@ __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
   }
 }
 
+// A lane's 8 partial sums of one expert row in LDS: two 16-byte halves, each
+// in a 1 KB run of the 64 lanes' halves (16-byte accesses of consecutive
+// lanes, no bank conflicts; lane * 8 + b strode 32 bytes).
+__device__ __forceinline__ int dwr_slot(int lane, int b) {
+  return (b >> 2) * 256 + lane * 4 + (b & 3);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ x,
                                                           const float* __restrict__ dr,
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ 
 #pragma unroll
       for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) s_acc[wave - 1][a][lane * 8 + b] = acc[a][b];
+        for (int b = 0; b < 8; ++b) s_acc[wave - 1][a][dwr_slot(lane, b)] = acc[a][b];
     }
     __syncthreads();
     if (wave == 0 && hok) {
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(256) void dwr_partial_kernel(const T* __restrict__ 
         for (int b = 0; b < 8; ++b) {
           float sum = acc[a][b];
 #pragma unroll
-          for (int w = 0; w < kDwrWaves - 1; ++w) sum += s_acc[w][a][lane * 8 + b];
+          for (int w = 0; w < kDwrWaves - 1; ++w) sum += s_acc[w][a][dwr_slot(lane, b)];
           v[b] = sum;
         }
         float* o = part + (int64_t(blockIdx.y) * E + e0 + a) * H + h;
