@@ -105,11 +105,11 @@ def sample_rows(N: int, n: int, seed: int = 0) -> np.ndarray:
 
 
 TOL_GRAD = {"fp32": 1e-5, "bf16": 2e-2}   # relative L2 of each gradient (per token / per matrix)
-# router-weight gradient, relative L2 per expert row: fp32 sums over up to 2^14
-# tokens (~sqrt(N) * 2^-24) times the softmax backward's cancellation; in bf16
-# the recomputed g and u are stored in bf16, so d alpha (and dr) carry
-# bf16-level error like every other bf16 gradient
-TOL_DWR = {"fp32": 1e-4, "bf16": 2e-2}
+# router-weight gradient, relative L2 per expert row (or the rounding bound of
+# dwr_rounding_bound where it is larger, i.e. where d alpha cancels): fp32
+# sums over up to 2^14 tokens (measured <= 8.4e-7); bf16 like every other
+# bf16 gradient
+TOL_DWR = {"fp32": 1e-5, "bf16": 2e-2}
 
 
 def arr_to_dev(a, dt: str, dev):
@@ -138,44 +138,108 @@ def rel_l2_per_matrix(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 
-def bf16_of(a: np.ndarray) -> np.ndarray:
-    """Round float64 values to bfloat16 (nearest even) and widen them back."""
-    from workloads.gen import round_to, to_f64
-    return to_f64(round_to(np.asarray(a, dtype=np.float64), "bf16"), "bf16")
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
 
 
-def dwr_bf16_h_shift(f: dict, route: dict, dy64: np.ndarray, k: int,
-                     norm_topk_prob: bool) -> np.ndarray:
-    """The part of the bf16 path's router-weight gradient [E, H] that comes
-    from recomputing g and u in bf16: its d alpha_{t,j} is dh_raw . SiLU(g~) u~
-    with g~, u~ the bf16-rounded projections (the backward's stored pairs)
-    instead of dh_raw . SiLU(g) u.  That change passes linearly through the
-    renormalisation (d p_S = d alpha / Z - (d alpha . p_S) / Z^2), the softmax
-    (d r = p (d p - p . d p)) and d W_r = d r^T x, so the shift is exact given
-    the rounding.  Where d alpha cancels (few tokens per expert), this shift
-    dominates the difference to the fp64 oracle."""
-    p, idx = route["p"], route["topk_idx"]
-    keep = route.get("keep")
-    N, E = p.shape
-    ddal = np.zeros((N, k))
-    for t in range(N):
-        for j in range(k):
-            if keep is not None and not keep[t, j]:
-                continue
-            e = idx[t, j]
-            g = f["Wg"][e] @ f["x"][t]
-            u = f["Wu"][e] @ f["x"][t]
-            gb, ub = bf16_of(g), bf16_of(u)
-            silu = lambda z: z / (1.0 + np.exp(-z))
-            dh_raw = f["Wd"][e].T @ dy64[t]
-            ddal[t, j] = dh_raw @ (silu(gb) * ub - silu(g) * u)
-    ps = np.take_along_axis(p, idx, axis=1)
+def dwr_rounding_bound(f: dict, route: dict, dy64: np.ndarray, k: int, norm_topk_prob: bool,
+                       dtype: str, sigmas: float = 5.0) -> np.ndarray:
+    """A bound [E, H] on the error of the computed dW_r that comes from the
+    rounding of the quantities d alpha is formed from, propagated exactly
+    through the (linear) rest of the router's backward: ``sigmas`` times the
+    standard deviation of that error under the probabilistic model of
+    rounding (independent errors, uniform within the rounding interval).
+
+    d alpha_{t,j} = sum_i dh_i * SiLU(g_i) * u_i with g = W_g x_t, u = W_u x_t,
+    dh = W_d^T dy_t (the selected expert's).  Where its terms cancel (few
+    tokens per expert), relative errors of g, u, dh of the size of the
+    storage rounding become large relative errors of d alpha and of the row
+    of dW_r it feeds.  Only the oracle's exact values and the arithmetic's
+    unit roundoffs enter: g and u stored in the dtype (a relative error of
+    at most u_s = 2^-8 for bf16, 2^-24 for fp32: variance (u_s v)^2 / 3);
+    fp32 accumulation of an n-term sum whose terms have magnitude sum S
+    (variance n (2^-24 S)^2 / 3); h = SiLU(g) u to first order in the errors
+    of g and u.  From d alpha on, the map to dW_r is linear: the
+    renormaliser's d p_S (sum_i p_i (d alpha_j - d alpha_i) + 1e-20 d alpha_j)
+    / Z^2 (zero for k = 1 up to the 1e-20 term), the softmax's
+    d r = p (d p - p . d p) and d W_r = d r^T x; variances add over the
+    independent slots and tokens.  Returns sigmas * the standard deviation of
+    each element."""
+    u_s = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+    u32 = 2.0 ** -24
+    x = f["x"]
+    N, H = x.shape
+    E, I = f["Wg"].shape[0], f["Wg"].shape[1]
+    p, idx, keep = route["p"], route["topk_idx"], route.get("keep")
+    var_dal = np.zeros((N, k))
+    for e in range(E):
+        tt, jj = np.nonzero(idx == e)
+        if keep is not None:
+            sel = np.asarray(keep)[tt, jj].astype(bool)
+            tt, jj = tt[sel], jj[sel]
+        if tt.size == 0:
+            continue
+        xe, dye = x[tt], dy64[tt]
+        Wg, Wu, Wd = f["Wg"][e], f["Wu"][e], f["Wd"][e]
+        g, u, d = xe @ Wg.T, xe @ Wu.T, dye @ Wd
+        G = np.abs(xe) @ np.abs(Wg).T
+        U = np.abs(xe) @ np.abs(Wu).T
+        D = np.abs(dye) @ np.abs(Wd)
+        sg = 1.0 / (1.0 + np.exp(-g))
+        s = g * sg
+        ds = sg * (1.0 + g * (1.0 - sg))  # SiLU'
+        var_g = ((u_s * g) ** 2 + H * (u32 * G) ** 2) / 3.0
+        var_u = ((u_s * u) ** 2 + H * (u32 * U) ** 2) / 3.0
+        var_d = H * (u32 * D) ** 2 / 3.0
+        var_h = (ds * u) ** 2 * var_g + s ** 2 * var_u
+        h = s * u
+        var_dal[tt, jj] = ((d ** 2) * var_h + (h ** 2) * var_d).sum(axis=1) + \
+            I * (u32 * np.abs(d * h).sum(axis=1)) ** 2 / 3.0
+    ps = np.take_along_axis(p, idx, axis=1)                       # [N, k]
+    # d p_S = A d alpha per token: A_jj = (sum_{i != j} p_i + 1e-20) / Z^2,
+    # A_ji = -p_i / Z^2 (renormalised), A = identity (raw weights)
     if norm_topk_prob:
-        Z = ps.sum(axis=1, keepdims=True) + 1e-20
-        dps = ddal / Z - (ddal * ps).sum(axis=1, keepdims=True) / Z ** 2
+        Z = ps.sum(axis=1) + 1e-20
+        A = np.repeat(-ps[:, None, :] / (Z ** 2)[:, None, None], k, axis=1)  # A[t, j, i]
+        diag = (ps.sum(axis=1, keepdims=True) - ps + 1e-20) / (Z ** 2)[:, None]
+        ar = np.arange(k)
+        A[:, ar, ar] = diag
     else:
-        dps = ddal
-    dp = np.zeros_like(p)
-    np.put_along_axis(dp, idx, dps, axis=1)
-    dr = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-    return dr.T @ f["x"]
+        A = np.broadcast_to(np.eye(k), (N, k, k)).copy()
+    # d p_te = sum_j [S_tj = e] (A d alpha)_j;  d r = p (d p - p . d p)
+    # T[t, e, i]: d r_te per unit d alpha_ti
+    P = np.zeros((N, E, k))
+    for j in range(k):
+        P[np.arange(N), idx[:, j], j] = 1.0
+    M = np.einsum("tej,tji->tei", P, A)                           # d p per d alpha
+    T = p[:, :, None] * (M - np.einsum("te,tei->ti", p, M)[:, None, :])
+    var_dr = np.einsum("tei,ti->te", T ** 2, var_dal)             # [N, E]
+    var_dwr = var_dr.T @ (x ** 2)                                 # [E, H]
+    return sigmas * np.sqrt(var_dwr)
+
+
+def check_dwr(got, ref: np.ndarray, bound: np.ndarray, dtype: str) -> None:
+    """Every expert row of dW_r within TOL_DWR relative L2, or within the
+    rounding bound of dwr_rounding_bound where the arithmetic itself cannot
+    give that accuracy (d alpha cancelling); a row whose reference is zero
+    must be zero."""
+    if not isinstance(got, np.ndarray):
+        got = got.detach().double().cpu().numpy()
+    for e in range(ref.shape[0]):
+        den = np.linalg.norm(ref[e])
+        diff = np.linalg.norm(got[e] - ref[e])
+        if den < 1e-12:
+            assert np.abs(got[e]).max() <= 1e-9, (e, np.abs(got[e]).max())
+            continue
+        slack = np.linalg.norm(bound[e])
+        assert diff <= max(TOL_DWR[dtype] * den, slack), (e, diff / den, slack / den)
+
+
+def dwr_bound_for(inputs: dict, ref: dict, dy, k: int, norm_topk_prob: bool) -> np.ndarray:
+    """dwr_rounding_bound for a parity case: its stored inputs, the oracle's
+    backward result (its routing) and the upstream gradient in storage dtype."""
+    from oracle.cases import widen
+    from workloads import to_f64
+
+    dt = inputs["dtype"]
+    return dwr_rounding_bound(widen(inputs), ref["route"], to_f64(dy, dt), k, norm_topk_prob, dt)

@@ -2,18 +2,18 @@
 backward cases with shapes, expert counts, k, dtype, residual, the raw
 top-k weights, z-loss and capacity drawn at random (H and I multiples of 64,
 as the ABI requires), each checked against the oracle to the bars of the
-fixed-shape tests (for dW_r on the bf16 path, where few tokens per expert
-can leave d alpha badly conditioned: the relative bar, or 2e-3 against the
-oracle shifted by the exact effect of the bf16-recomputed g, u).  The draw is fixed (seed below), so a
-failure names a reproducible case."""
+fixed-shape tests (dW_r: the relative bar plus an a-priori rounding bound,
+which is what remains where few tokens per expert leave d alpha badly
+conditioned).  The draw is fixed (seed below), so a failure names a
+reproducible case."""
 import numpy as np
 import pytest
 
 from oracle import moe_ffn, moe_ffn_bwd
 from oracle.cases import custom_workload, expected, make_case, widen
 from workloads import make_upstream, to_f64
-from gpu_util import (TOL_DWR, TOL_GRAD, TOL_Y, announce, arr_to_dev, check_routing,
-                      dwr_bf16_h_shift, rel_l2_per_matrix, rel_l2_per_token, to_dev, torch_dev,
+from gpu_util import (TOL_GRAD, TOL_Y, announce, arr_to_dev, check_dwr, check_routing,
+                      dwr_bound_for, rel_l2_per_matrix, rel_l2_per_token, to_dev, torch_dev,
                       y_to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -118,19 +118,6 @@ def test_random_backward(env, c):
     for n in ("dWg", "dWu", "dWd"):
         err = rel_l2_per_matrix(to64(getattr(g, n)), ref[n])
         assert err <= TOL_GRAD[c["dt"]], (n, err)
-    # dW_r: the relative bar; on the bf16 path, where d alpha cancels (few
-    # tokens per expert), against the oracle shifted by the exact effect of
-    # the bf16-recomputed g, u on d alpha, to 2e-3
-    got = to64(g.dWr)
-    shift = (dwr_bf16_h_shift(f, ref["route"], to_f64(dy, c["dt"]), w.k, c["norm"])
-             if c["dt"] == "bf16" else None)
-    for e in range(w.E):
-        den = np.linalg.norm(ref["dWr"][e])
-        diff = np.linalg.norm(got[e] - ref["dWr"][e])
-        if den < 1e-12:
-            assert np.abs(got[e]).max() <= 1e-9, (e, np.abs(got[e]).max())
-        elif diff > TOL_DWR[c["dt"]] * den:
-            assert shift is not None, (e, diff / den)
-            want = ref["dWr"][e] + shift[e]
-            err = np.linalg.norm(got[e] - want) / np.linalg.norm(want)
-            assert err <= 2e-3, (e, diff / den, err)
+    # dW_r: the relative bar plus the a-priori rounding bound (which is what
+    # remains where d alpha cancels, with few tokens per expert)
+    check_dwr(to64(g.dWr), ref["dWr"], dwr_bound_for(inp, ref, dy, w.k, c["norm"]), c["dt"])

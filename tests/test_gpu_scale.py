@@ -7,18 +7,17 @@ grouped GEMMs over many small, unequal groups.
 The router weights are scaled up (x6 for 64 experts) so that the fp64 top-k
 margin of 1e-3 holds for every token after at most a few redraws (with 64
 experts and the U(+-1/sqrt(H)) draw many probabilities sit within 1e-3 of
-each other).  Routing outputs are compared in full (bit-exact lists, alpha
-and aux to 1e-5); y, dx on sampled rows, the expert weight gradients on
-sampled units, dW_r in full where every row is taken.  Bars as elsewhere.
+each other).  Everything is compared in full: routing outputs (bit-exact
+lists, alpha and aux to 1e-5), y and dx on every token row, every expert's
+weight gradients.  Bars as elsewhere.
 """
 import numpy as np
 import pytest
 
-from oracle import moe_ffn_bwd_sampled
-from oracle.cases import custom_workload, enforce_margin, expected, make_case, widen
-from workloads import make_upstream, to_f64
+from oracle.cases import custom_workload, enforce_margin, expected, expected_bwd, make_case
+from workloads import make_upstream
 from gpu_util import (TOL_GRAD, TOL_Y, announce, arr_to_dev, check_routing, rel_l2_per_matrix,
-                      rel_l2_per_token, run_moe, sample_rows, to_dev, torch_dev, y_to_f64)
+                      rel_l2_per_token, run_moe, to_dev, torch_dev, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,26 +53,19 @@ def test_scale_forward(env, N, H, I, E, k, sc, dt):
                         seed=E + k)
     announce(f"scale forward N={N} H={H} I={I} E={E} k={k} {dt}: inputs (margin redraws)")
     inp = scaled_case(w, sc)
-    rows = sample_rows(N, 256)
-    ref = expected(w, inp, rows=rows)
+    ref = expected(w, inp)
     announce("scale forward: GPU")
     d = to_dev(inp, dev)
     out = run_moe(tm, d, w)
     torch.cuda.synchronize()
     check_routing(out, ref, k, E)
-    err = rel_l2_per_token(y_to_f64(out.y)[rows], ref["y"])
+    err = rel_l2_per_token(y_to_f64(out.y), ref["y"])
     assert err <= TOL_Y[dt], err
 
 
-def sample_units(I, n=24, seed=3):
-    edge = np.array([0, 31, 32, 63, 64, I - 64, I - 1])
-    rest = np.random.default_rng(seed).choice(I, size=n - len(edge), replace=False)
-    return np.unique(np.concatenate([edge[(edge >= 0) & (edge < I)], rest]))
-
-
 def test_scale_backward(env):
-    """64 experts, top-6, 4096 tokens: dx on sampled rows, weight gradients on
-    sampled units of every expert."""
+    """64 experts, top-6, 4096 tokens: every gradient against the oracle's
+    full backward (dx per token; dW_g, dW_u, dW_d per expert)."""
     torch, dev, tm = env
     N, H, I, E, k = 4096, 512, 256, 64, 6
     w = custom_workload(name="scale_bwd", N=N, H=H, I=I, E=E, k=k, coef=0.01, seed=71)
@@ -85,17 +77,10 @@ def test_scale_backward(env):
     g = tm.moe_ffn_bwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], arr_to_dev(dy, "bf16", dev),
                        k, w.coef)
     torch.cuda.synchronize()
-    rows = sample_rows(N, 48)
-    units = sample_units(I)
-    announce("scale backward: sampled oracle")
-    f = widen(inp)
-    ref = moe_ffn_bwd_sampled(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], k, w.coef,
-                              to_f64(dy, "bf16"), 1.0, True, rows=rows, units=units)
-    assert rel_l2_per_token(y_to_f64(g.dx)[ref["rows"]], ref["dx_rows"]) <= TOL_GRAD["bf16"]
+    announce("scale backward: oracle")
+    ref = expected_bwd(w, inp, dy)
+    assert rel_l2_per_token(y_to_f64(g.dx), ref["dx"]) <= TOL_GRAD["bf16"]
     to64 = lambda t: t.detach().double().cpu().numpy()
-    touched = ref["route"]["counts"] > 0
-    for n, gn, sl in (("dWg_u", "dWg", np.s_[:, units]), ("dWu_u", "dWu", np.s_[:, units]),
-                      ("dWd_u", "dWd", np.s_[:, :, units])):
-        got, want = to64(getattr(g, gn))[sl][touched], ref[n][touched]
-        err = rel_l2_per_matrix(got, want)
-        assert err <= TOL_GRAD["bf16"], (gn, err)
+    for n in ("dWg", "dWu", "dWd"):
+        err = rel_l2_per_matrix(to64(getattr(g, n)), ref[n])
+        assert err <= TOL_GRAD["bf16"], (n, err)
