@@ -1,19 +1,25 @@
 """Benchmark of the MiniMind FFN / top-k MoE forward (or backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--cold | --warm]
-                    [--pass fwd | bwd | train]
+                    [--pass fwd | bwd | train] [--no-others]
 
 A step is one full forward (every kernel of the path) over one batch of
-synthetic inputs already resident in device memory.  W untimed steps, then
-exactly K steps bracketed by device synchronisation; ``value`` is tokens/s
-over those K steps.  Decode-sized workloads (N*k <= 256) are timed cold by
-default: L2 and the Infinity Cache are flushed before every step, outside
-per-step events, by reading a 1 GiB buffer (a read leaves clean lines; a
-write would leave the caches full of dirty lines whose write-back then
-competes with the step), and ``value`` comes from those events.  A second pass of K steps records HIP events around every
-stage on the library's stream to get per-kernel durations, from which the
-dominant kernel's roofline fraction is computed.  The fp64 CPU oracle is then
-timed on a bounded sample of the same workload (rank 0, one GPU only).
+synthetic inputs already resident in device memory.  Default workload: the
+dense bf16 SwiGLU FFN, 16384 tokens, H 2048, I 6464 (the largest
+configuration).  W untimed steps, then exactly K timed steps.  By default
+each timed step starts with cold caches: L2 and the 256 MB Infinity Cache are
+flushed before every step, outside the step's own start / stop events, by
+reading a 1 GiB buffer (a read leaves clean lines; a write would leave the
+caches full of dirty lines whose write-back then competes with the step), and
+``value`` / ``ms_per_step`` come from those events.  The same K steps back to
+back with warm caches (bracketed by device synchronisation) and a captured
+graph replayed K times are reported alongside (``warm_ms_per_step``,
+``graph_ms_per_step``).  A further pass of K steps records HIP events around
+every stage on the library's stream to get per-kernel durations, from which
+the dominant kernel's roofline fraction is computed.  The other workloads'
+cold step times follow as ``other_workloads`` (``--no-others`` skips them).
+The fp64 CPU oracle is then timed on a bounded sample of the workload (rank
+0, one GPU only): median of 3 passes.
 
 With ``--pass bwd`` a step is one backward instead (routing and gate/up
 activations recomputed, then every gradient); its line carries its own metric
@@ -39,7 +45,10 @@ if ROOT not in sys.path:
 METRIC = "FFN/MoE fwd tokens/s + TFLOP/s (% bf16 MFMA peak) / GB/s (% HBM) on 1 GPU"
 METRIC_BWD = "FFN/MoE bwd tokens/s + TFLOP/s (% bf16 MFMA peak) on 1 GPU"
 METRIC_TRAIN = "FFN/MoE train step (fwd + bwd) tokens/s + TFLOP/s (% bf16 MFMA peak) on 1 GPU"
-DEFAULT_WORKLOAD = "moe_top1_n4096_h768_e4"
+DEFAULT_WORKLOAD = "dense_bf16_n16384_h2048_i6464"
+# the other configurations, timed cold after the headline (forward only)
+OTHER_WORKLOADS = ["moe_top1_n4096_h768_e4", "moe_top2_skew_n16384_h768_e8",
+                   "moe_decode_n32_h2048_e16", "dense_fp32_n100_h768_i2432"]
 
 # MI355X published peaks
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
@@ -142,19 +151,65 @@ def flops_bwd(w):
     return f
 
 
-def cpu_baseline_bwd(w, inputs, dy, budget_s=10.0):
-    """Time the fp64 oracle's backward (as it stands) on a bounded sample: the
-    first n tokens as a batch of their own (n grown by 4x until one pass takes
-    a quarter of the budget, at most all N), repeated until the budget is spent."""
-    from oracle.cases import widen
-    from oracle import swiglu_ffn_bwd, moe_ffn_bwd
-    from workloads import to_f64
-
+def host_info():
+    """The CPU the oracle runs on: model name, CPUs in this process's affinity
+    mask, and the BLAS threads numpy's matmuls actually use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        threads = affinity
+    return model, affinity, int(threads)
+
+
+def timed_sample(run, N, budget_s):
+    """Median rate of 3 passes of the oracle over the first n tokens, n grown
+    by 4x (at most N) until one pass takes a sixth of the budget."""
+    n = min(N, 64)
+    dt = run(n)
+    while n < N and dt < budget_s / 6:
+        n = min(N, n * 4)
+        dt = run(n)
+    times = sorted([dt] + [run(n) for _ in range(2)])
+    return n, times
+
+
+def baseline_record(n, times, N, what):
+    model, affinity, threads = host_info()
+    med = times[1]
+    return {
+        "value": n / med,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{what}: first {n} of {N} tokens, median of 3 passes "
+                  f"({', '.join(f'{t:.2f}' for t in times)} s)",
+        "cpu_model": model,
+        "affinity_cpus": affinity,
+        "blas_threads": threads,
+    }
+
+
+def cpu_baseline_bwd(w, inputs, dy, budget_s=20.0):
+    """Time the fp64 oracle's backward (as it stands) on a bounded sample:
+    the first n tokens as a batch of their own."""
+    from oracle.cases import widen
+    from oracle import swiglu_ffn_bwd, moe_ffn_bwd
+    from workloads import to_f64
+
     f = widen(inputs)
     g = to_f64(dy, w.dtype)
 
@@ -167,52 +222,27 @@ def cpu_baseline_bwd(w, inputs, dy, budget_s=10.0):
                         w.norm_topk_prob)
         return time.perf_counter() - t0
 
-    n = min(w.N, 64)
-    dt = run(n)
-    while n < w.N and dt < budget_s / 4:
-        n = min(w.N, n * 4)
-        dt = run(n)
-    reps, total = 1, dt
-    while total < budget_s:
-        total += run(n)
-        reps += 1
-    return {
-        "value": n * reps / total,
-        "unit": "tokens/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"fp64 numpy oracle backward, first {n} of {w.N} tokens of {w.name} as one "
-                  f"batch, {reps} passes, {total:.1f} s",
-    }
+    n, times = timed_sample(run, w.N, budget_s)
+    return baseline_record(n, times, w.N, f"fp64 numpy oracle backward on {w.name} (the first n "
+                                          f"tokens as one batch)")
 
 
 def cpu_baseline_train(w, inputs, dy):
     """A training step of the oracle: its forward and its backward timed as in
-    the other passes (about 6 s each), the per-token times added."""
-    f = cpu_baseline(w, inputs, budget_s=6.0)
-    b = cpu_baseline_bwd(w, inputs, dy, budget_s=6.0)
-    return {
-        "value": 1.0 / (1.0 / f["value"] + 1.0 / b["value"]),
-        "unit": "tokens/s",
-        "cores": max(f["cores"], b["cores"]),
-        "kind": "oracle",
-        "sample": f"forward: {f['sample']}; backward: {b['sample']}; per-token times added",
-    }
+    the other passes, the per-token times added."""
+    f = cpu_baseline(w, inputs, budget_s=12.0)
+    b = cpu_baseline_bwd(w, inputs, dy, budget_s=12.0)
+    return dict(f, value=1.0 / (1.0 / f["value"] + 1.0 / b["value"]),
+                sample=f"forward: {f['sample']}; backward: {b['sample']}; per-token times added")
 
 
-def cpu_baseline(w, inputs, budget_s=10.0):
+def cpu_baseline(w, inputs, budget_s=20.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload:
-    the first n tokens (n grown by 4x until one pass takes a quarter of the
-    budget, at most all N), repeated until the budget is spent."""
+    the outputs of the first n tokens."""
     import numpy as np
     from oracle.cases import widen
     from oracle import dense_ffn, moe_ffn, moe_route
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     f = widen(inputs)
 
     def run(n):
@@ -230,23 +260,96 @@ def cpu_baseline(w, inputs, budget_s=10.0):
             return time.perf_counter() - t0 - tr + tr * n / w.N
         return time.perf_counter() - t0
 
-    n = min(w.N, 64)
-    dt = run(n)
-    while n < w.N and dt < budget_s / 4:
-        n = min(w.N, n * 4)
-        dt = run(n)
-    reps, total = 1, dt
-    while total < budget_s:
-        total += run(n)
-        reps += 1
-    return {
-        "value": n * reps / total,
-        "unit": "tokens/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"fp64 numpy oracle, first {n} of {w.N} tokens of {w.name}, {reps} passes, "
-                  f"{total:.1f} s" + (" (routing of all tokens charged pro rata)" if w.kind == "moe" else ""),
-    }
+    n, times = timed_sample(run, w.N, budget_s)
+    return baseline_record(n, times, w.N, f"fp64 numpy oracle on {w.name}" +
+                           (" (routing of all tokens charged pro rata)" if w.kind == "moe" else ""))
+
+
+def forward_step(tm, w, d, dev, stream):
+    """One forward of the workload on preallocated outputs and workspace:
+    returns step(stage_events=None, stream=stream) and the device expert
+    offsets (MoE) or None."""
+    import torch
+
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    N, H, I, E, k = w.N, w.H, w.I, w.E, w.k
+    y = torch.empty((N, H), dtype=tdt, device=dev)
+    if w.kind == "dense":
+        ws = torch.empty(tm.ffn_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
+
+        def step(ev=None, st=stream):
+            tm.ffn_swiglu_fwd(d["x"], d["Wg"], d["Wu"], d["Wd"], y=y, workspace=ws,
+                              stream=st, stage_events=ev)
+        return step, None
+    ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8, device=dev)
+    idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+    alpha = torch.empty((N, k), dtype=torch.float32, device=dev)
+    aux = torch.empty((1,), dtype=torch.float32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+
+    def step(ev=None, st=stream):
+        tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef, y=y,
+                       topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
+                       norm_topk_prob=w.norm_topk_prob, return_lists=False, workspace=ws,
+                       stream=st, stage_events=ev)
+    return step, offs
+
+
+def step_bytes(w, touched):
+    """Algorithmic bytes of one forward: x read and y written once, the
+    weights of the experts that receive tokens once, W_router."""
+    el = w.elem_bytes()
+    ex = 1 if w.kind == "dense" else touched
+    b = 2 * w.N * w.H * el + 3 * ex * w.H * w.I * el
+    if w.kind == "moe":
+        b += w.E * w.H * 4
+    return b
+
+
+def time_other_workloads(tm, names, steps, warmup, dev, stream, flush):
+    """Cold step times of other workloads' forwards (caches flushed before each
+    step, events around the step only)."""
+    import numpy as np
+    import torch
+    from workloads import get, make_inputs
+
+    out = {}
+    for name in names:
+        w = get(name)
+        inputs = make_inputs(w)
+        t = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+                       .view(torch.bfloat16) if w.dtype == "bf16"
+                       else torch.from_numpy(np.ascontiguousarray(a)).to(dev))
+        d = {n: t(inputs[n]) for n in ("x", "Wg", "Wu", "Wd")}
+        if w.kind == "moe":
+            d["Wr"] = torch.from_numpy(np.ascontiguousarray(inputs["Wr"])).to(dev)
+        step, offs = forward_step(tm, w, d, dev, stream)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(steps):
+            flush()
+            s0.record(stream)
+            step()
+            s1.record(stream)
+            s1.synchronize()
+            per.append(s0.elapsed_time(s1))
+        ms = float(np.mean(per))
+        touched = int((np.diff(offs.cpu().numpy()) > 0).sum()) if offs is not None else 1
+        tf = w.flops() / (ms * 1e-3) / 1e12
+        gbs = step_bytes(w, touched) / (ms * 1e-3) / 1e9
+        rec = {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.N / (ms * 1e-3), 1),
+               "tflops": round(tf, 2), "frac_of_peak_flops": round(tf / PEAK_TFLOPS[w.dtype], 4),
+               "hbm_gbs": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+               "dtype": w.dtype, "cache": "cold", "steps": steps}
+        out[w.name] = rec
+        log(f"other workload {w.name}: {rec}")
+        del d, step, offs
+        torch.cuda.synchronize()
+    return out
 
 
 class _EventPair:
@@ -271,16 +374,19 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     cache = ap.add_mutually_exclusive_group()
     cache.add_argument("--cold", action="store_const", const="cold", dest="cache",
-                       help="flush L2 and the Infinity Cache before each step; time steps one by one "
-                            "(default for decode-sized workloads, N*k <= 256)")
+                       help="headline steps with L2 and the Infinity Cache flushed before each, "
+                            "timed one by one with events (default)")
     cache.add_argument("--warm", action="store_const", const="warm", dest="cache",
-                       help="back-to-back steps with warm caches (default otherwise)")
+                       help="headline steps back to back with warm caches (then the cold steps "
+                            "are the ones reported alongside)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-too", action="store_true",
-                    help="warm runs: also time the steps with cold caches (field cold_ms_per_step; "
-                         "off by default so that every kernel of a default run is a warm one)")
+    ap.add_argument("--no-alongside", action="store_true",
+                    help="skip the steps in the other cache mode (field warm_ms_per_step or "
+                         "cold_ms_per_step)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing (extra field graph_ms_per_step)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the cold step times of the other workloads (field other_workloads)")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "train"), default="fwd",
                     help="time the forward (default), the backward, or a training step (the "
                          "forward keeping g, u + the backward taking them)")
@@ -316,9 +422,7 @@ def main():
     train = args.which == "train"
     log(f"workload {w.name}: N={w.N} H={w.H} I={w.I} E={w.E} k={w.k} {w.dtype} {args.which}")
     decode_like = w.kind == "moe" and w.N * w.k <= 256
-    # Decode-sized steps stream their weights; with warm caches part of them
-    # would come from the 256 MB Infinity Cache, so they are timed cold.
-    cold = (args.cache or ("cold" if decode_like else "warm")) == "cold"
+    cold = (args.cache or "cold") == "cold"
     inputs = make_inputs(w)
 
     def dev_t(a, stored=True):
@@ -392,31 +496,13 @@ def main():
                 tm.moe_ffn_bwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], dyd, k, w.coef,
                                norm_topk_prob=w.norm_topk_prob, workspace=ws, stream=st,
                                stage_events=ev)
-    elif w.kind == "dense":
-        ws = torch.empty(tm.ffn_workspace_bytes(N, H, I, tdt), dtype=torch.uint8, device=dev)
-        y = torch.empty((N, H), dtype=tdt, device=dev)
-        names = tm.FFN_STAGE_NAMES
-
-        def step(ev=None, st=stream):
-            tm.ffn_swiglu_fwd(d["x"], d["Wg"], d["Wu"], d["Wd"], y=y, workspace=ws,
-                              stream=st, stage_events=ev)
-        make_events = lambda: tm.StageEvents(tm.FFN_STAGES)
     else:
-        ws = torch.empty(tm.moe_workspace_bytes(N, H, I, E, k, tdt), dtype=torch.uint8, device=dev)
-        y = torch.empty((N, H), dtype=tdt, device=dev)
-        idx = torch.empty((N, k), dtype=torch.int32, device=dev)
-        alpha = torch.empty((N, k), dtype=torch.float32, device=dev)
-        aux = torch.empty((1,), dtype=torch.float32, device=dev)
-        offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-        names = tm.MOE_STAGE_NAMES
+        step, offs = forward_step(tm, w, d, dev, stream)
+        names = tm.FFN_STAGE_NAMES if w.kind == "dense" else tm.MOE_STAGE_NAMES
+        nst = tm.FFN_STAGES if w.kind == "dense" else tm.MOE_STAGES
+        make_events = lambda: tm.StageEvents(nst)
 
-        def step(ev=None, st=stream):
-            tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef, y=y,
-                           topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
-                           return_lists=False, workspace=ws, stream=st, stage_events=ev)
-        make_events = lambda: tm.StageEvents(tm.MOE_STAGES)
-
-    flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev) if cold or args.cold_too else None
+    flush_buf = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
 
     def flush():  # evict L2 and the Infinity Cache with clean lines
         flush_buf.sum()
@@ -427,49 +513,57 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    if not cold:
+    def time_cold(nsteps):
+        """Per-step milliseconds, caches flushed before each step (outside
+        the step's events)."""
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        out = []
+        torch.cuda.synchronize()
+        for _ in range(nsteps):
+            flush()
+            s0.record(stream)
+            step()
+            s1.record(stream)
+            s1.synchronize()
+            out.append(s0.elapsed_time(s1))
+        torch.cuda.synchronize()
+        return out
+
+    def time_warm(nsteps):
+        """Milliseconds per step of nsteps back-to-back steps."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(nsteps):
             step()
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-        ms_step = elapsed * 1e3 / args.steps
+        return (time.perf_counter() - t0) * 1e3 / nsteps
+
+    step_pct = None
+    if cold:
+        per = time_cold(args.steps)
+        ms_step = sum(per) / len(per)
+        step_pct = {q: round(float(np.percentile(per, p_)), 5)
+                    for q, p_ in (("p10", 10), ("p50", 50), ("p90", 90))}
     else:
-        s0 = torch.cuda.Event(enable_timing=True)
-        s1 = torch.cuda.Event(enable_timing=True)
-        tot = 0.0
-        for _ in range(args.steps):
-            flush()
-            s0.record(stream)
-            step()
-            s1.record(stream)
-            s1.synchronize()
-            tot += s0.elapsed_time(s1)
-        ms_step = tot / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step")
+        ms_step = time_warm(args.steps)
+    log(f"timed {args.steps} {'cold' if cold else 'warm'} steps: {ms_step:.4f} ms/step")
 
-    # Warm workloads: the same K steps with L2 and the Infinity Cache flushed
-    # before each one (events around the step only), reported alongside.
-    cold_ms = None
-    if not cold and args.cold_too:
-        s0 = torch.cuda.Event(enable_timing=True)
-        s1 = torch.cuda.Event(enable_timing=True)
-        tot = 0.0
-        for _ in range(args.steps):
-            flush()
-            s0.record(stream)
-            step()
-            s1.record(stream)
-            s1.synchronize()
-            tot += s0.elapsed_time(s1)
-        cold_ms = tot / args.steps
-        log(f"cold steps: {cold_ms:.4f} ms/step")
+    # The same K steps in the other cache mode, reported alongside.
+    warm_ms = cold_ms = None
+    if not args.no_alongside:
+        if cold:
+            warm_ms = time_warm(args.steps)
+            log(f"warm steps: {warm_ms:.4f} ms/step")
+        else:
+            per = time_cold(args.steps)
+            cold_ms = sum(per) / len(per)
+            log(f"cold steps: {cold_ms:.4f} ms/step")
 
-    # The same step captured once in a HIP graph and replayed K times (warm
-    # runs only): the launch overhead that a caller capturing its loop saves.
+    # The same step captured once in a HIP graph and replayed K times (warm):
+    # the launch overhead that a caller capturing its loop saves.
     graph_ms = None
-    if not cold and not args.no_graph:
+    if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(None, torch.cuda.current_stream(dev))
@@ -482,7 +576,7 @@ def main():
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         del g
-        log(f"graph replays: {graph_ms:.4f} ms/step")
+        log(f"graph replays (warm): {graph_ms:.4f} ms/step")
 
     # Per-kernel durations: the same K steps again, each with its own start /
     # stop events per stage, stamped by the kernel dispatches themselves
@@ -588,12 +682,23 @@ def main():
         "mfma_frac": round(tflops / peak, 4),
         "stages_ms": stages_ms,
         "kernel_ms_per_step": pct(per_step.sum(axis=1)),
+        "step_ms": step_pct,
+        "warm_ms_per_step": None if warm_ms is None else round(warm_ms, 5),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "cold_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
         "experts_touched": touched,
         "pass": args.which,
         "roofline": roof,
     }
+    if not bwd and not train:
+        # the whole step against HBM: x, y, the touched weights and W_r once
+        gbs = step_bytes(w, touched if touched is not None else 1) / (ms_step * 1e-3) / 1e9
+        result["step_hbm_gbs"] = round(gbs, 1)
+        result["step_hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+    if not args.no_others and not bwd and not train:
+        others = [n for n in OTHER_WORKLOADS if n != w.name]
+        result["other_workloads"] = time_other_workloads(tm, others, min(args.steps, 20), 3,
+                                                         dev, stream, flush)
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on a bounded sample")
         if train:

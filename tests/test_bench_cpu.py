@@ -58,3 +58,32 @@ def test_backward_flops():
         u = bench.stage_units_bwd(w)
         gemm = sum(u[n][0] for n in ("dh_gemm", "dx_gemm", "dwgu_gemm", "dwd_gemm"))
         assert gemm == 12.0 * rows * w.H * w.I  # the recomputed g, u is not credited
+
+
+def test_cpu_baseline_record_names_the_host():
+    calls = []
+
+    def run(n):
+        calls.append(n)
+        return 1.0 if n >= 1024 else 0.01
+
+    n, times = bench.timed_sample(run, 4096, budget_s=6.0)
+    assert n == 1024 and calls == [64, 256, 1024, 1024, 1024] and len(times) == 3
+    rec = bench.baseline_record(n, times, 4096, "test")
+    assert rec["value"] == pytest.approx(1024 / 1.0)
+    assert rec["affinity_cpus"] == len(os.sched_getaffinity(0))
+    assert rec["cores"] == rec["blas_threads"] >= 1
+    assert rec["cpu_model"] and "median of 3" in rec["sample"]
+
+
+def test_step_bytes_count_touched_weights_once():
+    w = get("moe_decode_n32_h2048_e16")
+    el = w.elem_bytes()
+    assert bench.step_bytes(w, 16) == 2 * w.N * w.H * el + 3 * 16 * w.H * w.I * el + w.E * w.H * 4
+    d = get("dense_bf16_n16384_h2048_i6464")
+    assert bench.step_bytes(d, None) == 2 * d.N * d.H * 2 + 3 * d.H * d.I * 2
+
+
+def test_default_workload_is_the_largest_configuration():
+    from workloads.registry import WORKLOADS
+    assert bench.DEFAULT_WORKLOAD == max(WORKLOADS.values(), key=lambda w: w.flops()).name
