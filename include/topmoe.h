@@ -78,7 +78,8 @@ extern "C" {
 #define TOPMOE_ERR_HIP                  -5  /* a HIP runtime call or launch failed    */
 #define TOPMOE_ERR_BAD_ARG              -6  /* aux_coef, z_coef or capacity_factor negative or not
                                                finite; aux_grad or z_grad not finite; unknown
-                                               flag bits; misaligned pointer */
+                                               flag bits; misaligned pointer; a launch-shape
+                                               override that is not instantiated */
 
 /* ---- dtypes ------------------------------------------------------------ */
 #define TOPMOE_DTYPE_FP32 0
@@ -88,8 +89,8 @@ extern "C" {
 #define TOPMOE_FFN_STAGES 2  /* 0 gate/up GEMM + SiLU*up, 1 down GEMM                   */
 #define TOPMOE_MOE_STAGES 5  /* 0 router, 1 expert offsets + aux + token scatter,
                                 2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
-                                + alpha, 4 combine of the k slots (empty when k == 1
-                                and there is no capacity)                               */
+                                + alpha, 4 combine of the k slots (k == 1: empty, or
+                                under a capacity the rows of the dropped tokens)        */
 #define TOPMOE_FFN_BWD_STAGES 7  /* 0 weight transposes, 1 x / dy transposes,
                                     2 g, u GEMM (recomputed), 3 dh GEMM + dg, du,
                                     4 dx GEMM, 5 dWg + dWu GEMM, 6 dWd GEMM             */
@@ -110,6 +111,11 @@ extern "C" {
  * and arguments, so the router, the permutation and the grouped g, u GEMM
  * (stages 0, 1 and 4) are skipped. */
 #define TOPMOE_MOE_BWD_SAVED 2
+/* The module outside training (lesson 13, walkthrough step 6: the aux loss
+ * is computed only while training; otherwise it is a zero scalar): aux_loss
+ * and z_loss are 0 whatever aux_coef and z_coef say, and moe_ffn_bwd passes
+ * no gradient through them.  Everything else is unchanged. */
+#define TOPMOE_MOE_EVAL 4
 
 /* Workspace needed by ffn_swiglu_fwd: the SiLU(g)*u intermediate [N, I]
  * (dtype-sized elements), 256-byte aligned.  Returns 0 for invalid shapes. */
@@ -134,8 +140,8 @@ int ffn_swiglu_fwd(const void* x, const void* Wg, const void* Wu, const void* Wd
                    void* stream, void* const* stage_events);
 
 /* Workspace needed by moe_ffn_fwd (routing partials, permutation, the
- * SiLU(g)*u intermediate [N*k, I] and the k-slots [N*k, H] of alpha-scaled
- * expert outputs in the dtype).
+ * SiLU(g)*u intermediate [N*k, I] and, for k >= 2, the k-slots [N*k, H] of
+ * alpha-scaled expert outputs in the dtype).
  * Returns 0 for invalid shapes. */
 size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype);
 
@@ -153,7 +159,7 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
  *   z_coef               router z-loss coefficient (>= 0); 0 gives z_loss = 0
  *   capacity_factor      expert capacity factor (>= 0); 0 = no capacity (dropless,
  *                        the pages' module); a capacity of N or more drops nothing
- *   flags                0 or TOPMOE_MOE_RAW_TOPK_WEIGHTS
+ *   flags                0, or TOPMOE_MOE_RAW_TOPK_WEIGHTS and / or TOPMOE_MOE_EVAL
  *   y        [N, H]      output (dtype): y_t = residual_t (or 0) + the sum over
  *                        the selected (and kept) experts in ascending expert id
  *                        of alpha * Expert_e(x_t); with k >= 2 (or a capacity)
@@ -276,10 +282,16 @@ size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, in
  *   neither an expert gradient nor d alpha.
  *   x, Wr, Wg, Wu, Wd, N, H, I, E, k, aux_coef, z_coef, capacity_factor,
  *   flags, dtype    as for moe_ffn_fwd; flags may add TOPMOE_MOE_BWD_SAVED
+ *                   (TOPMOE_MOE_EVAL: no gradient through aux_loss, z_loss)
  *   dy [N, H]       upstream gradient of y (dtype)
  *   aux_grad        upstream gradient of aux_loss (1 when it is added to the
  *                   loss as is); finite
  *   z_grad          upstream gradient of z_loss; finite
+ *   aux_grad_scale, z_grad_scale
+ *                   optional (NULL = 1) float32 device scalars multiplying
+ *                   aux_grad / z_grad: an upstream gradient that is still on
+ *                   the device (autograd's) is read by the kernel, with no
+ *                   host synchronisation.  Their value is not validated.
  *   dx [N, H] (dtype), dWr [E, H] (float32), dWg, dWu [E, I, H], dWd [E, H, I]
  *                   (dtype) outputs; experts no token selected get zero
  *                   gradients.  N == 0 gives all-zero weight gradients.
@@ -289,6 +301,7 @@ size_t moe_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, in
  * aligned. */
 int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
                 const void* Wd, const void* dy, float aux_grad, float z_grad,
+                const float* aux_grad_scale, const float* z_grad_scale,
                 int64_t N, int64_t H, int64_t I, int E, int k, float aux_coef, float z_coef,
                 float capacity_factor, int flags, int dtype,
                 void* dx, float* dWr, void* dWg, void* dWu, void* dWd,
@@ -302,6 +315,28 @@ const char* topmoe_strerror(int status);
 int topmoe_version(void);
 
 /* ---- instrumentation helpers (not on the hot path) ---------------------- */
+/* Launch-shape override of one GEMM of the path, for tuning sweeps and tests.
+ *   gemm   TOPMOE_TILE_GATEUP (forward gate/up), TOPMOE_TILE_DOWN (forward down
+ *          and the backward's dx), TOPMOE_TILE_BWD_GU, TOPMOE_TILE_BWD_DH,
+ *          TOPMOE_TILE_WGRAD_GU (dW_g + dW_u), TOPMOE_TILE_WGRAD_D (dW_d)
+ *   shape  int[6] {block rows, block columns, wavefront rows, wavefront
+ *          columns, LDS row bytes, ring depth}, or NULL to clear the override
+ * Returns TOPMOE_ERR_BAD_ARG, changing nothing, if the library does not
+ * instantiate that shape for that GEMM.  Initial overrides come from the
+ * environment variables TOPMOE_GATEUP_TILE, TOPMOE_DOWN_TILE,
+ * TOPMOE_BWDGU_TILE, TOPMOE_BWDDH_TILE, TOPMOE_WGU_TILE, TOPMOE_WD_TILE
+ * ("BMxBNxWMxWNxRBxS"), read once, by the first call that plans a launch;
+ * while one of them names a shape that is not instantiated, the calls that
+ * would use it return TOPMOE_ERR_BAD_ARG before launching anything.  An
+ * override applies to every dtype for which the shape is instantiated. */
+#define TOPMOE_TILE_GATEUP 0
+#define TOPMOE_TILE_DOWN 1
+#define TOPMOE_TILE_BWD_GU 2
+#define TOPMOE_TILE_BWD_DH 3
+#define TOPMOE_TILE_WGRAD_GU 4
+#define TOPMOE_TILE_WGRAD_D 5
+int topmoe_set_tile_override(int gemm, const int* shape);
+
 /* Create / destroy n timing-enabled hipEvent_t handles. */
 int topmoe_events_create(int n, void** events);
 int topmoe_events_destroy(int n, void** events);

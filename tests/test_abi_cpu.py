@@ -35,7 +35,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.topmoe_version() == 140
+    assert L.topmoe_version() == 150
 
 
 def test_strerror_covers_codes(L):
@@ -50,9 +50,9 @@ def test_workspace_sizes(L):
     assert B.raw_ffn_workspace_bytes(100, 768, 2432, B.DTYPE_FP32) >= 100 * 2432 * 4
     assert B.raw_ffn_workspace_bytes(16384, 2048, 6464, B.DTYPE_BF16) >= 16384 * 6464 * 2
     # moe: intermediate [N*k, I] plus the k-slots [N*k, H] (dtype) when k >= 2
-    # (the slots exist for k = 1 too: an expert capacity routes k = 1 through them)
+    # (none for k = 1: the down GEMM writes y, also under a capacity)
     w1 = B.raw_moe_workspace_bytes(4096, 768, 2432, 4, 1, B.DTYPE_BF16)
-    assert 4096 * 2432 * 2 + 4096 * 768 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 768 * 2 + 4096 * 8 + 65536
+    assert 4096 * 2432 * 2 <= w1 < 4096 * 2432 * 2 + 4096 * 16 + 65536
     w2 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_BF16)
     assert w2 >= 32768 * 2432 * 2 + 32768 * 768 * 2
     w3 = B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_FP32)
@@ -117,6 +117,8 @@ def test_moe_validation_codes(L):
     assert moe_call(ws_bytes=need, alpha=FAKE + 2) == B.ERR_BAD_ARG
     assert moe_call(ws_bytes=need, residual=FAKE + 8) == B.ERR_BAD_ARG
     assert moe_call(ws_bytes=need, flags=2) == B.ERR_BAD_ARG
+    assert moe_call(ws_bytes=need, flags=8) == B.ERR_BAD_ARG
+    assert moe_call(flags=B.MOE_EVAL | B.MOE_RAW_TOPK_WEIGHTS) == B.ERR_WORKSPACE_TOO_SMALL
     assert moe_call(ws_bytes=need, flags=-1) == B.ERR_BAD_ARG
     assert moe_call(z_coef=-0.1) == B.ERR_BAD_ARG
     assert moe_call(z_coef=float("inf")) == B.ERR_BAD_ARG
@@ -147,8 +149,8 @@ def ffn_bwd_call(**over):
 
 
 def moe_bwd_call(**over):
-    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, aux_grad=1.0, z_grad=1.0, N=8,
-             H=64, I=64, E=4, k=2, coef=0.01, z_coef=0.0, capacity_factor=0.0, flags=0,
+    a = dict(x=FAKE, Wr=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, dy=FAKE, aux_grad=1.0, z_grad=1.0,
+             aux_grad_scale=None, z_grad_scale=None, N=8, H=64, I=64, E=4, k=2, coef=0.01, z_coef=0.0, capacity_factor=0.0, flags=0,
              dtype=B.DTYPE_BF16, dx=FAKE, dWr=FAKE, dWg=FAKE, dWu=FAKE, dWd=FAKE, ws=FAKE,
              ws_bytes=0, stream=None, events=None)
     a.update(over)
@@ -198,7 +200,9 @@ def test_bwd_validation_codes(L):
     assert moe_bwd_call(coef=-1.0) == B.ERR_BAD_ARG
     assert moe_bwd_call(aux_grad=float("nan")) == B.ERR_BAD_ARG
     assert moe_bwd_call(aux_grad=float("inf")) == B.ERR_BAD_ARG
-    assert moe_bwd_call(flags=4) == B.ERR_BAD_ARG
+    assert moe_bwd_call(flags=8) == B.ERR_BAD_ARG
+    assert moe_bwd_call(flags=B.MOE_EVAL) == B.ERR_WORKSPACE_TOO_SMALL  # a known flag
+    assert moe_bwd_call(aux_grad_scale=FAKE + 2) == B.ERR_BAD_ARG
     assert moe_bwd_call(z_grad=float("nan")) == B.ERR_BAD_ARG
     assert moe_bwd_call(z_coef=-1.0) == B.ERR_BAD_ARG
     assert moe_bwd_call(capacity_factor=float("inf")) == B.ERR_BAD_ARG
@@ -287,3 +291,81 @@ def test_torch_front_end_checks_caller_buffers():
         ops._buffer(torch.empty(64, 2, dtype=torch.uint8).t(), "saved", 16, cpu)
     ok = torch.empty(32, dtype=torch.float32)
     assert ops._buffer(ok, "saved", 128, cpu) is ok
+
+
+def test_tile_override_is_validated(L):
+    """A launch-shape override must name a shape the library instantiates for
+    that GEMM; a rejected one changes nothing."""
+    try:
+        with pytest.raises(B.TopmoeError, match="status -6"):
+            B.set_tile_override("gateup", "96x96x2x2x128x2")            # not instantiated
+        with pytest.raises(B.TopmoeError, match="status -6"):
+            B.set_tile_override("gateup", "256x256x4x2x128x2")          # LDS ring too big here
+        assert L.topmoe_set_tile_override(9, None) == B.ERR_BAD_ARG
+        B.set_tile_override("down", "256x256x4x2x128x2")
+        B.set_tile_override("gateup", (128, 128, 2, 4, 128, 3))
+        assert B.raw_moe_workspace_bytes(300, 64, 64, 4, 2, B.DTYPE_BF16) > 0
+    finally:
+        for g in B.TILE_SLOTS:
+            B.set_tile_override(g, None)
+
+
+def test_invalid_environment_override_fails_before_launch():
+    """The environment's overrides are read once; one that names a shape that
+    is not instantiated makes the calls that would use it fail validation."""
+    import subprocess
+    import sys
+
+    code = ("from top_moe_layer_amd import _binding as B\n"
+            "print(B.raw_ffn_workspace_bytes(64, 64, 64, B.DTYPE_BF16),"
+            " B.raw_moe_workspace_bytes(64, 64, 64, 4, 2, B.DTYPE_BF16))")
+    env = dict(os.environ, TOPMOE_DOWN_TILE="100x100x2x2x128x2")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=ROOT, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["0", "0"]
+    env = dict(os.environ, TOPMOE_DOWN_TILE="128x128x2x4x128x3")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       cwd=ROOT, timeout=60)
+    assert r.returncode == 0 and all(int(v) > 0 for v in r.stdout.split()), (r.stdout, r.stderr)
+
+
+def test_front_end_allocates_on_the_kernels_stream(monkeypatch):
+    """The torch front end makes the kernels' stream torch's current stream
+    while it allocates outputs and workspaces, so the caching allocator ties
+    them to that stream."""
+    torch = pytest.importorskip("torch")
+    from top_moe_layer_amd import ops
+
+    entered = []
+
+    class FakeCtx:
+        def __init__(self, s):
+            self.s = s
+
+        def __enter__(self):
+            entered.append(self.s)
+
+        def __exit__(self, *a):
+            entered.append("exit")
+
+    class FakeDev:
+        type = "cuda"
+
+    class FakeTensor(torch.Tensor):
+        pass
+
+    x = torch.zeros(2).as_subclass(FakeTensor)
+    monkeypatch.setattr(FakeTensor, "device", property(lambda self: FakeDev()))
+    monkeypatch.setattr(ops.torch.cuda, "stream", FakeCtx)
+    monkeypatch.setattr(ops, "_torch_stream", lambda dev, st: ("stream", st))
+    seen = []
+
+    @ops._on_caller_stream
+    def fn(x, *, stream=None):
+        seen.append((stream, list(entered)))
+        return 7
+
+    assert fn(x, stream=1234) == 7
+    assert seen == [(("stream", 1234), [("stream", 1234)])]
+    assert entered[-1] == "exit"

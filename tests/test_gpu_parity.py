@@ -203,6 +203,43 @@ def test_moe_single_expert_matches_dense(env):
     assert rel_l2_per_token(y_to_f64(yd), ref["y"]) <= TOL_Y["bf16"]
 
 
+def test_moe_eval_flag(env):
+    """Outside training the module's aux loss is a zero scalar ([L13] step 6);
+    everything else is the training-mode result, bit for bit."""
+    torch, dev, tm = env
+    w = custom_workload(name="moe_eval", N=300, H=128, I=128, E=8, k=2, coef=0.01, seed=31)
+    d = to_dev(make_case(w), dev)
+    announce("moe_ffn_fwd training=False")
+    a = tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], w.k, w.coef, z_coef=0.01)
+    b = tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], w.k, w.coef, z_coef=0.01,
+                       training=False)
+    torch.cuda.synchronize()
+    assert float(a.aux_loss.cpu()[0]) > 0 and float(a.z_loss.cpu()[0]) > 0
+    assert float(b.aux_loss.cpu()[0]) == 0.0 and float(b.z_loss.cpu()[0]) == 0.0
+    assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
+    assert torch.equal(a.topk_idx, b.topk_idx) and torch.equal(a.alpha, b.alpha)
+
+
+def test_moe_on_a_side_stream(env):
+    """A call on a stream other than the current one allocates its outputs and
+    workspace for that stream and gives the same bits."""
+    torch, dev, tm = env
+    w = custom_workload(name="moe_side", N=700, H=128, I=192, E=8, k=2, coef=0.01, seed=32)
+    d = to_dev(make_case(w), dev)
+    announce("moe_ffn_fwd on a side stream")
+    ref = run_moe(tm, d, w)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    out = tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], w.k, w.coef, stream=side)
+    junk = torch.full((1 << 22,), 7, dtype=torch.int32, device=dev)  # current-stream traffic
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(out.y.view(torch.int16), ref.y.view(torch.int16))
+    assert torch.equal(out.sorted_token_ids, ref.sorted_token_ids)
+
+
 def test_empty_inputs(env):
     torch, dev, tm = env
     announce("N = 0")

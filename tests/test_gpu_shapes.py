@@ -1,8 +1,7 @@
 """Every instantiated GEMM launch shape (block tile, wavefront grid, LDS row
-bytes, ring depth), forced through the planner's override, against the fp64
-oracle on dense and MoE cases with ragged tails."""
-import os
-
+bytes, ring depth), forced through the planner's override
+(topmoe_set_tile_override), against the fp64 oracle on dense and MoE cases
+with ragged tails."""
 import pytest
 
 from oracle.cases import custom_workload, expected, make_case
@@ -33,27 +32,21 @@ def env():
     return torch, dev, tm
 
 
-TILE_VARS = ("TOPMOE_GATEUP_TILE", "TOPMOE_DOWN_TILE", "TOPMOE_BWDGU_TILE", "TOPMOE_BWDDH_TILE",
-             "TOPMOE_WGU_TILE", "TOPMOE_WD_TILE")
-
-
 @pytest.fixture
 def shape_env():
-    saved = {k: os.environ.get(k) for k in TILE_VARS}
-    yield
-    for k, v in saved.items():
-        if v is None:
-            os.environ.pop(k, None)
-        else:
-            os.environ[k] = v
+    from top_moe_layer_amd import _binding as B
+
+    yield B.set_tile_override
+    for g in B.TILE_SLOTS:
+        B.set_tile_override(g, None)
 
 
 @pytest.mark.parametrize("shape", BF16_SHAPES)
 def test_shape_dense_and_moe(env, shape_env, shape):
     torch, dev, tm = env
     if shape not in GATEUP_TOO_BIG:
-        os.environ["TOPMOE_GATEUP_TILE"] = shape
-    os.environ["TOPMOE_DOWN_TILE"] = shape
+        shape_env("gateup", shape)
+    shape_env("down", shape)
     w = custom_workload(name="shape_dense", kind="dense", N=777, H=320, I=448, E=1, k=1,
                         coef=0.0, dtype="bf16", seed=11)
     inp = make_case(w)
@@ -75,12 +68,12 @@ def test_shape_dense_and_moe(env, shape_env, shape):
 
 
 # backward kinds: (override variable, shapes instantiated and valid for it)
-BWD_SHAPES = [("TOPMOE_BWDGU_TILE", s) for s in
+BWD_SHAPES = [("bwd_gu", s) for s in
               ("256x128x4x2x128x2", "128x128x2x4x128x2", "256x64x4x2x128x2")] + \
-             [("TOPMOE_BWDDH_TILE", s) for s in ("128x128x2x4x128x3", "128x128x2x4x128x2")] + \
-             [("TOPMOE_WGU_TILE", s) for s in
+             [("bwd_dh", s) for s in ("128x128x2x4x128x3", "128x128x2x4x128x2")] + \
+             [("wgrad_gu", s) for s in
               ("128x256x2x4x128x2", "128x128x2x4x128x3", "128x128x2x2x128x3", "64x64x2x2x128x3")] + \
-             [("TOPMOE_WD_TILE", s) for s in
+             [("wgrad_d", s) for s in
               ("128x256x2x4x128x2", "128x128x2x4x128x3", "256x128x4x2x128x3", "128x128x2x2x128x3",
                "64x64x2x2x128x3")]
 
@@ -96,7 +89,7 @@ def test_bwd_shape(env, shape_env, var, shape):
     from gpu_util import TOL_GRAD, arr_to_dev, rel_l2_per_matrix
 
     torch, dev, tm = env
-    os.environ[var] = shape
+    shape_env(var, shape)
     w = custom_workload(name="shape_bwd", N=700, H=192, I=320, E=5, k=2, coef=0.01, dtype="bf16",
                         seed=13)
     inp = make_case(w)

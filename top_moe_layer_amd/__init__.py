@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     StageEvents,
     TopmoeError,
     lib,
+    set_tile_override,
     strerror,
 )
 

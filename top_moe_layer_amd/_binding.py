@@ -24,6 +24,8 @@ DTYPE_FP32 = 0
 DTYPE_BF16 = 1
 MOE_RAW_TOPK_WEIGHTS = 1
 MOE_BWD_SAVED = 2
+MOE_EVAL = 4
+TILE_SLOTS = {"gateup": 0, "down": 1, "bwd_gu": 2, "bwd_dh": 3, "wgrad_gu": 4, "wgrad_d": 5}
 FFN_STAGES = 2
 MOE_STAGES = 5
 FFN_BWD_STAGES = 7
@@ -57,11 +59,12 @@ SIGNATURES = {
     "ffn_swiglu_bwd_saved": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                     _i32, _vp, _sz, _vp, _vp]),
     "moe_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
-    "moe_ffn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, _i64, _i32, _i32,
-                           _f32, _f32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
-                           _vp]),
+    "moe_ffn_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _f32, _f32, _vp, _vp, _i64, _i64, _i64,
+                           _i32, _i32, _f32, _f32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _sz, _vp, _vp]),
     "topmoe_strerror": (ctypes.c_char_p, [_i32]),
     "topmoe_version": (_i32, []),
+    "topmoe_set_tile_override": (_i32, [_i32, _vp]),
     "topmoe_events_create": (_i32, [_i32, _vp]),
     "topmoe_events_destroy": (_i32, [_i32, _vp]),
     "topmoe_event_elapsed_ms": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
@@ -161,12 +164,25 @@ def raw_ffn_swiglu_bwd_saved(x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, N, H, I, dtyp
                                           ws_bytes, stream, events))
 
 
-def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, N, H, I, E, k, coef, z_coef,
-                    capacity_factor, flags, dtype, dx, dWr, dWg, dWu, dWd, ws, ws_bytes, stream,
-                    events) -> int:
-    return int(lib().moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, N, H, I, E, k, coef,
-                                 z_coef, capacity_factor, flags, dtype, dx, dWr, dWg, dWu, dWd, ws,
-                                 ws_bytes, stream, events))
+def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, aux_grad_scale, z_grad_scale, N, H,
+                    I, E, k, coef, z_coef, capacity_factor, flags, dtype, dx, dWr, dWg, dWu, dWd,
+                    ws, ws_bytes, stream, events) -> int:
+    return int(lib().moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, aux_grad_scale,
+                                 z_grad_scale, N, H, I, E, k, coef, z_coef, capacity_factor, flags,
+                                 dtype, dx, dWr, dWg, dWu, dWd, ws, ws_bytes, stream, events))
+
+
+def set_tile_override(gemm: str, shape=None) -> None:
+    """Force the launch shape of one GEMM of the path (tuning sweeps, tests):
+    ``gemm`` one of TILE_SLOTS; ``shape`` "BMxBNxWMxWNxRBxS" or a 6-tuple, None
+    to clear.  Raises TopmoeError (bad argument) if it is not instantiated."""
+    arr = None
+    if shape is not None:
+        vals = [int(v) for v in shape.split("x")] if isinstance(shape, str) else list(shape)
+        if len(vals) != 6:
+            raise ValueError(f"shape needs 6 values, got {shape!r}")
+        arr = (ctypes.c_int * 6)(*vals)
+    check(lib().topmoe_set_tile_override(TILE_SLOTS[gemm], arr), f"set_tile_override({gemm})")
 
 
 class StageEvents:

@@ -72,9 +72,11 @@ class _MoEFunction(torch.autograd.Function):
         k, aux_coef, z_coef, capacity_factor, norm, has_res = ctx.cfg
         if dy is None:
             dy = torch.zeros_like(x)
-        # the C ABI takes the loss terms' upstream gradients as host scalars
-        aux_grad = float(daux.reshape(-1)[0]) if daux is not None else 0.0
-        z_grad = float(dz.reshape(-1)[0]) if dz is not None else 0.0
+        # the loss terms' upstream gradients stay on the device (the kernel
+        # reads them): no host synchronisation in the backward
+        f32 = lambda t: t.reshape(-1)[:1].to(torch.float32).contiguous()
+        aux_grad = f32(daux) if daux is not None else 0.0
+        z_grad = f32(dz) if dz is not None else 0.0
         g = ops.moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy.contiguous(), k, aux_coef, aux_grad=aux_grad,
                             norm_topk_prob=norm, z_coef=z_coef, z_grad=z_grad,
                             capacity_factor=capacity_factor, workspace=ctx.saved,

@@ -14,6 +14,14 @@ hipError_t launch_gemm_bf16(int kind, GemmShape sh, const GemmParams& p, int64_t
 hipError_t launch_gemm_f32(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
                            const Launch& s);
 
+bool gemm_shape_supported_bf16(int kind, const GemmShape& sh);
+bool gemm_shape_supported_f32(int kind, const GemmShape& sh);
+
+bool gemm_shape_supported(int kind, int dtype, const GemmShape& sh) {
+  return dtype == TOPMOE_DTYPE_FP32 ? gemm_shape_supported_f32(kind, sh)
+                                    : gemm_shape_supported_bf16(kind, sh);
+}
+
 hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
                        int64_t mtiles, const Launch& s) {
   return dtype == TOPMOE_DTYPE_FP32 ? launch_gemm_f32(kind, shape, p, mtiles, s)
@@ -68,7 +76,7 @@ bool nonneg_finite(float v) { return v >= 0.0f && !isinf(v); }
 
 extern "C" {
 
-int topmoe_version(void) { return 140; }
+int topmoe_version(void) { return 150; }
 
 const char* topmoe_strerror(int status) {
   switch (status) {
@@ -82,7 +90,8 @@ const char* topmoe_strerror(int status) {
     case TOPMOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case TOPMOE_ERR_BAD_ARG:
       return "invalid argument (aux_coef, z_coef or capacity_factor negative or not finite, "
-             "aux_grad or z_grad not finite, unknown flag bits, or a misaligned pointer)";
+             "aux_grad or z_grad not finite, unknown flag bits, a misaligned pointer, or a "
+             "launch-shape override that is not instantiated)";
   }
   return "unknown status";
 }
@@ -183,8 +192,12 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
     return TOPMOE_ERR_NULL_ARG;
   if (!nonneg_finite(aux_coef) || !nonneg_finite(z_coef) || !nonneg_finite(capacity_factor))
     return TOPMOE_ERR_BAD_ARG;
-  if (flags & ~TOPMOE_MOE_RAW_TOPK_WEIGHTS) return TOPMOE_ERR_BAD_ARG;
+  if (flags & ~(TOPMOE_MOE_RAW_TOPK_WEIGHTS | TOPMOE_MOE_EVAL)) return TOPMOE_ERR_BAD_ARG;
   const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
+  if (flags & TOPMOE_MOE_EVAL) {  // outside training the module adds no aux (or z) loss
+    aux_coef = 0.f;
+    z_coef = 0.f;
+  }
   if (workspace_bytes < pl.total) return TOPMOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
       !aligned(Wd, 16) || !aligned(residual, 16) || !aligned(y, 16) || !aligned(topk_idx, 4) ||
@@ -266,8 +279,8 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
     TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
   }
   TOPMOE_TRY(st.close(l2));
-  // 3: grouped down GEMM, alpha-scaled, into y (k == 1, no capacity) or the slots
-  const bool direct = k == 1 && cap == 0;
+  // 3: grouped down GEMM, alpha-scaled, into y (k == 1) or the slots
+  const bool direct = k == 1;
   const Launch l3 = st.at(3);
   GemmParams dn{};
   dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = direct ? y : slots;
@@ -277,10 +290,13 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   TOPMOE_TRY(launch_gemm(direct ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
                          pl.down_mtiles, l3));
   TOPMOE_TRY(st.close(l3));
-  // 4: fixed-order combine of the kept slots
+  // 4: fixed-order combine of the kept slots (k == 1 under a capacity: the
+  // dropped tokens' rows of y, which the down GEMM did not write)
   const Launch l4 = st.at(4);
   if (!direct)
     TOPMOE_TRY(launch_combine(slots, topk_idx, keep, residual, N, int(H), k, dtype, y, l4));
+  else if (cap > 0)
+    TOPMOE_TRY(launch_combine(nullptr, topk_idx, keep, residual, N, int(H), k, dtype, y, l4));
   TOPMOE_TRY(st.close(l4));
   return TOPMOE_OK;
 }
@@ -466,7 +482,8 @@ int ffn_swiglu_bwd_saved(const void* x, const void* Wg, const void* Wu, const vo
 }
 
 int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, const void* Wd,
-                const void* dy, float aux_grad, float z_grad, int64_t N, int64_t H, int64_t I,
+                const void* dy, float aux_grad, float z_grad, const float* aux_grad_scale,
+                const float* z_grad_scale, int64_t N, int64_t H, int64_t I,
                 int E, int k, float aux_coef, float z_coef, float capacity_factor, int flags,
                 int dtype, void* dx, float* dWr, void* dWg, void* dWu, void* dWd, void* workspace,
                 size_t workspace_bytes, void* stream, void* const* stage_events) {
@@ -479,7 +496,13 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   if (!nonneg_finite(aux_coef) || !nonneg_finite(z_coef) || !nonneg_finite(capacity_factor) ||
       !isfinite(aux_grad) || !isfinite(z_grad))
     return TOPMOE_ERR_BAD_ARG;
-  if (flags & ~(TOPMOE_MOE_RAW_TOPK_WEIGHTS | TOPMOE_MOE_BWD_SAVED)) return TOPMOE_ERR_BAD_ARG;
+  if (flags & ~(TOPMOE_MOE_RAW_TOPK_WEIGHTS | TOPMOE_MOE_BWD_SAVED | TOPMOE_MOE_EVAL))
+    return TOPMOE_ERR_BAD_ARG;
+  if (!aligned(aux_grad_scale, 4) || !aligned(z_grad_scale, 4)) return TOPMOE_ERR_BAD_ARG;
+  if (flags & TOPMOE_MOE_EVAL) {  // outside training: no aux or z-loss term
+    aux_coef = 0.f;
+    z_coef = 0.f;
+  }
   const int cap = capacity_of(capacity_factor, N, k, E);
   const bool renorm = (flags & TOPMOE_MOE_RAW_TOPK_WEIGHTS) == 0;
   const bool saved = (flags & TOPMOE_MOE_BWD_SAVED) != 0;
@@ -603,7 +626,7 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
     const double zscale = N > 0 ? double(z_grad) * double(z_coef) * 2.0 / double(N) : 0.0;
     TOPMOE_TRY(launch_router_bwd(probs, topk_idx, dal, pl.nt_h, counts_off, keep,
                                  z_coef != 0.f ? lse : nullptr, N, E, k, renorm, float(scale),
-                                 float(zscale), dr, l7));
+                                 aux_grad_scale, float(zscale), z_grad_scale, dr, l7));
   }
   TOPMOE_TRY(st.close(l7));
   // 8: dx = sum of the slots (ascending expert) + W_r^T dr
@@ -636,6 +659,8 @@ int moe_ffn_bwd(const void* x, const float* Wr, const void* Wg, const void* Wu, 
   TOPMOE_TRY(st.close(l11));
   return TOPMOE_OK;
 }
+
+int topmoe_set_tile_override(int gemm, const int* shape) { return set_tile_override(gemm, shape); }
 
 int topmoe_events_create(int n, void** events) {
   if (!events || n < 0) return TOPMOE_ERR_NULL_ARG;

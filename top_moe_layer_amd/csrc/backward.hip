@@ -202,7 +202,8 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float* __restrict__ probs, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ dalpha_part, int nt, const int32_t* __restrict__ counts_off,
     const uint8_t* __restrict__ keep, const float* __restrict__ lse, int64_t N, int E, int k,
-    bool renorm, float aux_scale, float z_scale, float* __restrict__ dr) {
+    bool renorm, float aux_scale, const float* __restrict__ aux_mul, float z_scale,
+    const float* __restrict__ z_mul, float* __restrict__ dr) {
   constexpr int TPW = 64 / EP;
   const int lane = int(threadIdx.x) & 63, wave = int(threadIdx.x) >> 6;
   const int u = lane / EP, e = lane - u * EP, base = u * EP;
@@ -241,6 +242,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     const float v = __shfl(dps, base + j, 64);
     if (ex == e) dp = v;
   }
+  // the loss terms' upstream gradients: host factors times optional device scalars
+  if (aux_mul != nullptr) aux_scale *= aux_mul[0];
+  if (z_mul != nullptr) z_scale *= z_mul[0];
   if (el && aux_scale != 0.f) dp += aux_scale * float(counts_off[e + 1] - counts_off[e]);
   const float dot = group_sum<EP>(el ? p * dp : 0.f);
   float g = p * (dp - dot);
@@ -434,13 +438,13 @@ template <int EP>
 hipError_t launch_router_bwd_ep(const float* probs, const int32_t* topk_idx,
                                 const float* dalpha_part, int nt, const int32_t* counts_off,
                                 const uint8_t* keep, const float* lse, int64_t N, int E, int k,
-                                bool renorm, float aux_scale, float z_scale, float* dr,
-                                const Launch& s) {
+                                bool renorm, float aux_scale, const float* aux_mul,
+                                float z_scale, const float* z_mul, float* dr, const Launch& s) {
   constexpr int TPB = 4 * (64 / EP);  // tokens per block
   const int64_t grid = (N + TPB - 1) / TPB;
   return launch_kernel(router_bwd_kernel<EP>, dim3(unsigned(grid)), dim3(256), 0, s, probs,
                        topk_idx, dalpha_part, nt, counts_off, keep, lse, N, E, k, renorm,
-                       aux_scale, z_scale, dr);
+                       aux_scale, aux_mul, z_scale, z_mul, dr);
 }
 
 }  // namespace
@@ -466,12 +470,12 @@ hipError_t launch_gather_transpose(int dtype, const GatherTransposeJobs& jobs, i
 hipError_t launch_router_bwd(const float* probs, const int32_t* topk_idx,
                              const float* dalpha_part, int nt, const int32_t* counts_off,
                              const uint8_t* keep, const float* lse, int64_t N, int E, int k,
-                             bool renorm, float aux_scale, float z_scale, float* dr,
-                             const Launch& s) {
+                             bool renorm, float aux_scale, const float* aux_mul,
+                             float z_scale, const float* z_mul, float* dr, const Launch& s) {
   if (N <= 0) return hipSuccess;
 #define TOPMOE_RB(EPV)                                                                       \
   return launch_router_bwd_ep<EPV>(probs, topk_idx, dalpha_part, nt, counts_off, keep, lse, N, \
-                                   E, k, renorm, aux_scale, z_scale, dr, s)
+                                   E, k, renorm, aux_scale, aux_mul, z_scale, z_mul, dr, s)
   if (E <= 1) TOPMOE_RB(1);
   if (E <= 2) TOPMOE_RB(2);
   if (E <= 4) TOPMOE_RB(4);

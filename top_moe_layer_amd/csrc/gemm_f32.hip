@@ -8,4 +8,8 @@ hipError_t launch_gemm_f32(int kind, GemmShape sh, const GemmParams& p, int64_t 
   return launch_gemm_dtype<float>(kind, sh, p, mtiles, s);
 }
 
+bool gemm_shape_supported_f32(int kind, const GemmShape& sh) {
+  return shape_supported_dtype<float>(kind, sh);
+}
+
 }  // namespace topmoe

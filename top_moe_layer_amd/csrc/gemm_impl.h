@@ -1012,6 +1012,56 @@ hipError_t launch_gemm_tiles(GemmShape sh, const GemmParams& p, int64_t mtiles, 
   return hipErrorInvalidValue;
 }
 
+// Whether launch_gemm_tiles<T, KIND> has shape `sh` (instantiated and valid).
+template <typename T, int KIND>
+bool shape_listed(const GemmShape& sh) {
+#define TOPMOE_HAS_SHAPE(BM_, BN_, WM_, WN_, RB_, S_)                                     \
+  if (sh.bm == (BM_) && sh.bn == (BN_) && sh.wm == (WM_) && sh.wn == (WN_) &&            \
+      sh.rb == (RB_) && sh.stages == (S_))                                               \
+    return shape_ok<BM_, BN_, WM_, WN_, RB_, S_, KIND>();
+  if constexpr (KIND == KIND_BWD_GU) {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_BWDGU_SHAPES_BF16(TOPMOE_HAS_SHAPE)
+    } else {
+      TOPMOE_BWD_SHAPES_F32(TOPMOE_HAS_SHAPE)
+    }
+  } else if constexpr (KIND == KIND_BWD_DH) {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_BWDDH_SHAPES_BF16(TOPMOE_HAS_SHAPE)
+    } else {
+      TOPMOE_BWD_SHAPES_F32(TOPMOE_HAS_SHAPE)
+    }
+  } else if constexpr (KindTraits<KIND>::KGROUP) {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_WGRAD_SHAPES_BF16(TOPMOE_HAS_SHAPE)
+    } else {
+      TOPMOE_WGRAD_SHAPES_F32(TOPMOE_HAS_SHAPE)
+    }
+  } else {
+    if constexpr (sizeof(T) == 2) {
+      TOPMOE_GEMM_SHAPES_BF16(TOPMOE_HAS_SHAPE)
+    } else {
+      TOPMOE_GEMM_SHAPES_F32(TOPMOE_HAS_SHAPE)
+    }
+  }
+#undef TOPMOE_HAS_SHAPE
+  return false;
+}
+
+template <typename T>
+bool shape_supported_dtype(int kind, const GemmShape& sh) {
+  switch (kind) {
+    case KIND_GATEUP: return shape_listed<T, KIND_GATEUP>(sh);
+    case KIND_DOWN_Y: return shape_listed<T, KIND_DOWN_Y>(sh);
+    case KIND_DOWN_SLOTS: return shape_listed<T, KIND_DOWN_SLOTS>(sh);
+    case KIND_BWD_GU: return shape_listed<T, KIND_BWD_GU>(sh);
+    case KIND_BWD_DH: return shape_listed<T, KIND_BWD_DH>(sh);
+    case KIND_WGRAD2: return shape_listed<T, KIND_WGRAD2>(sh);
+    case KIND_WGRAD1: return shape_listed<T, KIND_WGRAD1>(sh);
+  }
+  return false;
+}
+
 template <typename T>
 hipError_t launch_gemm_dtype(int kind, GemmShape sh, const GemmParams& p, int64_t mtiles,
                              const Launch& s) {

@@ -39,20 +39,6 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, unsigned s
                             L.start, L.stop, 0);
 }
 
-enum GemmKind {
-  KIND_GATEUP = 0,      // h = SiLU(A Wg^T) * (A Wu^T), rows gathered from x
-  KIND_DOWN_Y = 1,      // y[token] = alpha * (h Wd^T), written in the output dtype
-  KIND_DOWN_SLOTS = 2,  // slot[entry] = alpha * (h Wd^T), in the operand dtype
-  // backward
-  KIND_BWD_GU = 3,      // g, u = x Wg^T, x Wu^T (rows gathered from x): writes the pairs
-                        // (g, u) row-major and h^T in padded group columns
-  KIND_WGRAD2 = 4,      // out0 = A0 B^T, out1 = A1 B^T per group, K = the group's padded rows
-  KIND_WGRAD1 = 5,      // out0 = A0 B^T per group, K = the group's padded rows
-  KIND_BWD_DH = 6,      // dh = alpha * dy Wd (rows gathered from dy), with the pairs (g, u):
-                        // writes [dg | du] row-major, dg^T / du^T in padded group columns and
-                        // per-row partial sums of dh_raw . h (d alpha)
-};
-
 struct GemmParams {
   const void* A;           // gate/up, bwd gu: x [N, K]; bwd dh: dy [N, K];
                            // down: h or [dg|du] [rows, K];
@@ -156,8 +142,8 @@ hipError_t launch_gather_transpose(int dtype, const GatherTransposeJobs& jobs, i
 hipError_t launch_router_bwd(const float* probs, const int32_t* topk_idx,
                              const float* dalpha_part, int nt, const int32_t* counts_off,
                              const uint8_t* keep, const float* lse, int64_t N, int E, int k,
-                             bool renorm, float aux_scale, float z_scale, float* dr,
-                             const Launch& s);
+                             bool renorm, float aux_scale, const float* aux_mul,
+                             float z_scale, const float* z_mul, float* dr, const Launch& s);
 hipError_t launch_combine_bwd(const void* slots, const int32_t* topk_idx, const uint8_t* keep,
                               const float* dr, const float* Wr, int64_t N, int H, int E, int k,
                               int dtype, void* dx, const Launch& s);

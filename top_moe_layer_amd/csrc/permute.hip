@@ -236,7 +236,9 @@ __device__ __forceinline__ void store16<bf16_t>(bf16_t* p, const float (&v)[8]) 
 // rounded to the output dtype, like the terms the pages' index_add_
 // accumulates), in ascending expert id, accumulated in fp32 and rounded once.
 // The residual may alias y: each thread reads its residual piece before
-// writing the same piece of y.
+// writing the same piece of y.  Without slots (k == 1 under a capacity, where
+// the down GEMM wrote the kept tokens' rows of y) only the tokens whose entry
+// was dropped are written: y = residual (or 0).
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slots,
                                                       const int32_t* __restrict__ topk_idx,
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
   if (gid >= N * hv) return;
   const int64_t t = gid / hv;
   const int h = int(gid - t * hv) * V;
+  if (slots == nullptr && keep[t] != 0) return;  // kept: written by the down GEMM
   const int32_t* ids = topk_idx + t * k;
   float acc[V];
   if (residual != nullptr) {
@@ -265,6 +268,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
       if (e > prev && e < best_e) { best_e = e; best_j = j; }
     }
     prev = best_e;
+    if (slots == nullptr) break;
     if (keep != nullptr && keep[t * k + best_j] == 0) continue;  // dropped by the capacity
     float v[V];
     load16<T>(slots + (t * k + best_j) * H + h, v);

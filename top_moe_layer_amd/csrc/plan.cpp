@@ -3,6 +3,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/topmoe.h"
 
@@ -56,23 +57,64 @@ GemmShape choose(const Cand* cands, int n, int64_t M, int64_t Nout, int64_t K, i
   return best;
 }
 
-// "BMxBNxWMxWNxRBxS" (or "BMxBNxS" for a 2x2 wavefront grid with 128-byte
-// rows) from the environment, for launch-shape sweeps; it must name an
-// instantiated shape, otherwise the launch reports an invalid value.
-bool env_shape(const char* name, GemmShape* out) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return false;
+// ---- launch-shape overrides (tuning sweeps, tests).  One slot per GEMM of
+// the path; each holds "none", a shape, or "invalid" (an environment value
+// that is not an instantiated shape: every plan that would use it fails).
+constexpr int kSlots = 6;
+const char* const kSlotEnv[kSlots] = {"TOPMOE_GATEUP_TILE", "TOPMOE_DOWN_TILE",
+                                      "TOPMOE_BWDGU_TILE", "TOPMOE_BWDDH_TILE",
+                                      "TOPMOE_WGU_TILE", "TOPMOE_WD_TILE"};
+const int kSlotKind[kSlots] = {KIND_GATEUP, KIND_DOWN_Y, KIND_BWD_GU, KIND_BWD_DH, KIND_WGRAD2,
+                               KIND_WGRAD1};
+
+struct Override {
+  int state = 0;  // 0 none, 1 shape, -1 invalid
+  GemmShape sh;
+};
+
+struct Overrides {
+  std::mutex mu;
+  bool env_read = false;
+  Override slot[kSlots];
+};
+
+Overrides& overrides() {
+  static Overrides o;
+  return o;
+}
+
+bool parse_shape(const char* v, GemmShape* out) {
   GemmShape g;
-  if (std::sscanf(v, "%dx%dx%dx%dx%dx%d", &g.bm, &g.bn, &g.wm, &g.wn, &g.rb, &g.stages) == 6) {
-    *out = g;
-    return true;
+  char tail = 0;
+  if (std::sscanf(v, "%dx%dx%dx%dx%dx%d%c", &g.bm, &g.bn, &g.wm, &g.wn, &g.rb, &g.stages,
+                  &tail) != 6)
+    return false;
+  *out = g;
+  return true;
+}
+
+// The override of a slot for `dtype`: TOPMOE_OK with *sh replaced when one is
+// set, TOPMOE_ERR_BAD_ARG when the one set is not an instantiated shape for
+// this GEMM and dtype.  The environment is read once, at the first call.
+int apply_override(int slot, int dtype, GemmShape* sh) {
+  Overrides& o = overrides();
+  std::lock_guard<std::mutex> lock(o.mu);
+  if (!o.env_read) {
+    o.env_read = true;
+    for (int i = 0; i < kSlots; ++i) {
+      const char* v = std::getenv(kSlotEnv[i]);
+      if (!v || !*v) continue;
+      GemmShape g;
+      o.slot[i].state = parse_shape(v, &g) ? 1 : -1;
+      o.slot[i].sh = g;
+    }
   }
-  GemmShape h;
-  if (std::sscanf(v, "%dx%dx%d", &h.bm, &h.bn, &h.stages) == 3) {
-    *out = h;
-    return true;
-  }
-  return false;
+  const Override& ov = o.slot[slot];
+  if (ov.state == 0) return TOPMOE_OK;
+  if (ov.state < 0 || !gemm_shape_supported(kSlotKind[slot], dtype, ov.sh))
+    return TOPMOE_ERR_BAD_ARG;
+  *sh = ov.sh;
+  return TOPMOE_OK;
 }
 
 // Launch-shape tables: rates measured on MI355X over the dense bf16
@@ -110,43 +152,51 @@ bool weight_streaming(int64_t M, int groups) { return M <= int64_t(groups) * 32;
 
 GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 2);
-  GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
-                                             : choose(kGateupBf16, 3, M, Nout, K, groups, 2);
-  env_shape("TOPMOE_GATEUP_TILE", &sh);
-  return sh;
+  return weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
+                                     : choose(kGateupBf16, 3, M, Nout, K, groups, 2);
 }
 
 GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype) {
   if (dtype == TOPMOE_DTYPE_FP32) return choose(kFp32, 2, M, Nout, K, groups, 1);
-  GemmShape sh = weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
-                                             : choose(kDownBf16, 5, M, Nout, K, groups, 1);
-  env_shape("TOPMOE_DOWN_TILE", &sh);
-  return sh;
+  return weight_streaming(M, groups) ? GemmShape{64, 128, 2, 4, 128, 3}
+                                     : choose(kDownBf16, 5, M, Nout, K, groups, 1);
 }
 
 // ---- backward launch shapes (bf16 candidates measured on MI355X; fp32 the
-// register-light tiles).  Environment overrides as for the forward.
-GemmShape bwd_shape(const char* env, GemmShape bf16, GemmShape f32, int dtype) {
-  GemmShape sh = dtype == TOPMOE_DTYPE_FP32 ? f32 : bf16;
-  env_shape(env, &sh);
-  return sh;
-}
-
+// register-light tiles).
 GemmShape gu_tile(int dtype) {
-  return bwd_shape("TOPMOE_BWDGU_TILE", GemmShape{256, 128, 4, 2, 128, 2},
-                   GemmShape{128, 64, 2, 2, 128, 2}, dtype);
+  return dtype == TOPMOE_DTYPE_FP32 ? GemmShape{128, 64, 2, 2, 128, 2}
+                                    : GemmShape{256, 128, 4, 2, 128, 2};
 }
 GemmShape dh_tile(int dtype) {
-  return bwd_shape("TOPMOE_BWDDH_TILE", GemmShape{128, 128, 2, 4, 128, 3},
-                   GemmShape{64, 64, 2, 2, 128, 3}, dtype);
+  return dtype == TOPMOE_DTYPE_FP32 ? GemmShape{64, 64, 2, 2, 128, 3}
+                                    : GemmShape{128, 128, 2, 4, 128, 3};
 }
 GemmShape wgu_tile(int dtype) {
-  return bwd_shape("TOPMOE_WGU_TILE", GemmShape{128, 256, 2, 4, 128, 2},
-                   GemmShape{128, 64, 2, 2, 128, 2}, dtype);
+  return dtype == TOPMOE_DTYPE_FP32 ? GemmShape{128, 64, 2, 2, 128, 2}
+                                    : GemmShape{128, 256, 2, 4, 128, 2};
 }
 GemmShape wd_tile(int dtype) {
-  return bwd_shape("TOPMOE_WD_TILE", GemmShape{256, 128, 4, 2, 128, 3},
-                   GemmShape{128, 64, 2, 2, 128, 2}, dtype);
+  return dtype == TOPMOE_DTYPE_FP32 ? GemmShape{128, 64, 2, 2, 128, 2}
+                                    : GemmShape{256, 128, 4, 2, 128, 3};
+}
+
+int set_tile_override(int slot, const int* shape) {
+  if (slot < 0 || slot >= kSlots) return TOPMOE_ERR_BAD_ARG;
+  Overrides& o = overrides();
+  std::lock_guard<std::mutex> lock(o.mu);
+  o.env_read = true;  // an explicit setting replaces what the environment said
+  if (shape == nullptr) {
+    o.slot[slot].state = 0;
+    return TOPMOE_OK;
+  }
+  const GemmShape g{shape[0], shape[1], shape[2], shape[3], shape[4], shape[5]};
+  if (!gemm_shape_supported(kSlotKind[slot], TOPMOE_DTYPE_BF16, g) &&
+      !gemm_shape_supported(kSlotKind[slot], TOPMOE_DTYPE_FP32, g))
+    return TOPMOE_ERR_BAD_ARG;
+  o.slot[slot].state = 1;
+  o.slot[slot].sh = g;
+  return TOPMOE_OK;
 }
 
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
@@ -159,6 +209,9 @@ int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
   q.N = N; q.H = H; q.I = I; q.dtype = dtype; q.elem = elem_bytes(dtype);
   q.up = choose_gateup_tile(N, I, H, 1, dtype);
   q.down = choose_down_tile(N, H, I, 1, dtype);
+  int st = apply_override(0, dtype, &q.up);
+  if (st == TOPMOE_OK) st = apply_override(1, dtype, &q.down);
+  if (st != TOPMOE_OK) return st;
   q.off_h = 0;
   q.total = align_up(size_t(N) * size_t(I) * q.elem);
   if (q.total == 0) q.total = kAlign;
@@ -202,6 +255,9 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.nblk = int((N + tb - 1) / tb);
   q.up = choose_gateup_tile(rows, I, H, E, dtype);
   q.down = choose_down_tile(rows, H, I, E, dtype);
+  int st = apply_override(0, dtype, &q.up);
+  if (st == TOPMOE_OK) st = apply_override(1, dtype, &q.down);
+  if (st != TOPMOE_OK) return st;
   q.up_mtiles = grouped_mtiles_bound(rows, E, q.up.bm);
   q.down_mtiles = grouped_mtiles_bound(rows, E, q.down.bm);
   size_t o = 0;
@@ -215,8 +271,8 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_sorted = o;     o = align_up(o + size_t(rows) * 4);
   q.off_alpha_g = o;    o = align_up(o + size_t(rows) * 4);
   q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);
-  q.off_slots = o;  // k-slots; also for k = 1 so that a capacity can drop rows
-  o = align_up(o + size_t(rows) * size_t(H) * q.elem);
+  q.off_slots = o;  // k-slots (k >= 2 only: with k = 1 the down GEMM writes y itself)
+  if (k > 1) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
   q.total = o == 0 ? kAlign : o;
   *p = q;
   return TOPMOE_OK;
@@ -238,6 +294,14 @@ int plan_ffn_bwd(int64_t N, int64_t H, int64_t I, int dtype, FfnBwdPlan* p) {
   q.dx = choose_down_tile(N, H, 2 * I, 1, dtype);
   q.wgu = wgu_tile(dtype);
   q.wd = wd_tile(dtype);
+  {
+    GemmShape* sh[5] = {&q.gu, &q.dh, &q.dx, &q.wgu, &q.wd};
+    const int slot[5] = {2, 3, 1, 4, 5};
+    for (int i = 0; i < 5; ++i) {
+      const int so = apply_override(slot[i], dtype, sh[i]);
+      if (so != TOPMOE_OK) return so;
+    }
+  }
   const size_t e = size_t(el);
   size_t o = 0;
   q.off_wgT = o;  o = align_up(o + size_t(H) * size_t(2 * I) * e);
@@ -272,6 +336,14 @@ int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBw
   q.dx = choose_down_tile(rows, H, 2 * I, E, dtype);
   q.wgu = wgu_tile(dtype);
   q.wd = wd_tile(dtype);
+  {
+    GemmShape* sh[5] = {&q.gu, &q.dh, &q.dx, &q.wgu, &q.wd};
+    const int slot[5] = {2, 3, 1, 4, 5};
+    for (int i = 0; i < 5; ++i) {
+      const int so = apply_override(slot[i], dtype, sh[i]);
+      if (so != TOPMOE_OK) return so;
+    }
+  }
   q.gu_mtiles = grouped_mtiles_bound(rows, E, q.gu.bm);
   q.dh_mtiles = grouped_mtiles_bound(rows, E, q.dh.bm);
   q.dx_mtiles = grouped_mtiles_bound(rows, E, q.dx.bm);

@@ -8,6 +8,20 @@
 
 namespace topmoe {
 
+enum GemmKind {
+  KIND_GATEUP = 0,      // h = SiLU(A Wg^T) * (A Wu^T), rows gathered from x
+  KIND_DOWN_Y = 1,      // y[token] = alpha * (h Wd^T), written in the output dtype
+  KIND_DOWN_SLOTS = 2,  // slot[entry] = alpha * (h Wd^T), in the operand dtype
+  // backward
+  KIND_BWD_GU = 3,      // g, u = x Wg^T, x Wu^T (rows gathered from x): writes the pairs
+                        // (g, u) row-major and h^T in padded group columns
+  KIND_WGRAD2 = 4,      // out0 = A0 B^T, out1 = A1 B^T per group, K = the group's padded rows
+  KIND_WGRAD1 = 5,      // out0 = A0 B^T per group, K = the group's padded rows
+  KIND_BWD_DH = 6,      // dh = alpha * dy Wd (rows gathered from dy), with the pairs (g, u):
+                        // writes [dg | du] row-major, dg^T / du^T in padded group columns and
+                        // per-row partial sums of dh_raw . h (d alpha)
+};
+
 constexpr size_t kAlign = 256;
 constexpr int kDwrChunk = 64;   // tokens per partial of the router-weight gradient
 
@@ -118,6 +132,17 @@ int plan_moe_bwd(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoeBw
 // Launch shape for an M x Nout x K GEMM with `groups` row groups (experts).
 GemmShape choose_gateup_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype);
 GemmShape choose_down_tile(int64_t M, int64_t Nout, int64_t K, int groups, int dtype);
+
+// Whether the GEMM kernels of `kind` (a GemmKind) are instantiated with
+// launch shape `sh` for `dtype` (defined beside the kernels; host code).
+bool gemm_shape_supported(int kind, int dtype, const GemmShape& sh);
+
+// Launch-shape overrides, for tuning sweeps and tests: one per GEMM of the
+// path (the TOPMOE_TILE_* slots of include/topmoe.h).  Initialised once from
+// the environment (TOPMOE_GATEUP_TILE, TOPMOE_DOWN_TILE, TOPMOE_BWDGU_TILE,
+// TOPMOE_BWDDH_TILE, TOPMOE_WGU_TILE, TOPMOE_WD_TILE: "BMxBNxWMxWNxRBxS"),
+// then set through set_tile_override.
+int set_tile_override(int slot, const int* shape);
 
 // Upper bound on the number of BM-row tiles over `groups` groups of total M rows.
 inline int64_t grouped_mtiles_bound(int64_t M, int groups, int bm) {

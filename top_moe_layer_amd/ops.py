@@ -1,8 +1,15 @@
 """Torch-tensor front end of the C ABI: shape / dtype checks, output and
-workspace allocation through PyTorch, the current HIP stream.  Nothing here
-computes any part of the forward pass."""
+workspace allocation through PyTorch, the caller's HIP stream (the current one
+by default).  Nothing here computes any part of the forward pass.
+
+Every tensor these functions allocate (outputs and internal workspaces) is
+allocated while the stream the kernels run on is torch's current stream, so
+the caching allocator ties the memory to that stream: an internal workspace
+released on return is only handed out again to work ordered after these
+kernels on the same stream."""
 from __future__ import annotations
 
+import functools
 from dataclasses import dataclass
 from typing import Optional
 
@@ -44,6 +51,30 @@ def _stream(device, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(device, stream):
+    """The torch stream object the kernels will run on: the current stream of
+    ``device`` when ``stream`` is None, an ExternalStream for a raw handle."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _on_caller_stream(fn):
+    """Run ``fn`` with the kernels' stream as torch's current stream, so that
+    the tensors it allocates belong to that stream (see the module docstring).
+    Tensors that are not on a GPU pass through to ``fn``'s own checks."""
+    @functools.wraps(fn)
+    def wrapped(x, *args, stream=None, **kw):
+        if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+            return fn(x, *args, stream=stream, **kw)
+        ts = _torch_stream(x.device, stream)
+        with torch.cuda.stream(ts):
+            return fn(x, *args, stream=ts, **kw)
+    return wrapped
+
+
 def _buffer(t: torch.Tensor, name: str, nbytes: int, device) -> torch.Tensor:
     """A caller-provided byte buffer: on the device, contiguous, large enough."""
     if not isinstance(t, torch.Tensor):
@@ -71,6 +102,7 @@ def moe_workspace_bytes(N: int, H: int, I: int, E: int, k: int, dtype: torch.dty
     return B.raw_moe_workspace_bytes(N, H, I, E, k, _dtype_code(dtype))
 
 
+@_on_caller_stream
 def ffn_swiglu_fwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor, *,
                    residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None,
@@ -129,6 +161,7 @@ class MoeOutput:
     z_loss: Optional[torch.Tensor] = None
 
 
+@_on_caller_stream
 def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
                 Wd: torch.Tensor, k: int, aux_coef: float, *,
                 residual: Optional[torch.Tensor] = None, norm_topk_prob: bool = True,
@@ -138,7 +171,8 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
                 expert_offsets: Optional[torch.Tensor] = None,
                 sorted_token_ids: Optional[torch.Tensor] = None, return_lists: bool = True,
                 workspace: Optional[torch.Tensor] = None, saved: Optional[torch.Tensor] = None,
-                stream=None, stage_events: Optional[B.StageEvents] = None) -> MoeOutput:
+                training: bool = True, stream=None,
+                stage_events: Optional[B.StageEvents] = None) -> MoeOutput:
     """Top-k MoE FFN forward.  x [..., H]; Wr [E, H] float32; Wg, Wu [E, I, H];
     Wd [E, H, I].  Returns y (x's shape), topk_idx / alpha [N, k], aux_loss [1]
     and, when ``return_lists``, expert_offsets [E+1] and sorted_token_ids [N*k].
@@ -149,7 +183,8 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     then hold the kept tokens).  ``saved`` (a backward workspace,
     moe_bwd_workspace_bytes long): also keep the routing, g, u and h there
     for ``moe_ffn_bwd(..., workspace=saved, from_saved=True)``; the outputs
-    are the same either way."""
+    are the same either way.  ``training`` False is the module outside
+    training: aux_loss (and z_loss) are zero whatever the coefficients."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -186,7 +221,7 @@ def moe_ffn_fwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     if nbytes == 0:
         B.check(B.ERR_BAD_SHAPE, "moe_ffn_fwd")
     ws = _workspace(nbytes, dev, workspace)
-    flags = 0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS
+    flags = (0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS) | (0 if training else B.MOE_EVAL)
     args = (_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(rf), N, H, I, E, k,
             float(aux_coef), float(z_coef), float(capacity_factor), flags, code, _ptr(y),
             _ptr(topk_idx), _ptr(alpha), _ptr(aux_loss), _ptr(z_loss), _ptr(expert_offsets),
@@ -229,6 +264,7 @@ class MoeGrads:
     dWd: torch.Tensor
 
 
+@_on_caller_stream
 def ffn_swiglu_bwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
                    dy: torch.Tensor, *, workspace: Optional[torch.Tensor] = None,
                    from_saved: bool = False, stream=None,
@@ -267,10 +303,11 @@ def ffn_swiglu_bwd(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torc
     return FfnGrads(dx.view(x.shape), dWg, dWu, dWd)
 
 
+@_on_caller_stream
 def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
                 Wd: torch.Tensor, dy: torch.Tensor, k: int, aux_coef: float, *,
-                aux_grad: float = 1.0, norm_topk_prob: bool = True, z_coef: float = 0.0,
-                z_grad: float = 1.0, capacity_factor: float = 0.0,
+                aux_grad=1.0, norm_topk_prob: bool = True, z_coef: float = 0.0,
+                z_grad=1.0, capacity_factor: float = 0.0,
                 workspace: Optional[torch.Tensor] = None, from_saved: bool = False, stream=None,
                 stage_events: Optional[B.StageEvents] = None) -> MoeGrads:
     """Gradients of the top-k MoE FFN (and of ``aux_grad`` * aux_loss and
@@ -278,7 +315,9 @@ def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
     [E, H] float32, dWg, dWu [E, I, H], dWd [E, H, I].  The routing (with the
     same capacity) is recomputed from x and Wr.  ``from_saved``: ``workspace``
     is the ``saved`` buffer of a training forward on the same inputs and
-    arguments, and neither the routing nor g, u are recomputed."""
+    arguments, and neither the routing nor g, u are recomputed.  ``aux_grad``
+    and ``z_grad`` are floats or one-element float32 device tensors (read by
+    the kernel: no host synchronisation)."""
     dev = x.device
     H = x.shape[-1]
     E, I = Wg.shape[0], Wg.shape[1]
@@ -303,8 +342,18 @@ def moe_ffn_bwd(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.T
         raise ValueError("from_saved needs the training forward's saved buffer as workspace")
     ws = _workspace(nbytes, dev, workspace)
     flags = (0 if norm_topk_prob else B.MOE_RAW_TOPK_WEIGHTS) | (B.MOE_BWD_SAVED if from_saved else 0)
+
+    def scalar(v, name):  # (host factor, device scalar or None)
+        if isinstance(v, torch.Tensor):
+            t = v.reshape(-1)
+            _need(t, name, (1,), torch.float32, dev)
+            return 1.0, t
+        return float(v), None
+
+    ag, ag_t = scalar(aux_grad, "aux_grad")
+    zg, zg_t = scalar(z_grad, "z_grad")
     st = B.raw_moe_ffn_bwd(_ptr(xf), _ptr(Wr), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(dyf),
-                           float(aux_grad), float(z_grad), N, H, I, E, k, float(aux_coef),
+                           ag, zg, _ptr(ag_t), _ptr(zg_t), N, H, I, E, k, float(aux_coef),
                            float(z_coef), float(capacity_factor), flags, code,
                            _ptr(dx), _ptr(dWr), _ptr(dWg), _ptr(dWu), _ptr(dWd), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(dev, stream),
