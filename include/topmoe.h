@@ -80,6 +80,8 @@ extern "C" {
                                                finite; aux_grad or z_grad not finite; unknown
                                                flag bits; misaligned pointer; a launch-shape
                                                override that is not instantiated */
+#define TOPMOE_ERR_SCRATCH_TOO_SMALL    -7  /* moe_ffn_fwd_noalloc: the problem's workspace
+                                               exceeds the fixed scratch */
 
 /* ---- dtypes ------------------------------------------------------------ */
 #define TOPMOE_DTYPE_FP32 0
@@ -191,6 +193,28 @@ int moe_ffn_fwd(const void* x, const float* Wr, const void* Wg, const void* Wu,
                 float* z_loss, int32_t* expert_offsets, int32_t* sorted_token_ids,
                 void* workspace, size_t workspace_bytes,
                 void* stream, void* const* stage_events);
+
+/* ---- no allocation ------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the MoE
+ * forward with its workspace in a fixed scratch array that the library holds
+ * in device memory, one per GPU it runs on, from the first use until the
+ * process ends (TOPMOE_NOALLOC_SCRATCH_BYTES: 64 MiB).  Arguments,
+ * outputs, errors and results are those of moe_ffn_fwd (the same bits)
+ * without the workspace pair; a problem whose moe_workspace_bytes() exceeds
+ * the scratch returns TOPMOE_ERR_SCRATCH_TOO_SMALL before anything else
+ * happens.  The call allocates nothing: the scratch's device address is
+ * looked up once per device (the device current at the call must be the
+ * stream's).  All calls on one GPU share its scratch, so calls that overlap
+ * on one GPU (other streams, other host threads) race: serialise them.  The
+ * scratch keeps the last call's contents; nothing in it needs clearing. */
+#define TOPMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_ffn_fwd_noalloc(const void* x, const float* Wr, const void* Wg, const void* Wu,
+                        const void* Wd, const void* residual, int64_t N, int64_t H, int64_t I,
+                        int E, int k, float aux_coef, float z_coef, float capacity_factor,
+                        int flags, int dtype, void* y, int32_t* topk_idx, float* alpha,
+                        float* aux_loss, float* z_loss, int32_t* expert_offsets,
+                        int32_t* sorted_token_ids, void* stream, void* const* stage_events);
 
 /* ---- backward ------------------------------------------------------------
  * Gradients of the forward above (same shapes, dtypes and flags).  The

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_strerror_covers_codes(L):
     for code in (B.OK, B.ERR_NULL_ARG, B.ERR_BAD_SHAPE, B.ERR_UNSUPPORTED_DTYPE,
-                 B.ERR_WORKSPACE_TOO_SMALL, B.ERR_HIP, B.ERR_BAD_ARG):
+                 B.ERR_WORKSPACE_TOO_SMALL, B.ERR_HIP, B.ERR_BAD_ARG, B.ERR_SCRATCH_TOO_SMALL):
         assert B.strerror(code) != "unknown status"
     assert B.strerror(-99) == "unknown status"
 
@@ -369,3 +369,13 @@ def test_front_end_allocates_on_the_kernels_stream(monkeypatch):
     assert fn(x, stream=1234) == 7
     assert seen == [(("stream", 1234), [("stream", 1234)])]
     assert entered[-1] == "exit"
+
+
+def test_noalloc_size_limit_checked_first(L):
+    """The no-allocation forward rejects a problem whose workspace exceeds its
+    fixed scratch before touching any device (shape errors come first)."""
+    args = lambda N, k: (FAKE, FAKE, FAKE, FAKE, FAKE, None, N, 768, 2432, 8, k, 0.01, 0.0, 0.0, 0,
+                         B.DTYPE_BF16, FAKE, FAKE, FAKE, FAKE, None, None, None, None, None)
+    assert B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_BF16) > B.NOALLOC_SCRATCH_BYTES
+    assert B.raw_moe_ffn_fwd_noalloc(*args(16384, 2)) == B.ERR_SCRATCH_TOO_SMALL
+    assert B.raw_moe_ffn_fwd_noalloc(*args(16384, 9)) == B.ERR_BAD_SHAPE

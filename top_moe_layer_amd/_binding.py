@@ -20,6 +20,8 @@ ERR_UNSUPPORTED_DTYPE = -3
 ERR_WORKSPACE_TOO_SMALL = -4
 ERR_HIP = -5
 ERR_BAD_ARG = -6
+ERR_SCRATCH_TOO_SMALL = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DTYPE_FP32 = 0
 DTYPE_BF16 = 1
 MOE_RAW_TOPK_WEIGHTS = 1
@@ -48,6 +50,9 @@ SIGNATURES = {
     "moe_ffn_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32, _f32,
                            _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                            _vp]),
+    "moe_ffn_fwd_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                   _f32, _f32, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp]),
     "ffn_swiglu_fwd_train": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz,
                                     _vp, _sz, _vp, _vp]),
     "moe_ffn_fwd_train": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
@@ -127,6 +132,14 @@ def raw_moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef, ca
     return int(lib().moe_ffn_fwd(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef,
                                  capacity_factor, flags, dtype, y, topk_idx, alpha, aux, z_loss,
                                  offsets, sorted_ids, ws, ws_bytes, stream, events))
+
+
+def raw_moe_ffn_fwd_noalloc(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef, z_coef,
+                            capacity_factor, flags, dtype, y, topk_idx, alpha, aux, z_loss,
+                            offsets, sorted_ids, stream, events) -> int:
+    return int(lib().moe_ffn_fwd_noalloc(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, coef,
+                                         z_coef, capacity_factor, flags, dtype, y, topk_idx,
+                                         alpha, aux, z_loss, offsets, sorted_ids, stream, events))
 
 
 def raw_ffn_swiglu_fwd_train(x, Wg, Wu, Wd, residual, y, N, H, I, dtype, ws, ws_bytes, saved,

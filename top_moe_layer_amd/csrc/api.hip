@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "plan.h"
 
@@ -88,6 +90,9 @@ const char* topmoe_strerror(int status) {
     case TOPMOE_ERR_UNSUPPORTED_DTYPE: return "dtype must be TOPMOE_DTYPE_FP32 or TOPMOE_DTYPE_BF16";
     case TOPMOE_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the *_workspace_bytes() size";
     case TOPMOE_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case TOPMOE_ERR_SCRATCH_TOO_SMALL:
+      return "the problem needs more workspace (moe_workspace_bytes()) than the fixed scratch "
+             "of moe_ffn_fwd_noalloc (TOPMOE_NOALLOC_SCRATCH_BYTES, 64 MiB)";
     case TOPMOE_ERR_BAD_ARG:
       return "invalid argument (aux_coef, z_coef or capacity_factor negative or not finite, "
              "aux_grad or z_grad not finite, unknown flag bits, a misaligned pointer, or a "
@@ -344,6 +349,61 @@ int moe_ffn_fwd_train(const void* x, const float* Wr, const void* Wg, const void
                       capacity_factor, flags, dtype, y, topk_idx, alpha, aux_loss, z_loss,
                       expert_offsets, sorted_token_ids, workspace, workspace_bytes, saved,
                       saved_bytes, true, stream, stage_events);
+}
+
+}  // extern "C"
+
+// The workspace of moe_ffn_fwd_noalloc, for callers that cannot allocate:
+// a fixed array in device memory that every GPU the library runs on holds
+// until the process ends.  In host code `scratch` is only a stand-in for the
+// array; its device address comes from hipGetSymbolAddress.
+constexpr size_t kNoallocScratchBytes = TOPMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};  // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return TOPMOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return TOPMOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TOPMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_fwd_noalloc(const void* x, const float* Wr, const void* Wg, const void* Wu,
+                        const void* Wd, const void* residual, int64_t N, int64_t H, int64_t I,
+                        int E, int k, float aux_coef, float z_coef, float capacity_factor,
+                        int flags, int dtype, void* y, int32_t* topk_idx, float* alpha,
+                        float* aux_loss, float* z_loss, int32_t* expert_offsets,
+                        int32_t* sorted_token_ids, void* stream, void* const* stage_events) {
+  MoePlan pl;
+  const int status = plan_moe(N, H, I, E, k, dtype, &pl);
+  if (status != TOPMOE_OK) return status;
+  if (pl.total > kNoallocScratchBytes) return TOPMOE_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  const int st = scratch_on_current_device(&ws);
+  if (st != TOPMOE_OK) return st;
+  // every buffer the forward reads from its workspace it first writes in the
+  // same call, so nothing there needs clearing between calls
+  return moe_fwd_impl(x, Wr, Wg, Wu, Wd, residual, N, H, I, E, k, aux_coef, z_coef,
+                      capacity_factor, flags, dtype, y, topk_idx, alpha, aux_loss, z_loss,
+                      expert_offsets, sorted_token_ids, ws, kNoallocScratchBytes, nullptr, 0,
+                      false, stream, stage_events);
 }
 
 size_t ffn_bwd_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype) {
