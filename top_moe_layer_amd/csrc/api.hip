@@ -115,6 +115,25 @@ size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dt
 
 namespace {
 
+// The down projection (into y, or into the k-slots): one GEMM, or with a K
+// split the GEMM's chunks into fp32 partials and the reduce that sums them in
+// order and applies the epilogue (the stage's start event on the first
+// launch, its stop event on the second).
+hipError_t launch_down(int dtype, const GemmShape& sh, const GemmParams& p, int64_t mtiles,
+                       bool slots, const Launch& L) {
+  if (p.ksplit <= 1)
+    return launch_gemm(slots ? KIND_DOWN_SLOTS : KIND_DOWN_Y, dtype, sh, p, mtiles, L);
+  Launch first = L, second = L;
+  first.stop = nullptr;
+  second.start = nullptr;
+  hipError_t e = launch_gemm(KIND_DOWN_PARTIAL, dtype, sh, p, mtiles, first);
+  if (e != hipSuccess) return e;
+  e = launch_splitk_reduce(p.partial, p.ksplit, p.M, p.Nout, p.offsets, p.E, p.entries, p.alpha,
+                           p.k, slots ? nullptr : p.residual, dtype, slots, p.out, second);
+  L.launched = first.launched || second.launched;
+  return e;
+}
+
 // The dense forward; with `saved` (a backward workspace) the gate/up
 // projection also keeps the pairs (g, u) and h^T there for
 // ffn_swiglu_bwd_saved.
@@ -166,7 +185,9 @@ int ffn_fwd_impl(const void* x, const void* Wg, const void* Wu, const void* Wd,
     dn.A = h; dn.B0 = Wd; dn.B1 = nullptr; dn.out = y; dn.residual = residual;
     dn.entries = nullptr; dn.offsets = nullptr; dn.alpha = nullptr;
     dn.M = N; dn.E = 1; dn.k = 1; dn.Nout = int(H); dn.K = int(I);
-    TOPMOE_TRY(launch_gemm(KIND_DOWN_Y, dtype, pl.down, dn, (N + pl.down.bm - 1) / pl.down.bm, l1));
+    dn.ksplit = pl.down_ksplit; dn.kchunk = pl.down_kchunk;
+    dn.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+    TOPMOE_TRY(launch_down(dtype, pl.down, dn, (N + pl.down.bm - 1) / pl.down.bm, false, l1));
   }
   TOPMOE_TRY(st.close(l1));
   return TOPMOE_OK;
@@ -292,8 +313,9 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   dn.residual = direct ? residual : nullptr;  // otherwise added by the combine
   dn.entries = sorted_entry; dn.offsets = offsets; dn.alpha = alpha_g;
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
-  TOPMOE_TRY(launch_gemm(direct ? KIND_DOWN_Y : KIND_DOWN_SLOTS, dtype, pl.down, dn,
-                         pl.down_mtiles, l3));
+  dn.ksplit = pl.down_ksplit; dn.kchunk = pl.down_kchunk;
+  dn.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  TOPMOE_TRY(launch_down(dtype, pl.down, dn, pl.down_mtiles, !direct, l3));
   TOPMOE_TRY(st.close(l3));
   // 4: fixed-order combine of the kept slots (k == 1 under a capacity: the
   // dropped tokens' rows of y, which the down GEMM did not write)

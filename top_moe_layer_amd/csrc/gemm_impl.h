@@ -174,6 +174,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   constexpr int NA = KT_::NA, NB = KT_::NB, NP = KT_::NP;
   constexpr bool META = KT_::META;      // per-row entry / alpha in the epilogue
   constexpr bool KGROUP = KT_::KGROUP;  // groups along K (weight gradients)
+  // split K (the down projection): each work item is one K chunk of a tile
+  constexpr bool SPLIT = KIND == KIND_DOWN_PARTIAL;
   constexpr bool PAD = KGROUP || KIND == KIND_BWD_GU || KIND == KIND_BWD_DH;  // padded group columns
   constexpr int NW = WM * WN;                // wavefronts: WM along rows x WN along columns
   constexpr int NTHR = 64 * NW;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   }
 
   struct Tile {
-    int e, rows, n0, kt, koff;
+    int e, rows, n0, kt, koff, chunk;
     int64_t row0;
   };
   // ---- work list.
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   } else {
     total_mt = p.offsets == nullptr ? int((p.M + BM - 1) / BM)
                                     : __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
-    total = total_mt * nt_count;
+    total = total_mt * nt_count * (SPLIT ? p.ksplit : 1);
     per = (total + 7) >> 3;
     nbx = int(gridDim.x >> 3);
     lb = int(blockIdx.x >> 3);
@@ -309,8 +311,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       const int c = s_off[kg_e + 1] - s_off[kg_e];
       t.kt = ((c + 63) & ~63) / EPS;
       t.koff = s_poff[kg_e];
+      t.chunk = 0;
     } else {
-      const int L = xbase + lb + j * nbx;
+      int L = xbase + lb + j * nbx;
+      t.chunk = 0;
+      if constexpr (SPLIT) {  // chunk-major: the tiles of one K chunk, then the next chunk's
+        const int tiles = total_mt * nt_count;
+        t.chunk = L / tiles;
+        L -= t.chunk * tiles;
+      }
       const int first_m = (L / (GM * nt_count)) * GM;
       const int gsz = min(total_mt - first_m, GM);
       const int in_group = L - first_m * nt_count;
@@ -318,6 +327,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       t.n0 = (in_group / gsz) * BN;
       t.kt = KTu;
       t.koff = 0;
+      if constexpr (SPLIT) {  // the chunk's slices (every chunk holds at least one)
+        const int k0 = t.chunk * p.kchunk;
+        t.kt = min(p.kchunk, KTu - k0);
+        t.koff = k0 * EPS;
+      }
       if (p.offsets == nullptr) {
         t.e = 0;
         t.row0 = int64_t(mt) * BM;
@@ -339,6 +353,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
     t.kt = __builtin_amdgcn_readfirstlane(t.kt);
     t.koff = __builtin_amdgcn_readfirstlane(t.koff);
+    if constexpr (SPLIT) t.chunk = __builtin_amdgcn_readfirstlane(t.chunk);
     t.row0 = __builtin_amdgcn_readfirstlane(int(t.row0));
     return t;
   };
@@ -388,7 +403,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
         n = n < p.Nout ? n : p.Nout - 1;
         const void* b = which == 0 ? p.B0 : (NB > 1 && which == 1) ? p.B1 : p.B2;
         sbase[j] = static_cast<const char*>(b) +
-                   (KGROUP ? kbytes : int64_t(t.e) * p.Nout * rowbytes);
+                   (KGROUP ? kbytes
+                           : int64_t(t.e) * p.Nout * rowbytes + (SPLIT ? kbytes : int64_t(0)));
         voff[j] = uint32_t(n) * uint32_t(rowbytes) + uint32_t(chunk * 16);
       }
     }
@@ -771,11 +787,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
             quad_transpose(b, q4);
             if (ok) store4<T>(static_cast<T*>(p.out) + (t.row0 + rl + ro) * p.Nout + col, b);
           } else {
+            // (with a K split: the chunk's raw sums, in grouped row order)
             float b[4];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) b[w] = acc[0][i][j][4 * vq + w] * a4[w];
+            for (int w = 0; w < 4; ++w) b[w] = acc[0][i][j][4 * vq + w] * (SPLIT ? 1.f : a4[w]);
             quad_transpose(b, q4);
-            if constexpr (KIND == KIND_DOWN_Y) {
+            if constexpr (SPLIT) {
+              const int64_t o = (int64_t(t.chunk) * p.M + t.row0 + rl + ro) * p.Nout + col;
+              if (ok) store4<float>(p.partial + o, b);
+            } else if constexpr (KIND == KIND_DOWN_Y) {
               const int64_t o = (ent / p.k) * p.Nout + col;
               if (ok) {
                 if (p.residual != nullptr) {
@@ -799,7 +819,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   // starts in slot 0 and the ring streams straight on into the next tile
   // (its first S slices are issued during this tile's last S steps);
   // otherwise each tile fills and drains the ring on its own.
-  const bool stream = !KGROUP && (KTu % S) == 0;
+  const bool stream = !KGROUP && !SPLIT && (KTu % S) == 0;
   Tile cur = decode(0);
   load_rows(cur, rid);
   make_src(cur, rid);
@@ -883,10 +903,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 }
 
 // Blocks of one kernel that fit on the device at once (CUs x resident
-// blocks per CU), queried once per kernel and device.
+// blocks per CU), queried once per kernel and device (`cached` belongs to the
+// kernel: every instantiation of the launcher below has its own).
 template <typename K>
-int resident_blocks(K kernel, int threads) {
-  static int cached[64] = {};
+int resident_blocks(K kernel, int threads, int (&cached)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   if (cached[dev] == 0) {
@@ -914,11 +934,14 @@ hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, const Launch& s) {
     if (te <= 0 || grid > 0x7fffffff) return te <= 0 ? hipSuccess : hipErrorInvalidValue;
     return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
   } else {
-    if (mtiles * nt <= 0) return hipSuccess;
+    // work items: tiles (times the K chunks of a split down projection)
+    const int64_t items = mtiles * nt * (KIND == KIND_DOWN_PARTIAL ? int64_t(p.ksplit) : 1);
+    if (items <= 0) return hipSuccess;
     // persistent grid: at most the blocks resident at once, in whole rounds of
-    // the 8 XCDs (blocks beyond the real tile count exit at once)
-    const int64_t cap = resident_blocks(kernel, 64 * WM * WN) / 8 * 8;
-    int64_t grid = (mtiles * nt + 7) / 8 * 8;
+    // the 8 XCDs (blocks beyond the real item count exit at once)
+    static int cached[64] = {};
+    const int64_t cap = resident_blocks(kernel, 64 * WM * WN, cached) / 8 * 8;
+    int64_t grid = (items + 7) / 8 * 8;
     if (grid > cap && cap >= 8) grid = cap;
     return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
   }
@@ -1054,6 +1077,7 @@ bool shape_supported_dtype(int kind, const GemmShape& sh) {
     case KIND_GATEUP: return shape_listed<T, KIND_GATEUP>(sh);
     case KIND_DOWN_Y: return shape_listed<T, KIND_DOWN_Y>(sh);
     case KIND_DOWN_SLOTS: return shape_listed<T, KIND_DOWN_SLOTS>(sh);
+    case KIND_DOWN_PARTIAL: return shape_listed<T, KIND_DOWN_PARTIAL>(sh);
     case KIND_BWD_GU: return shape_listed<T, KIND_BWD_GU>(sh);
     case KIND_BWD_DH: return shape_listed<T, KIND_BWD_DH>(sh);
     case KIND_WGRAD2: return shape_listed<T, KIND_WGRAD2>(sh);
@@ -1069,6 +1093,7 @@ hipError_t launch_gemm_dtype(int kind, GemmShape sh, const GemmParams& p, int64_
     case KIND_GATEUP: return launch_gemm_tiles<T, KIND_GATEUP>(sh, p, mtiles, s);
     case KIND_DOWN_Y: return launch_gemm_tiles<T, KIND_DOWN_Y>(sh, p, mtiles, s);
     case KIND_DOWN_SLOTS: return launch_gemm_tiles<T, KIND_DOWN_SLOTS>(sh, p, mtiles, s);
+    case KIND_DOWN_PARTIAL: return launch_gemm_tiles<T, KIND_DOWN_PARTIAL>(sh, p, mtiles, s);
     case KIND_BWD_GU: return launch_gemm_tiles<T, KIND_BWD_GU>(sh, p, mtiles, s);
     case KIND_BWD_DH: return launch_gemm_tiles<T, KIND_BWD_DH>(sh, p, mtiles, s);
     case KIND_WGRAD2: return launch_gemm_tiles<T, KIND_WGRAD2>(sh, p, mtiles, s);

@@ -68,6 +68,12 @@ struct GemmParams {
   int64_t kcount;          // wgrad with offsets == NULL: rows of the single group
   int E, k;
   int Nout, K;
+  // down projections: the K slices split into ksplit chunks of kchunk slices
+  // (ksplit <= 1: none); chunk c of a tile writes its raw fp32 accumulators
+  // to partial [ksplit, M, Nout] (grouped rows) and launch_splitk_reduce
+  // applies the epilogue to their sum
+  int ksplit, kchunk;
+  float* partial;
 };
 
 enum RouterMode {
@@ -102,6 +108,17 @@ hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint
 
 hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, float* z_loss,
                               const Launch& s);
+
+// The down projection's epilogue over split-K partial sums: for each grouped
+// row r < (offsets ? offsets[E] : M) and column c, s = sum over the ksplit
+// chunks in order of partial[chunk][r][c]; then y[entry / k][c] =
+// (residual) + alpha[r] * s rounded once (slots == false) or
+// out[entry][c] = alpha[r] * s in the dtype (slots == true); entries / alpha
+// NULL = identity / 1.
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int Nout,
+                                const int32_t* offsets, int E, const int32_t* entries,
+                                const float* alpha, int k, const void* residual, int dtype,
+                                bool slots, void* out, const Launch& s);
 
 hipError_t launch_gemm(int kind, int dtype, GemmShape shape, const GemmParams& p,
                        int64_t mtiles, const Launch& s);

@@ -278,6 +278,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
   store16<T>(y + t * H + h, acc);
 }
 
+// The down projection's epilogue over split-K partial sums (grouped row r,
+// four columns per thread): the chunks' fp32 sums added in chunk order, then
+// alpha, the entry's destination and the residual as in the GEMM's own
+// epilogue, rounded once.
+template <typename T, bool SLOTS>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    const float* __restrict__ partial, int ksplit, int64_t M, int Nout,
+    const int32_t* __restrict__ offsets, int E, const int32_t* __restrict__ entries,
+    const float* __restrict__ alpha, int k, const T* residual, T* out) {
+  const int nq = Nout / 4;
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rows = offsets != nullptr ? int64_t(offsets[E]) : M;
+  if (gid >= rows * nq) return;
+  const int64_t r = gid / nq;
+  const int c = int(gid - r * nq) * 4;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int ch = 0; ch < ksplit; ++ch) {
+    float v[4];
+    load4<float>(partial + (int64_t(ch) * M + r) * Nout + c, v);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sum[w] += v[w];
+  }
+  const float a = alpha != nullptr ? alpha[r] : 1.f;
+  const int64_t ent = entries != nullptr ? int64_t(entries[r]) : r;
+  float b[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) b[w] = sum[w] * a;
+  if constexpr (SLOTS) {
+    store4<T>(out + ent * Nout + c, b);
+  } else {
+    const int64_t o = (ent / k) * Nout + c;
+    if (residual != nullptr) {
+      float rr[4];
+      load4<T>(residual + o, rr);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) b[w] = rr[w] + b[w];
+    }
+    store4<T>(out + o, b);
+  }
+}
+
 __global__ void empty_route_kernel(int E, int32_t* offsets, float* aux, float* z_loss) {
   const int tid = threadIdx.x;
   if (tid <= E) offsets[tid] = 0;
@@ -317,6 +358,26 @@ hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint
   return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
                        static_cast<const bf16_t*>(slots), topk_idx, keep,
                        static_cast<const bf16_t*>(residual), N, H, k, static_cast<bf16_t*>(y));
+}
+
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int Nout,
+                                const int32_t* offsets, int E, const int32_t* entries,
+                                const float* alpha, int k, const void* residual, int dtype,
+                                bool slots, void* out, const Launch& s) {
+  const int64_t work = M * (Nout / 4);
+  if (work <= 0) return hipSuccess;
+  const dim3 grid(unsigned((work + 255) / 256));
+#define TOPMOE_RED(T, SL)                                                                   \
+  return launch_kernel(splitk_reduce_kernel<T, SL>, grid, dim3(256), 0, s, partial, ksplit, M, \
+                       Nout, offsets, E, entries, alpha, k, static_cast<const T*>(residual),  \
+                       static_cast<T*>(out))
+  if (dtype == TOPMOE_DTYPE_FP32) {
+    if (slots) TOPMOE_RED(float, true);
+    TOPMOE_RED(float, false);
+  }
+  if (slots) TOPMOE_RED(bf16_t, true);
+  TOPMOE_RED(bf16_t, false);
+#undef TOPMOE_RED
 }
 
 hipError_t launch_empty_route(int E, int32_t* offsets, float* aux, float* z_loss,

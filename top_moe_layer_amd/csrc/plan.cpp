@@ -199,6 +199,25 @@ int set_tile_override(int slot, const int* shape) {
   return TOPMOE_OK;
 }
 
+void choose_down_split(int64_t tiles, int64_t K, int elem, const GemmShape& sh, int* ksplit,
+                       int* kchunk) {
+  const int64_t kt = K * elem / sh.rb;  // K slices
+  *ksplit = 1;
+  *kchunk = int(kt);
+  // Few output tiles and a long K (the 100-token fp32 FFN: 24 tiles, 76
+  // slices): the tiles' K loops run one after another on a few CUs while the
+  // others idle.  Chunks of K fill the CUs, and a small kernel adds the chunks'
+  // fp32 partial sums in order and applies the epilogue.
+  if (tiles <= 0 || tiles >= 128 || kt < 8) return;
+  int64_t want = (256 + tiles - 1) / tiles;
+  if (want > kt / 4) want = kt / 4;
+  if (want > 16) want = 16;
+  if (want < 2) return;
+  const int64_t cs = (kt + want - 1) / want;
+  *kchunk = int(cs);
+  *ksplit = int((kt + cs - 1) / cs);  // every chunk non-empty
+}
+
 int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
   if (!dtype_ok(dtype)) return TOPMOE_ERR_UNSUPPORTED_DTYPE;
   if (N < 0 || H < 64 || I < 64 || H % 64 || I % 64) return TOPMOE_ERR_BAD_SHAPE;
@@ -212,9 +231,13 @@ int plan_ffn(int64_t N, int64_t H, int64_t I, int dtype, FfnPlan* p) {
   int st = apply_override(0, dtype, &q.up);
   if (st == TOPMOE_OK) st = apply_override(1, dtype, &q.down);
   if (st != TOPMOE_OK) return st;
+  choose_down_split((N + q.down.bm - 1) / q.down.bm * ((H + q.down.bn - 1) / q.down.bn), I,
+                    q.elem, q.down, &q.down_ksplit, &q.down_kchunk);
   q.off_h = 0;
-  q.total = align_up(size_t(N) * size_t(I) * q.elem);
-  if (q.total == 0) q.total = kAlign;
+  size_t o = align_up(size_t(N) * size_t(I) * q.elem);
+  q.off_partial = o;
+  if (q.down_ksplit > 1) o = align_up(o + size_t(q.down_ksplit) * size_t(N) * size_t(H) * 4);
+  q.total = o == 0 ? kAlign : o;
   *p = q;
   return TOPMOE_OK;
 }
@@ -273,6 +296,10 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);
   q.off_slots = o;  // k-slots (k >= 2 only: with k = 1 the down GEMM writes y itself)
   if (k > 1) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
+  choose_down_split(q.down_mtiles * ((H + q.down.bn - 1) / q.down.bn), I, q.elem, q.down,
+                    &q.down_ksplit, &q.down_kchunk);
+  q.off_partial = o;
+  if (q.down_ksplit > 1) o = align_up(o + size_t(q.down_ksplit) * size_t(rows) * size_t(H) * 4);
   q.total = o == 0 ? kAlign : o;
   *p = q;
   return TOPMOE_OK;

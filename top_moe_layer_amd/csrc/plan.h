@@ -17,6 +17,8 @@ enum GemmKind {
                         // (g, u) row-major and h^T in padded group columns
   KIND_WGRAD2 = 4,      // out0 = A0 B^T, out1 = A1 B^T per group, K = the group's padded rows
   KIND_WGRAD1 = 5,      // out0 = A0 B^T per group, K = the group's padded rows
+  KIND_DOWN_PARTIAL = 7,  // the down projection split along K: each work item (a tile and a
+                          // K chunk) writes its raw fp32 sums to GemmParams::partial
   KIND_BWD_DH = 6,      // dh = alpha * dy Wd (rows gathered from dy), with the pairs (g, u):
                         // writes [dg | du] row-major, dg^T / du^T in padded group columns and
                         // per-row partial sums of dh_raw . h (d alpha)
@@ -41,7 +43,10 @@ struct FfnPlan {
   int dtype = 0;
   int elem = 0;            // bytes per x / W / y element
   GemmShape up, down;      // gate/up and down GEMM tiles
+  int down_ksplit = 1;     // K chunks of the down GEMM (1: not split)
+  int down_kchunk = 0;     // K slices per chunk
   size_t off_h = 0;        // SiLU(g)*u intermediate [N, I]
+  size_t off_partial = 0;  // f32 [down_ksplit, N, H] split-K partial sums (when split)
   size_t total = 0;        // workspace bytes
 };
 
@@ -66,8 +71,10 @@ struct MoePlan {
   size_t off_sorted = 0;      // int32 [N*k] entry ids (t*k + j) grouped by expert
   size_t off_alpha_g = 0;     // f32   [N*k] alpha of each grouped row
   size_t off_h = 0;           // elem  [N*k, I] SiLU(g)*u in grouped row order
-  size_t off_slots = 0;       // elem  [N*k, H] alpha-scaled expert outputs (k >= 2, or
-                              // any k under an expert capacity)
+  size_t off_slots = 0;       // elem  [N*k, H] alpha-scaled expert outputs (k >= 2)
+  int down_ksplit = 1;        // K chunks of the down GEMM (1: not split)
+  int down_kchunk = 0;        // K slices per chunk
+  size_t off_partial = 0;     // f32   [down_ksplit, N*k, H] split-K partial sums
   size_t total = 0;
 };
 
@@ -143,6 +150,12 @@ bool gemm_shape_supported(int kind, int dtype, const GemmShape& sh);
 // TOPMOE_BWDDH_TILE, TOPMOE_WGU_TILE, TOPMOE_WD_TILE: "BMxBNxWMxWNxRBxS"),
 // then set through set_tile_override.
 int set_tile_override(int slot, const int* shape);
+
+// K split of a down projection of `tiles` output tiles over K: chunks of
+// *kchunk slices (RB bytes of each row), *ksplit of them, each non-empty;
+// *ksplit = 1 when the tiles alone occupy at least half the CUs.
+void choose_down_split(int64_t tiles, int64_t K, int elem, const GemmShape& sh, int* ksplit,
+                       int* kchunk);
 
 // Upper bound on the number of BM-row tiles over `groups` groups of total M rows.
 inline int64_t grouped_mtiles_bound(int64_t M, int groups, int bm) {
