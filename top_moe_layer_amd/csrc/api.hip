@@ -280,13 +280,31 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
                            psum_part, z_part, l0));
   TOPMOE_TRY(st.close(l0));
   // 1: expert offsets, aux (and z) loss, stable scatter of entries into expert
-  // groups (under a capacity: of the kept entries)
+  // groups (under a capacity: of the kept entries).  Decode-sized calls
+  // (few entries, the 64 x 128 weight-streaming tiles) skip this launch: each
+  // block of the two GEMMs groups the entries itself (GemmParams::inl_topk)
+  // and one extra block of the gate/up launch writes these outputs.
+  const bool inline_route = !train && cap == 0 && pl.rows <= kInlineMaxEntries &&
+                            pl.up.bm == 64 && pl.up.bn == 128 && pl.down.bm == 64 &&
+                            pl.down.bn == 128 && pl.down_ksplit <= 1;
   const Launch l1 = st.at(1);
-  TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k, pl.tb,
-                            N, aux_coef, z_coef, cap, offsets, counts_off, aux_loss, z_loss,
-                            sorted_entry, alpha_g, sorted_token_ids, keep, topk_keep, alpha_keep,
-                            offsets_out, l1));
+  if (!inline_route)
+    TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k,
+                              pl.tb, N, aux_coef, z_coef, cap, offsets, counts_off, aux_loss,
+                              z_loss, sorted_entry, alpha_g, sorted_token_ids, keep, topk_keep,
+                              alpha_keep, offsets_out, l1));
   TOPMOE_TRY(st.close(l1));
+  auto set_inline = [&](GemmParams& g, bool outputs) {
+    g.offsets = nullptr; g.entries = nullptr; g.alpha = nullptr;
+    g.inl_topk = topk_idx; g.inl_alpha = alpha; g.inl_n = int(pl.rows); g.inl_nblk = pl.nblk;
+    g.inl_tokens = N; g.inl_coef = aux_coef; g.inl_z_coef = z_coef;
+    if (outputs) {
+      g.inl_outputs = 1;
+      g.inl_offsets_out = expert_offsets; g.inl_sorted_out = sorted_token_ids;
+      g.inl_psum_part = psum_part; g.inl_z_part = z_part;
+      g.inl_aux_out = aux_loss; g.inl_z_out = z_loss;
+    }
+  };
   // 2: grouped gate/up GEMM + SiLU * up (training: the backward's g, u
   // projection, keeping the pairs and h^T in `saved`, h row-major as well)
   const Launch l2 = st.at(2);
@@ -302,6 +320,7 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
     up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
     up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
     up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
+    if (inline_route) set_inline(up, true);
     TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
   }
   TOPMOE_TRY(st.close(l2));
@@ -315,6 +334,7 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   dn.ksplit = pl.down_ksplit; dn.kchunk = pl.down_kchunk;
   dn.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  if (inline_route) set_inline(dn, false);
   TOPMOE_TRY(launch_down(dtype, pl.down, dn, pl.down_mtiles, !direct, l3));
   TOPMOE_TRY(st.close(l3));
   // 4: fixed-order combine of the kept slots (k == 1 under a capacity: the

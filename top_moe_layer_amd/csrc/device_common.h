@@ -182,13 +182,19 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wavefront.
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int w = __shfl_up(v, o, 64);
-    if (lane >= o) v += w;
-  }
+// Inclusive prefix sum across the 64 lanes of a wavefront, with DPP lane
+// moves (no LDS round trips): within each row of 16 lanes add the values
+// shifted down by 1, 2, 4 and 8 lanes (lanes shifted in from outside the row
+// add 0), then add the last lane of row 0 to row 1 and of row 2 to row 3
+// (row_bcast:15), then lane 31 to rows 2 and 3 (row_bcast:31).  Integer
+// sums, so the result does not depend on the order.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int /*lane*/) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
   return v;
 }
 

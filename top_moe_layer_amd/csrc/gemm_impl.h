@@ -236,8 +236,114 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   // offsets (or one group), and with PAD the padded offsets: each group's
   // rows rounded up to 64, which is where they sit in the transposed
   // (K-major) activations of the weight gradients.  Cached in LDS.
-  const int G = p.offsets != nullptr ? p.E : 1;
-  if (p.offsets != nullptr || PAD) {
+  // In-block routing (GemmParams::inl_topk): only the decode-sized forward
+  // tiles (64 x 128) carry it.
+  constexpr bool INL = !KGROUP && !PAD && BM == 64 && BN == 128 &&
+                       (KIND == KIND_GATEUP || KIND == KIND_DOWN_Y || KIND == KIND_DOWN_SLOTS);
+  static_assert(!INL || NTHR >= kInlineMaxEntries, "in-block routing: one entry per thread");
+  constexpr int IMAX = INL ? kInlineMaxEntries : 1;
+  __shared__ int s_ient[IMAX];       // grouped row -> entry id (t*k + j)
+  __shared__ float s_ialpha[IMAX];   // grouped row -> alpha
+  __shared__ int s_icnt[INL ? 64 : 1];
+  __shared__ int s_iw[INL ? NW * 64 : 1];
+  __shared__ double s_ips[INL ? 64 : 1];
+  const bool inl = INL && p.inl_topk != nullptr;
+  const bool grouped = p.offsets != nullptr || inl;
+  const int G = grouped ? p.E : 1;
+  // the extra block of an in-block-routed gate/up launch (routing outputs only)
+  const bool outs_block = INL && KIND == KIND_GATEUP && inl && p.inl_outputs != 0 &&
+                          blockIdx.x == gridDim.x - 1;
+  if constexpr (INL) {
+    if (inl) {
+      // The entries (t*k + j order, one per thread) grouped by expert as the
+      // permutation kernel groups them.  Each wavefront counts its entries per
+      // expert with ballots (an entry's rank among its wavefront's entries of
+      // the same expert: the matching lanes below it); wavefront 0 turns the
+      // counts into per-wavefront prefixes, expert totals and exclusive
+      // offsets; each entry then lands at offset + earlier wavefronts' count
+      // + rank in its wavefront.
+      const int e = tid < p.inl_n ? p.inl_topk[tid] : -1;
+      const float a = (META && tid < p.inl_n) ? p.inl_alpha[tid] : 0.f;
+      const bool valid = e >= 0;
+      // this wavefront's row of counts: cleared and written by the wavefront
+      // itself (its LDS operations complete in order)
+      s_iw[wid * 64 + lane] = 0;
+      uint64_t peers = 0ull;
+      uint64_t todo = __ballot(valid);
+      while (todo) {
+        const int leader = __ffsll((long long)todo) - 1;
+        const int le = __builtin_amdgcn_readlane(e, leader);  // scalar: no LDS round trip
+        const uint64_t m = __ballot(valid && e == le);
+        if (valid && e == le) peers = m;
+        todo &= ~m;
+      }
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+      const int in_wave = __popcll(peers & below);
+      if (valid && in_wave == 0) s_iw[wid * 64 + e] = __popcll(peers);
+      __syncthreads();
+      if (tid < 64) {  // lane = expert
+        int run = 0;
+        for (int w = 0; w < NW; ++w) {
+          const int c = s_iw[w * 64 + lane];
+          s_iw[w * 64 + lane] = run;
+          run += c;
+        }
+        const int c = lane < G ? run : 0;
+        // one scan for the entries (low half) and the row tiles (high half):
+        // at most 512 entries and 72 tiles, so neither half carries over
+        const int both = wave_inclusive_scan(c | (((c + BM - 1) / BM) << 16), lane);
+        const int incl = both & 0xffff;
+        if (lane < G) s_off[lane] = incl - c;
+        if (lane == G - 1) s_off[G] = incl;
+        s_scan[lane] = both >> 16;
+        s_icnt[lane] = c;
+      }
+      __syncthreads();
+      if (valid) {
+        const int d = s_off[e] + s_iw[wid * 64 + e] + in_wave;
+        s_ient[d] = tid;
+        s_ialpha[d] = a;
+      }
+      __syncthreads();
+      if (outs_block) {
+        // The routing outputs of the permutation kernel.  aux = E * coef *
+        // sum_e c_e * (sum_t p_{t,e}) / N^2 and z = z_coef * sum lse^2 / N:
+        // fp64 sums in the permutation kernel's order (per expert, lanes
+        // stride over the router blocks, then a wavefront sum; then the
+        // wavefront sum of the c_e terms), so both paths give the same bits.
+        if (p.inl_offsets_out != nullptr && tid <= G) p.inl_offsets_out[tid] = s_off[tid];
+        if (p.inl_sorted_out != nullptr)
+          for (int d = tid; d < p.inl_n; d += NTHR) p.inl_sorted_out[d] = s_ient[d] / p.k;
+        const int nb = p.inl_nblk;
+        const double n = double(p.inl_tokens);
+        const bool aux = p.inl_aux_out != nullptr && p.inl_psum_part != nullptr;
+        if (aux) {
+          for (int g = wid; g < G; g += NW) {
+            double ps = 0.0;
+            for (int b = lane; b < nb; b += 64) ps += double(p.inl_psum_part[int64_t(g) * nb + b]);
+            ps = wave_sum(ps);
+            if (lane == 0) s_ips[g] = ps;
+          }
+        }
+        if (wid == NW - 1 && p.inl_z_out != nullptr && p.inl_z_part != nullptr) {
+          double z = 0.0;
+          for (int b = lane; b < nb; b += 64) z += double(p.inl_z_part[b]);
+          z = wave_sum(z);
+          if (lane == 0)
+            *p.inl_z_out = (p.inl_z_coef != 0.f && n > 0) ? float(double(p.inl_z_coef) * z / n) : 0.f;
+        }
+        __syncthreads();
+        if (aux && wid == 0) {
+          const double term = wave_sum(lane < G ? double(s_icnt[lane]) * s_ips[lane] : 0.0);
+          if (lane == 0)
+            *p.inl_aux_out = (p.inl_coef != 0.f && n > 0) ?
+                float(double(p.E) * double(p.inl_coef) * term / (n * n)) : 0.f;
+        }
+        return;
+      }
+    }
+  }
+  if (!inl && (p.offsets != nullptr || PAD)) {
     if (tid < 64) {
       int c = 0;
       if (lane < G) {
@@ -285,11 +391,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
     kg_idx = int(blockIdx.x & 7) * c + (j - kg_e * c);
     n_my = (kg_e < G && kg_idx < te) ? 1 : 0;
   } else {
-    total_mt = p.offsets == nullptr ? int((p.M + BM - 1) / BM)
-                                    : __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
+    total_mt = !grouped ? int((p.M + BM - 1) / BM)
+                        : __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
     total = total_mt * nt_count * (SPLIT ? p.ksplit : 1);
     per = (total + 7) >> 3;
-    nbx = int(gridDim.x >> 3);
+    nbx = int((gridDim.x - (INL && KIND == KIND_GATEUP && inl && p.inl_outputs != 0 ? 1 : 0)) >> 3);
     lb = int(blockIdx.x >> 3);
     xbase = int(blockIdx.x & 7) * per;
     for (int l = lb; l < per && xbase + l < total; l += nbx) ++n_my;
@@ -332,7 +438,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
         t.kt = min(p.kchunk, KTu - k0);
         t.koff = k0 * EPS;
       }
-      if (p.offsets == nullptr) {
+      if (!grouped) {
         t.e = 0;
         t.row0 = int64_t(mt) * BM;
         const int64_t left = p.M - t.row0;
@@ -373,7 +479,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       const int lr = (NA == 2 && r >= BM) ? r - BM : r;
       int gr = int(t.row0) + (lr < t.rows ? lr : t.rows - 1);
       if (!is_a) gr = 0;
-      rid[j] = (KT_::GATHER && p.entries != nullptr && is_a) ? p.entries[gr] / p.k : gr;
+      int ent = gr;
+      if constexpr (INL) {
+        if (inl) ent = s_ient[gr];
+      }
+      if (!inl && p.entries != nullptr) ent = p.entries[gr];
+      rid[j] = (KT_::GATHER && is_a && (inl || p.entries != nullptr)) ? ent / p.k : gr;
     }
   };
   int32_t rid[LPW];          // A-row indices of the next tile
@@ -507,6 +618,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       const int64_t g = t.row0 + (tid < t.rows ? tid : t.rows - 1);
       m_ent = p.entries != nullptr ? p.entries[g] : int(g);
       m_alpha = p.alpha != nullptr ? p.alpha[g] : 1.f;
+      if constexpr (INL) {
+        if (inl) {
+          m_ent = s_ient[g];
+          m_alpha = s_ialpha[g];
+        }
+      }
     }
   };
   // dh kind: the tile's (g, u) pairs, fetched with the metadata so that their
@@ -943,6 +1060,8 @@ hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, const Launch& s) {
     const int64_t cap = resident_blocks(kernel, 64 * WM * WN, cached) / 8 * 8;
     int64_t grid = (items + 7) / 8 * 8;
     if (grid > cap && cap >= 8) grid = cap;
+    // in-block routing: one more block, which writes the routing outputs
+    if (KIND == KIND_GATEUP && p.inl_topk != nullptr && p.inl_outputs != 0) ++grid;
     return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
   }
 }

@@ -74,7 +74,32 @@ struct GemmParams {
   // applies the epilogue to their sum
   int ksplit, kchunk;
   float* partial;
+  // In-block routing (few entries, forward kinds with 64-row tiles): when
+  // inl_topk is not NULL, every block groups the inl_n = N * k entries of
+  // inl_topk [N, k] (and their weights inl_alpha) by expert itself -- the
+  // expert offsets, the stable order of entries within an expert, the rows'
+  // alpha -- instead of reading offsets / entries / alpha.  With
+  // inl_outputs (gate/up only) the launch has one block more, the last,
+  // which takes no tile and writes the routing outputs that the permutation
+  // kernel would have: inl_offsets_out [E+1] and inl_sorted_out [N*k] (each
+  // when not NULL), and aux / z-loss from the router's per-block partials
+  // (inl_psum_part [E, inl_nblk], inl_z_part [inl_nblk]) into inl_aux_out /
+  // inl_z_out (each when not NULL).
+  const int32_t* inl_topk;
+  const float* inl_alpha;
+  int inl_n, inl_nblk, inl_outputs;
+  int32_t* inl_offsets_out;
+  int32_t* inl_sorted_out;
+  const float* inl_psum_part;
+  const float* inl_z_part;
+  float* inl_aux_out;
+  float* inl_z_out;
+  float inl_coef, inl_z_coef;
+  int64_t inl_tokens;
 };
+
+// Most entries (N * k) the in-block routing of a GEMM takes.
+constexpr int kInlineMaxEntries = 512;
 
 enum RouterMode {
   ROUTER_MODE_LDS = 0,    // W_router staged in LDS, 16 tokens per wavefront pass
