@@ -11,11 +11,11 @@ Page citations:
   [DEMO] minimind3.com, chapter 4 example script
   [NOTE] "MiniMind study notes 08: FeedForward and MoE"
 
-Readings where the pages are silent or ambiguous (all listed in the design doc):
+Readings where the pages are silent or ambiguous:
   * top-k slot order: probability descending, ties to the lower expert id
     (the pages call topk with sorted=False, which fixes no order);
-  * y accumulates the selected experts in ascending expert id (the pages loop
-    ``for i, expert in enumerate(self.experts)``);
+  * y accumulates the selected experts in ascending expert id (the pages' module
+    visits the experts in index order);
   * aux for k > 1 keeps the one-hot load as [k, E] and broadcasts, exactly as
     the module code does, so uniform routing gives k * coef.
 """
@@ -113,8 +113,9 @@ def renorm_weights(p, idx, normalize=True):
 
 
 def expert_lists(idx, E):
-    """Per-expert token lists ([L13] section 3 step 5: ``mask = topk_idx == i``,
-    ``token_idx = mask.any(-1).nonzero()``): L_e = ascending tokens that chose e.
+    """Per-expert token lists ([L13] section 3 step 5: a token belongs to expert
+    e's list when e is among its selections; the list is in token order):
+    L_e = ascending tokens that chose e.
 
     Returns counts [E], offsets [E+1] (exclusive prefix sum) and
     sorted_token_ids = concatenation of L_0, ..., L_{E-1}.
