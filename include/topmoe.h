@@ -92,7 +92,10 @@ extern "C" {
 #define TOPMOE_MOE_STAGES 5  /* 0 router, 1 expert offsets + aux + token scatter,
                                 2 grouped gate/up GEMM + SiLU*up, 3 grouped down GEMM
                                 + alpha, 4 combine of the k slots (k == 1: empty, or
-                                under a capacity the rows of the dropped tokens)        */
+                                under a capacity the rows of the dropped tokens).
+                                Decode-sized inference calls do stage 1 (and, with
+                                E <= 16, stage 0) inside the GEMM launches: such a
+                                stage launches no kernel                                */
 #define TOPMOE_FFN_BWD_STAGES 7  /* 0 weight transposes, 1 x / dy transposes,
                                     2 g, u GEMM (recomputed), 3 dh GEMM + dg, du,
                                     4 dx GEMM, 5 dWg + dWu GEMM, 6 dWd GEMM             */

@@ -273,20 +273,27 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
     return TOPMOE_OK;
   }
 
+  // Decode-sized inference calls take every token against every expert in
+  // the gate/up projection (the weights stream the same; the MFMAs were idle)
+  // and route in extra blocks of that same launch; the down projection then
+  // groups the entries itself.
+  const bool inline_ok = !train && cap == 0 && pl.rows <= kInlineMaxEntries &&
+                         pl.up.bm == 64 && pl.up.bn == 128 && pl.down.bm == 64 &&
+                         pl.down.bn == 128 && pl.down_ksplit <= 1;
+  const bool allx = inline_ok && pl.allx;
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   const Launch l0 = st.at(0);
-  TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, renorm, pl.tb, pl.nblk,
-                           pl.router_mode, topk_idx, alpha, probs, lse, count_part,
-                           psum_part, z_part, l0));
+  if (!allx)
+    TOPMOE_TRY(launch_router(x, Wr, dtype, N, int(H), E, k, renorm, pl.tb, pl.nblk,
+                             pl.router_mode, topk_idx, alpha, probs, lse, count_part,
+                             psum_part, z_part, l0));
   TOPMOE_TRY(st.close(l0));
   // 1: expert offsets, aux (and z) loss, stable scatter of entries into expert
   // groups (under a capacity: of the kept entries).  Decode-sized calls
   // (few entries, the 64 x 128 weight-streaming tiles) skip this launch: each
   // block of the two GEMMs groups the entries itself (GemmParams::inl_topk)
   // and one extra block of the gate/up launch writes these outputs.
-  const bool inline_route = !train && cap == 0 && pl.rows <= kInlineMaxEntries &&
-                            pl.up.bm == 64 && pl.up.bn == 128 && pl.down.bm == 64 &&
-                            pl.down.bn == 128 && pl.down_ksplit <= 1;
+  const bool inline_route = inline_ok;
   const Launch l1 = st.at(1);
   if (!inline_route)
     TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k,
@@ -320,8 +327,18 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
     up.A = x; up.B0 = Wg; up.B1 = Wu; up.out = h;
     up.entries = sorted_entry; up.offsets = offsets; up.alpha = nullptr;
     up.M = pl.rows; up.E = E; up.k = k; up.Nout = int(I); up.K = int(H);
-    if (inline_route) set_inline(up, true);
-    TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, pl.up_mtiles, l2));
+    int64_t up_mtiles = pl.up_mtiles;
+    if (allx) {
+      up.entries = nullptr; up.offsets = nullptr;
+      up.allx_n = N;
+      up_mtiles = int64_t(E) * ((N + pl.up.bm - 1) / pl.up.bm);
+      up.rt_wr = Wr; up.rt_blocks = pl.nblk; up.rt_tb = pl.tb; up.rt_renorm = renorm ? 1 : 0;
+      up.rt_n = N; up.rt_topk = topk_idx; up.rt_alpha = alpha;
+      up.rt_count = count_part; up.rt_psum = psum_part; up.rt_zpart = z_part;
+    } else if (inline_route) {
+      set_inline(up, true);
+    }
+    TOPMOE_TRY(launch_gemm(KIND_GATEUP, dtype, pl.up, up, up_mtiles, l2));
   }
   TOPMOE_TRY(st.close(l2));
   // 3: grouped down GEMM, alpha-scaled, into y (k == 1) or the slots
@@ -334,7 +351,8 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   dn.M = pl.rows; dn.E = E; dn.k = k; dn.Nout = int(H); dn.K = int(I);
   dn.ksplit = pl.down_ksplit; dn.kchunk = pl.down_kchunk;
   dn.partial = reinterpret_cast<float*>(ws + pl.off_partial);
-  if (inline_route) set_inline(dn, false);
+  if (inline_route) set_inline(dn, allx);  // with every token against every expert, the
+  if (allx) dn.allx_n = N;                  // down launch writes the routing outputs
   TOPMOE_TRY(launch_down(dtype, pl.down, dn, pl.down_mtiles, !direct, l3));
   TOPMOE_TRY(st.close(l3));
   // 4: fixed-order combine of the kept slots (k == 1 under a capacity: the

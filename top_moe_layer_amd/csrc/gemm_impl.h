@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "router_impl.h"
 
 namespace topmoe {
 
@@ -228,6 +229,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // the router blocks of a decode gate/up launch (LDS: the ring, unused here)
+  if constexpr (KIND == KIND_GATEUP && BM == 64 && BN == 128 && NTHR >= 256) {
+    if (p.rt_blocks > 0 && int(blockIdx.x) >= int(gridDim.x) - p.rt_blocks) {
+      int* s_rcnt = reinterpret_cast<int*>(ring0);
+      float(*s_rpart)[64] = reinterpret_cast<float(*)[64]>(ring0 + 256);
+      float(*s_rps)[64] = reinterpret_cast<float(*)[64]>(ring0 + 256 + 1024);
+      rt::route_split_block_upto16<T>(static_cast<const T*>(p.A), p.rt_wr, p.rt_n, p.K, p.E, p.k,
+                                      p.rt_renorm != 0, p.rt_tb,
+                                      int(blockIdx.x) - (int(gridDim.x) - p.rt_blocks),
+                                      p.rt_blocks, p.rt_topk, p.rt_alpha, p.rt_count, p.rt_psum,
+                                      p.rt_zpart, s_rcnt, s_rpart, s_rps);
+      return;
+    }
+  }
   const int nt_count = (p.Nout + BN - 1) / BN;
   const int KTu = KGROUP ? 0 : p.K / EPS;  // K slices of every tile (row-grouped kinds)
   const int64_t rowbytes = int64_t(p.K) * int64_t(sizeof(T));  // A and B row pitch
@@ -248,11 +263,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   __shared__ int s_iw[INL ? NW * 64 : 1];
   __shared__ double s_ips[INL ? 64 : 1];
   const bool inl = INL && p.inl_topk != nullptr;
-  const bool grouped = p.offsets != nullptr || inl;
+  const bool allx = INL && p.allx_n > 0;  // every token against every expert
+  const bool grouped = p.offsets != nullptr || inl || allx;
   const int G = grouped ? p.E : 1;
-  // the extra block of an in-block-routed gate/up launch (routing outputs only)
-  const bool outs_block = INL && KIND == KIND_GATEUP && inl && p.inl_outputs != 0 &&
-                          blockIdx.x == gridDim.x - 1;
+  // the extra block of an in-block-routed launch (routing outputs only)
+  const bool outs_block = INL && inl && p.inl_outputs != 0 && blockIdx.x == gridDim.x - 1;
   if constexpr (INL) {
     if (inl) {
       // The entries (t*k + j order, one per thread) grouped by expert as the
@@ -343,7 +358,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
       }
     }
   }
-  if (!inl && (p.offsets != nullptr || PAD)) {
+  if (allx && !inl) {  // E groups of the N rows of A, in order
+    if (tid < 64) {
+      const int n = int(p.allx_n), mt = (n + BM - 1) / BM;
+      if (lane <= G) s_off[lane] = lane * n;
+      s_scan[lane] = (lane < G ? lane + 1 : G) * mt;
+    }
+    __syncthreads();
+  } else if (!inl && (p.offsets != nullptr || PAD)) {
     if (tid < 64) {
       int c = 0;
       if (lane < G) {
@@ -398,7 +420,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
                         : __builtin_amdgcn_readfirstlane(s_scan[p.E - 1]);
     total = total_mt * nt_count * (SPLIT ? p.ksplit : 1);
     per = (total + 7) >> 3;
-    nbx = int((gridDim.x - (INL && KIND == KIND_GATEUP && inl && p.inl_outputs != 0 ? 1 : 0)) >> 3);
+    const int extra = (INL && inl && p.inl_outputs != 0 ? 1 : 0) +
+                      (KIND == KIND_GATEUP && p.rt_blocks > 0 ? p.rt_blocks : 0);
+    nbx = int((gridDim.x - extra) >> 3);
     lb = int(blockIdx.x >> 3);
     xbase = int(blockIdx.x & 7) * per;
     for (int l = lb; l < per && xbase + l < total; l += nbx) ++n_my;
@@ -487,7 +511,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
         if (inl) ent = s_ient[gr];
       }
       if (!inl && p.entries != nullptr) ent = p.entries[gr];
-      rid[j] = (KT_::GATHER && is_a && (inl || p.entries != nullptr)) ? ent / p.k : gr;
+      int row = (KT_::GATHER && is_a && (inl || p.entries != nullptr)) ? ent / p.k : gr;
+      if constexpr (INL) {
+        // every token against every expert: gate/up reads token gr - e N;
+        // the down projection reads entry (t, j)'s row e N + t
+        if (allx && is_a)
+          row = inl ? int(t.e) * int(p.allx_n) + ent / p.k : gr - int(t.e) * int(p.allx_n);
+      }
+      rid[j] = row;
     }
   };
   int32_t rid[LPW];          // A-row indices of the next tile
@@ -1064,7 +1095,9 @@ hipError_t launch_gemm_t(const GemmParams& p, int64_t mtiles, const Launch& s) {
     int64_t grid = (items + 7) / 8 * 8;
     if (grid > cap && cap >= 8) grid = cap;
     // in-block routing: one more block, which writes the routing outputs
-    if (KIND == KIND_GATEUP && p.inl_topk != nullptr && p.inl_outputs != 0) ++grid;
+    if (p.inl_topk != nullptr && p.inl_outputs != 0) ++grid;
+    // router blocks riding on a decode gate/up launch
+    if (KIND == KIND_GATEUP && p.rt_blocks > 0) grid += p.rt_blocks;
     return launch_kernel(kernel, dim3(unsigned(grid)), dim3(64 * WM * WN), 0, s, p);
   }
 }

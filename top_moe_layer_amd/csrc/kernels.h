@@ -79,10 +79,10 @@ struct GemmParams {
   // inl_topk [N, k] (and their weights inl_alpha) by expert itself -- the
   // expert offsets, the stable order of entries within an expert, the rows'
   // alpha -- instead of reading offsets / entries / alpha.  With
-  // inl_outputs (gate/up only) the launch has one block more, the last,
-  // which takes no tile and writes the routing outputs that the permutation
-  // kernel would have: inl_offsets_out [E+1] and inl_sorted_out [N*k] (each
-  // when not NULL), and aux / z-loss from the router's per-block partials
+  // inl_outputs the launch has one block more, the last, which takes no
+  // tile and writes the routing outputs that the permutation kernel would
+  // have: inl_offsets_out [E+1] and inl_sorted_out [N*k] (each when not
+  // NULL), and aux / z-loss from the router's per-block partials
   // (inl_psum_part [E, inl_nblk], inl_z_part [inl_nblk]) into inl_aux_out /
   // inl_z_out (each when not NULL).
   const int32_t* inl_topk;
@@ -96,10 +96,26 @@ struct GemmParams {
   float* inl_z_out;
   float inl_coef, inl_z_coef;
   int64_t inl_tokens;
+  // Every token against every expert (decode-sized calls, gate/up): with
+  // allx_n = N > 0 the groups are the E experts, each of the N rows of A in
+  // order (group e's row t is A row t, written to out row e * N + t); the
+  // down projection, with in-block routing, then reads entry (t, j) of
+  // expert e from A row e * N + t.
+  int64_t allx_n;
+  // Router blocks riding on a gate/up launch (rt_blocks > 0, E <= 16): the
+  // last rt_blocks blocks route tokens [b * rt_tb, b * rt_tb + rt_tb) of A
+  // against rt_wr [E, K] exactly as the split router kernel does, writing
+  // rt_topk / rt_alpha [N, k] and the per-block partials rt_count /
+  // rt_psum [E, rt_blocks] and rt_zpart [rt_blocks].
+  const float* rt_wr;
+  int rt_blocks, rt_tb, rt_renorm;
+  int64_t rt_n;
+  int32_t* rt_topk;
+  float* rt_alpha;
+  int32_t* rt_count;
+  float* rt_psum;
+  float* rt_zpart;
 };
-
-// Most entries (N * k) the in-block routing of a GEMM takes.
-constexpr int kInlineMaxEntries = 512;
 
 enum RouterMode {
   ROUTER_MODE_LDS = 0,    // W_router staged in LDS, 16 tokens per wavefront pass

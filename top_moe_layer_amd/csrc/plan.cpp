@@ -293,11 +293,15 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_keep = o;       o = align_up(o + size_t(rows));
   q.off_sorted = o;     o = align_up(o + size_t(rows) * 4);
   q.off_alpha_g = o;    o = align_up(o + size_t(rows) * 4);
-  q.off_h = o;          o = align_up(o + size_t(rows) * size_t(I) * q.elem);
-  q.off_slots = o;  // k-slots (k >= 2 only: with k = 1 the down GEMM writes y itself)
-  if (k > 1) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
   choose_down_split(q.down_mtiles * ((H + q.down.bn - 1) / q.down.bn), I, q.elem, q.down,
                     &q.down_ksplit, &q.down_kchunk);
+  const bool streaming64 = q.up.bm == 64 && q.up.bn == 128 && q.down.bm == 64 && q.down.bn == 128;
+  q.allx = q.router_mode == 1 && q.tb == 1 && E <= 16 && rows <= kInlineMaxEntries &&
+           streaming64 && q.down_ksplit <= 1;
+  const int64_t h_rows = q.allx && int64_t(E) * N > rows ? int64_t(E) * N : rows;
+  q.off_h = o;          o = align_up(o + size_t(h_rows) * size_t(I) * q.elem);
+  q.off_slots = o;  // k-slots (k >= 2 only: with k = 1 the down GEMM writes y itself)
+  if (k > 1) o = align_up(o + size_t(rows) * size_t(H) * q.elem);
   q.off_partial = o;
   if (q.down_ksplit > 1) o = align_up(o + size_t(q.down_ksplit) * size_t(rows) * size_t(H) * 4);
   q.total = o == 0 ? kAlign : o;

@@ -50,6 +50,9 @@ struct FfnPlan {
   size_t total = 0;        // workspace bytes
 };
 
+// Most entries (N * k) the in-block routing of a GEMM takes.
+constexpr int kInlineMaxEntries = 512;
+
 struct MoePlan {
   int64_t N = 0, H = 0, I = 0;
   int E = 0, k = 0, dtype = 0;
@@ -75,6 +78,11 @@ struct MoePlan {
   int down_ksplit = 1;        // K chunks of the down GEMM (1: not split)
   int down_kchunk = 0;        // K slices per chunk
   size_t off_partial = 0;     // f32   [down_ksplit, N*k, H] split-K partial sums
+  // decode-sized calls (split router, E <= 16, both projections on the 64 x
+  // 128 weight-streaming tile, in-block routing): the gate/up projection can
+  // take every token against every expert (h then holds E * N rows, group
+  // e's row t at e * N + t), with the router's blocks in the same launch
+  bool allx = false;
   size_t total = 0;
 };
 
