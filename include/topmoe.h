@@ -364,6 +364,32 @@ int topmoe_version(void);
 #define TOPMOE_TILE_WGRAD_D 5
 int topmoe_set_tile_override(int gemm, const int* shape);
 
+/* The launch plan moe_ffn_fwd (inference, flags without effect on it) follows
+ * for a problem, computed on the host without touching a GPU: info[i] for
+ * i < n receives field i below (-1 past the last).  Returns TOPMOE_OK, or the
+ * status moe_ffn_fwd would return for the sizes, dtype or capacity factor
+ * (NULL info with n > 0: TOPMOE_ERR_NULL_ARG). */
+#define TOPMOE_PATH_ROUTER_LAYOUT 0  /* 0: W_router in LDS, 16 tokens per pass;
+                                        1: one token at a time, H split over
+                                        four wavefronts; 2: as 0, 16 lanes per token */
+#define TOPMOE_PATH_ROUTER_TOKENS 1  /* tokens per router block                  */
+#define TOPMOE_PATH_ROUTER_BLOCKS 2  /* router blocks                            */
+#define TOPMOE_PATH_UP_BM 3          /* gate/up tile rows, columns, ring depth   */
+#define TOPMOE_PATH_UP_BN 4
+#define TOPMOE_PATH_UP_RING 5
+#define TOPMOE_PATH_DOWN_BM 6        /* down tile rows, columns, ring depth      */
+#define TOPMOE_PATH_DOWN_BN 7
+#define TOPMOE_PATH_DOWN_RING 8
+#define TOPMOE_PATH_DOWN_KSPLIT 9    /* K chunks of the down projection (1: none) */
+#define TOPMOE_PATH_INBLOCK 10       /* 1: the GEMMs group the entries themselves
+                                        (no permutation launch)                  */
+#define TOPMOE_PATH_ROUTER_IN_UP 11  /* 1: the router runs as blocks of the gate/up
+                                        launch, which takes every token against
+                                        every expert (no router launch)          */
+#define TOPMOE_PATH_FIELDS 12
+int moe_ffn_fwd_path(int64_t N, int64_t H, int64_t I, int E, int k, float capacity_factor,
+                     int dtype, int32_t* info, int n);
+
 /* Create / destroy n timing-enabled hipEvent_t handles. */
 int topmoe_events_create(int n, void** events);
 int topmoe_events_destroy(int n, void** events);

@@ -35,7 +35,7 @@ def test_header_declares_expected_functions():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.topmoe_version() == 150
+    assert L.topmoe_version() == 151
 
 
 def test_strerror_covers_codes(L):
@@ -379,3 +379,26 @@ def test_noalloc_size_limit_checked_first(L):
     assert B.raw_moe_workspace_bytes(16384, 768, 2432, 8, 2, B.DTYPE_BF16) > B.NOALLOC_SCRATCH_BYTES
     assert B.raw_moe_ffn_fwd_noalloc(*args(16384, 2)) == B.ERR_SCRATCH_TOO_SMALL
     assert B.raw_moe_ffn_fwd_noalloc(*args(16384, 9)) == B.ERR_BAD_SHAPE
+
+
+def test_forward_path(L):
+    """The launch plan the forward follows (host logic): decode-sized calls
+    route inside the GEMM launches, a capacity or a large batch does not."""
+    dec = B.moe_fwd_path(32, 2048, 1408, 16, 2, B.DTYPE_BF16)
+    assert dec == dict(router_layout=1, router_tokens=1, router_blocks=32, up_bm=64, up_bn=128,
+                       up_ring=3, down_bm=64, down_bn=128, down_ring=3, down_ksplit=1, inblock=1,
+                       router_in_up=1)
+    capped = B.moe_fwd_path(32, 2048, 1408, 16, 2, B.DTYPE_BF16, capacity_factor=1.25)
+    assert capped["inblock"] == 0 and capped["router_in_up"] == 0
+    many_experts = B.moe_fwd_path(37, 192, 320, 64, 6, B.DTYPE_BF16)
+    assert many_experts["inblock"] == 1 and many_experts["router_in_up"] == 0
+    top1 = B.moe_fwd_path(4096, 768, 2432, 4, 1, B.DTYPE_BF16)
+    assert top1["inblock"] == 0 and top1["router_in_up"] == 0 and top1["router_blocks"] * top1[
+        "router_tokens"] >= 4096
+    # fields past the last read -1; errors as moe_ffn_fwd reports them
+    info = (ctypes.c_int32 * (len(B.PATH_FIELDS) + 2))()
+    assert L.moe_ffn_fwd_path(32, 2048, 1408, 16, 2, 0.0, B.DTYPE_BF16, info, len(info)) == B.OK
+    assert list(info)[-2:] == [-1, -1]
+    assert L.moe_ffn_fwd_path(32, 2048, 1408, 16, 2, -1.0, B.DTYPE_BF16, info, 4) == B.ERR_BAD_ARG
+    assert L.moe_ffn_fwd_path(32, 2048, 1408, 16, 2, 0.0, B.DTYPE_BF16, None, 4) == B.ERR_NULL_ARG
+    assert L.moe_ffn_fwd_path(32, 2048, 1408, 0, 2, 0.0, B.DTYPE_BF16, info, 4) == B.ERR_BAD_SHAPE

@@ -1,8 +1,10 @@
 """Decode-sized MoE calls (at most 512 entries on the 64 x 128 weight-streaming
 tiles) group the entries by expert inside the two GEMM kernels instead of in
-the permutation kernel; block 0 of the gate/up GEMM writes the offsets, the
-token lists, aux and the z-loss.  Every output against the oracle: lists and
-offsets bit-exact, alpha / aux / z to 1e-5, y to the bf16 bar."""
+the permutation kernel; an extra block of one of the GEMM launches writes the
+offsets, the token lists, aux and the z-loss.  With E <= 16 and one token per
+router block the router itself runs as blocks of the gate/up launch, which
+takes every token against every expert.  Every output against the oracle:
+lists and offsets bit-exact, alpha / aux / z to 1e-5, y to the bf16 bar."""
 import numpy as np
 import pytest
 
@@ -23,20 +25,24 @@ def env():
     return torch, dev, tm
 
 
-CASES = [  # N, H, I, E, k, z_coef, residual
-    (32, 2048, 1408, 16, 2, 0.001, True),
-    (1, 256, 384, 8, 2, 0.0, False),
-    (5, 128, 256, 4, 1, 0.002, False),
-    (100, 256, 512, 8, 2, 0.0, True),
-    (256, 128, 128, 16, 2, 0.001, False),   # 512 entries, the most in-block routing takes
-    (37, 192, 320, 64, 6, 0.0, False),
+CASES = [  # N, H, I, E, k, z_coef, residual, (in-block routing, router in the gate/up launch)
+    (32, 2048, 1408, 16, 2, 0.001, True, (1, 1)),
+    (1, 256, 384, 8, 2, 0.0, False, (1, 1)),
+    (5, 128, 256, 4, 1, 0.002, False, (1, 1)),      # k = 1: the down GEMM writes y
+    (100, 256, 512, 8, 2, 0.0, True, (0, 0)),       # split-K down projection: permutation kernel
+    (256, 128, 128, 16, 2, 0.001, False, (1, 0)),   # 512 entries, the most in-block routing
+                                                    # takes; the LDS router layout
+    (37, 192, 320, 64, 6, 0.0, False, (1, 0)),      # E > 16: the router launch stays
 ]
 
 
-@pytest.mark.parametrize("N,H,I,E,k,zc,res", CASES)
-def test_inline_routing(env, N, H, I, E, k, zc, res):
+@pytest.mark.parametrize("N,H,I,E,k,zc,res,path", CASES)
+def test_inline_routing(env, N, H, I, E, k, zc, res, path):
     torch, dev, tm = env
     from top_moe_layer_amd import _binding as B
+
+    plan = B.moe_fwd_path(N, H, I, E, k, B.DTYPE_BF16)
+    assert (plan["inblock"], plan["router_in_up"]) == path, plan
 
     w = custom_workload(name="inl", N=N, H=H, I=I, E=E, k=k, coef=0.01, residual=res,
                         seed=N * 7 + E)

@@ -19,7 +19,9 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     StageEvents,
     TopmoeError,
+    PATH_FIELDS,
     lib,
+    moe_fwd_path,
     set_tile_override,
     strerror,
 )

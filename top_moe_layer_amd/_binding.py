@@ -70,6 +70,7 @@ SIGNATURES = {
     "topmoe_strerror": (ctypes.c_char_p, [_i32]),
     "topmoe_version": (_i32, []),
     "topmoe_set_tile_override": (_i32, [_i32, _vp]),
+    "moe_ffn_fwd_path": (_i32, [_i64, _i64, _i64, _i32, _i32, _f32, _i32, _vp, _i32]),
     "topmoe_events_create": (_i32, [_i32, _vp]),
     "topmoe_events_destroy": (_i32, [_i32, _vp]),
     "topmoe_event_elapsed_ms": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
@@ -183,6 +184,19 @@ def raw_moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, aux_grad_scale, z_g
     return int(lib().moe_ffn_bwd(x, Wr, Wg, Wu, Wd, dy, aux_grad, z_grad, aux_grad_scale,
                                  z_grad_scale, N, H, I, E, k, coef, z_coef, capacity_factor, flags,
                                  dtype, dx, dWr, dWg, dWu, dWd, ws, ws_bytes, stream, events))
+
+
+PATH_FIELDS = ["router_layout", "router_tokens", "router_blocks", "up_bm", "up_bn", "up_ring",
+               "down_bm", "down_bn", "down_ring", "down_ksplit", "inblock", "router_in_up"]
+
+
+def moe_fwd_path(N, H, I, E, k, dtype, capacity_factor=0.0) -> dict:
+    """The launch plan of moe_ffn_fwd for a problem (host only, no GPU):
+    a dict of PATH_FIELDS (include/topmoe.h, TOPMOE_PATH_*)."""
+    info = (ctypes.c_int32 * len(PATH_FIELDS))()
+    check(lib().moe_ffn_fwd_path(N, H, I, E, k, float(capacity_factor), dtype, info,
+                                 len(PATH_FIELDS)), "moe_ffn_fwd_path")
+    return dict(zip(PATH_FIELDS, (int(v) for v in info)))
 
 
 def set_tile_override(gemm: str, shape=None) -> None:

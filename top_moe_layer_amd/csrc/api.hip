@@ -78,7 +78,7 @@ bool nonneg_finite(float v) { return v >= 0.0f && !isinf(v); }
 
 extern "C" {
 
-int topmoe_version(void) { return 150; }
+int topmoe_version(void) { return 151; }
 
 const char* topmoe_strerror(int status) {
   switch (status) {
@@ -109,6 +109,21 @@ size_t ffn_workspace_bytes(int64_t N, int64_t H, int64_t I, int dtype) {
 size_t moe_workspace_bytes(int64_t N, int64_t H, int64_t I, int E, int k, int dtype) {
   MoePlan pl;
   return plan_moe(N, H, I, E, k, dtype, &pl) == TOPMOE_OK ? pl.total : 0;
+}
+
+int moe_ffn_fwd_path(int64_t N, int64_t H, int64_t I, int E, int k, float capacity_factor,
+                     int dtype, int32_t* info, int n) {
+  if (n > 0 && !info) return TOPMOE_ERR_NULL_ARG;
+  if (!nonneg_finite(capacity_factor)) return TOPMOE_ERR_BAD_ARG;
+  MoePlan pl;
+  const int status = plan_moe(N, H, I, E, k, dtype, &pl);
+  if (status != TOPMOE_OK) return status;
+  const bool inl = capacity_of(capacity_factor, N, k, E) == 0 && pl.inline_ok;
+  const int32_t v[TOPMOE_PATH_FIELDS] = {
+      pl.router_mode, pl.tb, pl.nblk, pl.up.bm, pl.up.bn, pl.up.stages, pl.down.bm,
+      pl.down.bn, pl.down.stages, pl.down_ksplit, inl ? 1 : 0, inl && pl.allx ? 1 : 0};
+  for (int i = 0; i < n; ++i) info[i] = i < TOPMOE_PATH_FIELDS ? v[i] : -1;
+  return TOPMOE_OK;
 }
 
 }  // extern "C"
@@ -277,10 +292,8 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   // the gate/up projection (the weights stream the same; the MFMAs were idle)
   // and route in extra blocks of that same launch; the down projection then
   // groups the entries itself.
-  const bool inline_ok = !train && cap == 0 && pl.rows <= kInlineMaxEntries &&
-                         pl.up.bm == 64 && pl.up.bn == 128 && pl.down.bm == 64 &&
-                         pl.down.bn == 128 && pl.down_ksplit <= 1;
-  const bool allx = inline_ok && pl.allx;
+  const bool inline_route = !train && cap == 0 && pl.inline_ok;
+  const bool allx = inline_route && pl.allx;
   // 0: router, softmax, top-k, alpha, per-block counts and sums of p
   const Launch l0 = st.at(0);
   if (!allx)
@@ -293,7 +306,6 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   // (few entries, the 64 x 128 weight-streaming tiles) skip this launch: each
   // block of the two GEMMs groups the entries itself (GemmParams::inl_topk)
   // and one extra block of the gate/up launch writes these outputs.
-  const bool inline_route = inline_ok;
   const Launch l1 = st.at(1);
   if (!inline_route)
     TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k,

@@ -296,8 +296,8 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   choose_down_split(q.down_mtiles * ((H + q.down.bn - 1) / q.down.bn), I, q.elem, q.down,
                     &q.down_ksplit, &q.down_kchunk);
   const bool streaming64 = q.up.bm == 64 && q.up.bn == 128 && q.down.bm == 64 && q.down.bn == 128;
-  q.allx = q.router_mode == 1 && q.tb == 1 && E <= 16 && rows <= kInlineMaxEntries &&
-           streaming64 && q.down_ksplit <= 1;
+  q.inline_ok = rows <= kInlineMaxEntries && streaming64 && q.down_ksplit <= 1;
+  q.allx = q.inline_ok && q.router_mode == 1 && q.tb == 1 && E <= 16;
   const int64_t h_rows = q.allx && int64_t(E) * N > rows ? int64_t(E) * N : rows;
   q.off_h = o;          o = align_up(o + size_t(h_rows) * size_t(I) * q.elem);
   q.off_slots = o;  // k-slots (k >= 2 only: with k = 1 the down GEMM writes y itself)

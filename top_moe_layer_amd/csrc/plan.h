@@ -78,10 +78,14 @@ struct MoePlan {
   int down_ksplit = 1;        // K chunks of the down GEMM (1: not split)
   int down_kchunk = 0;        // K slices per chunk
   size_t off_partial = 0;     // f32   [down_ksplit, N*k, H] split-K partial sums
-  // decode-sized calls (split router, E <= 16, both projections on the 64 x
-  // 128 weight-streaming tile, in-block routing): the gate/up projection can
-  // take every token against every expert (h then holds E * N rows, group
-  // e's row t at e * N + t), with the router's blocks in the same launch
+  // few entries (at most kInlineMaxEntries), both projections on the 64 x 128
+  // weight-streaming tile, the down projection unsplit: inference calls
+  // without a capacity group the entries inside the GEMMs (in-block routing)
+  bool inline_ok = false;
+  // and with the split router at one token per block and E <= 16, the
+  // gate/up projection can take every token against every expert (h then
+  // holds E * N rows, group e's row t at e * N + t), with the router's blocks
+  // in the same launch
   bool allx = false;
   size_t total = 0;
 };
