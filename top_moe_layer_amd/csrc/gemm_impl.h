@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // the router blocks of a decode gate/up launch (LDS: the ring, unused here)
-  if constexpr (KIND == KIND_GATEUP && BM == 64 && BN == 128 && NTHR >= 256) {
+  if constexpr (KIND == KIND_GATEUP && BM == 64 && BN == 128 && NTHR >= kInlineMaxEntries) {
     if (p.rt_blocks > 0 && int(blockIdx.x) >= int(gridDim.x) - p.rt_blocks) {
       int* s_rcnt = reinterpret_cast<int*>(ring0);
       float(*s_rpart)[64] = reinterpret_cast<float(*)[64]>(ring0 + 256);
@@ -252,10 +252,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(GemmParams p) {
   // rows rounded up to 64, which is where they sit in the transposed
   // (K-major) activations of the weight gradients.  Cached in LDS.
   // In-block routing (GemmParams::inl_topk): only the decode-sized forward
-  // tiles (64 x 128) carry it.
-  constexpr bool INL = !KGROUP && !PAD && BM == 64 && BN == 128 &&
+  // tiles (64 x 128, one thread per entry) carry it.
+  constexpr bool INL = !KGROUP && !PAD && BM == 64 && BN == 128 && NTHR >= kInlineMaxEntries &&
                        (KIND == KIND_GATEUP || KIND == KIND_DOWN_Y || KIND == KIND_DOWN_SLOTS);
-  static_assert(!INL || NTHR >= kInlineMaxEntries, "in-block routing: one entry per thread");
   constexpr int IMAX = INL ? kInlineMaxEntries : 1;
   __shared__ int s_ient[IMAX];       // grouped row -> entry id (t*k + j)
   __shared__ float s_ialpha[IMAX];   // grouped row -> alpha

@@ -295,7 +295,11 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
   q.off_alpha_g = o;    o = align_up(o + size_t(rows) * 4);
   choose_down_split(q.down_mtiles * ((H + q.down.bn - 1) / q.down.bn), I, q.elem, q.down,
                     &q.down_ksplit, &q.down_kchunk);
-  const bool streaming64 = q.up.bm == 64 && q.up.bn == 128 && q.down.bm == 64 && q.down.bn == 128;
+  // the 64 x 128 tiles of eight wavefronts carry the in-block routing (one
+  // entry per thread)
+  const bool streaming64 = q.up.bm == 64 && q.up.bn == 128 && q.down.bm == 64 &&
+                           q.down.bn == 128 && q.up.wm * q.up.wn * 64 >= kInlineMaxEntries &&
+                           q.down.wm * q.down.wn * 64 >= kInlineMaxEntries;
   q.inline_ok = rows <= kInlineMaxEntries && streaming64 && q.down_ksplit <= 1;
   q.allx = q.inline_ok && q.router_mode == 1 && q.tb == 1 && E <= 16;
   const int64_t h_rows = q.allx && int64_t(E) * N > rows ? int64_t(E) * N : rows;
