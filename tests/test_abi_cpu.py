@@ -390,6 +390,8 @@ def test_forward_path(L):
                        router_in_up=1)
     capped = B.moe_fwd_path(32, 2048, 1408, 16, 2, B.DTYPE_BF16, capacity_factor=1.25)
     assert capped["inblock"] == 0 and capped["router_in_up"] == 0
+    more_tokens = B.moe_fwd_path(200, 2048, 1408, 16, 2, B.DTYPE_BF16)
+    assert more_tokens["inblock"] == 1 and more_tokens["router_in_up"] == 0
     many_experts = B.moe_fwd_path(37, 192, 320, 64, 6, B.DTYPE_BF16)
     assert many_experts["inblock"] == 1 and many_experts["router_in_up"] == 0
     top1 = B.moe_fwd_path(4096, 768, 2432, 4, 1, B.DTYPE_BF16)

@@ -33,6 +33,9 @@ CASES = [  # N, H, I, E, k, z_coef, residual, (in-block routing, router in the g
     (256, 128, 128, 16, 2, 0.001, False, (1, 0)),   # 512 entries, the most in-block routing
                                                     # takes; the LDS router layout
     (37, 192, 320, 64, 6, 0.0, False, (1, 0)),      # E > 16: the router launch stays
+    (64, 1024, 512, 16, 1, 0.001, True, (1, 1)),    # one full row tile of tokens
+    (16, 2048, 1408, 16, 4, 0.0, False, (1, 1)),
+    (200, 2048, 1408, 16, 2, 0.0, True, (1, 0)),    # more tokens than one row tile
 ]
 
 

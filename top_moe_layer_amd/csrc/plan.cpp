@@ -301,7 +301,13 @@ int plan_moe(int64_t N, int64_t H, int64_t I, int E, int k, int dtype, MoePlan* 
                            q.down.bn == 128 && q.up.wm * q.up.wn * 64 >= kInlineMaxEntries &&
                            q.down.wm * q.down.wn * 64 >= kInlineMaxEntries;
   q.inline_ok = rows <= kInlineMaxEntries && streaming64 && q.down_ksplit <= 1;
-  q.allx = q.inline_ok && q.router_mode == 1 && q.tb == 1 && E <= 16;
+  // Every token against every expert only while that costs no MFMA time
+  // (one row tile per expert) and the tiles and router blocks of the launch
+  // fit on the chip's 256 CUs at once (the router blocks are the launch's
+  // last: they must not wait for tiles to finish).
+  const int64_t up_tiles_allx = int64_t(E) * ((I + q.up.bn - 1) / q.up.bn);
+  q.allx = q.inline_ok && q.router_mode == 1 && q.tb == 1 && E <= 16 && N <= q.up.bm &&
+           up_tiles_allx + q.nblk <= 256;
   const int64_t h_rows = q.allx && int64_t(E) * N > rows ? int64_t(E) * N : rows;
   q.off_h = o;          o = align_up(o + size_t(h_rows) * size_t(I) * q.elem);
   q.off_slots = o;  // k-slots (k >= 2 only: with k = 1 the down GEMM writes y itself)

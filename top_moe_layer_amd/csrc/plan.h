@@ -82,10 +82,10 @@ struct MoePlan {
   // weight-streaming tile, the down projection unsplit: inference calls
   // without a capacity group the entries inside the GEMMs (in-block routing)
   bool inline_ok = false;
-  // and with the split router at one token per block and E <= 16, the
-  // gate/up projection can take every token against every expert (h then
-  // holds E * N rows, group e's row t at e * N + t), with the router's blocks
-  // in the same launch
+  // and with the split router at one token per block, E <= 16 and at most
+  // one row tile of tokens, the gate/up projection can take every token
+  // against every expert (h then holds E * N rows, group e's row t at
+  // e * N + t), with the router's blocks in the same launch
   bool allx = false;
   size_t total = 0;
 };
