@@ -41,11 +41,18 @@ def replay_checks(torch, dev, graph, outs, want, other_call):
         torch.cuda.synchronize()
 
 
-def test_graph_moe_forward(env):
+@pytest.mark.parametrize("N,H,I,E,k,fused_router", [
+    (600, 128, 192, 8, 2, 0),
+    (32, 2048, 1408, 16, 2, 1),   # decode-sized: router and grouping inside the GEMM launches
+])
+def test_graph_moe_forward(env, N, H, I, E, k, fused_router):
     torch, dev, tm = env
-    w = custom_workload(name="graph_moe", N=600, H=128, I=192, E=8, k=2, coef=0.01, seed=31)
+    from top_moe_layer_amd import _binding as B
+
+    assert B.moe_fwd_path(N, H, I, E, k, B.DTYPE_BF16)["router_in_up"] == fused_router
+    w = custom_workload(name="graph_moe", N=N, H=H, I=I, E=E, k=k, coef=0.01, seed=31)
     d = to_dev(make_case(w), dev)
-    d2 = to_dev(make_case(custom_workload(name="graph_moe2", N=600, H=128, I=192, E=8, k=2,
+    d2 = to_dev(make_case(custom_workload(name="graph_moe2", N=N, H=H, I=I, E=E, k=k,
                                           coef=0.01, seed=32)), dev)
     N, H, E, k = w.N, w.H, w.E, w.k
     ws = torch.empty(tm.moe_workspace_bytes(N, H, w.I, E, k, torch.bfloat16), dtype=torch.uint8,
@@ -61,7 +68,7 @@ def test_graph_moe_forward(env):
                        topk_idx=idx, alpha=alpha, aux_loss=aux, expert_offsets=offs,
                        return_lists=False, workspace=ws, stream=stream)
 
-    announce("graph capture of moe_ffn_fwd N=600 E=8 k=2")
+    announce(f"graph capture of moe_ffn_fwd N={N} H={H} I={I} E={E} k={k}")
     call(d)
     torch.cuda.synchronize()
     want = {"y": y.clone(), "idx": idx.clone(), "alpha": alpha.clone(), "aux": aux.clone(),
