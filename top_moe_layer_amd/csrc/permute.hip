@@ -238,8 +238,9 @@ __device__ __forceinline__ void store16<bf16_t>(bf16_t* p, const float (&v)[8]) 
 // The residual may alias y: each thread reads its residual piece before
 // writing the same piece of y.  Without slots (k == 1 under a capacity, where
 // the down GEMM wrote the kept tokens' rows of y) only the tokens whose entry
-// was dropped are written: y = residual (or 0).
-template <typename T>
+// was dropped are written: y = residual (or 0).  K2: k == 2 with slots, both
+// slot pieces loaded at once (one memory latency after the ids, not two).
+template <typename T, bool K2>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slots,
                                                       const int32_t* __restrict__ topk_idx,
                                                       const uint8_t* __restrict__ keep,
@@ -259,6 +260,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ slot
   } else {
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  }
+  if constexpr (K2) {
+    const int first = ids[1] < ids[0] ? 1 : 0;  // the lower expert id is added first
+    const bool keep0 = keep == nullptr || keep[t * 2 + first] != 0;
+    const bool keep1 = keep == nullptr || keep[t * 2 + (1 - first)] != 0;
+    float v0[V], v1[V];
+    load16<T>(slots + (t * 2 + first) * H + h, v0);
+    load16<T>(slots + (t * 2 + (1 - first)) * H + h, v1);
+    if (keep0) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += v0[i];
+    }
+    if (keep1) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += v1[i];
+    }
+    store16<T>(y + t * H + h, acc);
+    return;
   }
   int prev = -1;
   for (int r = 0; r < k; ++r) {
@@ -351,13 +370,18 @@ hipError_t launch_combine(const void* slots, const int32_t* topk_idx, const uint
   const int64_t work = N * (H / (dtype == TOPMOE_DTYPE_FP32 ? 4 : 8));  // 16-byte pieces
   if (work <= 0) return hipSuccess;
   const int64_t grid = (work + 255) / 256;
-  if (dtype == TOPMOE_DTYPE_FP32)
-    return launch_kernel(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
-                         static_cast<const float*>(slots), topk_idx, keep,
-                         static_cast<const float*>(residual), N, H, k, static_cast<float*>(y));
-  return launch_kernel(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(slots), topk_idx, keep,
-                       static_cast<const bf16_t*>(residual), N, H, k, static_cast<bf16_t*>(y));
+  const bool k2 = slots != nullptr && k == 2;
+#define TOPMOE_COMBINE(T, K2)                                                                \
+  return launch_kernel(combine_kernel<T, K2>, dim3(grid), dim3(256), 0, s,                   \
+                       static_cast<const T*>(slots), topk_idx, keep,                         \
+                       static_cast<const T*>(residual), N, H, k, static_cast<T*>(y))
+  if (dtype == TOPMOE_DTYPE_FP32) {
+    if (k2) TOPMOE_COMBINE(float, true);
+    TOPMOE_COMBINE(float, false);
+  }
+  if (k2) TOPMOE_COMBINE(bf16_t, true);
+  TOPMOE_COMBINE(bf16_t, false);
+#undef TOPMOE_COMBINE
 }
 
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int Nout,
