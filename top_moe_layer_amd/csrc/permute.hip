@@ -312,15 +312,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   if (gid >= rows * nq) return;
   const int64_t r = gid / nq;
   const int c = int(gid - r * nq) * 4;
-  float sum[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int ch = 0; ch < ksplit; ++ch) {
-    float v[4];
-    load4<float>(partial + (int64_t(ch) * M + r) * Nout + c, v);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) sum[w] += v[w];
-  }
   const float a = alpha != nullptr ? alpha[r] : 1.f;
   const int64_t ent = entries != nullptr ? int64_t(entries[r]) : r;
+  // the first kMaxDownSplit chunks' pieces all in flight at once, then added
+  // in chunk order (a longer split, which the planner does not make, adds the
+  // rest one by one)
+  float v[kMaxDownSplit][4];
+#pragma unroll
+  for (int ch = 0; ch < kMaxDownSplit; ++ch)
+    if (ch < ksplit) load4<float>(partial + (int64_t(ch) * M + r) * Nout + c, v[ch]);
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ch = 0; ch < kMaxDownSplit; ++ch)
+    if (ch < ksplit) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sum[w] += v[ch][w];
+    }
+  for (int ch = kMaxDownSplit; ch < ksplit; ++ch) {
+    float u[4];
+    load4<float>(partial + (int64_t(ch) * M + r) * Nout + c, u);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sum[w] += u[w];
+  }
   float b[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) b[w] = sum[w] * a;

@@ -211,7 +211,7 @@ void choose_down_split(int64_t tiles, int64_t K, int elem, const GemmShape& sh, 
   if (tiles <= 0 || tiles >= 128 || kt < 8) return;
   int64_t want = (256 + tiles - 1) / tiles;
   if (want > kt / 4) want = kt / 4;
-  if (want > 6) want = 6;  // measured: more chunks of few slices each stream slower
+  if (want > kMaxDownSplit) want = kMaxDownSplit;  // measured: more chunks of few slices each stream slower
   if (want < 2) return;
   const int64_t cs = (kt + want - 1) / want;
   *kchunk = int(cs);

@@ -50,6 +50,9 @@ struct FfnPlan {
   size_t total = 0;        // workspace bytes
 };
 
+// Most K chunks of a split down projection.
+constexpr int kMaxDownSplit = 6;
+
 // Most entries (N * k) the in-block routing of a GEMM takes.
 constexpr int kInlineMaxEntries = 512;
 
