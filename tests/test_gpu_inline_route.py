@@ -80,3 +80,28 @@ def test_inline_routing(env, N, H, I, E, k, zc, res, path):
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int16), out.y.view(torch.int16))
     assert torch.equal(aux2, out.aux_loss)
+
+
+@pytest.mark.parametrize("N,H,I,E,k,norm,training", [
+    (32, 2048, 1408, 16, 2, False, True),   # router inside the gate/up launch, alpha = p_S
+    (32, 2048, 1408, 16, 2, True, False),   # the module outside training: aux = 0
+    (37, 192, 320, 64, 6, False, True),     # in-block grouping with the router launch
+])
+def test_inline_routing_flags(env, N, H, I, E, k, norm, training):
+    torch, dev, tm = env
+    w = custom_workload(name="inl_flags", N=N, H=H, I=I, E=E, k=k, coef=0.01, seed=N * 5 + E)
+    inp = make_case(w)
+    f = widen(inp)
+    ref = moe_ffn(f["x"], f["Wr"], f["Wg"], f["Wu"], f["Wd"], k, w.coef, norm_topk_prob=norm)
+    announce(f"moe_ffn_fwd in-block routing flags N={N} E={E} k={k} norm={norm} training={training}")
+    d = to_dev(inp, dev)
+    out = tm.moe_ffn_fwd(d["x"], d["Wr"], d["Wg"], d["Wu"], d["Wd"], k, w.coef,
+                         norm_topk_prob=norm, training=training)
+    torch.cuda.synchronize()
+    if training:
+        check_routing(out, ref, k, E, exact_order=k < E)
+    else:
+        assert float(out.aux_loss.cpu()[0]) == 0.0
+        assert np.array_equal(out.topk_idx.cpu().numpy(), ref["topk_idx"])
+    err = rel_l2_per_token(y_to_f64(out.y), ref["y"])
+    assert err <= TOL_Y["bf16"], err
