@@ -36,6 +36,8 @@ CASES = [  # N, H, I, E, k, z_coef, residual, (in-block routing, router in the g
     (64, 1024, 512, 16, 1, 0.001, True, (1, 1)),    # one full row tile of tokens
     (16, 2048, 1408, 16, 4, 0.0, False, (1, 1)),
     (200, 2048, 1408, 16, 2, 0.0, True, (1, 0)),    # more tokens than one row tile
+    (8, 256, 256, 1, 1, 0.001, True, (1, 1)),       # one expert
+    (8, 256, 256, 2, 2, 0.0, False, (1, 1)),        # k = E
 ]
 
 
