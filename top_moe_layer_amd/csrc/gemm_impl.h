@@ -29,6 +29,13 @@
 //             written to y[t] (k == 1 or dense; plus the residual stream when
 //             given, rounded once) or to the slot of entry (t, j) (k >= 2, in
 //             the operand dtype) for the fixed-order combine.
+//
+// Decode-sized inference calls (the 64 x 128 tiles of eight wavefronts) can
+// group the entries by expert in every block's prologue instead of reading
+// the permutation kernel's lists (GemmParams::inl_*), and with at most one
+// row tile of tokens and E <= 16 the gate/up launch takes every token against
+// every expert while its last blocks run the router (GemmParams::allx_n,
+// rt_*).
 #pragma once
 
 #include "device_common.h"
