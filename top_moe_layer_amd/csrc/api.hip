@@ -305,7 +305,8 @@ int moe_fwd_impl(const void* x, const float* Wr, const void* Wg, const void* Wu,
   // groups (under a capacity: of the kept entries).  Decode-sized calls
   // (few entries, the 64 x 128 weight-streaming tiles) skip this launch: each
   // block of the two GEMMs groups the entries itself (GemmParams::inl_topk)
-  // and one extra block of the gate/up launch writes these outputs.
+  // and one extra block of the gate/up launch (of the down launch when the
+  // router runs inside the gate/up launch) writes these outputs.
   const Launch l1 = st.at(1);
   if (!inline_route)
     TOPMOE_TRY(launch_permute(count_part, psum_part, z_part, topk_idx, alpha, pl.nblk, E, k,
